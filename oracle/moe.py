@@ -1,0 +1,290 @@
+"""Plain NumPy float64 reference of the top-k MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the product
+path imports this module.
+
+Every input is widened exactly to float64 (float32 and bfloat16 values are all
+exactly representable), and every step below is computed in float64 in the
+order the pages give it. The top-k decision is therefore taken on float64
+logits, the precision of the pages' own NumPy code.
+
+Steps, with the passage each follows:
+
+1. router logits ``x @ W_router`` (+ optional per-expert bias) --
+   ML Grind "Mixture-of-Experts (MoE) Routing", Algorithm step 1; the bias is
+   the ``bias`` argument of ``router()`` in "Mixture of Experts: the
+   Sparsely-Gated Layer", section "The code", stage (1) SCORE.
+2. ``probs = softmax(logits)`` per row, max-subtracted -- ML Grind, Algorithm
+   step 1; the max subtraction as in Bendersky's ``softmax_lastdim``.
+3. top-k experts by descending logit, ties to the lower expert index (a
+   stable sort of the negated logits) -- ML Grind, Algorithm step 2 and "Edge
+   cases and conventions".
+4. gates = softmax over the k chosen logits -- ML Grind, Algorithm step 2.
+   (Equal to renormalised probabilities: Sparsely-Gated Layer, "The one
+   formula", KeepTopK/softmax row.)
+5. Switch loss ``aux = E * sum_e f_e * P_e`` with ``f_e`` the share of the T*k
+   routing slots that chose e and ``P_e`` the mean router probability --
+   ML Grind, Algorithm, load-balancing step.
+6. capacity ``floor(capacity_factor * T * k / E)``; per expert, the routed
+   tokens in ascending token order, the first ``capacity`` kept and the rest
+   dropped ("first come, first served") -- ML Grind, Follow-up; Sparsely-Gated
+   Layer, "Switch: top-1, one loss, and a rate limit" and ``moe_forward`` in
+   "The code".
+7. each expert runs only on its kept tokens; outputs added back weighted by
+   their gate, dropped slots add nothing and gates are not renormalised after
+   a drop -- ML Grind, Algorithm step 3 and "Constraints"; Sparsely-Gated
+   Layer, ``moe_forward``.
+
+Experts: linear ``x @ W`` (ML Grind, Background), two-layer ReLU
+``relu(x @ Wh) @ Wo`` without biases (Sparsely-Gated Layer ``expert_forward``;
+Bendersky ``FFParams``), and SwiGLU ``(silu(x @ W1) * (x @ W3)) @ W2`` with
+``silu(z) = z / (1 + exp(-z))`` (ML Grind, Background names SwiGLU experts; the
+form is the textbook one).
+
+Pins (the ``-m "not gpu"`` tests): the three worked examples of ML Grind, the
+top_k = 1 convention, the token-0 gates printed on the Sparsely-Gated Layer
+page, its capacity/drop table, the k = E and uniform-router closed forms,
+identity-weight closed forms of each expert, permutation equivariance, and a
+second, per-token implementation (``moe_forward_per_token``) on tiny random
+inputs. There is no printed worked example of the absolute output values at
+the large configurations; those are covered by the structural pins only.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --- routing -----------------------------------------------------------------
+
+def router_logits(x, w_router, bias=None) -> np.ndarray:
+    """Step 1: ``x @ W_router`` (+ bias), float64, (T, E)."""
+    logits = _f64(x) @ _f64(w_router)
+    if bias is not None:
+        logits = logits + _f64(bias)[None, :]
+    return logits
+
+
+def softmax_rows(z: np.ndarray) -> np.ndarray:
+    """Step 2: row softmax with the row maximum subtracted first."""
+    z = _f64(z)
+    m = z.max(axis=-1, keepdims=True)
+    ez = np.exp(z - m)
+    return ez / ez.sum(axis=-1, keepdims=True)
+
+
+def top_k_sorted(logits: np.ndarray, k: int) -> np.ndarray:
+    """Step 3: the k largest logits per row, best first, ties -> lower index."""
+    order = np.argsort(-_f64(logits), axis=-1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def gates_from_logits(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Step 4: softmax over the k chosen logits, aligned with ``idx``."""
+    chosen = np.take_along_axis(_f64(logits), idx, axis=-1)
+    return softmax_rows(chosen)
+
+
+def switch_aux_loss(idx: np.ndarray, probs: np.ndarray, E: int) -> float:
+    """Step 5: ``E * sum_e f_e * P_e``; f counts routed slots before capacity."""
+    T, k = idx.shape
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.float64)
+    f = counts / (T * k)
+    P = _f64(probs).mean(axis=0)
+    return float(E * np.sum(f * P))
+
+
+# --- dispatch ----------------------------------------------------------------
+
+def capacity_slots(capacity_factor: float, T: int, k: int, E: int) -> Optional[int]:
+    """Step 6: ``floor(capacity_factor * T * k / E)``; None when there is no limit."""
+    if capacity_factor is None or capacity_factor <= 0:
+        return None
+    return int(math.floor(capacity_factor * T * k / E))
+
+
+def dispatch_from_indices(idx: np.ndarray, E: int, capacity: Optional[int]) -> dict:
+    """Step 6: per-expert counts, kept slots, expert-contiguous order.
+
+    Returns ``counts`` (E,) routed slots before capacity, ``kept`` (E,),
+    ``offsets`` (E+1,) exclusive prefix sum of ``kept``, ``perm`` (R,) the kept
+    slot ids ``t*k + j`` in (expert, token) order, ``slot_row`` (T*k,) the row
+    of each slot in that order or -1 when dropped, and ``dropped``.
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    kept = np.zeros(E, dtype=np.int64)
+    per_expert = []
+    for e in range(E):
+        hit = idx == e  # (T, k); at most one True per row
+        sent = np.flatnonzero(hit.any(axis=1))  # routed tokens, ascending
+        counts[e] = sent.size
+        if capacity is not None and sent.size > capacity:
+            sent = sent[:capacity]  # first come, first served
+        kept[e] = sent.size
+        j = np.argmax(hit[sent], axis=1)  # the rank j at which token t chose e
+        per_expert.append(sent * k + j)
+    offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
+    perm = np.concatenate(per_expert).astype(np.int64) if per_expert else np.zeros(0, np.int64)
+    slot_row = np.full(T * k, -1, dtype=np.int64)
+    slot_row[perm] = np.arange(perm.size)
+    return dict(counts=counts, kept=kept, offsets=offsets, perm=perm, slot_row=slot_row,
+                dropped=int(T * k - perm.size))
+
+
+# --- experts -----------------------------------------------------------------
+
+def silu(z):
+    """``z * sigmoid(z) = z / (1 + exp(-z))``."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_forward(kind: str, xr: np.ndarray, w1, w2=None, w3=None) -> np.ndarray:
+    """One expert on the rows ``xr``; the weights are that expert's matrices."""
+    xr = _f64(xr)
+    if kind == "linear":
+        return xr @ _f64(w1)
+    if kind == "relu2":
+        return np.maximum(xr @ _f64(w1), 0.0) @ _f64(w2)
+    if kind == "swiglu":
+        return (silu(xr @ _f64(w1)) * (xr @ _f64(w3))) @ _f64(w2)
+    raise ValueError(f"unknown expert kind {kind!r}")
+
+
+def _expert_weights(e, w1, w2, w3):
+    return w1[e], (None if w2 is None else w2[e]), (None if w3 is None else w3[e])
+
+
+# --- the layer ----------------------------------------------------------------
+
+def moe_forward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=None,
+                capacity_factor: float = 0.0, tokens: Optional[Sequence[int]] = None) -> dict:
+    """The layer forward, steps 1-7.
+
+    ``w1``/``w3`` are (E, D, DH) (``w1`` is (E, D, D_out) for a linear expert),
+    ``w2`` is (E, DH, D_out). Expert weights are widened to float64 one expert
+    at a time. ``tokens`` restricts the expert evaluation (step 7) to those
+    token rows; routing, dispatch and the loss always cover every token, since
+    which slots an expert keeps depends on all earlier tokens. Rows not in
+    ``tokens`` are left zero.
+    """
+    x = np.asarray(x)
+    T = x.shape[0]
+    E = np.asarray(w_router).shape[1]
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must satisfy 1 <= top_k <= E")
+    logits = router_logits(x, w_router, bias)
+    probs = softmax_rows(logits)
+    idx = top_k_sorted(logits, top_k)
+    gates = gates_from_logits(logits, idx)
+    aux = switch_aux_loss(idx, probs, E)
+    cap = capacity_slots(capacity_factor, T, top_k, E)
+    disp = dispatch_from_indices(idx, E, cap)
+
+    d_out = np.asarray(w1).shape[2] if kind == "linear" else np.asarray(w2).shape[2]
+    out = np.zeros((T, d_out), dtype=np.float64)
+    want = None
+    if tokens is not None:
+        want = np.zeros(T, dtype=bool)
+        want[np.asarray(tokens, dtype=np.int64)] = True
+    flat_gates = gates.reshape(-1)
+    for e in range(E):
+        rows = disp["perm"][disp["offsets"][e]:disp["offsets"][e + 1]]  # slot ids
+        if want is not None:
+            rows = rows[want[rows // top_k]]
+        if rows.size == 0:
+            continue  # idle expert: no work
+        t = rows // top_k
+        y = expert_forward(kind, x[t], *_expert_weights(e, w1, w2, w3))
+        # one slot per (token, expert), so no two rows of t repeat here
+        out[t] += flat_gates[rows][:, None] * y
+    return dict(output=out, expert_indices=idx, gates=gates, aux_loss=aux, logits=logits,
+                probs=probs, capacity=cap, **disp)
+
+
+def _expert_one_token(kind: str, xt: np.ndarray, w1, w2=None, w3=None) -> np.ndarray:
+    """One expert on one token, column by column (vector dot products only)."""
+    def vecmat(v, W):
+        W = _f64(W)
+        return np.array([float(np.dot(v, W[:, c])) for c in range(W.shape[1])])
+
+    if kind == "linear":
+        return vecmat(xt, w1)
+    if kind == "relu2":
+        h = np.array([max(v, 0.0) for v in vecmat(xt, w1)])
+        return vecmat(h, w2)
+    if kind == "swiglu":
+        a = vecmat(xt, w1)
+        g = vecmat(xt, w3)
+        h = np.array([(ai / (1.0 + math.exp(-ai)) if ai > -700 else 0.0) * gi
+                      for ai, gi in zip(a, g)])
+        return vecmat(h, w2)
+    raise ValueError(f"unknown expert kind {kind!r}")
+
+
+def moe_forward_per_token(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=None,
+                          capacity_factor: float = 0.0) -> dict:
+    """A second, independent implementation: token by token, plain Python.
+
+    The shape of Bendersky's ``moe`` loop ("A Minimal Numpy Implementation")
+    and of ML Grind's ``y_t = sum_j gates[t, j] * expert(x_t)``. The top-k uses
+    Python's ``sorted`` with an explicit (-logit, index) key, the softmaxes use
+    ``math.exp``, and a slot is kept when fewer than ``capacity`` earlier
+    tokens chose the same expert. For tiny inputs only.
+    """
+    x = _f64(x)
+    W = _f64(w_router)
+    T, _ = x.shape
+    E = W.shape[1]
+    b = np.zeros(E) if bias is None else _f64(bias)
+    rows_idx, rows_gate, rows_prob = [], [], []
+    for t in range(T):
+        logit = [float(np.dot(x[t], W[:, e])) + float(b[e]) for e in range(E)]
+        order = sorted(range(E), key=lambda e: (-logit[e], e))[:top_k]
+        m = max(logit)
+        ez = [math.exp(v - m) for v in logit]
+        s = sum(ez)
+        rows_prob.append([v / s for v in ez])
+        mk = max(logit[e] for e in order)
+        gz = [math.exp(logit[e] - mk) for e in order]
+        gs = sum(gz)
+        rows_idx.append(order)
+        rows_gate.append([v / gs for v in gz])
+    counts = [0] * E
+    for order in rows_idx:
+        for e in order:
+            counts[e] += 1
+    P = [sum(rows_prob[t][e] for t in range(T)) / T for e in range(E)]
+    aux = E * sum((counts[e] / (T * top_k)) * P[e] for e in range(E))
+
+    cap = None
+    if capacity_factor and capacity_factor > 0:
+        cap = int(math.floor(capacity_factor * T * top_k / E))
+    seen = [0] * E
+    kept = [[False] * top_k for _ in range(T)]
+    for t in range(T):
+        for j, e in enumerate(rows_idx[t]):
+            kept[t][j] = cap is None or seen[e] < cap
+            seen[e] += 1
+
+    d_out = np.asarray(w1).shape[2] if kind == "linear" else np.asarray(w2).shape[2]
+    out = np.zeros((T, d_out))
+    for t in range(T):
+        for j, e in enumerate(rows_idx[t]):
+            if kept[t][j]:
+                y = _expert_one_token(kind, x[t], *_expert_weights(e, w1, w2, w3))
+                out[t] += rows_gate[t][j] * y
+    return dict(output=out, expert_indices=np.array(rows_idx, dtype=np.int64),
+                gates=np.array(rows_gate), aux_loss=float(aux),
+                counts=np.array(counts, dtype=np.int64),
+                kept_mask=np.array(kept, dtype=bool))
