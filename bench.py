@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Throughput of the MoE layer forward on one MI355X.
+
+A step is one moe_forward (route -> dispatch -> expert up GEMM -> expert down GEMM ->
+combine, plus the Switch loss) over one batch of seeded synthetic input that is already
+resident in HBM. Default workload: the Mixtral-shaped SwiGLU layer (T=4096 tokens, D=4096,
+DH=14336, E=8 experts, top-2, bf16 storage with fp32 accumulation, no capacity limit).
+
+Prints ONE JSON line on stdout. Besides the required fields it carries:
+  roofline      the dominant kernel (the expert up-projection GEMM) against bf16 MFMA peak,
+                timed with HIP events recorded around it inside every timed step;
+  stages        per-stage device time and its roofline figure;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def device_tensor(a):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(I, tokens: int) -> dict:
+    """The oracle as it stands, on the first `tokens` tokens of the same inputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    sp = I.spec
+    sub = slice(0, tokens)
+    t0 = time.perf_counter()
+    oracle.moe_forward(I.values("x")[sub], I.values("w_router"), sp.top_k, sp.kind,
+                       I.values("w1"), I.values("w2"), I.values("w3"), bias=I.bias,
+                       capacity_factor=sp.capacity_factor)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.moe_forward (NumPy float64) on the first {tokens} tokens of the "
+                      f"same seeded inputs, all {sp.E} experts' weights widened to float64; "
+                      f"{dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_swiglu_bf16")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-baseline-tokens", type=int, default=192)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X: the layer runs on a single GPU (no sharding, no "
+              "collectives), so --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from expert_ffn_layer_router_amd import accounting as A
+    from expert_ffn_layer_router_amd import binding as B
+    from synth import make_inputs, spec
+
+    sp = spec(args.config)
+    log(f"[bench] generating {sp.name} inputs (seed {args.seed})")
+    I = make_inputs(sp, seed=args.seed)
+    p = B.Problem.from_spec(sp)
+    dev = {n: device_tensor(getattr(I, n)) for n in ("x", "w_router", "bias", "w1", "w3", "w2")}
+    outs = B.alloc_outputs(p)
+    ws = B.alloc_workspace(p)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        B.moe_forward_timed(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"],
+                            dev["w2"], outs["out"], outs["expert_indices"], outs["gates"],
+                            outs["aux_loss"], outs["expert_counts"], outs["expert_offsets"],
+                            outs["slot_row"], ws, None if ev is None else ev.events)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [B.StageEvents() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stage_ms = {k: float(np.mean([e.elapsed_ms()[k] for e in events])) for k in B.STAGES}
+    for e in events:
+        e.close()
+
+    offsets = outs["expert_offsets"].cpu().numpy()
+    R = int(offsets[-1])
+    T, D, DH, Do, E, k = sp.T, sp.D, sp.DH, sp.D_out, sp.E, sp.top_k
+    es = 2 if sp.dtype == "bf16" else 4
+    peak_tf = BF16_PEAK_TFLOPS if sp.dtype == "bf16" else FP32_PEAK_TFLOPS
+    used_tokens = int(np.count_nonzero((outs["slot_row"].view(T, k) >= 0).any(dim=1).cpu()))
+
+    # algorithmic work per launch
+    if sp.kind == "linear":
+        up_flops, down_flops = 2 * D * Do * R, 0
+        up_w = E * D * Do * es
+    else:
+        up_mult = 4 if sp.kind == "swiglu" else 2
+        up_flops, down_flops = up_mult * D * DH * R, 2 * DH * Do * R
+        up_w = (2 if sp.kind == "swiglu" else 1) * E * D * DH * es
+    route_b = A.route_bytes(T, D, E, k, es)
+    combine_b = A.combine_bytes(T, k, R, Do, es)
+
+    def tf(fl, ms_):
+        return fl / (ms_ * 1e-3) / 1e12 if ms_ > 0 else 0.0
+
+    def gbs(b, ms_):
+        return b / (ms_ * 1e-3) / 1e9 if ms_ > 0 else 0.0
+
+    up_tf = tf(up_flops, stage_ms["expert_up"])
+    stages = {
+        "route": {"us": stage_ms["route"] * 1e3, "GB/s": gbs(route_b, stage_ms["route"]),
+                  "hbm_frac": gbs(route_b, stage_ms["route"]) / HBM_PEAK_GBS,
+                  "algorithmic_bytes": route_b},
+        "dispatch": {"us": stage_ms["dispatch"] * 1e3},
+        "expert_up": {"us": stage_ms["expert_up"] * 1e3, "TFLOP/s": up_tf,
+                      "mfma_frac": up_tf / peak_tf, "algorithmic_flops": up_flops},
+        "expert_down": {"us": stage_ms["expert_down"] * 1e3,
+                        "TFLOP/s": tf(down_flops, stage_ms["expert_down"]),
+                        "mfma_frac": tf(down_flops, stage_ms["expert_down"]) / peak_tf,
+                        "algorithmic_flops": down_flops},
+        "combine": {"us": stage_ms["combine"] * 1e3, "GB/s": gbs(combine_b, stage_ms["combine"]),
+                    "hbm_frac": gbs(combine_b, stage_ms["combine"]) / HBM_PEAK_GBS,
+                    "algorithmic_bytes": combine_b},
+    }
+    result = {
+        "metric": "MoE layer forward tokens/s at 1 MI355X",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sp.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0, sigma) inputs and random-init weights)",
+        "config": {"workload": sp.description, "T": T, "D": D, "DH": DH, "E": E, "top_k": k,
+                   "expert": sp.kind, "capacity_factor": sp.capacity_factor,
+                   "kept_slots": R, "dropped_slots": T * k - R, "used_tokens": used_tokens},
+        "roofline": {"kernel": "expert up-projection grouped GEMM (stage expert_up)",
+                     "bound": "mfma", "achieved": up_tf, "peak": peak_tf, "unit": "TFLOP/s",
+                     "frac": up_tf / peak_tf, "traffic": None,
+                     "algorithmic_flops_per_launch": up_flops,
+                     "launch_us": stage_ms["expert_up"] * 1e3,
+                     "weight_bytes": up_w},
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_baseline_tokens, T)
+        log(f"[bench] CPU oracle baseline on {n} tokens")
+        result["cpu_baseline"] = cpu_baseline(I, n)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,298 @@
+// The C ABI (include/moe.h): host-side checks, workspace layout, and the launch sequence of
+// each entry point. Nothing here allocates memory or synchronises with the device.
+#include <math.h>
+
+#include "common.hpp"
+
+using namespace moe;
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->kind != MOE_EXPERT_LINEAR && p->kind != MOE_EXPERT_RELU2 && p->kind != MOE_EXPERT_SWIGLU)
+    return MOE_ERR_UNSUPPORTED;
+  if (p->T < 0 || p->D < 1 || p->D_out < 1 || p->E < 1) return MOE_ERR_INVALID_ARG;
+  if (p->kind != MOE_EXPERT_LINEAR && p->DH < 1) return MOE_ERR_INVALID_ARG;
+  if (p->top_k < 1 || p->top_k > p->E) return MOE_ERR_INVALID_ARG;
+  if (!(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;  // NaN
+  if (p->E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  // slot and row ids are int32; element offsets are int64
+  if (p->T * (int64_t)p->top_k > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (p->D > (int64_t)INT32_MAX || p->D_out > (int64_t)INT32_MAX || p->DH > (int64_t)INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
+  if (p->dtype == MOE_BF16) {
+    if (p->D % 8 || p->D_out % 8) return MOE_ERR_UNSUPPORTED;
+    if (p->kind != MOE_EXPERT_LINEAR && p->DH % 8) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+int64_t capacity_of(const moe_problem* p) {
+  if (!(p->capacity_factor > 0.0)) return -1;
+  const double c = floor(p->capacity_factor * (double)p->T * (double)p->top_k / (double)p->E);
+  if (c >= (double)INT32_MAX) return (int64_t)INT32_MAX;
+  return (int64_t)c;
+}
+
+Problem internal(const moe_problem* p) {
+  Problem q;
+  q.T = p->T;
+  q.D = p->D;
+  q.DH = p->kind == MOE_EXPERT_LINEAR ? 0 : p->DH;
+  q.D_out = p->D_out;
+  q.E = p->E;
+  q.top_k = p->top_k;
+  q.capacity = capacity_of(p);
+  q.dtype = p->dtype;
+  q.kind = p->kind;
+  return q;
+}
+
+// Byte offsets of every scratch region inside the caller's workspace.
+struct Layout {
+  size_t psum, pcnt;    // routing partials: (route blocks, E) float64 and int32
+  size_t blkc, lrank;   // dispatch: (dispatch blocks, E) int32 and (T*k) int32
+  size_t perm;          // moe_forward's own permutation, (T*k) int32
+  size_t hbuf;          // expert hidden activations, (T*k, DH)
+  size_t ybuf;          // moe_forward's expert outputs, (T*k, D_out)
+  size_t route_end, dispatch_end, ffn_end, total;
+};
+
+Layout layout_of(const Problem& q) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t es = elem_size(q.dtype);
+  const size_t slots = (size_t)q.slots();
+  L.psum = take((size_t)route_blocks(q) * q.E * sizeof(double));
+  L.pcnt = take((size_t)route_blocks(q) * q.E * sizeof(int32_t));
+  L.route_end = off;
+  L.blkc = take((size_t)dispatch_blocks(q) * q.E * sizeof(int32_t));
+  L.lrank = take(slots * sizeof(int32_t));
+  L.dispatch_end = off;
+  L.hbuf = take(q.kind == MOE_EXPERT_LINEAR ? 0 : slots * (size_t)q.DH * es);
+  L.ffn_end = off;
+  L.perm = take(slots * sizeof(int32_t));
+  L.ybuf = take(slots * (size_t)q.D_out * es);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+void mark(hipEvent_t* ev, int i, hipStream_t s) {
+  if (ev) hipEventRecord(ev[i], s);
+}
+
+// The expert FFN over expert-ordered rows; `gather` (nullable) maps rows to token rows of A.
+// `ev` (nullable) receives the stage markers of the up and down GEMMs.
+hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, const int32_t* offsets,
+                       const void* w1, const void* w3, const void* w2, void* hbuf, void* y,
+                       hipStream_t s, hipEvent_t* ev) {
+  GroupedGemm g{};
+  g.A = A;
+  g.lda = q.D;
+  g.a_gather = gather;
+  g.gather_div = q.top_k;
+  g.offsets = offsets;
+  g.E = q.E;
+  g.max_rows = q.slots();
+  g.dtype = q.dtype;
+  g.K = q.D;
+  g.B0 = w1;
+  const bool linear = q.kind == MOE_EXPERT_LINEAR;
+  g.B1 = (q.kind == MOE_EXPERT_SWIGLU) ? w3 : nullptr;
+  g.C = linear ? y : hbuf;
+  g.N = linear ? q.D_out : q.DH;
+  g.epilogue = linear ? EPI_NONE : (q.kind == MOE_EXPERT_SWIGLU ? EPI_SWIGLU : EPI_RELU);
+  mark(ev, 2 * MOE_STAGE_EXPERT_UP, s);
+  hipError_t err = launch_grouped_gemm(g, s);
+  mark(ev, 2 * MOE_STAGE_EXPERT_UP + 1, s);
+  mark(ev, 2 * MOE_STAGE_EXPERT_DOWN, s);
+  if (err == hipSuccess && !linear) {
+    GroupedGemm d{};
+    d.A = hbuf;
+    d.lda = q.DH;
+    d.a_gather = nullptr;
+    d.gather_div = 1;
+    d.B0 = w2;
+    d.B1 = nullptr;
+    d.C = y;
+    d.offsets = offsets;
+    d.E = q.E;
+    d.K = q.DH;
+    d.N = q.D_out;
+    d.max_rows = q.slots();
+    d.epilogue = EPI_NONE;
+    d.dtype = q.dtype;
+    err = launch_grouped_gemm(d, s);
+  }
+  mark(ev, 2 * MOE_STAGE_EXPERT_DOWN + 1, s);
+  return err;
+}
+
+bool weights_ok(const moe_problem* p, const void* w1, const void* w3, const void* w2) {
+  if (!w1) return false;
+  if (p->kind == MOE_EXPERT_SWIGLU && !w3) return false;
+  if (p->kind != MOE_EXPERT_LINEAR && !w2) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: a null required pointer or a size out of range";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: a shape, dtype or expert kind this library does not handle";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_check_problem(const moe_problem* p) { return check_problem(p); }
+
+int64_t moe_capacity(const moe_problem* p) {
+  if (check_problem(p) != MOE_OK) return -2;
+  return capacity_of(p);
+}
+
+size_t moe_workspace_size(const moe_problem* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return layout_of(internal(p)).total;
+}
+
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* expert_indices, float* gates,
+                     float* aux_loss, int32_t* expert_counts, float* logits_out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aux_loss) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !w_router || !expert_indices || !gates)) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q);
+  st = check_ws(ws, ws_bytes, L.route_end);
+  if (st != MOE_OK) return st;
+  hipError_t err = launch_route(q, x, w_router, router_bias, expert_indices, gates, logits_out,
+                                at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), stream);
+  if (err == hipSuccess)
+    err = launch_aux_finalize(q, at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), aux_loss,
+                              expert_counts, stream);
+  return hip_status(err);
+}
+
+moe_status moe_dispatch(const moe_problem* p, const int32_t* expert_indices, const void* x,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                        int32_t* slot_row, void* x_perm, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!expert_indices || !perm || !slot_row)) return MOE_ERR_INVALID_ARG;
+  if (x_perm && !x && p->T > 0) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q);
+  st = check_ws(ws, ws_bytes, L.dispatch_end);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm,
+                                    slot_row, x_perm, at<int32_t>(ws, L.blkc),
+                                    at<int32_t>(ws, L.lrank), stream));
+}
+
+moe_status moe_expert_ffn(const moe_problem* p, const void* x_perm, const int32_t* expert_offsets,
+                          const void* w1, const void* w3, const void* w2, void* y_perm, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !weights_ok(p, w1, w3, w2)) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x_perm || !y_perm)) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q);
+  st = check_ws(ws, ws_bytes, L.ffn_end);
+  if (st != MOE_OK) return st;
+  if (q.T == 0) return MOE_OK;
+  return hip_status(run_experts(q, x_perm, nullptr, expert_offsets, w1, w3, w2,
+                                at<void>(ws, L.hbuf), y_perm, stream, nullptr));
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot_row,
+                       const float* gates, void* out, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!y_perm || !slot_row || !gates || !out)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(internal(p), y_perm, slot_row, gates, out, stream));
+}
+
+moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, const void* w1, const void* w3,
+                             const void* w2, void* out, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* slot_row, void* ws, size_t ws_bytes, hipStream_t stream,
+                             hipEvent_t* ev) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aux_loss || !expert_counts || !expert_offsets || !weights_ok(p, w1, w3, w2))
+    return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !w_router || !out || !expert_indices || !gates || !slot_row))
+    return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  mark(ev, 2 * MOE_STAGE_ROUTE, stream);
+  hipError_t err = launch_route(q, x, w_router, router_bias, expert_indices, gates, nullptr,
+                                at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), stream);
+  if (err == hipSuccess)
+    err = launch_aux_finalize(q, at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), aux_loss,
+                              nullptr, stream);
+  mark(ev, 2 * MOE_STAGE_ROUTE + 1, stream);
+  mark(ev, 2 * MOE_STAGE_DISPATCH, stream);
+  if (err == hipSuccess)
+    err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
+                          nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream);
+  mark(ev, 2 * MOE_STAGE_DISPATCH + 1, stream);
+  if (err == hipSuccess)
+    err = run_experts(q, x, perm, expert_offsets, w1, w3, w2, at<void>(ws, L.hbuf),
+                      at<void>(ws, L.ybuf), stream, ev);
+  mark(ev, 2 * MOE_STAGE_COMBINE, stream);
+  if (err == hipSuccess) err = launch_combine(q, at<void>(ws, L.ybuf), slot_row, gates, out, stream);
+  mark(ev, 2 * MOE_STAGE_COMBINE + 1, stream);
+  return hip_status(err);
+}
+
+moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router,
+                       const float* router_bias, const void* w1, const void* w3, const void* w2,
+                       void* out, int32_t* expert_indices, float* gates, float* aux_loss,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_forward_timed(p, x, w_router, router_bias, w1, w3, w2, out, expert_indices, gates,
+                           aux_loss, expert_counts, expert_offsets, slot_row, ws, ws_bytes,
+                           stream, nullptr);
+}
+
+}  // extern "C"

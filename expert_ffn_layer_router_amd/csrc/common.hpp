@@ -1,0 +1,103 @@
+// Shared device helpers and the internal launcher interface of the MoE library.
+// Written for gfx950 (CDNA4): 64-lane wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 256;
+
+// Tokens per block of the routing kernel; the per-block partial sums of the
+// router probabilities and the per-block expert counts are indexed by it.
+constexpr int kRouteTokensPerBlock = 32;
+// Tokens per block of the dispatch count/rank kernel (4 waves, one token per lane).
+constexpr int kDispatchTokensPerBlock = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// float -> bfloat16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ double load_as_f64(const float* p, int64_t i) { return (double)p[i]; }
+__device__ __forceinline__ double load_as_f64(const uint16_t* p, int64_t i) {
+  return (double)bf16_to_f32(p[i]);
+}
+__device__ __forceinline__ float load_as_f32(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float load_as_f32(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+__device__ __forceinline__ void store_from_f32(float* p, int64_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void store_from_f32(uint16_t* p, int64_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------------------------------
+// Internal launchers (one translation unit each). All return hipGetLastError().
+
+struct Problem {
+  int64_t T, D, DH, D_out;
+  int E, top_k;
+  int64_t capacity;  // -1: no limit
+  int dtype, kind;
+  int64_t slots() const { return T * (int64_t)top_k; }
+};
+
+// Routing: logits, softmax, top-k, gates, per-block probability sums and counts.
+hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
+                        int32_t* idx, float* gates, float* logits_out, double* psum_blk,
+                        int32_t* count_blk, hipStream_t s);
+int64_t route_blocks(const Problem& p);
+// Sum of the per-block partials -> aux loss (and the per-expert counts, if asked).
+hipError_t launch_aux_finalize(const Problem& p, const double* psum_blk, const int32_t* count_blk,
+                               float* aux, int32_t* counts_out, hipStream_t s);
+
+// Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
+int64_t dispatch_blocks(const Problem& p);
+hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_row,
+                           void* x_perm, int32_t* blk_counts, int32_t* local_rank,
+                           hipStream_t s);
+
+// Grouped expert GEMM over expert-ordered rows.
+enum Epilogue { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
+struct GroupedGemm {
+  const void* A;            // rows of length K (row-major), element type = dtype
+  int64_t lda;
+  const int32_t* a_gather;  // optional: row r of A is A[a_gather[r] / gather_div]
+  int gather_div;
+  const void* B0;           // (E, K, N) row-major
+  const void* B1;           // second (E, K, N) for SwiGLU, else null
+  void* C;                  // (rows, N) row-major, ldc = N
+  const int32_t* offsets;   // (E+1) expert row offsets, device
+  int E;
+  int64_t K, N;
+  int64_t max_rows;         // upper bound of offsets[E] (grid sizing)
+  int epilogue;
+  int dtype;
+};
+hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
+
+// Combine: out[t] = sum_j gates[t,j] * y[slot_row[t*k+j]].
+hipError_t launch_combine(const Problem& p, const void* y, const int32_t* slot_row,
+                          const float* gates, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) top-k Mixture-of-Experts layer forward.
+ *
+ * The layer, as the source pages define it:
+ *   logits = x @ W_router (+ bias)                      (T, E)
+ *   probs  = softmax(logits) per row
+ *   expert_indices[t] = the top_k experts by descending logit (ties: lower index)
+ *   gates[t]          = softmax of those top_k logits
+ *   aux_loss = E * sum_e f_e * P_e,  f_e = count_e / (T * top_k),  P_e = mean_t probs[t, e]
+ *   capacity = floor(capacity_factor * T * top_k / E) slots per expert (when > 0); an
+ *              expert keeps its routed tokens in ascending token order up to capacity and
+ *              drops the rest
+ *   output[t] = sum over kept slots j of gates[t, j] * expert_{expert_indices[t, j]}(x[t])
+ * Sources: ML Grind "Mixture-of-Experts (MoE) Routing" (Algorithm; Inputs; Expected Return
+ * Format; Edge cases and conventions; Follow-up) and "Mixture of Experts: the Sparsely-Gated
+ * Layer" (The one formula; Switch: top-1, one loss, and a rate limit; The code).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer argument is a DEVICE pointer unless marked "host". The library never
+ *   allocates or frees memory and keeps no state between calls; the caller owns every
+ *   buffer. Scratch memory comes from the caller's workspace `ws` of `ws_bytes` bytes
+ *   (256-byte aligned), sized by moe_workspace_size().
+ * - Matrices are row-major. Weights follow the pages' "x @ W" convention, (in, out):
+ *   W_router (D, E); w1, w3 (E, D, DH); w2 (E, DH, D_out); a linear expert is w1 (E, D, D_out).
+ * - `dtype` is the storage type of x, the router and expert weights, x_perm, y_perm and out.
+ *   MOE_F32: float32 storage, float32 expert arithmetic. MOE_BF16: bfloat16 storage, float32
+ *   accumulation, the expert hidden activation rounded to bfloat16 (round to nearest even).
+ *   Routing decisions (top-k), gates and the loss are computed from logits that equal the
+ *   exact logits to within a certified bound; a token whose decision that bound cannot
+ *   certify is recomputed in float64. Gates and aux_loss are float32, indices int32.
+ * - A "slot" is a (token t, rank j) pair with id s = t * top_k + j. Buffers indexed by rows
+ *   of expert-ordered data are sized for the worst case, T * top_k rows; the number of kept
+ *   rows R = expert_offsets[E] stays on the device (the host never synchronises).
+ * - Arguments are checked on the host before anything is launched. On any error nothing is
+ *   written and nothing is launched. After the launches, a launch failure is reported as
+ *   MOE_ERR_HIP; faults during execution surface at the caller's next stream
+ *   synchronisation. NaN or Inf inputs give unspecified (but memory-safe) results.
+ * - All work is enqueued on `stream` (0 = the null stream), in stream order; calls are
+ *   reentrant. Outputs must not alias inputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a null required pointer, a size out of range, top_k not in [1, E] */
+  MOE_ERR_UNSUPPORTED = 2, /* E > 256, an unknown dtype/kind, widths not multiples of 8 in bf16 */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_size(), or ws misaligned */
+  MOE_ERR_HIP = 4          /* a HIP launch error */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* The expert FFN (names as on the pages: D, DH, NEXP, TOPK).
+ * LINEAR: x @ W (ML Grind, Background).
+ * RELU2:  relu(x @ Wh) @ Wo, no biases (Sparsely-Gated Layer, expert_forward).
+ * SWIGLU: (silu(x @ W1) * (x @ W3)) @ W2, silu(z) = z / (1 + exp(-z)). */
+typedef enum moe_expert_kind {
+  MOE_EXPERT_LINEAR = 0,
+  MOE_EXPERT_RELU2 = 1,
+  MOE_EXPERT_SWIGLU = 2
+} moe_expert_kind;
+
+/* The problem statement (host struct). */
+typedef struct moe_problem {
+  int64_t T;              /* tokens, >= 0 (T = 0 is a valid empty call) */
+  int64_t D;              /* model width d, >= 1 */
+  int64_t DH;             /* expert hidden width, >= 1 (ignored for LINEAR) */
+  int64_t D_out;          /* expert output width, >= 1 */
+  int32_t E;              /* experts, 1..256 */
+  int32_t top_k;          /* experts per token, 1..E */
+  double capacity_factor; /* <= 0: no capacity limit */
+  int32_t dtype;          /* moe_dtype */
+  int32_t kind;           /* moe_expert_kind */
+} moe_problem;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* moe_status_string(moe_status s);
+
+/* Checks a problem statement (host only). Returns MOE_OK, MOE_ERR_INVALID_ARG or
+ * MOE_ERR_UNSUPPORTED. */
+moe_status moe_check_problem(const moe_problem* p);
+
+/* Slots per expert: floor(capacity_factor * T * top_k / E) computed in double, or -1 when
+ * capacity_factor <= 0 (no limit). Host only; -2 for an invalid problem.
+ * (Sparsely-Gated Layer, "Switch: top-1, one loss, and a rate limit".) */
+int64_t moe_capacity(const moe_problem* p);
+
+/* Bytes of workspace that moe_forward needs; every other entry point needs at most this
+ * much. Host only; 0 for an invalid problem. */
+size_t moe_workspace_size(const moe_problem* p);
+
+/* Router, softmax, top-k, gates and the Switch loss (ML Grind, Algorithm steps 1, 2 and the
+ * load-balancing step).
+ *   x (T, D), w_router (D, E) in p->dtype; router_bias (E) float32 or NULL.
+ *   Outputs: expert_indices (T, top_k) int32, best first; gates (T, top_k) float32, each row
+ *   summing to 1; aux_loss (1) float32; expert_counts (E) int32 routed slots per expert before
+ *   capacity, or NULL; logits_out (T, E) float32 copy of the router logits, or NULL. */
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* expert_indices, float* gates,
+                     float* aux_loss, int32_t* expert_counts, float* logits_out, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Dispatch (ML Grind, Algorithm step 3 "gather the tokens routed to it"; capacity as in
+ * the Sparsely-Gated Layer page's moe_forward, first come, first served).
+ *   expert_indices (T, top_k) int32 in [0, E) with distinct entries per row (unchecked);
+ *   x (T, D) in p->dtype, or NULL when x_perm is NULL.
+ *   Outputs: expert_counts (E) int32 before capacity; expert_offsets (E+1) int32, the
+ *   exclusive prefix sum of kept_e = min(count_e, capacity); perm (T*top_k) int32, perm[r] =
+ *   the slot placed at expert-ordered row r for r < R (rows of one expert in ascending token
+ *   order; entries from R on are left untouched); slot_row (T*top_k) int32, the row of slot s
+ *   or -1 when s was dropped; x_perm (T*top_k, D) in p->dtype, x_perm[r] = x[perm[r] / top_k]
+ *   for r < R, or NULL to skip the copy. */
+moe_status moe_dispatch(const moe_problem* p, const int32_t* expert_indices, const void* x,
+                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* perm,
+                        int32_t* slot_row, void* x_perm, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* The experts, each on its own rows only (ML Grind, Algorithm step 3 and Constraints):
+ * y_perm[r] = expert_e(x_perm[r]) for expert_offsets[e] <= r < expert_offsets[e+1].
+ *   x_perm (T*top_k, D); w1 (E, D, DH) or (E, D, D_out) for LINEAR; w3 (E, D, DH) for SWIGLU,
+ *   else NULL; w2 (E, DH, D_out), NULL for LINEAR; y_perm (T*top_k, D_out); all in p->dtype.
+ *   Rows from R on are neither read nor written. */
+moe_status moe_expert_ffn(const moe_problem* p, const void* x_perm, const int32_t* expert_offsets,
+                          const void* w1, const void* w3, const void* w2, void* y_perm, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Gate-weighted combine back in token order (ML Grind, Algorithm step 3 formula):
+ * out[t] = sum_{j < top_k, slot_row[t*top_k+j] >= 0} gates[t, j] * y_perm[slot_row[...]],
+ * accumulated in float32 in ascending j and rounded once to p->dtype. A dropped slot adds
+ * nothing and gates are not renormalised; a token with every slot dropped gets zeros.
+ *   y_perm (T*top_k, D_out); slot_row (T*top_k) int32; gates (T, top_k) float32;
+ *   out (T, D_out). No workspace. */
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot_row,
+                       const float* gates, void* out, hipStream_t stream);
+
+/* The whole layer: route, dispatch, experts, combine, loss, on one stream, with no host
+ * synchronisation. Arguments as in the stage functions above; expert_counts,
+ * expert_offsets and slot_row are outputs (required). */
+moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router,
+                       const float* router_bias, const void* w1, const void* w3, const void* w2,
+                       void* out, int32_t* expert_indices, float* gates, float* aux_loss,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stages of moe_forward, in launch order, for moe_forward_timed. */
+enum {
+  MOE_STAGE_ROUTE = 0,       /* router GEMM, softmax, top-k, gates; loss partials and loss */
+  MOE_STAGE_DISPATCH = 1,    /* histogram + ranks, scan + capacity, placement */
+  MOE_STAGE_EXPERT_UP = 2,   /* first expert GEMM (+ activation); the whole expert if LINEAR */
+  MOE_STAGE_EXPERT_DOWN = 3, /* second expert GEMM (empty for LINEAR) */
+  MOE_STAGE_COMBINE = 4,     /* gate-weighted combine */
+  MOE_NUM_STAGES = 5
+};
+
+/* moe_forward with per-stage timing: `stage_events` holds 2 * MOE_NUM_STAGES events that the
+ * caller created (hipEventCreate); event 2s is recorded on `stream` right before stage s and
+ * event 2s+1 right after it, so hipEventElapsedTime(events[2s], events[2s+1]) is the device
+ * time of stage s once the stream has reached it. NULL stage_events behaves as moe_forward.
+ * (Per-stage device timing of the layer; the work is identical to moe_forward.) */
+moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, const void* w1, const void* w3,
+                             const void* w2, void* out, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* slot_row, void* ws, size_t ws_bytes, hipStream_t stream,
+                             hipEvent_t* stage_events);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MOE_H */

@@ -2,15 +2,18 @@
 
 Recipe (the same on every machine):
 
-* generator: ``numpy.random.default_rng(seed)`` (PCG64), seed 0 unless stated;
+* generators: PCG64 streams ``default_rng(SeedSequence([seed, tensor, expert]))``,
+  one per tensor and, for expert weights, one per expert (so experts can be drawn
+  in parallel); seed 0 unless stated; tensor ids: x 0, router weights 1, router
+  bias 2, first expert matrix 3, third (SwiGLU) matrix 4, last matrix 5; expert
+  is 0 for the non-expert tensors;
 * every tensor is drawn with ``standard_normal(n, dtype=float32)`` and scaled by
   its standard deviation in float32; for bfloat16 layers the values are then
   rounded to bfloat16 (round to nearest, ties to even) and the rounded values are
   what both the GPU and the oracle receive;
-* draw order: x (T, D); router weights (D, E); the router bias (E) when it is
-  drawn; then the expert weights expert by expert: first matrix (E, D, DH) (or
-  (E, D, D_out) for a linear expert), third matrix (E, D, DH) for SwiGLU, last
-  matrix (E, DH, D_out);
+* shapes: x (T, D); router weights (D, E); router bias (E); first matrix
+  (E, D, DH) (or (E, D, D_out) for a linear expert), third matrix (E, D, DH) for
+  SwiGLU, last matrix (E, DH, D_out);
 * a Zipf-skewed bias is not drawn: expert e gets ``-ln(e + 1)``, so that
   ``softmax(bias)`` is proportional to ``1 / rank`` with rank = e + 1.
 
@@ -22,10 +25,14 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional, Union
 
 import numpy as np
+
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 Std = Union[float, str]  # a number, or "fanin" for 1/sqrt(fan_in)
 
@@ -142,6 +149,13 @@ class LayerInputs:
         return a
 
 
+X_ID, ROUTER_ID, BIAS_ID, W1_ID, W3_ID, W2_ID = range(6)
+
+
+def _rng(seed: int, tensor: int, expert: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, tensor, expert]))
+
+
 def _draw(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
     n = int(np.prod(shape))
     a = rng.standard_normal(n, dtype=np.float32)
@@ -152,39 +166,48 @@ def _draw(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray
     return a
 
 
-def _draw_experts(rng, E, shape, std, dtype) -> np.ndarray:
+def _draw_experts(seed, tensor, E, shape, std, dtype) -> np.ndarray:
     out = np.empty((E,) + tuple(shape), dtype=np.uint16 if dtype == "bf16" else np.float32)
-    for e in range(E):
-        out[e] = _draw(rng, shape, std, dtype)
+
+    def one(e):
+        out[e] = _draw(_rng(seed, tensor, e), shape, std, dtype)
+
+    n = int(np.prod(shape))
+    if E > 1 and n >= (1 << 20):
+        with ThreadPoolExecutor(min(E, _THREADS)) as ex:
+            list(ex.map(one, range(E)))
+    else:
+        for e in range(E):
+            one(e)
     return out
 
 
 def make_inputs(sp: LayerSpec, seed: int = 0, router_zero: bool = False) -> LayerInputs:
-    """Draw the inputs of layer ``sp`` from ``default_rng(seed)``.
+    """Draw the inputs of layer ``sp`` from the seeded streams described above.
 
-    ``router_zero`` draws the router weights (so the stream stays aligned) and
-    then sets them to zero: the uniform-router case.
+    ``router_zero`` sets the router weights to zero (the uniform-router case) and
+    leaves every other tensor as drawn.
     """
-    rng = np.random.default_rng(seed)
-    x = _draw(rng, (sp.T, sp.D), _std(sp.x_std, sp.D), sp.dtype)
-    w_router = _draw(rng, (sp.D, sp.E), _std(sp.router_std, sp.D), sp.dtype)
+    x = _draw(_rng(seed, X_ID), (sp.T, sp.D), _std(sp.x_std, sp.D), sp.dtype)
+    w_router = _draw(_rng(seed, ROUTER_ID), (sp.D, sp.E), _std(sp.router_std, sp.D), sp.dtype)
     if router_zero:
         w_router = np.zeros_like(w_router)
     bias = None
     if sp.bias == "normal":
-        bias = rng.standard_normal(sp.E, dtype=np.float32)
+        bias = _rng(seed, BIAS_ID).standard_normal(sp.E, dtype=np.float32)
     elif sp.bias == "zipf":
         bias = (-np.log(np.arange(1, sp.E + 1, dtype=np.float64))).astype(np.float32)
     elif sp.bias != "none":
         raise ValueError(f"unknown bias rule {sp.bias!r}")
+    wstd = _std(sp.w_std, sp.D)
     if sp.kind == "linear":
-        w1 = _draw_experts(rng, sp.E, (sp.D, sp.D_out), _std(sp.w_std, sp.D), sp.dtype)
+        w1 = _draw_experts(seed, W1_ID, sp.E, (sp.D, sp.D_out), wstd, sp.dtype)
         return LayerInputs(sp, x, w_router, bias, w1, None, None)
-    w1 = _draw_experts(rng, sp.E, (sp.D, sp.DH), _std(sp.w_std, sp.D), sp.dtype)
+    w1 = _draw_experts(seed, W1_ID, sp.E, (sp.D, sp.DH), wstd, sp.dtype)
     w3 = None
     if sp.kind == "swiglu":
-        w3 = _draw_experts(rng, sp.E, (sp.D, sp.DH), _std(sp.w_std, sp.D), sp.dtype)
+        w3 = _draw_experts(seed, W3_ID, sp.E, (sp.D, sp.DH), wstd, sp.dtype)
     elif sp.kind != "relu2":
         raise ValueError(f"unknown expert kind {sp.kind!r}")
-    w2 = _draw_experts(rng, sp.E, (sp.DH, sp.D_out), _std(sp.w2_std, sp.DH), sp.dtype)
+    w2 = _draw_experts(seed, W2_ID, sp.E, (sp.DH, sp.D_out), _std(sp.w2_std, sp.DH), sp.dtype)
     return LayerInputs(sp, x, w_router, bias, w1, w3, w2)

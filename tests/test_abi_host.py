@@ -1,0 +1,141 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and its
+host-side checks behave as include/moe.h states. No GPU and no kernel launch."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from expert_ffn_layer_router_amd import binding as B
+from golden_io import load
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "moe.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_stages():
+    names = declared_functions()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def P(**kw):
+    base = dict(T=64, D=32, DH=48, D_out=32, E=8, top_k=2, capacity_factor=0.0, dtype="bf16",
+                kind="swiglu")
+    base.update(kw)
+    return B.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,want", [
+    ({}, B.MOE_OK),
+    (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(D=0), B.MOE_ERR_INVALID_ARG),
+    (dict(DH=0), B.MOE_ERR_INVALID_ARG),
+    (dict(DH=0, kind="linear"), B.MOE_OK),
+    (dict(E=0, top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(E=257, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=256, top_k=256), B.MOE_OK),
+    (dict(D=36), B.MOE_ERR_UNSUPPORTED),
+    (dict(D=36, dtype="f32"), B.MOE_OK),
+    (dict(DH=44), B.MOE_ERR_UNSUPPORTED),
+    (dict(D_out=12), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=0), B.MOE_OK),
+    (dict(T=2**30, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(capacity_factor=float("nan")), B.MOE_ERR_INVALID_ARG),
+])
+def test_problem_checks(kw, want):
+    assert B.check_problem(P(**kw)) == want
+
+
+def test_capacity_matches_the_pages_table():
+    """capacity = floor(factor * T * k / E): the Sparsely-Gated Layer page's table."""
+    g = load("sparsely_gated_capacity.txt")
+    for f, cap in zip(g["factors"], g["capacities"]):
+        assert B.capacity(P(T=g["T"], E=g["E"], top_k=1, capacity_factor=f)) == cap
+    assert B.capacity(P(capacity_factor=0.0)) == -1
+    assert B.capacity(P(capacity_factor=-1.0)) == -1
+    assert B.capacity(P(T=64, E=8, top_k=1, capacity_factor=1.1)) == 8
+    assert B.capacity(P(T=16, E=8, top_k=1, capacity_factor=0.05)) == 0
+    # the two capacity configurations: 1.25 * 8192 * 1 / 64 and 2.0 * 16384 * 6 / 64
+    assert B.capacity(P(T=8192, D=1024, DH=4096, D_out=1024, E=64, top_k=1,
+                        capacity_factor=1.25)) == 160
+    assert B.capacity(P(T=16384, D=2048, DH=1408, D_out=2048, E=64, top_k=6,
+                        capacity_factor=2.0)) == 3072
+    assert B.capacity(P(top_k=0)) == -2
+
+
+def test_workspace_size():
+    assert B.workspace_size(P(top_k=0)) == 0
+    a = B.workspace_size(P(T=100))
+    b = B.workspace_size(P(T=1000))
+    assert 0 < a < b
+    # forward keeps the hidden activations and the expert outputs of every slot
+    p = P(T=1000)
+    assert b >= p.T * p.top_k * (p.DH + p.D_out) * 2
+    assert B.workspace_size(P(T=0)) >= 0
+
+
+def _call(fn, p, *ptrs, ws_bytes=0):
+    lib = B.lib()
+    return getattr(lib, fn)(ctypes.byref(p.c()), *ptrs)
+
+
+def test_error_paths_return_before_any_launch():
+    """Invalid arguments are reported from host checks alone (no device is touched)."""
+    lib = B.lib()
+    fake = 1 << 20  # never dereferenced: every call below fails its host checks first
+    p_bad = P(top_k=0)
+    assert lib.moe_route(ctypes.byref(p_bad.c()), fake, fake, None, fake, fake, fake, None,
+                         None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    p = P()
+    # missing aux_loss
+    assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, None, None, None,
+                         fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    # workspace too small / misaligned / missing
+    assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, fake, None, None,
+                         fake, 16, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, fake, None, None,
+                         fake + 8, 1 << 30, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, fake, None, None,
+                         None, 0, None) == B.MOE_ERR_WORKSPACE
+    # SwiGLU without its third matrix; ReLU without its second
+    assert lib.moe_expert_ffn(ctypes.byref(p.c()), fake, fake, fake, None, fake, fake, fake,
+                              1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn(ctypes.byref(P(kind="relu2").c()), fake, fake, fake, None, None,
+                              fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    # dispatch without offsets; combine without gates
+    assert lib.moe_dispatch(ctypes.byref(p.c()), fake, fake, fake, None, fake, fake, None, fake,
+                            1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(p.c()), fake, fake, None, fake, None) == \
+        B.MOE_ERR_INVALID_ARG
+    # forward: unsupported expert count, null problem
+    assert lib.moe_forward(ctypes.byref(P(E=300, top_k=2).c()), *([fake] * 14), 1 << 30,
+                           None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward(None, *([fake] * 14), 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert B.status_string(s).startswith("MOE_")
+    assert "unknown" in B.status_string(99)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        B._ptr(torch.zeros(4))

@@ -1,0 +1,282 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Routing and dispatch (expert_indices, counts, offsets, perm, slot_row / the drop set)
+must match bit-exactly; gates and aux_loss within 1e-6 relative; outputs within
+max-abs-rel 2e-2 in bf16 and 1e-5 in fp32 (max |gpu - ref| / max |ref| per tensor).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (AUX_TOL, GATE_TOL, OUT_TOL, check_routing, device_inputs, max_abs_rel,
+                      rel_err, run_forward, run_oracle, to_dev, to_host)
+from synth import make_inputs, spec
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# Sizes the oracle finishes in seconds that still span several tiles with ragged tails.
+MID_CASES = {
+    "swiglu_e8_k2": spec("mixtral_swiglu_bf16", T=700, D=256, DH=384, E=8),
+    "swiglu_zipf_cap": spec("fine_grained_zipf_bf16", T=1000, D=512, DH=320),
+    "relu_top1_cap": spec("switch_top1_cap_bf16", T=1500, D=256, DH=512),
+    "linear_bf16": spec("tiny_linear_f32", T=300, D=128, D_out=200, E=4, dtype="bf16"),
+    "swiglu_k_equals_E": spec("mixtral_swiglu_bf16", T=100, D=64, DH=64, E=4, top_k=4),
+    "swiglu_one_expert": spec("mixtral_swiglu_bf16", T=130, D=64, DH=72, E=1, top_k=1),
+    "relu_256_experts": spec("switch_top1_cap_bf16", T=600, D=64, DH=64, E=256, top_k=8,
+                             capacity_factor=0.0),
+    "relu_f32_ragged": spec("small_relu_f32", T=333, D=40, DH=70, E=5, top_k=3,
+                            capacity_factor=1.3),
+    "swiglu_f32": spec("small_relu_f32", T=50, D=12, DH=20, E=6, top_k=2, kind="swiglu"),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny_linear_f32", "small_relu_f32"])
+def test_small_configs(name):
+    sp = spec(name)
+    _say(f"[gpu] forward {name} {sp}")
+    I = make_inputs(sp)
+    g, r = run_forward(I), run_oracle(I)
+    check_routing(g, r)
+    assert max_abs_rel(g["out"], r["output"]) <= OUT_TOL[sp.dtype]
+
+
+def test_tiny_zero_router_gives_aux_one():
+    """W_router = 0: all logits tie, experts 0 and 1 are chosen, and aux_loss = 1.0."""
+    I = make_inputs(spec("tiny_linear_f32"), router_zero=True)
+    g, r = run_forward(I), run_oracle(I)
+    check_routing(g, r)
+    assert g["aux_loss"][0] == 1.0
+    assert (g["expert_indices"] == np.array([0, 1])).all()
+    assert (g["gates"] == 0.5).all()
+    assert max_abs_rel(g["out"], r["output"]) <= OUT_TOL["f32"]
+
+
+@pytest.mark.parametrize("name", sorted(MID_CASES))
+def test_mid_size_forward(name):
+    sp = MID_CASES[name]
+    _say(f"[gpu] forward {name} {sp}")
+    I = make_inputs(sp, seed=7)
+    g, r = run_forward(I), run_oracle(I)
+    check_routing(g, r)
+    err = max_abs_rel(g["out"], r["output"])
+    _say(f"  out max-abs-rel {err:.3e}, dropped {r['dropped']}")
+    assert err <= OUT_TOL[sp.dtype]
+    # rows whose every slot was dropped are exact zeros
+    T, k = g["expert_indices"].shape
+    all_dropped = (r["slot_row"].reshape(T, k) < 0).all(axis=1)
+    assert (g["out"][all_dropped] == 0).all()
+
+
+def test_top1_output_is_the_chosen_expert():
+    """top_k = 1: gate exactly 1 and the output is the expert's output for that token."""
+    sp = spec("switch_top1_cap_bf16", T=400, D=128, DH=256, E=16, capacity_factor=0.0)
+    I = make_inputs(sp, seed=3)
+    g, r = run_forward(I), run_oracle(I)
+    check_routing(g, r)
+    assert (g["gates"] == 1.0).all()
+    assert max_abs_rel(g["out"], r["output"]) <= OUT_TOL["bf16"]
+
+
+def test_capacity_zero_drops_everything():
+    sp = spec("fine_grained_zipf_bf16", T=200, D=64, DH=64, capacity_factor=0.01)
+    I = make_inputs(sp, seed=2)
+    g, r = run_forward(I), run_oracle(I)
+    assert r["capacity"] == 0
+    check_routing(g, r)
+    assert (g["slot_row"] == -1).all() and (g["expert_offsets"] == 0).all()
+    assert (g["out"] == 0).all()
+
+
+def test_empty_batch():
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("mixtral_swiglu_bf16", T=0, D=64, DH=64, E=8)
+    I = make_inputs(sp)
+    p = B.Problem.from_spec(sp)
+    d = device_inputs(I)
+    outs = B.forward(p, d["x"], d["w_router"], d["bias"], d["w1"], d["w3"], d["w2"])
+    torch.cuda.synchronize()
+    assert outs["out"].numel() == 0
+    assert outs["aux_loss"].item() == 0.0
+    assert (outs["expert_offsets"] == 0).all() and (outs["expert_counts"] == 0).all()
+
+
+def test_deterministic():
+    sp = MID_CASES["swiglu_zipf_cap"]
+    I = make_inputs(sp, seed=11)
+    a, b = run_forward(I), run_forward(I)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+# --- stage by stage, each from oracle-made inputs ----------------------------------------
+
+def test_route_stage_logits():
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("fine_grained_zipf_bf16", T=777, D=512, DH=64)
+    I = make_inputs(sp, seed=5)
+    r = run_oracle(I)
+    p = B.Problem.from_spec(sp)
+    d = device_inputs(I)
+    T, k, E = sp.T, sp.top_k, sp.E
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    aux = torch.empty(1, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ws = B.alloc_workspace(p)
+    B.moe_route(p, d["x"], d["w_router"], d["bias"], idx, gates, aux, counts, logits, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(idx), r["expert_indices"])
+    assert np.array_equal(to_host(counts), r["counts"])
+    assert rel_err(to_host(gates), r["gates"]) <= GATE_TOL
+    assert rel_err(to_host(aux)[0], r["aux_loss"]) <= AUX_TOL
+    # the exported logits are the float32 rounding of the router logits
+    assert max_abs_rel(to_host(logits), r["logits"]) <= 1e-6
+
+
+@pytest.mark.parametrize("cf", [0.0, 1.0, 2.0])
+def test_dispatch_stage_from_oracle_indices(cf):
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("fine_grained_zipf_bf16", T=1234, D=96, DH=64, capacity_factor=cf)
+    I = make_inputs(sp, seed=8)
+    r = run_oracle(I)
+    p = B.Problem.from_spec(sp)
+    T, k, E = sp.T, sp.top_k, sp.E
+    idx = torch.from_numpy(r["expert_indices"].astype(np.int32)).cuda()
+    x = to_dev(I.x)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    slot_row = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    x_perm = torch.zeros((T * k, sp.D), dtype=torch.bfloat16, device="cuda")
+    ws = B.alloc_workspace(p)
+    B.moe_dispatch(p, idx, x, counts, offsets, perm, slot_row, x_perm, ws)
+    torch.cuda.synchronize()
+    R = int(r["offsets"][-1])
+    assert np.array_equal(to_host(counts), r["counts"])
+    assert np.array_equal(to_host(offsets), r["offsets"])
+    assert np.array_equal(to_host(perm)[:R], r["perm"])
+    assert (to_host(perm)[R:] == -7).all()  # rows from R on are untouched
+    assert np.array_equal(to_host(slot_row), r["slot_row"])
+    xp = x_perm[:R].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(xp, I.x[r["perm"] // k])  # a bit copy of the token rows
+
+
+@pytest.mark.parametrize("kind,dtype", [("swiglu", "bf16"), ("relu2", "bf16"), ("linear", "bf16"),
+                                        ("swiglu", "f32"), ("relu2", "f32")])
+def test_expert_ffn_stage(kind, dtype):
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    base = "tiny_linear_f32" if kind == "linear" else "mixtral_swiglu_bf16"
+    kw = dict(T=900, D=192, E=6, top_k=2, kind=kind, dtype=dtype)
+    if kind == "linear":
+        kw["D_out"] = 136
+    else:
+        kw["DH"] = 200
+    sp = spec(base, **kw)
+    I = make_inputs(sp, seed=9)
+    r = run_oracle(I)
+    p = B.Problem.from_spec(sp)
+    k = sp.top_k
+    R = int(r["offsets"][-1])
+    x_perm_np = I.x[r["perm"] // k]
+    x_perm = torch.zeros((sp.T * k, sp.D), dtype=torch.bfloat16 if dtype == "bf16" else
+                         torch.float32, device="cuda")
+    x_perm[:R] = to_dev(x_perm_np)
+    offsets = torch.from_numpy(r["offsets"].astype(np.int32)).cuda()
+    d = device_inputs(I)
+    y = torch.zeros((sp.T * k, sp.D_out), dtype=x_perm.dtype, device="cuda")
+    ws = B.alloc_workspace(p)
+    B.moe_expert_ffn(p, x_perm, offsets, d["w1"], d["w3"], d["w2"], y, ws)
+    torch.cuda.synchronize()
+    got = to_host(y)[:R]
+    ref = np.zeros((R, sp.D_out))
+    xs = I.values("x")
+    for e in range(sp.E):
+        lo, hi = r["offsets"][e], r["offsets"][e + 1]
+        if hi > lo:
+            ref[lo:hi] = oracle.expert_forward(
+                kind, xs[r["perm"][lo:hi] // k], I.values("w1")[e],
+                None if I.w2 is None else I.values("w2")[e],
+                None if I.w3 is None else I.values("w3")[e])
+    assert max_abs_rel(got, ref) <= OUT_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_combine_stage(dtype):
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("fine_grained_zipf_bf16", T=513, D=64, DH=64, dtype=dtype)
+    I = make_inputs(sp, seed=12)
+    r = run_oracle(I)
+    p = B.Problem.from_spec(sp)
+    T, k = sp.T, sp.top_k
+    rng = np.random.default_rng(99)
+    y = rng.standard_normal((T * k, sp.D_out)).astype(np.float32)
+    if dtype == "bf16":
+        from synth import bf16_bits_to_f32, f32_to_bf16_bits
+        y_bits = f32_to_bf16_bits(y)
+        y = bf16_bits_to_f32(y_bits)
+        y_dev = to_dev(y_bits)
+    else:
+        y_dev = to_dev(y)
+    g32 = r["gates"].astype(np.float32)
+    out = torch.empty((T, sp.D_out), dtype=y_dev.dtype, device="cuda")
+    B.moe_combine(p, y_dev, torch.from_numpy(r["slot_row"].astype(np.int32)).cuda(),
+                  torch.from_numpy(g32).cuda(), out)
+    torch.cuda.synchronize()
+    ref = np.zeros((T, sp.D_out))
+    for t in range(T):
+        for j in range(k):
+            s = r["slot_row"][t * k + j]
+            if s >= 0:
+                ref[t] += float(g32[t, j]) * y[s].astype(np.float64)
+    tol = 1e-2 if dtype == "bf16" else 1e-6
+    assert max_abs_rel(to_host(out), ref) <= tol
+
+
+# --- the five configurations at full size ---------------------------------------------------
+
+FULL = ["switch_top1_cap_bf16", "mixtral_swiglu_bf16", "fine_grained_zipf_bf16"]
+
+
+def _sample_tokens(r, T, k, n_rand=40, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set(range(8)) | set(range(T - 8, T))
+    pick |= set(rng.choice(T, size=min(n_rand, T), replace=False).tolist())
+    dropped = np.flatnonzero((r["slot_row"].reshape(T, k) < 0).any(axis=1))
+    if dropped.size:
+        pick |= set(rng.choice(dropped, size=min(8, dropped.size), replace=False).tolist())
+    # the last kept row of each of a few experts (ragged tile tails)
+    for e in np.flatnonzero(r["kept"] > 0)[:8]:
+        pick.add(int(r["perm"][r["offsets"][e + 1] - 1] // k))
+    return np.array(sorted(pick))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_config(name):
+    sp = spec(name)
+    _say(f"[gpu] full-size {name}: generating inputs")
+    I = make_inputs(sp)
+    _say(f"[gpu] full-size {name}: GPU forward")
+    g = run_forward(I)
+    r_route = run_oracle(I, tokens=[])
+    check_routing(g, r_route)
+    tokens = _sample_tokens(r_route, sp.T, sp.top_k)
+    _say(f"[gpu] full-size {name}: oracle on {tokens.size} sampled tokens")
+    r = run_oracle(I, tokens=tokens)
+    err = max_abs_rel(g["out"][tokens], r["output"][tokens])
+    _say(f"  sampled out max-abs-rel {err:.3e}; dropped {r['dropped']} of {sp.slots}")
+    assert err <= OUT_TOL[sp.dtype]
