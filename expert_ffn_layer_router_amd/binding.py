@@ -68,7 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_size.restype = ctypes.c_size_t
         L.moe_workspace_size.argtypes = [_PP]
         L.moe_route.restype = ctypes.c_int
-        L.moe_route.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_route.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                _P]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_ffn.restype = ctypes.c_int
@@ -150,10 +151,10 @@ def workspace_size(p: Problem) -> int:
 
 
 def moe_route(p: Problem, x, w_router, router_bias, expert_indices, gates, aux_loss,
-              expert_counts=None, logits_out=None, ws=None, stream=None):
+              expert_counts=None, logits_out=None, uncertified=None, ws=None, stream=None):
     _check(lib().moe_route(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(router_bias),
                            _ptr(expert_indices), _ptr(gates), _ptr(aux_loss),
-                           _ptr(expert_counts), _ptr(logits_out), _ptr(ws),
+                           _ptr(expert_counts), _ptr(logits_out), _ptr(uncertified), _ptr(ws),
                            0 if ws is None else ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_route")
 

@@ -55,7 +55,7 @@ Problem internal(const moe_problem* p) {
 
 // Byte offsets of every scratch region inside the caller's workspace.
 struct Layout {
-  size_t psum, pcnt;    // routing partials: (route blocks, E) float64 and int32
+  size_t route;         // routing scratch (partials, transposed router, partial logits)
   size_t blkc, lrank;   // dispatch: (dispatch blocks, E) int32 and (T*k) int32
   size_t perm;          // moe_forward's own permutation, (T*k) int32
   size_t hbuf;          // expert hidden activations, (T*k, DH)
@@ -73,8 +73,7 @@ Layout layout_of(const Problem& q) {
   };
   const size_t es = elem_size(q.dtype);
   const size_t slots = (size_t)q.slots();
-  L.psum = take((size_t)route_blocks(q) * q.E * sizeof(double));
-  L.pcnt = take((size_t)route_blocks(q) * q.E * sizeof(int32_t));
+  L.route = take(route_ws_bytes(q));
   L.route_end = off;
   L.blkc = take((size_t)dispatch_blocks(q) * q.E * sizeof(int32_t));
   L.lrank = take(slots * sizeof(int32_t));
@@ -187,8 +186,8 @@ size_t moe_workspace_size(const moe_problem* p) {
 
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* router_bias, int32_t* expert_indices, float* gates,
-                     float* aux_loss, int32_t* expert_counts, float* logits_out, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+                     float* aux_loss, int32_t* expert_counts, float* logits_out,
+                     int32_t* uncertified, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
   if (!aux_loss) return MOE_ERR_INVALID_ARG;
@@ -198,10 +197,9 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
   st = check_ws(ws, ws_bytes, L.route_end);
   if (st != MOE_OK) return st;
   hipError_t err = launch_route(q, x, w_router, router_bias, expert_indices, gates, logits_out,
-                                at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), stream);
+                                uncertified, at<void>(ws, L.route), stream);
   if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), aux_loss,
-                              expert_counts, stream);
+    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, expert_counts, stream);
   return hip_status(err);
 }
 
@@ -266,10 +264,9 @@ moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_
   int32_t* perm = at<int32_t>(ws, L.perm);
   mark(ev, 2 * MOE_STAGE_ROUTE, stream);
   hipError_t err = launch_route(q, x, w_router, router_bias, expert_indices, gates, nullptr,
-                                at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), stream);
+                                nullptr, at<void>(ws, L.route), stream);
   if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<double>(ws, L.psum), at<int32_t>(ws, L.pcnt), aux_loss,
-                              nullptr, stream);
+    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream);
   mark(ev, 2 * MOE_STAGE_ROUTE + 1, stream);
   mark(ev, 2 * MOE_STAGE_DISPATCH, stream);
   if (err == hipSuccess)

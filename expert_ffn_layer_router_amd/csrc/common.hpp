@@ -62,13 +62,18 @@ struct Problem {
 };
 
 // Routing: logits, softmax, top-k, gates, per-block probability sums and counts.
-hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
-                        int32_t* idx, float* gates, float* logits_out, double* psum_blk,
-                        int32_t* count_blk, hipStream_t s);
+// `ws` is the routing scratch (route_ws_bytes bytes, 256-byte aligned).
 int64_t route_blocks(const Problem& p);
+int route_splits(const Problem& p);
+size_t route_ws_bytes(const Problem& p);
+// `uncertified` (nullable, device) receives the number of tokens whose decision was
+// recomputed in float64 (always 0 for float32 layers, which are float64 throughout).
+hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
+                        int32_t* idx, float* gates, float* logits_out, int32_t* uncertified,
+                        void* ws, hipStream_t s);
 // Sum of the per-block partials -> aux loss (and the per-expert counts, if asked).
-hipError_t launch_aux_finalize(const Problem& p, const double* psum_blk, const int32_t* count_blk,
-                               float* aux, int32_t* counts_out, hipStream_t s);
+hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* counts_out,
+                               hipStream_t s);
 
 // Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
 int64_t dispatch_blocks(const Problem& p);
@@ -95,6 +100,8 @@ struct GroupedGemm {
   int dtype;
 };
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
+// bf16, 256 x 256 tiles (expert_gemm_bf16.hip).
+hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s);
 
 // Combine: out[t] = sum_j gates[t,j] * y[slot_row[t*k+j]].
 hipError_t launch_combine(const Problem& p, const void* y, const int32_t* slot_row,

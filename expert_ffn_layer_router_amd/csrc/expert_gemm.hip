@@ -15,51 +15,10 @@
 // repacked in registers). Optional row gather: row r of A is A[a_gather[r] / gather_div],
 // which lets the layer feed token rows straight from x without a permuted copy.
 #include "common.hpp"
+#include "tile_schedule.hpp"
 
 namespace moe {
 namespace {
-
-// Maps M-tile id `tile` to (expert, first row, rows in tile). Every wave computes the same
-// answer independently. Returns false past the last tile.
-__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int E, int BM,
-                                          int tile, int& e_out, int& row0, int& rows) {
-  const int lane = lane_id();
-  int n[4], tiles[4], mine = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = 4 * lane + q;
-    n[q] = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-    tiles[q] = (n[q] + BM - 1) / BM;
-    mine += tiles[q];
-  }
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  const int excl = incl - mine;
-  const unsigned long long own = __ballot(tile >= excl && tile < incl);
-  if (own == 0ull) return false;
-  const int owner = __ffsll((long long)own) - 1;
-  int e = -1, mt = 0;
-  int run = excl;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (e < 0 && tile < run + tiles[q]) {
-      e = 4 * lane + q;
-      mt = tile - run;
-    }
-    run += tiles[q];
-  }
-  e = __shfl(e, owner);
-  mt = __shfl(mt, owner);
-  const int start = offsets[e] + mt * BM;
-  e_out = e;
-  row0 = start;
-  rows = min(BM, offsets[e + 1] - start);
-  return true;
-}
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
@@ -300,6 +259,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const GroupedGemm g)
 
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {
   if (g.max_rows <= 0 || g.N <= 0) return hipSuccess;
+  // the 256 x 256 kernel needs K % 64 == 0; other bf16 shapes take the 128 x 128 kernel
+  if (g.dtype == MOE_BF16 && g.K % 64 == 0) return launch_grouped_gemm_bf16_256(g, s);
   if (g.dtype == MOE_BF16) {
     const int64_t mt = (g.max_rows + kBM - 1) / kBM + g.E;
     const dim3 grid((unsigned)mt, (unsigned)((g.N + kBN - 1) / kBN));

@@ -3,13 +3,32 @@
 // (ML Grind "Mixture-of-Experts (MoE) Routing", Algorithm steps 1 and 2 and the
 // load-balancing step; ties go to the lower expert index, "Edge cases and conventions".)
 //
-// One wavefront owns one token at a time; lane l holds experts l, l+64, l+128, l+192
+// The selection runs one wavefront per token: lane l holds experts l, l+64, l+128, l+192
 // (E <= 256), so the softmax and the top-k are wave-wide shuffles over registers.
-// Logits here are accumulated in float64 from exactly widened inputs: the products of two
-// float32 (or bfloat16) values are exact in float64, so these logits are within a few
-// float64 ulps of the exact ones.
+//
+// float32 layers: the logits are accumulated in float64 from exactly widened inputs (a
+// product of two float32 values is exact in float64), one wave per token.
+//
+// bfloat16 layers (the HBM-bound path):
+//  1. prep:   the router weights are transposed to (E, D) and max_e ||W[:, e]||_2 is taken.
+//  2. logits: bf16 MFMA (16x16x32) over tiles of 64 tokens x all experts, the K range split
+//             over blocks when there are too few token tiles to fill the chip. Every MFMA
+//             sums 32 exact bf16 products into a zeroed float32 accumulator, and that
+//             result is folded into float64 at once, so float32 rounding never accumulates
+//             past 32 terms. Each split writes float32 partial logits and partial ||x_t||^2.
+//  3. select: partials summed in float64 in split order, bias added. A rigorous bound B_t on
+//             |logit - exact logit| is formed from the accumulation error of every 32-term
+//             MFMA sum (Cauchy-Schwarz: <= 32 * 2^-23 * ||x_t|| * ||W_e||), the rounding of
+//             the partials to float32, and the float64 sums. If two consecutive logits among
+//             the k+1 largest are within 2 B_t, the decision is not certified and the token's
+//             logits are recomputed in float64 from the exact products; otherwise the order of
+//             the computed logits is the order of the exact ones. Either way the top-k equals
+//             the one taken on exact logits. The k chosen logits are then recomputed exactly
+//             (k dot products in float64) and the gates come from those; the probabilities
+//             that feed the loss come from the float64-folded MFMA logits.
 #include <float.h>
 #include <limits.h>
+#include <math.h>
 
 #include "common.hpp"
 
@@ -17,8 +36,13 @@ namespace moe {
 namespace {
 
 constexpr int kEPL = kMaxExperts / kWave;  // experts per lane
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / kWave;
+
+// MFMA logits tiling
+constexpr int kLT = 64;     // tokens per block (4 waves x 16)
+constexpr int kLKB = 256;   // K per stage (LDS router chunk, A registers)
+constexpr int kMinKSplit = 256;
 
 __device__ __forceinline__ double wave_max(double v) {
 #pragma unroll
@@ -35,8 +59,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 
 template <typename TIn>
 __device__ __forceinline__ void logits_f64(const TIn* __restrict__ x, const TIn* __restrict__ w,
-                                           const float* __restrict__ bias, int64_t t, int64_t D,
-                                           int E, double lg[kEPL]) {
+                                           int64_t t, int64_t D, int E, double lg[kEPL]) {
   const int lane = lane_id();
 #pragma unroll
   for (int i = 0; i < kEPL; ++i) lg[i] = 0.0;
@@ -50,50 +73,106 @@ __device__ __forceinline__ void logits_f64(const TIn* __restrict__ x, const TIn*
       if (e < E) lg[i] = fma(xv, load_as_f64(wr, e), lg[i]);
     }
   }
-  if (bias) {
+}
+
+// Exact-product float64 logits of one bf16 token from the transposed router (E, D).
+// Experts go in groups of 8: lane l works on expert 8g + l % 8 over the D-slices
+// c = l / 8 (mod 8), with independent 16-byte loads, and the 8 slice sums of an expert
+// are combined with three xor-shuffles (a fixed order).
+__device__ __forceinline__ void logits_f64_bf16_rows(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ wt, int64_t t,
+                                                     int64_t D, int E, double lg[kEPL]) {
+  const int lane = lane_id();
+  const uint4* xr = (const uint4*)(x + t * D);
+  const int64_t nc = D / 8;
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) lg[i] = 0.0;
+  for (int g = 0; g < (E + 7) / 8; ++g) {
+    const int e = 8 * g + (lane & 7);
+    double a0 = 0.0, a1 = 0.0;
+    if (e < E) {
+      const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
+#pragma unroll 4
+      for (int64_t c = lane >> 3; c < nc; c += 8) {
+        const uint4 xv = xr[c], wv = wr[c];
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          a0 = fma((double)__uint_as_float(xw[q] << 16), (double)__uint_as_float(ww[q] << 16), a0);
+          a1 = fma((double)__uint_as_float(xw[q] & 0xffff0000u),
+                   (double)__uint_as_float(ww[q] & 0xffff0000u), a1);
+        }
+      }
+    }
+    double v = a0 + a1;
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    // lanes with l % 8 == e % 8 now hold expert 8g + l % 8; hand each to its owner lane
 #pragma unroll
     for (int i = 0; i < kEPL; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E) lg[i] += (double)bias[e];
+      const int mine = lane + kWave * i;
+      const double got = __shfl(v, mine & 7);
+      if ((mine >> 3) == g) lg[i] = got;
     }
   }
 }
 
-// Softmax over all E logits (probabilities, for the loss) and the top-k selection with
-// gates. Writes the token's index and gate rows; returns its probabilities and the
-// selection mask in registers.
-__device__ __forceinline__ void select_token(int E, int k, int64_t t, const double lg[kEPL],
-                                             double prob[kEPL], bool sel[kEPL],
-                                             int32_t* __restrict__ idx,
-                                             float* __restrict__ gates) {
+// Exact-product float64 logits of the k chosen experts of one bf16 token (gates need the
+// differences of these to ~1e-7 absolute, which a float32 partial cannot carry when the
+// logits are large): the wave splits D, each lane summing 8-element slices in float64.
+__device__ __forceinline__ void chosen_logits_f64(const uint16_t* __restrict__ x,
+                                                  const uint16_t* __restrict__ wt,
+                                                  const float* __restrict__ bias, int64_t t,
+                                                  int64_t D, int k, const int my_e[kEPL],
+                                                  double my_v[kEPL]) {
   const int lane = lane_id();
-  double m = -DBL_MAX;
+  const uint4* xr = (const uint4*)(x + t * D);
+  for (int j = 0; j < k; ++j) {
+    int e = 0;
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i)
-    if (lane + kWave * i < E) m = fmax(m, lg[i]);
-  m = wave_max(m);
-  double s = 0.0;
+    for (int i = 0; i < kEPL; ++i)
+      if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
+    const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll 4
+    for (int64_t c = lane; c < D / 8; c += kWave) {
+      const uint4 xv = xr[c], wv = wr[c];
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
-    prob[i] = (lane + kWave * i < E) ? exp(lg[i] - m) : 0.0;
-    s += prob[i];
-    sel[i] = false;
+      for (int q = 0; q < 4; ++q) {
+        a0 = fma((double)__uint_as_float(xw[q] << 16), (double)__uint_as_float(ww[q] << 16), a0);
+        a1 = fma((double)__uint_as_float(xw[q] & 0xffff0000u),
+                 (double)__uint_as_float(ww[q] & 0xffff0000u), a1);
+      }
+    }
+    double v = wave_sum(a0 + a1);
+    if (bias) v += (double)bias[e];
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i)
+      if (j == lane + kWave * i) my_v[i] = v;
   }
-  s = wave_sum(s);
-#pragma unroll
-  for (int i = 0; i < kEPL; ++i) prob[i] /= s;
+}
 
-  // k rounds of a wave-wide argmax over the not-yet-chosen experts:
-  // larger logit first, equal logits -> smaller expert index.
-  double my_v[kEPL];
-  int my_e[kEPL];
+// k rounds of a wave-wide argmax over the not-yet-chosen experts: larger logit first,
+// equal logits -> smaller expert index. Lane j (+64i) keeps the j-th choice. When
+// `want_gap`, one more round finds the best unchosen logit, and the smallest difference
+// between consecutive values of the chosen sequence (extended by that one) is returned.
+__device__ __forceinline__ double topk_rounds(int E, int k, const double lg[kEPL], bool sel[kEPL],
+                                              double my_v[kEPL], int my_e[kEPL],
+                                              bool want_gap) {
+  const int lane = lane_id();
 #pragma unroll
   for (int i = 0; i < kEPL; ++i) {
+    sel[i] = false;
     my_v[i] = 0.0;
     my_e[i] = 0;
   }
-  double v0 = 0.0;
-  for (int j = 0; j < k; ++j) {
+  double prev = 0.0, min_gap = DBL_MAX;
+  const int rounds = (want_gap && k < E) ? k + 1 : k;
+  for (int j = 0; j < rounds; ++j) {
     double bv = -DBL_MAX;
     int be = INT_MAX;
 #pragma unroll
@@ -113,7 +192,9 @@ __device__ __forceinline__ void select_token(int E, int k, int64_t t, const doub
         be = oe;
       }
     }
-    if (j == 0) v0 = bv;
+    if (j > 0) min_gap = fmin(min_gap, prev - bv);
+    prev = bv;
+    if (j == k) break;  // the extra round only measures the boundary gap
 #pragma unroll
     for (int i = 0; i < kEPL; ++i) {
       if (be == lane + kWave * i) sel[i] = true;
@@ -123,7 +204,31 @@ __device__ __forceinline__ void select_token(int E, int k, int64_t t, const doub
       }
     }
   }
-  // gates: softmax over the chosen logits (max = the first chosen one)
+  return min_gap;
+}
+
+// Probabilities over all experts (returned in prob[]), and the index/gate rows.
+__device__ __forceinline__ void finish_token(int E, int k, int64_t t, const double lg[kEPL],
+                                             const double my_v[kEPL], const int my_e[kEPL],
+                                             double prob[kEPL], int32_t* __restrict__ idx,
+                                             float* __restrict__ gates) {
+  const int lane = lane_id();
+  double m = -DBL_MAX;
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i)
+    if (lane + kWave * i < E) m = fmax(m, lg[i]);
+  m = wave_max(m);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) {
+    prob[i] = (lane + kWave * i < E) ? exp(lg[i] - m) : 0.0;
+    s += prob[i];
+  }
+  s = wave_sum(s);
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) prob[i] /= s;
+  // gates: softmax over the chosen logits, shifted by the first (largest) of them
+  const double v0 = __shfl(my_v[0], 0);
   double ev[kEPL];
   double gs = 0.0;
 #pragma unroll
@@ -142,47 +247,36 @@ __device__ __forceinline__ void select_token(int E, int k, int64_t t, const doub
   }
 }
 
-template <typename TIn>
-__global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
-    int64_t T, int64_t D, int E, int k, const TIn* __restrict__ x, const TIn* __restrict__ w,
-    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ gates,
-    float* __restrict__ logits_out, double* __restrict__ psum_blk,
-    int32_t* __restrict__ count_blk) {
-  __shared__ double s_psum[kRouteWaves][kMaxExperts];
-  __shared__ int s_cnt[kRouteWaves][kMaxExperts];
-  const int wv = wave_id(), lane = lane_id();
+// Per-block partials of sum_t probs[t, e] and of the expert counts, in fixed order.
+struct BlockPartials {
   double psum[kEPL];
   int cnt[kEPL];
+  __device__ void zero() {
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
-    psum[i] = 0.0;
-    cnt[i] = 0;
-  }
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
-  for (int q = wv; q < kRouteTokensPerBlock; q += kRouteWaves) {
-    const int64_t t = t0 + q;
-    if (t >= T) break;
-    double lg[kEPL], prob[kEPL];
-    bool sel[kEPL];
-    logits_f64(x, w, bias, t, D, E, lg);
-    if (logits_out) {
-#pragma unroll
-      for (int i = 0; i < kEPL; ++i) {
-        const int e = lane + kWave * i;
-        if (e < E) logits_out[t * E + e] = (float)lg[i];
-      }
+    for (int i = 0; i < kEPL; ++i) {
+      psum[i] = 0.0;
+      cnt[i] = 0;
     }
-    select_token(E, k, t, lg, prob, sel, idx, gates);
+  }
+  __device__ void add(const double prob[kEPL], const bool sel[kEPL]) {
 #pragma unroll
     for (int i = 0; i < kEPL; ++i) {
       psum[i] += prob[i];
       cnt[i] += sel[i] ? 1 : 0;
     }
   }
+};
+
+__device__ __forceinline__ void write_block_partials(const BlockPartials& bp, int E,
+                                                     double* __restrict__ psum_blk,
+                                                     int32_t* __restrict__ count_blk) {
+  __shared__ double s_psum[kRouteWaves][kMaxExperts];
+  __shared__ int s_cnt[kRouteWaves][kMaxExperts];
+  const int wv = wave_id(), lane = lane_id();
 #pragma unroll
   for (int i = 0; i < kEPL; ++i) {
-    s_psum[wv][lane + kWave * i] = psum[i];
-    s_cnt[wv][lane + kWave * i] = cnt[i];
+    s_psum[wv][lane + kWave * i] = bp.psum[i];
+    s_cnt[wv][lane + kWave * i] = bp.cnt[i];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
@@ -198,6 +292,243 @@ __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
   }
 }
 
+__device__ __forceinline__ void add_bias(const float* __restrict__ bias, int E, double lg[kEPL]) {
+  if (!bias) return;
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) lg[i] += (double)bias[e];
+  }
+}
+
+__device__ __forceinline__ void write_logits(float* __restrict__ logits_out, int64_t t, int E,
+                                             const double lg[kEPL]) {
+  if (!logits_out) return;
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < kEPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) logits_out[t * E + e] = (float)lg[i];
+  }
+}
+
+// ---- float32 layers -----------------------------------------------------------------------
+
+template <typename TIn>
+__global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
+    int64_t T, int64_t D, int E, int k, const TIn* __restrict__ x, const TIn* __restrict__ w,
+    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ gates,
+    float* __restrict__ logits_out, double* __restrict__ psum_blk,
+    int32_t* __restrict__ count_blk) {
+  BlockPartials bp;
+  bp.zero();
+  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
+  for (int q = wave_id(); q < kRouteTokensPerBlock; q += kRouteWaves) {
+    const int64_t t = t0 + q;
+    if (t >= T) break;
+    double lg[kEPL], prob[kEPL], my_v[kEPL];
+    int my_e[kEPL];
+    bool sel[kEPL];
+    logits_f64(x, w, t, D, E, lg);
+    add_bias(bias, E, lg);
+    write_logits(logits_out, t, E, lg);
+    topk_rounds(E, k, lg, sel, my_v, my_e, false);
+    finish_token(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    bp.add(prob, sel);
+  }
+  write_block_partials(bp, E, psum_blk, count_blk);
+}
+
+// ---- bfloat16 layers ----------------------------------------------------------------------
+
+// wt[e][d] = w[d][e]; wnorm[e] = ||w[:, e]||_2 (float64). One block per expert; the sum of
+// squares is reduced in a fixed order (per-thread, then an LDS tree).
+__global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
+                                                          const uint16_t* __restrict__ w,
+                                                          uint16_t* __restrict__ wt,
+                                                          double* __restrict__ wnorm) {
+  __shared__ double s_part[256];
+  const int e = blockIdx.x;
+  double acc = 0.0;
+#pragma unroll 4
+  for (int64_t d = threadIdx.x; d < D; d += 256) {
+    const uint16_t v = w[d * E + e];
+    wt[(int64_t)e * D + d] = v;
+    const double f = (double)bf16_to_f32(v);
+    acc = fma(f, f, acc);
+  }
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if ((int)threadIdx.x < h) s_part[threadIdx.x] += s_part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) wnorm[e] = sqrt(s_part[0]);
+}
+
+template <int NT>  // tiles of 16 experts
+__global__ __launch_bounds__(256) void route_logits_mfma_kernel(
+    int64_t T, int64_t D, int E, int64_t kc, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wt, float* __restrict__ part, float* __restrict__ xsq) {
+  __shared__ __align__(16) uint16_t sB[NT * 16][kLKB + 8];
+  const int lane = lane_id(), wv = wave_id();
+  const int64_t t0 = (int64_t)blockIdx.x * kLT + wv * 16;
+  const int s = blockIdx.y;
+  const int64_t kbeg = (int64_t)s * kc;
+  const int64_t kend = min(D, kbeg + kc);
+  const int64_t row = t0 + (lane & 15);
+  const bool row_ok = row < T;
+  const int koff = 8 * (lane >> 4);
+  const uint16_t* xr = x + (row_ok ? row : 0) * D + koff;
+
+  double acc[NT][4];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[n][v] = 0.0;
+  float xs = 0.f;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kSteps = kLKB / 32;
+
+  uint4 a_next[kSteps];
+  auto load_a = [&](int64_t kb, uint4 (&dst)[kSteps]) {
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int64_t kk = kb + 32 * j + koff;
+      dst[j] = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok && kk < kend) dst[j] = *(const uint4*)(xr + kb + 32 * j);
+    }
+  };
+  load_a(kbeg, a_next);
+  for (int64_t kb = kbeg; kb < kend; kb += kLKB) {
+    uint4 a[kSteps];
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) a[j] = a_next[j];
+    __syncthreads();  // previous chunk's LDS reads are done
+    for (int i = threadIdx.x; i < NT * 16 * (kLKB / 8); i += 256) {
+      const int e = i / (kLKB / 8), q = i % (kLKB / 8);
+      const int64_t kk = kb + 8 * q;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (e < E && kk < kend) v = *(const uint4*)(wt + (int64_t)e * D + kk);
+      *(uint4*)&sB[e][8 * q] = v;
+    }
+    if (kb + kLKB < kend) load_a(kb + kLKB, a_next);  // in flight during this chunk
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[j]);
+      const uint32_t aw[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = __uint_as_float(aw[q] << 16), hi = __uint_as_float(aw[q] & 0xffff0000u);
+        xs = fmaf(lo, lo, xs);
+        xs = fmaf(hi, hi, xs);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const bf16x8 bv = *(const bf16x8*)&sB[n * 16 + (lane & 15)][32 * j + koff];
+        const f32x4 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, zero4, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[n][v] += (double)c[v];
+      }
+    }
+  }
+  // lanes l, l^16, l^32, l^48 hold the same token row
+  xs += __shfl_xor(xs, 16);
+  xs += __shfl_xor(xs, 32);
+  // 16x16 accumulator layout: lane l holds expert column l % 16, token rows 4*(l/16) + v
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t t = t0 + 4 * (lane >> 4) + v;
+      const int e = n * 16 + (lane & 15);
+      if (t < T && e < E) part[((int64_t)s * T + t) * E + e] = (float)acc[n][v];
+    }
+  if (lane < 16 && row_ok) xsq[(int64_t)s * T + row] = xs;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_select_kernel(
+    int64_t T, int64_t D, int E, int k, int S, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wt, const double* __restrict__ wnorm,
+    const float* __restrict__ part, const float* __restrict__ xsq, const float* __restrict__ bias,
+    int32_t* __restrict__ idx, float* __restrict__ gates, float* __restrict__ logits_out,
+    double* __restrict__ psum_blk, int32_t* __restrict__ count_blk, int32_t* __restrict__ nflag) {
+  const int lane = lane_id();
+  double wmax = 0.0;
+  for (int e = 0; e < E; ++e) wmax = fmax(wmax, wnorm[e]);
+  BlockPartials bp;
+  bp.zero();
+  int flagged = 0;
+  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
+  for (int q = wave_id(); q < kRouteTokensPerBlock; q += kRouteWaves) {
+    const int64_t t = t0 + q;
+    if (t >= T) break;
+    double lg[kEPL], prob[kEPL], my_v[kEPL];
+    int my_e[kEPL];
+    bool sel[kEPL];
+    double rnd = 0.0, xn2 = 0.0, ab[kEPL];
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) {
+      lg[i] = 0.0;
+      ab[i] = 0.0;
+    }
+    // partials in split order; 8 splits' loads issued together
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float pv[8][kEPL], xv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool ok = s0 + q < S;
+        xv[q] = ok ? xsq[(int64_t)(s0 + q) * T + t] : 0.f;
+#pragma unroll
+        for (int i = 0; i < kEPL; ++i) {
+          const int e = lane + kWave * i;
+          pv[q][i] = (ok && e < E) ? part[((int64_t)(s0 + q) * T + t) * E + e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        xn2 += (double)xv[q];
+#pragma unroll
+        for (int i = 0; i < kEPL; ++i) {
+          lg[i] += (double)pv[q][i];
+          ab[i] += fabs((double)pv[q][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i) rnd = fmax(rnd, ab[i]);
+    add_bias(bias, E, lg);
+    double lmax = 0.0;
+#pragma unroll
+    for (int i = 0; i < kEPL; ++i)
+      if (lane + kWave * i < E) lmax = fmax(lmax, fabs(lg[i]));
+    rnd = wave_max(rnd);
+    lmax = wave_max(lmax);
+    // |computed - exact| bound: every 32-term MFMA sum within 32 * 2^-23 of its sum of
+    // |products|, summed by Cauchy-Schwarz; the float32 sum of squares padded by D * 2^-23;
+    // the float32 rounding of each partial; the float64 additions.
+    const double gamma = 32.0 * 0x1p-23;
+    const double B = gamma * sqrt(xn2 * (1.0 + (double)D * 0x1p-23)) * wmax * (1.0 + 1e-6) +
+                     rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30;
+    const double gap = topk_rounds(E, k, lg, sel, my_v, my_e, true);
+    if (!(gap > 2.0 * B)) {
+      ++flagged;
+      logits_f64_bf16_rows(x, wt, t, D, E, lg);
+      add_bias(bias, E, lg);
+      topk_rounds(E, k, lg, sel, my_v, my_e, false);
+    } else {
+      chosen_logits_f64(x, wt, bias, t, D, k, my_e, my_v);
+    }
+    write_logits(logits_out, t, E, lg);
+    finish_token(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    bp.add(prob, sel);
+  }
+  write_block_partials(bp, E, psum_blk, count_blk);
+  if (nflag && lane == 0 && flagged) atomicAdd(nflag, flagged);
+}
+
 // aux = E * sum_e (count_e / (T k)) * (sum_t probs[t, e] / T), partials summed in block order.
 __global__ __launch_bounds__(kMaxExperts) void aux_finalize_kernel(
     int64_t nblk, int E, int64_t T, int k, const double* __restrict__ psum_blk,
@@ -208,9 +539,20 @@ __global__ __launch_bounds__(kMaxExperts) void aux_finalize_kernel(
   if (e < E) {
     double P = 0.0;
     int64_t c = 0;
-    for (int64_t b = 0; b < nblk; ++b) {
-      P += psum_blk[b * E + e];
-      c += count_blk[b * E + e];
+    constexpr int kChunk = 16;  // independent loads in flight, summed in block order
+    for (int64_t b0 = 0; b0 < nblk; b0 += kChunk) {
+      double pv[kChunk];
+      int cv[kChunk];
+#pragma unroll
+      for (int q = 0; q < kChunk; ++q) {
+        pv[q] = (b0 + q < nblk) ? psum_blk[(b0 + q) * E + e] : 0.0;
+        cv[q] = (b0 + q < nblk) ? count_blk[(b0 + q) * E + e] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kChunk; ++q) {
+        P += pv[q];
+        c += cv[q];
+      }
     }
     if (counts_out) counts_out[e] = (int32_t)c;
     s_term[e] = (T > 0) ? ((double)c / ((double)T * (double)k)) * (P / (double)T) : 0.0;
@@ -223,33 +565,112 @@ __global__ __launch_bounds__(kMaxExperts) void aux_finalize_kernel(
   }
 }
 
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+// ---- scratch layout -------------------------------------------------------------------------
+
+size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct RouteScratch {
+  double* psum;
+  int32_t* pcnt;
+  uint16_t* wt;
+  double* wnorm;
+  float* part;
+  float* xsq;
+  size_t bytes;
+};
+
+RouteScratch route_scratch(const Problem& p, void* base) {
+  RouteScratch r{};
+  char* b = (char*)base;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    char* q = b ? b + off : nullptr;
+    off = a256(off + n);
+    return q;
+  };
+  const int64_t nblk = route_blocks(p);
+  r.psum = (double*)take((size_t)nblk * p.E * sizeof(double));
+  r.pcnt = (int32_t*)take((size_t)nblk * p.E * sizeof(int32_t));
+  if (p.dtype == MOE_BF16) {
+    const int S = route_splits(p);
+    r.wt = (uint16_t*)take((size_t)p.E * p.D * sizeof(uint16_t));
+    r.wnorm = (double*)take((size_t)p.E * sizeof(double));
+    r.part = (float*)take((size_t)S * p.T * p.E * sizeof(float));
+    r.xsq = (float*)take((size_t)S * p.T * sizeof(float));
+  }
+  r.bytes = off;
+  return r;
+}
+
 }  // namespace
 
 int64_t route_blocks(const Problem& p) {
   return (p.T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
 }
 
+// Splits of the router's K range: enough blocks to fill the chip, each split at least
+// kMinKSplit deep, and the float32 partials (written and read back) at most a quarter of
+// the bytes of x.
+int route_splits(const Problem& p) {
+  const int64_t nblk = (p.T + kLT - 1) / kLT;
+  int S = 1;
+  while (nblk * (2 * S) <= 1024 && p.D / (2 * S) >= kMinKSplit &&
+         16 * (int64_t)(2 * S) * p.E <= p.D)
+    S *= 2;
+  return S;
+}
+
+size_t route_ws_bytes(const Problem& p) { return route_scratch(p, nullptr).bytes; }
+
 hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
-                        int32_t* idx, float* gates, float* logits_out, double* psum_blk,
-                        int32_t* count_blk, hipStream_t s) {
+                        int32_t* idx, float* gates, float* logits_out, int32_t* uncertified,
+                        void* ws, hipStream_t s) {
+  const RouteScratch r = route_scratch(p, ws);
   const int64_t nblk = route_blocks(p);
-  if (nblk == 0) return hipSuccess;
-  if (p.dtype == MOE_BF16) {
-    hipLaunchKernelGGL(route_f64_kernel<uint16_t>, dim3((unsigned)nblk), dim3(kRouteThreads), 0,
-                       s, p.T, p.D, p.E, p.top_k, (const uint16_t*)x, (const uint16_t*)w_router,
-                       bias, idx, gates, logits_out, psum_blk, count_blk);
-  } else {
+  if (uncertified) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, uncertified);
+  if (nblk == 0) return hipGetLastError();
+  if (p.dtype != MOE_BF16) {
     hipLaunchKernelGGL(route_f64_kernel<float>, dim3((unsigned)nblk), dim3(kRouteThreads), 0, s,
                        p.T, p.D, p.E, p.top_k, (const float*)x, (const float*)w_router, bias, idx,
-                       gates, logits_out, psum_blk, count_blk);
+                       gates, logits_out, r.psum, r.pcnt);
+    return hipGetLastError();
   }
+  const int S = route_splits(p);
+  int64_t kc = (p.D + S - 1) / S;
+  kc = (kc + 31) / 32 * 32;
+  hipLaunchKernelGGL(router_prep_kernel, dim3(p.E), dim3(256), 0, s, p.D, p.E,
+                     (const uint16_t*)w_router, r.wt, r.wnorm);
+  const dim3 lgrid((unsigned)((p.T + kLT - 1) / kLT), (unsigned)S);
+  const int NT = (p.E + 15) / 16;
+  const uint16_t* xb = (const uint16_t*)x;
+  if (NT <= 1)
+    hipLaunchKernelGGL(route_logits_mfma_kernel<1>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
+                       xb, r.wt, r.part, r.xsq);
+  else if (NT <= 2)
+    hipLaunchKernelGGL(route_logits_mfma_kernel<2>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
+                       xb, r.wt, r.part, r.xsq);
+  else if (NT <= 4)
+    hipLaunchKernelGGL(route_logits_mfma_kernel<4>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
+                       xb, r.wt, r.part, r.xsq);
+  else if (NT <= 8)
+    hipLaunchKernelGGL(route_logits_mfma_kernel<8>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
+                       xb, r.wt, r.part, r.xsq);
+  else
+    hipLaunchKernelGGL(route_logits_mfma_kernel<16>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
+                       xb, r.wt, r.part, r.xsq);
+  hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)nblk), dim3(kRouteThreads), 0, s, p.T,
+                     p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias, idx, gates,
+                     logits_out, r.psum, r.pcnt, uncertified);
   return hipGetLastError();
 }
 
-hipError_t launch_aux_finalize(const Problem& p, const double* psum_blk, const int32_t* count_blk,
-                               float* aux, int32_t* counts_out, hipStream_t s) {
+hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* counts_out,
+                               hipStream_t s) {
+  const RouteScratch r = route_scratch(p, ws);
   hipLaunchKernelGGL(aux_finalize_kernel, dim3(1), dim3(kMaxExperts), 0, s, route_blocks(p), p.E,
-                     p.T, p.top_k, psum_blk, count_blk, aux, counts_out);
+                     p.T, p.top_k, r.psum, r.pcnt, aux, counts_out);
   return hipGetLastError();
 }
 

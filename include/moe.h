@@ -105,11 +105,14 @@ size_t moe_workspace_size(const moe_problem* p);
  *   x (T, D), w_router (D, E) in p->dtype; router_bias (E) float32 or NULL.
  *   Outputs: expert_indices (T, top_k) int32, best first; gates (T, top_k) float32, each row
  *   summing to 1; aux_loss (1) float32; expert_counts (E) int32 routed slots per expert before
- *   capacity, or NULL; logits_out (T, E) float32 copy of the router logits, or NULL. */
+ *   capacity, or NULL; logits_out (T, E) float32 copy of the router logits, or NULL;
+ *   uncertified (1) int32, or NULL: the number of tokens whose top-k order the fast bf16
+ *   logits could not certify and that were therefore recomputed in float64 (0 for MOE_F32).
+ *   With T = 0, aux_loss is 0 and expert_counts are zeros. */
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* router_bias, int32_t* expert_indices, float* gates,
-                     float* aux_loss, int32_t* expert_counts, float* logits_out, void* ws,
-                     size_t ws_bytes, hipStream_t stream);
+                     float* aux_loss, int32_t* expert_counts, float* logits_out,
+                     int32_t* uncertified, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Dispatch (ML Grind, Algorithm step 3 "gather the tokens routed to it"; capacity as in
  * the Sparsely-Gated Layer page's moe_forward, first come, first served).

@@ -101,18 +101,18 @@ def test_error_paths_return_before_any_launch():
     fake = 1 << 20  # never dereferenced: every call below fails its host checks first
     p_bad = P(top_k=0)
     assert lib.moe_route(ctypes.byref(p_bad.c()), fake, fake, None, fake, fake, fake, None,
-                         None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+                         None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     p = P()
     # missing aux_loss
     assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, None, None, None,
-                         fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+                         None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     # workspace too small / misaligned / missing
     assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, fake, None, None,
-                         fake, 16, None) == B.MOE_ERR_WORKSPACE
+                         None, fake, 16, None) == B.MOE_ERR_WORKSPACE
     assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, fake, None, None,
-                         fake + 8, 1 << 30, None) == B.MOE_ERR_WORKSPACE
+                         None, fake + 8, 1 << 30, None) == B.MOE_ERR_WORKSPACE
     assert lib.moe_route(ctypes.byref(p.c()), fake, fake, None, fake, fake, fake, None, None,
-                         None, 0, None) == B.MOE_ERR_WORKSPACE
+                         None, None, 0, None) == B.MOE_ERR_WORKSPACE
     # SwiGLU without its third matrix; ReLU without its second
     assert lib.moe_expert_ffn(ctypes.byref(p.c()), fake, fake, fake, None, fake, fake, fake,
                               1 << 30, None) == B.MOE_ERR_INVALID_ARG

@@ -134,7 +134,7 @@ def test_route_stage_logits():
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
     ws = B.alloc_workspace(p)
-    B.moe_route(p, d["x"], d["w_router"], d["bias"], idx, gates, aux, counts, logits, ws)
+    B.moe_route(p, d["x"], d["w_router"], d["bias"], idx, gates, aux, counts, logits, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(idx), r["expert_indices"])
     assert np.array_equal(to_host(counts), r["counts"])
@@ -280,3 +280,72 @@ def test_full_size_config(name):
     err = max_abs_rel(g["out"][tokens], r["output"][tokens])
     _say(f"  sampled out max-abs-rel {err:.3e}; dropped {r['dropped']} of {sp.slots}")
     assert err <= OUT_TOL[sp.dtype]
+
+
+# --- the certified bf16 routing decision ---------------------------------------------------
+
+def _route(I, sp):
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    p = B.Problem.from_spec(sp)
+    d = device_inputs(I)
+    T, k, E = sp.T, sp.top_k, sp.E
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    aux = torch.empty(1, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    unc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    ws = B.alloc_workspace(p)
+    B.moe_route(p, d["x"], d["w_router"], d["bias"], idx, gates, aux, counts, None, unc, ws)
+    torch.cuda.synchronize()
+    return dict(expert_indices=to_host(idx), gates=to_host(gates), aux_loss=to_host(aux),
+                counts=to_host(counts), uncertified=int(unc.item()))
+
+
+def _check_route(g, r):
+    assert np.array_equal(g["expert_indices"], r["expert_indices"])
+    assert np.array_equal(g["counts"], r["counts"])
+    assert rel_err(g["gates"], r["gates"]) <= GATE_TOL
+    assert rel_err(g["aux_loss"][0], r["aux_loss"]) <= AUX_TOL
+
+
+def test_bf16_zero_router_ties_fall_back_to_float64():
+    """All logits tie at 0: nothing can be certified, every token is recomputed, and the
+    ties go to the lower expert index as in the oracle; aux_loss is 1."""
+    sp = spec("fine_grained_zipf_bf16", T=300, D=256, DH=64, bias="none")
+    I = make_inputs(sp, seed=4, router_zero=True)
+    g, r = _route(I, sp), run_oracle(I, tokens=[])
+    _check_route(g, r)
+    assert g["uncertified"] == sp.T
+    assert (g["expert_indices"] == np.arange(sp.top_k)).all()
+    assert abs(float(g["aux_loss"][0]) - 1.0) <= 1e-6
+
+
+def test_bf16_near_ties_are_decided_exactly():
+    """Router columns 0 and 1 differ in one element by one bf16 ulp of its smallest entry,
+    so the tokens that rank both of them near the top have gaps far below the float32
+    accumulation error; the fallback must decide them as the exact logits do."""
+    sp = spec("mixtral_swiglu_bf16", T=2000, D=1024, DH=64, E=8, top_k=2)
+    I = make_inputs(sp, seed=6)
+    w = I.w_router.copy()
+    w[:, 1] = w[:, 0]
+    vals = np.abs(I.values("w_router")[:, 0])
+    d = int(np.argmin(np.where(vals > 0, vals, np.inf)))
+    w[d, 1] = w[d, 0] + 1  # the next bf16 magnitude: one ulp of a tiny weight
+    I.w_router = w
+    g, r = _route(I, sp), run_oracle(I, tokens=[])
+    _check_route(g, r)
+    both = (np.sort(r["expert_indices"], axis=1)[:, :2] == [0, 1]).all(axis=1)
+    assert both.sum() > 10 and g["uncertified"] >= both.sum()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_uncertified_tokens_are_rare(name):
+    """On the pages' workloads only a small share of tokens needs the float64 recompute."""
+    sp = spec(name)
+    I = make_inputs(sp)
+    g = _route(I, sp)
+    r = run_oracle(I, tokens=[])
+    _check_route(g, r)
+    _say(f"  {name}: {g['uncertified']} of {sp.T} tokens recomputed in float64")
+    assert g["uncertified"] <= 0.05 * sp.T
