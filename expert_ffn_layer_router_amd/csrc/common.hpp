@@ -14,7 +14,7 @@ constexpr int kMaxExperts = 256;
 
 // Tokens per block of the routing kernel; the per-block partial sums of the
 // router probabilities and the per-block expert counts are indexed by it.
-constexpr int kRouteTokensPerBlock = 32;
+constexpr int kRouteTokensPerBlock = 16;
 // Tokens per block of the dispatch count/rank kernel (4 waves, one token per lane).
 constexpr int kDispatchTokensPerBlock = 256;
 

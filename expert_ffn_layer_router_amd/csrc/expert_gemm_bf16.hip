@@ -14,25 +14,27 @@
 //    Each thread loads an 8 (K) x 8 (N) block with eight 16-byte loads, transposes it in
 //    registers and writes eight 16-byte K-runs, so every wave then reads its MFMA B operands
 //    with conflict-free ds_read_b128 (row stride 144 bytes).
-//  * BK = 64 per stage (K % 64 == 0 is required); A is double-buffered in registers and B
+//  * BK = 64 per stage (K % 128 == 0 is required); A is double-buffered in registers and B
 //    in LDS, so the global loads of stage s+1 are in flight while stage s computes. Loads
 //    are never masked: rows and columns past the tile read valid memory whose results are
 //    never stored.
 //  * SwiGLU: the 256 columns interleave 16-column tiles of W1 and W3 for the same 128
 //    output columns, so each lane holds the gate and the up value of the same output and the
 //    epilogue silu(gate) * up needs no data exchange.
-//  * Tile order: M-tiles fastest, so the tiles of one expert that share a weight column block
-//    are adjacent, and blockIdx is remapped so each XCD (blocks b with the same b % 8) works
-//    on a contiguous range of that order and shares its weight tiles in its own L2.
+//  * Tile order: expert by expert, in blocks of (that expert's M-tiles) x 8 column tiles with
+//    the M-tiles fastest; blockIdx is remapped so each XCD (blocks b with the same b % 8)
+//    works through a contiguous range of that order. The ~32 tiles an XCD runs at once then
+//    share a few activation row blocks and a few weight column blocks in its own L2.
 #include "common.hpp"
 #include "tile_schedule.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = 256, kBK = 64;
 constexpr int kLds = kBK + 8;  // elements per LDS column (144 bytes)
 constexpr int kThreads = 256;
+constexpr int kTileBlockN = 8;  // column tiles per L2-sharing block of one expert
 
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return (a & 0xffffu) | (b << 16);
@@ -104,50 +106,61 @@ __device__ __forceinline__ bf16x8 read_b(const uint16_t* sb, int c, int t, int l
   return *(const bf16x8*)&sb[(32 * c + (lane & 31)) * kLds + 16 * t + 8 * (lane >> 5)];
 }
 
-__device__ __forceinline__ void read_bs(const uint16_t* sb, int t, int lane, bf16x8 (&b)[8]) {
+template <int NTW>
+__device__ __forceinline__ void read_bs(const uint16_t* sb, int t, int lane, bf16x8 (&b)[NTW]) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = read_b(sb, c, t, lane);
+  for (int c = 0; c < NTW; ++c) b[c] = read_b(sb, c, t, lane);
 }
 
-__device__ __forceinline__ void mfma_step(const uint4 (&ra)[2][4], int t, const bf16x8 (&b)[8],
-                                          f32x16 (&acc)[2][8]) {
+template <int NTW>
+__device__ __forceinline__ void mfma_step(const uint4 (&ra)[2][4], int t, const bf16x8 (&b)[NTW],
+                                          f32x16 (&acc)[2][NTW]) {
   const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[0][t]);
   const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[1][t]);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < NTW; ++c) {
     acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
     acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
   }
 }
 
-// 4 k-steps of 16, each 2 row tiles x 8 column tiles of v_mfma_f32_32x32x16_bf16. The 8 B
-// operands of k-step t+1 are read from LDS while the 16 MFMAs of k-step t run.
+// 4 k-steps of 16, each 2 row tiles x NTW column tiles of v_mfma_f32_32x32x16_bf16. The B
+// operands of k-step t+1 are read from LDS while the MFMAs of k-step t run; scheduling
+// fences keep the compiler from sinking those reads next to their uses.
+template <int NTW>
 __device__ __forceinline__ void compute_stage(const uint16_t* sb, const uint4 (&ra)[2][4],
-                                              int lane, f32x16 (&acc)[2][8]) {
-  bf16x8 b0[8], b1[8];
-  read_bs(sb, 0, lane, b0);
-  read_bs(sb, 1, lane, b1);
-  mfma_step(ra, 0, b0, acc);
-  read_bs(sb, 2, lane, b0);
-  mfma_step(ra, 1, b1, acc);
-  read_bs(sb, 3, lane, b1);
-  mfma_step(ra, 2, b0, acc);
-  mfma_step(ra, 3, b1, acc);
+                                              int lane, f32x16 (&acc)[2][NTW]) {
+  bf16x8 b0[NTW], b1[NTW];
+  read_bs<NTW>(sb, 0, lane, b0);
+  __builtin_amdgcn_sched_barrier(0);
+  read_bs<NTW>(sb, 1, lane, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step<NTW>(ra, 0, b0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_bs<NTW>(sb, 2, lane, b0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step<NTW>(ra, 1, b1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  read_bs<NTW>(sb, 3, lane, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step<NTW>(ra, 2, b0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_step<NTW>(ra, 3, b1, acc);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const GroupedGemm g,
-                                                                    int mt_max) {
+// NTW = column tiles of 32 per wave: 8 gives 256 x 256 tiles at one block per CU, 4 gives
+// 256 x 128 tiles with two blocks per CU (each wave hides the other's LDS latency).
+template <int EPI, int NTW>
+__global__ __launch_bounds__(kThreads, 8 / NTW) void gemm_bf16_256_kernel(const GroupedGemm g,
+                                                                          int nt) {
   constexpr bool kSwiGLU = EPI == EPI_SWIGLU;
+  constexpr int kBN = 32 * NTW;
   __shared__ __align__(16) uint16_t sB[2][kBN * kLds];
 
   // XCD-aware order: XCD x (= blockIdx % 8) takes the x-th contiguous eighth of the tiles.
-  const int G = gridDim.x;  // a multiple of 8
   const int b = blockIdx.x;
-  const int L = (b & 7) * (G >> 3) + (b >> 3);
-  const int m_tile = L % mt_max, n_tile = L / mt_max;
-  int e, row0, rows;
-  if (!find_tile(g.offsets, g.E, kBM, m_tile, e, row0, rows)) return;
+  int e, row0, rows, n_tile;
+  if (!find_tile_2d(g.offsets, g.E, kBM, nt, kTileBlockN, b, e, row0, rows, n_tile)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t K = g.K, N = g.N;
@@ -169,19 +182,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     aoff[mi] = (uint32_t)((src * g.lda + koff) * 2);
   }
 
-  // B: thread -> (8-column block cb of the 256 tile columns, 8-row group kq of the stage)
+  // B: thread -> (8-column block cb of the tile columns, 8-row group kq of the stage). With
+  // 128-column tiles the upper 128 threads load a copy of the lower half's blocks (so every
+  // thread issues the same loads and the wait counts stay static) and do not store them.
   const int cb = tid >> 3, kq = tid & 7;
+  const bool b_loader = cb < kBN / 8;
   BLoader bl;
   {
     int64_t col;
     const uint16_t* Wm;
+    const int cbl = cb % (kBN / 8);
     if (kSwiGLU) {
-      const int c = cb >> 2;  // tile column block of 32: even -> W1, odd -> W3
+      const int c = cbl >> 2;  // tile column block of 32: even -> W1, odd -> W3
       Wm = (const uint16_t*)((c & 1) ? g.B1 : g.B0);
-      col = n0 + 32 * (c >> 1) + 8 * (cb & 3);
+      col = n0 + 32 * (c >> 1) + 8 * (cbl & 3);
     } else {
       Wm = (const uint16_t*)g.B0;
-      col = n0 + 8 * cb;
+      col = n0 + 8 * cbl;
     }
     bl.base = (const char*)(Wm + (int64_t)e * K * N);
     bl.col_off = (uint32_t)((col < N ? col : 0) * 2);
@@ -190,48 +207,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     bl.kq = kq;
   }
 
-  f32x16 acc[2][8];
+  f32x16 acc[2][NTW];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < NTW; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][c][v] = 0.f;
 
-  const bool active = 64 * wv < rows;  // this wave has rows to compute
-  const int nst = (int)(K / kBK);
+  const bool active = 64 * wv < rows;  // this wave has rows to store
+  const int nst = (int)(K / kBK);       // even: K % (2 * kBK) == 0 is required
   uint4 ra0[2][4], ra1[2][4], rb[8];
 
   load_a(abase, aoff, 0, ra0);
   load_b(bl, 0, rb);
-  store_b(sB[0], cb, kq, rb);
+  if (b_loader) store_b(sB[0], cb, kq, rb);
   __syncthreads();
 
   // Stage s computes from registers ra(s%2) and LDS buffer s%2 while the loads of stage s+1
-  // are in flight; B of stage s+1 then goes to the other LDS buffer. The loop body has no
-  // conditional loads, so the wait before each compute covers only that stage's operands.
-  int s = 0;
-  for (; s + 2 < nst; s += 2) {
-    load_a(abase, aoff, (int64_t)(s + 1) * kBK, ra1);
-    load_b(bl, (int64_t)(s + 1) * kBK, rb);
-    if (active) compute_stage(sB[0], ra0, lane, acc);
-    store_b(sB[1], cb, kq, rb);
+  // are in flight; B of stage s+1 then goes to the other LDS buffer. Every iteration is the
+  // same (no tail, no conditional loads), so each wait covers exactly the operands it needs;
+  // the prefetch past the last stage re-reads the last stage (valid memory) and is unused.
+  // Every wave computes, including waves whose rows are all past the tile (their results are
+  // not stored): a branch around the MFMAs would make the compiler copy accumulators.
+  for (int s = 0; s < nst; s += 2) {
+    const int64_t k1 = (int64_t)(s + 1) * kBK;
+    const int64_t k2 = (int64_t)min(s + 2, nst - 1) * kBK;
+    load_a(abase, aoff, k1, ra1);
+    load_b(bl, k1, rb);
+    compute_stage<NTW>(sB[0], ra0, lane, acc);
+    if (b_loader) store_b(sB[1], cb, kq, rb);
     __syncthreads();
-    load_a(abase, aoff, (int64_t)(s + 2) * kBK, ra0);
-    load_b(bl, (int64_t)(s + 2) * kBK, rb);
-    if (active) compute_stage(sB[1], ra1, lane, acc);
-    store_b(sB[0], cb, kq, rb);
+    load_a(abase, aoff, k2, ra0);
+    load_b(bl, k2, rb);
+    compute_stage<NTW>(sB[1], ra1, lane, acc);
+    if (b_loader) store_b(sB[0], cb, kq, rb);
     __syncthreads();
-  }
-  if (s + 1 < nst) {  // two stages left
-    load_a(abase, aoff, (int64_t)(s + 1) * kBK, ra1);
-    load_b(bl, (int64_t)(s + 1) * kBK, rb);
-    if (active) compute_stage(sB[0], ra0, lane, acc);
-    store_b(sB[1], cb, kq, rb);
-    __syncthreads();
-    if (active) compute_stage(sB[1], ra1, lane, acc);
-  } else if (active) {  // one stage left
-    compute_stage(sB[0], ra0, lane, acc);
   }
 
   if (!active) return;
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       uint16_t* crow = C + (int64_t)(row0 + r) * N;
       if (kSwiGLU) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < NTW / 2; ++q) {
           const int64_t col = n0 + 32 * q + (lane & 31);
           if (col < N) {
             const float gt = acc[mi][2 * q][v], up = acc[mi][2 * q + 1][v];
@@ -255,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < NTW; ++c) {
           const int64_t col = n0 + 32 * c + (lane & 31);
           if (col < N) {
             float val = acc[mi][c][v];
@@ -267,9 +278,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     }
 }
 
-}  // namespace
-
-hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s) {
+template <int NTW>
+hipError_t launch_ntw(const GroupedGemm& g, hipStream_t s) {
+  constexpr int kBN = 32 * NTW;
   const int64_t mt_max = (g.max_rows + kBM - 1) / kBM + g.E;
   const int64_t cols = (g.epilogue == EPI_SWIGLU) ? kBN / 2 : kBN;
   const int64_t nt = (g.N + cols - 1) / cols;
@@ -278,19 +289,25 @@ hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s) {
   const dim3 grid((unsigned)G);
   switch (g.epilogue) {
     case EPI_NONE:
-      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_NONE>, grid, dim3(kThreads), 0, s, g,
-                         (int)mt_max);
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI_NONE, NTW>), grid, dim3(kThreads), 0, s, g,
+                         (int)nt);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s, g,
-                         (int)mt_max);
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI_RELU, NTW>), grid, dim3(kThreads), 0, s, g,
+                         (int)nt);
       break;
     default:
-      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s, g,
-                         (int)mt_max);
+      hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI_SWIGLU, NTW>), grid, dim3(kThreads), 0, s, g,
+                         (int)nt);
       break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s) {
+  return launch_ntw<8>(g, s);
 }
 
 }  // namespace moe

@@ -57,115 +57,129 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-template <typename TIn>
+template <typename TIn, int EPL>
 __device__ __forceinline__ void logits_f64(const TIn* __restrict__ x, const TIn* __restrict__ w,
-                                           int64_t t, int64_t D, int E, double lg[kEPL]) {
+                                           int64_t t, int64_t D, int E, double lg[EPL]) {
   const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) lg[i] = 0.0;
+  for (int i = 0; i < EPL; ++i) lg[i] = 0.0;
   const TIn* xr = x + t * D;
   for (int64_t d = 0; d < D; ++d) {
     const double xv = load_as_f64(xr, d);
     const TIn* wr = w + d * E;
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const int e = lane + kWave * i;
       if (e < E) lg[i] = fma(xv, load_as_f64(wr, e), lg[i]);
     }
   }
 }
 
-// Exact-product float64 logits of one bf16 token from the transposed router (E, D).
-// Experts go in groups of 8: lane l works on expert 8g + l % 8 over the D-slices
-// c = l / 8 (mod 8), with independent 16-byte loads, and the 8 slice sums of an expert
-// are combined with three xor-shuffles (a fixed order).
-__device__ __forceinline__ void logits_f64_bf16_rows(const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ wt, int64_t t,
-                                                     int64_t D, int E, double lg[kEPL]) {
-  const int lane = lane_id();
-  const uint4* xr = (const uint4*)(x + t * D);
-  const int64_t nc = D / 8;
+__device__ __forceinline__ double dot8_f64(const uint4& xv, const uint4& wv) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  double a = 0.0, b = 0.0;
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) lg[i] = 0.0;
-  for (int g = 0; g < (E + 7) / 8; ++g) {
-    const int e = 8 * g + (lane & 7);
-    double a0 = 0.0, a1 = 0.0;
-    if (e < E) {
-      const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
-#pragma unroll 4
-      for (int64_t c = lane >> 3; c < nc; c += 8) {
-        const uint4 xv = xr[c], wv = wr[c];
-        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-        const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          a0 = fma((double)__uint_as_float(xw[q] << 16), (double)__uint_as_float(ww[q] << 16), a0);
-          a1 = fma((double)__uint_as_float(xw[q] & 0xffff0000u),
-                   (double)__uint_as_float(ww[q] & 0xffff0000u), a1);
-        }
-      }
-    }
-    double v = a0 + a1;
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    // lanes with l % 8 == e % 8 now hold expert 8g + l % 8; hand each to its owner lane
-#pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
-      const int mine = lane + kWave * i;
-      const double got = __shfl(v, mine & 7);
-      if ((mine >> 3) == g) lg[i] = got;
-    }
+  for (int q = 0; q < 4; ++q) {
+    a = fma((double)__uint_as_float(xw[q] << 16), (double)__uint_as_float(ww[q] << 16), a);
+    b = fma((double)__uint_as_float(xw[q] & 0xffff0000u),
+            (double)__uint_as_float(ww[q] & 0xffff0000u), b);
   }
+  return a + b;
 }
 
 // Exact-product float64 logits of the k chosen experts of one bf16 token (gates need the
 // differences of these to ~1e-7 absolute, which a float32 partial cannot carry when the
-// logits are large): the wave splits D, each lane summing 8-element slices in float64.
+// logits are large). Up to kCG experts per pass over D: each lane takes 16-byte slices
+// c = lane (mod 64) of x and of the kCG weight rows, all loads of a pass in flight at once.
+constexpr int kCG = 4;  // chosen experts per pass over D
+
+template <int EPL>
 __device__ __forceinline__ void chosen_logits_f64(const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ wt,
                                                   const float* __restrict__ bias, int64_t t,
-                                                  int64_t D, int k, const int my_e[kEPL],
-                                                  double my_v[kEPL]) {
+                                                  int64_t D, int k, const int my_e[EPL],
+                                                  double my_v[EPL]) {
   const int lane = lane_id();
   const uint4* xr = (const uint4*)(x + t * D);
-  for (int j = 0; j < k; ++j) {
-    int e = 0;
+  const int64_t nc = D / 8;
+  for (int j0 = 0; j0 < k; j0 += kCG) {
+    const int nj = min(kCG, k - j0);
+    const uint4* wr[kCG];
+    int ev[kCG];
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i)
-      if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
-    const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
-    double a0 = 0.0, a1 = 0.0;
-#pragma unroll 4
-    for (int64_t c = lane; c < D / 8; c += kWave) {
-      const uint4 xv = xr[c], wv = wr[c];
-      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-      const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+    for (int jj = 0; jj < kCG; ++jj) {
+      const int j = j0 + (jj < nj ? jj : 0);
+      int e = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0 = fma((double)__uint_as_float(xw[q] << 16), (double)__uint_as_float(ww[q] << 16), a0);
-        a1 = fma((double)__uint_as_float(xw[q] & 0xffff0000u),
-                 (double)__uint_as_float(ww[q] & 0xffff0000u), a1);
-      }
+      for (int i = 0; i < EPL; ++i)
+        if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
+      ev[jj] = e;
+      wr[jj] = (const uint4*)(wt + (int64_t)e * D);
     }
-    double v = wave_sum(a0 + a1);
-    if (bias) v += (double)bias[e];
+    double acc[kCG];
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i)
-      if (j == lane + kWave * i) my_v[i] = v;
+    for (int jj = 0; jj < kCG; ++jj) acc[jj] = 0.0;
+#pragma unroll 2
+    for (int64_t c = lane; c < nc; c += kWave) {
+      const uint4 xv = xr[c];
+      uint4 wv[kCG];
+#pragma unroll
+      for (int jj = 0; jj < kCG; ++jj) wv[jj] = wr[jj][c];  // duplicates of row j0 past nj
+#pragma unroll
+      for (int jj = 0; jj < kCG; ++jj) acc[jj] += dot8_f64(xv, wv[jj]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < kCG; ++jj) {
+      if (jj >= nj) break;
+      double v = wave_sum(acc[jj]);
+      if (bias) v += (double)bias[ev[jj]];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (j0 + jj == lane + kWave * i) my_v[i] = v;
+    }
   }
+}
+
+// Exact-product float64 logits of all E experts of one bf16 token, computed by a whole
+// 1024-thread block (thread i: expert i / P over the 16-byte slices i % P (mod P)), then
+// summed over the P slices in order. Result in s_out[0..E).
+__device__ __forceinline__ void block_logits_f64(const uint16_t* __restrict__ x,
+                                                 const uint16_t* __restrict__ wt, int64_t t,
+                                                 int64_t D, int E, double* s_red,
+                                                 double* s_out) {
+  int NE = 1;
+  while (NE < E) NE <<= 1;
+  const int P = 1024 / NE;
+  const int i = threadIdx.x, p = i % P, e = i / P;
+  const uint4* xr = (const uint4*)(x + t * D);
+  double acc = 0.0;
+  if (e < E) {
+    const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
+#pragma unroll 4
+    for (int64_t c = p; c < D / 8; c += P) acc += dot8_f64(xr[c], wr[c]);
+  }
+  s_red[i] = acc;
+  __syncthreads();
+  if (i < E) {
+    double v = 0.0;
+    for (int q = 0; q < P; ++q) v += s_red[i * P + q];
+    s_out[i] = v;
+  }
+  __syncthreads();
 }
 
 // k rounds of a wave-wide argmax over the not-yet-chosen experts: larger logit first,
 // equal logits -> smaller expert index. Lane j (+64i) keeps the j-th choice. When
 // `want_gap`, one more round finds the best unchosen logit, and the smallest difference
 // between consecutive values of the chosen sequence (extended by that one) is returned.
-__device__ __forceinline__ double topk_rounds(int E, int k, const double lg[kEPL], bool sel[kEPL],
-                                              double my_v[kEPL], int my_e[kEPL],
+template <int EPL>
+__device__ __forceinline__ double topk_rounds(int E, int k, const double lg[EPL], bool sel[EPL],
+                                              double my_v[EPL], int my_e[EPL],
                                               bool want_gap) {
   const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     sel[i] = false;
     my_v[i] = 0.0;
     my_e[i] = 0;
@@ -176,7 +190,7 @@ __device__ __forceinline__ double topk_rounds(int E, int k, const double lg[kEPL
     double bv = -DBL_MAX;
     int be = INT_MAX;
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const int e = lane + kWave * i;
       if (e < E && !sel[i] && (lg[i] > bv || (lg[i] == bv && e < be))) {
         bv = lg[i];
@@ -196,7 +210,7 @@ __device__ __forceinline__ double topk_rounds(int E, int k, const double lg[kEPL
     prev = bv;
     if (j == k) break;  // the extra round only measures the boundary gap
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       if (be == lane + kWave * i) sel[i] = true;
       if (j == lane + kWave * i) {
         my_v[i] = bv;
@@ -208,37 +222,38 @@ __device__ __forceinline__ double topk_rounds(int E, int k, const double lg[kEPL
 }
 
 // Probabilities over all experts (returned in prob[]), and the index/gate rows.
-__device__ __forceinline__ void finish_token(int E, int k, int64_t t, const double lg[kEPL],
-                                             const double my_v[kEPL], const int my_e[kEPL],
-                                             double prob[kEPL], int32_t* __restrict__ idx,
+template <int EPL>
+__device__ __forceinline__ void finish_token(int E, int k, int64_t t, const double lg[EPL],
+                                             const double my_v[EPL], const int my_e[EPL],
+                                             double prob[EPL], int32_t* __restrict__ idx,
                                              float* __restrict__ gates) {
   const int lane = lane_id();
   double m = -DBL_MAX;
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i)
+  for (int i = 0; i < EPL; ++i)
     if (lane + kWave * i < E) m = fmax(m, lg[i]);
   m = wave_max(m);
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     prob[i] = (lane + kWave * i < E) ? exp(lg[i] - m) : 0.0;
     s += prob[i];
   }
   s = wave_sum(s);
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) prob[i] /= s;
+  for (int i = 0; i < EPL; ++i) prob[i] /= s;
   // gates: softmax over the chosen logits, shifted by the first (largest) of them
   const double v0 = __shfl(my_v[0], 0);
-  double ev[kEPL];
+  double ev[EPL];
   double gs = 0.0;
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     ev[i] = (lane + kWave * i < k) ? exp(my_v[i] - v0) : 0.0;
     gs += ev[i];
   }
   gs = wave_sum(gs);
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     const int j = lane + kWave * i;
     if (j < k) {
       idx[t * k + j] = my_e[i];
@@ -248,42 +263,44 @@ __device__ __forceinline__ void finish_token(int E, int k, int64_t t, const doub
 }
 
 // Per-block partials of sum_t probs[t, e] and of the expert counts, in fixed order.
+template <int EPL>
 struct BlockPartials {
-  double psum[kEPL];
-  int cnt[kEPL];
+  double psum[EPL];
+  int cnt[EPL];
   __device__ void zero() {
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       psum[i] = 0.0;
       cnt[i] = 0;
     }
   }
-  __device__ void add(const double prob[kEPL], const bool sel[kEPL]) {
+  __device__ void add(const double prob[EPL], const bool sel[EPL]) {
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       psum[i] += prob[i];
       cnt[i] += sel[i] ? 1 : 0;
     }
   }
 };
 
-__device__ __forceinline__ void write_block_partials(const BlockPartials& bp, int E,
+template <int WAVES, int EPL>
+__device__ __forceinline__ void write_block_partials(const BlockPartials<EPL>& bp, int E,
                                                      double* __restrict__ psum_blk,
                                                      int32_t* __restrict__ count_blk) {
-  __shared__ double s_psum[kRouteWaves][kMaxExperts];
-  __shared__ int s_cnt[kRouteWaves][kMaxExperts];
+  __shared__ double s_psum[WAVES][kMaxExperts];
+  __shared__ int s_cnt[WAVES][kMaxExperts];
   const int wv = wave_id(), lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     s_psum[wv][lane + kWave * i] = bp.psum[i];
     s_cnt[wv][lane + kWave * i] = bp.cnt[i];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+  for (int e = threadIdx.x; e < E; e += WAVES * kWave) {
     double a = 0.0;
     int c = 0;
 #pragma unroll
-    for (int q = 0; q < kRouteWaves; ++q) {
+    for (int q = 0; q < WAVES; ++q) {
       a += s_psum[q][e];
       c += s_cnt[q][e];
     }
@@ -292,22 +309,24 @@ __device__ __forceinline__ void write_block_partials(const BlockPartials& bp, in
   }
 }
 
-__device__ __forceinline__ void add_bias(const float* __restrict__ bias, int E, double lg[kEPL]) {
+template <int EPL>
+__device__ __forceinline__ void add_bias(const float* __restrict__ bias, int E, double lg[EPL]) {
   if (!bias) return;
   const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     const int e = lane + kWave * i;
     if (e < E) lg[i] += (double)bias[e];
   }
 }
 
+template <int EPL>
 __device__ __forceinline__ void write_logits(float* __restrict__ logits_out, int64_t t, int E,
-                                             const double lg[kEPL]) {
+                                             const double lg[EPL]) {
   if (!logits_out) return;
   const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < kEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     const int e = lane + kWave * i;
     if (e < E) logits_out[t * E + e] = (float)lg[i];
   }
@@ -315,29 +334,29 @@ __device__ __forceinline__ void write_logits(float* __restrict__ logits_out, int
 
 // ---- float32 layers -----------------------------------------------------------------------
 
-template <typename TIn>
+template <typename TIn, int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
     int64_t T, int64_t D, int E, int k, const TIn* __restrict__ x, const TIn* __restrict__ w,
     const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ gates,
     float* __restrict__ logits_out, double* __restrict__ psum_blk,
     int32_t* __restrict__ count_blk) {
-  BlockPartials bp;
+  BlockPartials<EPL> bp;
   bp.zero();
   const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
   for (int q = wave_id(); q < kRouteTokensPerBlock; q += kRouteWaves) {
     const int64_t t = t0 + q;
     if (t >= T) break;
-    double lg[kEPL], prob[kEPL], my_v[kEPL];
-    int my_e[kEPL];
-    bool sel[kEPL];
-    logits_f64(x, w, t, D, E, lg);
-    add_bias(bias, E, lg);
-    write_logits(logits_out, t, E, lg);
-    topk_rounds(E, k, lg, sel, my_v, my_e, false);
-    finish_token(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    double lg[EPL], prob[EPL], my_v[EPL];
+    int my_e[EPL];
+    bool sel[EPL];
+    logits_f64<TIn, EPL>(x, w, t, D, E, lg);
+    add_bias<EPL>(bias, E, lg);
+    write_logits<EPL>(logits_out, t, E, lg);
+    topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);
+    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
     bp.add(prob, sel);
   }
-  write_block_partials(bp, E, psum_blk, count_blk);
+  write_block_partials<kRouteWaves, EPL>(bp, E, psum_blk, count_blk);
 }
 
 // ---- bfloat16 layers ----------------------------------------------------------------------
@@ -449,60 +468,64 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
   if (lane < 16 && row_ok) xsq[(int64_t)s * T + row] = xs;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_select_kernel(
+constexpr int kSelWaves = kRouteTokensPerBlock;  // one token per wave
+constexpr int kSelThreads = kSelWaves * kWave;
+
+template <int EPL>
+__global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     int64_t T, int64_t D, int E, int k, int S, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wt, const double* __restrict__ wnorm,
     const float* __restrict__ part, const float* __restrict__ xsq, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ gates, float* __restrict__ logits_out,
     double* __restrict__ psum_blk, int32_t* __restrict__ count_blk, int32_t* __restrict__ nflag) {
-  const int lane = lane_id();
+  __shared__ int s_flag[kSelWaves];
+  __shared__ double s_red[kSelThreads];
+  __shared__ double s_lg[kMaxExperts];
+  const int lane = lane_id(), wv = wave_id();
+  const int64_t t = (int64_t)blockIdx.x * kRouteTokensPerBlock + wv;
+  const bool valid = t < T;
   double wmax = 0.0;
   for (int e = 0; e < E; ++e) wmax = fmax(wmax, wnorm[e]);
-  BlockPartials bp;
-  bp.zero();
-  int flagged = 0;
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
-  for (int q = wave_id(); q < kRouteTokensPerBlock; q += kRouteWaves) {
-    const int64_t t = t0 + q;
-    if (t >= T) break;
-    double lg[kEPL], prob[kEPL], my_v[kEPL];
-    int my_e[kEPL];
-    bool sel[kEPL];
-    double rnd = 0.0, xn2 = 0.0, ab[kEPL];
+
+  double lg[EPL], prob[EPL], my_v[EPL];
+  int my_e[EPL];
+  bool sel[EPL];
+  bool flagged = false;
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) {
-      lg[i] = 0.0;
-      ab[i] = 0.0;
-    }
-    // partials in split order; 8 splits' loads issued together
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      float pv[8][kEPL], xv[8];
+  for (int i = 0; i < EPL; ++i) lg[i] = 0.0;
+  if (valid) {
+    double rnd = 0.0, xn2 = 0.0, ab[EPL];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+    for (int i = 0; i < EPL; ++i) ab[i] = 0.0;
+    // partials in split order; 4 splits' loads issued together
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float pv[4][EPL], xv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
         const bool ok = s0 + q < S;
         xv[q] = ok ? xsq[(int64_t)(s0 + q) * T + t] : 0.f;
 #pragma unroll
-        for (int i = 0; i < kEPL; ++i) {
+        for (int i = 0; i < EPL; ++i) {
           const int e = lane + kWave * i;
           pv[q][i] = (ok && e < E) ? part[((int64_t)(s0 + q) * T + t) * E + e] : 0.f;
         }
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < 4; ++q) {
         xn2 += (double)xv[q];
 #pragma unroll
-        for (int i = 0; i < kEPL; ++i) {
+        for (int i = 0; i < EPL; ++i) {
           lg[i] += (double)pv[q][i];
           ab[i] += fabs((double)pv[q][i]);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i) rnd = fmax(rnd, ab[i]);
-    add_bias(bias, E, lg);
+    for (int i = 0; i < EPL; ++i) rnd = fmax(rnd, ab[i]);
+    add_bias<EPL>(bias, E, lg);
     double lmax = 0.0;
 #pragma unroll
-    for (int i = 0; i < kEPL; ++i)
+    for (int i = 0; i < EPL; ++i)
       if (lane + kWave * i < E) lmax = fmax(lmax, fabs(lg[i]));
     rnd = wave_max(rnd);
     lmax = wave_max(lmax);
@@ -512,56 +535,94 @@ __global__ __launch_bounds__(kRouteThreads) void route_select_kernel(
     const double gamma = 32.0 * 0x1p-23;
     const double B = gamma * sqrt(xn2 * (1.0 + (double)D * 0x1p-23)) * wmax * (1.0 + 1e-6) +
                      rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30;
-    const double gap = topk_rounds(E, k, lg, sel, my_v, my_e, true);
-    if (!(gap > 2.0 * B)) {
-      ++flagged;
-      logits_f64_bf16_rows(x, wt, t, D, E, lg);
-      add_bias(bias, E, lg);
-      topk_rounds(E, k, lg, sel, my_v, my_e, false);
-    } else {
-      chosen_logits_f64(x, wt, bias, t, D, k, my_e, my_v);
+    const double gap = topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, true);
+    flagged = !(gap > 2.0 * B);
+    if (!flagged) chosen_logits_f64<EPL>(x, wt, bias, t, D, k, my_e, my_v);
+  }
+  if (lane == 0) s_flag[wv] = flagged ? 1 : 0;
+  __syncthreads();
+  // uncertified tokens: the whole block recomputes their logits exactly, one at a time
+  int nfl = 0;
+  for (int w2 = 0; w2 < kSelWaves; ++w2) {
+    if (!s_flag[w2]) continue;  // block-uniform
+    ++nfl;
+    block_logits_f64(x, wt, (int64_t)blockIdx.x * kRouteTokensPerBlock + w2, D, E, s_red, s_lg);
+    if (wv == w2) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        lg[i] = (e < E) ? s_lg[e] : 0.0;
+      }
+      add_bias<EPL>(bias, E, lg);
+      topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);  // chosen values are exact already
     }
-    write_logits(logits_out, t, E, lg);
-    finish_token(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    __syncthreads();
+  }
+  BlockPartials<EPL> bp;
+  bp.zero();
+  if (valid) {
+    write_logits<EPL>(logits_out, t, E, lg);
+    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
     bp.add(prob, sel);
   }
-  write_block_partials(bp, E, psum_blk, count_blk);
-  if (nflag && lane == 0 && flagged) atomicAdd(nflag, flagged);
+  write_block_partials<kSelWaves, EPL>(bp, E, psum_blk, count_blk);
+  if (nflag && threadIdx.x == 0 && nfl) atomicAdd(nflag, nfl);
 }
 
-// aux = E * sum_e (count_e / (T k)) * (sum_t probs[t, e] / T), partials summed in block order.
-__global__ __launch_bounds__(kMaxExperts) void aux_finalize_kernel(
+// aux = E * sum_e (count_e / (T k)) * (sum_t probs[t, e] / T). 1024 threads: thread i sums
+// the blocks b = p (mod P) of expert e = i / P, in block order; the P part sums are then
+// added in order, and the E terms in expert order.
+constexpr int kAuxThreads = 1024;
+
+__global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int64_t nblk, int E, int64_t T, int k, const double* __restrict__ psum_blk,
     const int32_t* __restrict__ count_blk, float* __restrict__ aux,
     int32_t* __restrict__ counts_out) {
+  __shared__ double s_p[kAuxThreads];
+  __shared__ int64_t s_c[kAuxThreads];
   __shared__ double s_term[kMaxExperts];
-  const int e = threadIdx.x;
+  int NE = 1;
+  while (NE < E) NE <<= 1;
+  const int P = kAuxThreads / NE;
+  const int i = threadIdx.x, p = i % P, e = i / P;
+  double pacc = 0.0;
+  int64_t cacc = 0;
   if (e < E) {
-    double P = 0.0;
-    int64_t c = 0;
-    constexpr int kChunk = 16;  // independent loads in flight, summed in block order
-    for (int64_t b0 = 0; b0 < nblk; b0 += kChunk) {
+    constexpr int kChunk = 8;  // independent loads in flight
+    for (int64_t b0 = p; b0 < nblk; b0 += (int64_t)P * kChunk) {
       double pv[kChunk];
       int cv[kChunk];
 #pragma unroll
       for (int q = 0; q < kChunk; ++q) {
-        pv[q] = (b0 + q < nblk) ? psum_blk[(b0 + q) * E + e] : 0.0;
-        cv[q] = (b0 + q < nblk) ? count_blk[(b0 + q) * E + e] : 0;
+        const int64_t b = b0 + (int64_t)q * P;
+        pv[q] = (b < nblk) ? psum_blk[b * E + e] : 0.0;
+        cv[q] = (b < nblk) ? count_blk[b * E + e] : 0;
       }
 #pragma unroll
       for (int q = 0; q < kChunk; ++q) {
-        P += pv[q];
-        c += cv[q];
+        pacc += pv[q];
+        cacc += cv[q];
       }
     }
-    if (counts_out) counts_out[e] = (int32_t)c;
-    s_term[e] = (T > 0) ? ((double)c / ((double)T * (double)k)) * (P / (double)T) : 0.0;
+  }
+  s_p[i] = pacc;
+  s_c[i] = cacc;
+  __syncthreads();
+  if (i < E) {
+    double Pe = 0.0;
+    int64_t c = 0;
+    for (int q = 0; q < P; ++q) {
+      Pe += s_p[i * P + q];
+      c += s_c[i * P + q];
+    }
+    if (counts_out) counts_out[i] = (int32_t)c;
+    s_term[i] = (T > 0) ? ((double)c / ((double)T * (double)k)) * (Pe / (double)T) : 0.0;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int q = 0; q < E; ++q) s += s_term[q];
-    *aux = (float)((double)E * s);
+  if (i == 0) {
+    double acc = 0.0;
+    for (int q = 0; q < E; ++q) acc += s_term[q];
+    *aux = (float)((double)E * acc);
   }
 }
 
@@ -631,10 +692,19 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
   const int64_t nblk = route_blocks(p);
   if (uncertified) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, uncertified);
   if (nblk == 0) return hipGetLastError();
+  const int epl = (p.E + kWave - 1) / kWave;
   if (p.dtype != MOE_BF16) {
-    hipLaunchKernelGGL(route_f64_kernel<float>, dim3((unsigned)nblk), dim3(kRouteThreads), 0, s,
-                       p.T, p.D, p.E, p.top_k, (const float*)x, (const float*)w_router, bias, idx,
-                       gates, logits_out, r.psum, r.pcnt);
+#define MOE_ROUTE_F64(EPLV)                                                                      \
+  hipLaunchKernelGGL((route_f64_kernel<float, EPLV>), dim3((unsigned)nblk), dim3(kRouteThreads), \
+                     0, s, p.T, p.D, p.E, p.top_k, (const float*)x, (const float*)w_router, bias, \
+                     idx, gates, logits_out, r.psum, r.pcnt)
+    if (epl <= 1)
+      MOE_ROUTE_F64(1);
+    else if (epl <= 2)
+      MOE_ROUTE_F64(2);
+    else
+      MOE_ROUTE_F64(4);
+#undef MOE_ROUTE_F64
     return hipGetLastError();
   }
   const int S = route_splits(p);
@@ -660,16 +730,24 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
   else
     hipLaunchKernelGGL(route_logits_mfma_kernel<16>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
                        xb, r.wt, r.part, r.xsq);
-  hipLaunchKernelGGL(route_select_kernel, dim3((unsigned)nblk), dim3(kRouteThreads), 0, s, p.T,
-                     p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias, idx, gates,
-                     logits_out, r.psum, r.pcnt, uncertified);
+#define MOE_ROUTE_SELECT(EPLV)                                                                 \
+  hipLaunchKernelGGL((route_select_kernel<EPLV>), dim3((unsigned)nblk), dim3(kSelThreads), 0, s, \
+                     p.T, p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias, idx,     \
+                     gates, logits_out, r.psum, r.pcnt, uncertified)
+  if (epl <= 1)
+    MOE_ROUTE_SELECT(1);
+  else if (epl <= 2)
+    MOE_ROUTE_SELECT(2);
+  else
+    MOE_ROUTE_SELECT(4);
+#undef MOE_ROUTE_SELECT
   return hipGetLastError();
 }
 
 hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* counts_out,
                                hipStream_t s) {
   const RouteScratch r = route_scratch(p, ws);
-  hipLaunchKernelGGL(aux_finalize_kernel, dim3(1), dim3(kMaxExperts), 0, s, route_blocks(p), p.E,
+  hipLaunchKernelGGL(aux_finalize_kernel, dim3(1), dim3(kAuxThreads), 0, s, route_blocks(p), p.E,
                      p.T, p.top_k, r.psum, r.pcnt, aux, counts_out);
   return hipGetLastError();
 }
