@@ -30,6 +30,55 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector
 
 
+# HBM traffic of the expert up-projection GEMM, per launch, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE, KiB summed over the launch) over this same command. Each
+# counter is divided by what it reads per byte for a plain device copy of known size
+# (--copy-calibration-mib): FETCH_SIZE reads 0.500 KiB per KiB copied, WRITE_SIZE 1.000.
+# The figures hold only for the kernel sources whose hash is given; once those change
+# the field is reported as null until the counters are taken again.
+GEMM_SOURCES = ("expert_ffn_layer_router_amd/csrc/expert_gemm_bf16.hip",
+                "expert_ffn_layer_router_amd/csrc/tile_schedule.hpp",
+                "expert_ffn_layer_router_amd/csrc/common.hpp")
+FETCH_PER_BYTE = 0.500
+WRITE_PER_BYTE = 1.000
+MEASURED_TRAFFIC = {
+    # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
+    "mixtral_swiglu_bf16": ("2a6a9f6f02154555afc3f302237e929073062c35edfad44322cf3e66fbeca349",
+                            2584028.40625, 229376.015625),
+}
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str):
+    rec = MEASURED_TRAFFIC.get(config)
+    if rec is None or rec[0] != gemm_source_hash():
+        return None
+    _, fetch_kib, write_kib = rec
+    return (fetch_kib / FETCH_PER_BYTE + write_kib / WRITE_PER_BYTE) * 1024.0
+
+
+def copy_calibration(mib: int) -> int:
+    """A plain device-to-device copy of `mib` MiB, three times: the known-size kernel that
+    calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+    return 0
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -44,24 +93,29 @@ def device_tensor(a):
     return torch.from_numpy(a).cuda()
 
 
-def cpu_baseline(I, tokens: int) -> dict:
-    """The oracle as it stands, on the first `tokens` tokens of the same inputs."""
-    import numpy as np
+def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4) -> dict:
+    """The oracle as it stands, on the first `tokens` tokens of the same inputs, repeated
+    until at least `min_seconds` of wall time (at most `max_passes` passes)."""
     from threadpoolctl import threadpool_info
 
     import oracle
     sp = I.spec
-    sub = slice(0, tokens)
-    t0 = time.perf_counter()
-    oracle.moe_forward(I.values("x")[sub], I.values("w_router"), sp.top_k, sp.kind,
-                       I.values("w1"), I.values("w2"), I.values("w3"), bias=I.bias,
-                       capacity_factor=sp.capacity_factor)
+    x = I.values("x")[:tokens]
+    wr, w1, w2, w3 = I.values("w_router"), I.values("w1"), I.values("w2"), I.values("w3")
+    passes, t0 = 0, time.perf_counter()
+    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.moe_forward(x, wr, sp.top_k, sp.kind, w1, w2, w3, bias=I.bias,
+                           capacity_factor=sp.capacity_factor)
+        passes += 1
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle.moe_forward (NumPy float64) on the first {tokens} tokens of the "
-                      f"same seeded inputs, all {sp.E} experts' weights widened to float64; "
-                      f"{dt:.1f} s wall"}
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    return {"value": passes * tokens / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"oracle.moe_forward (NumPy float64, BLAS on {threads} threads) over the "
+                      f"first {tokens} of {sp.T} tokens of the same seeded inputs, {passes} "
+                      f"pass(es), {dt:.1f} s wall; each pass widens every expert's weights to "
+                      f"float64 one expert at a time"}
 
 
 def main() -> int:
@@ -71,8 +125,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_swiglu_bf16")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-baseline-tokens", type=int, default=192)
+    ap.add_argument("--cpu-baseline-tokens", type=int, default=0,
+                    help="tokens in the CPU oracle sample (0: the whole batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -80,6 +137,9 @@ def main() -> int:
         print("bench.py measures one MI355X: the layer runs on a single GPU (no sharding, no "
               "collectives), so --gpus must be 1", file=sys.stderr)
         return 2
+
+    if args.copy_calibration_mib > 0:
+        return copy_calibration(args.copy_calibration_mib)
 
     import numpy as np
     import torch
@@ -179,14 +239,14 @@ def main() -> int:
                    "kept_slots": R, "dropped_slots": T * k - R, "used_tokens": used_tokens},
         "roofline": {"kernel": "expert up-projection grouped GEMM (stage expert_up)",
                      "bound": "mfma", "achieved": up_tf, "peak": peak_tf, "unit": "TFLOP/s",
-                     "frac": up_tf / peak_tf, "traffic": None,
+                     "frac": up_tf / peak_tf, "traffic": measured_traffic(sp.name),
                      "algorithmic_flops_per_launch": up_flops,
                      "launch_us": stage_ms["expert_up"] * 1e3,
                      "weight_bytes": up_w},
         "stages": stages,
     }
     if not args.no_cpu_baseline:
-        n = min(args.cpu_baseline_tokens, T)
+        n = min(args.cpu_baseline_tokens, T) if args.cpu_baseline_tokens > 0 else T
         log(f"[bench] CPU oracle baseline on {n} tokens")
         result["cpu_baseline"] = cpu_baseline(I, n)
     print(json.dumps(result), flush=True)
