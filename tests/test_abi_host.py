@@ -139,3 +139,26 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         B._ptr(torch.zeros(4))
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package and its binding import nothing from oracle/ (the oracle is test
+    infrastructure only), checked both on the sources and in a fresh interpreter."""
+    import subprocess
+    import sys
+    pkg = Path(B.__file__).resolve().parent
+    for f in list(pkg.rglob("*.py")) + list(pkg.rglob("*.hip")) + list(pkg.rglob("*.hpp")):
+        text = f.read_text()
+        assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+        assert "oracle/" not in text, f
+    code = ("import sys, expert_ffn_layer_router_amd as m; "
+            "from expert_ffn_layer_router_amd import binding, accounting; binding.lib(); "
+            "assert not any(k == 'oracle' or k.startswith('oracle.') for k in sys.modules)")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=str(pkg.parent))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", tmp_path / "libmoe.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
