@@ -2,250 +2,225 @@
 // layer: each expert runs only on its own rows, ML Grind "Mixture-of-Experts (MoE) Routing",
 // Constraints; SwiGLU and ReLU experts as on the ML Grind and Sparsely-Gated Layer pages).
 //
-// Tiling (one 256-thread block per 256 x 256 output tile, one block per CU):
-//  * 4 waves stacked along M; wave w owns rows 64w .. 64w+63 of the tile and all 256
-//    columns, i.e. 4 x 16 MFMA tiles of 16x16 (v_mfma_f32_16x16x32_bf16) and 256 fp32
-//    accumulators per lane.
-//  * A (activations, K-contiguous rows) goes straight from global memory into the MFMA
-//    operand registers: lane l of m-tile i loads row 16i + l%16, K values 8(l/16)..+7, which
-//    is exactly the operand layout. No LDS, and a row gather (token rows of x through the
-//    dispatch permutation) costs nothing extra.
-//  * B (expert weights, (K, N) row-major, N-contiguous) is shared by the 4 waves through LDS.
-//    Each thread loads an 8 (K) x 8 (N) block with eight 16-byte loads, transposes it in
-//    registers and writes eight 16-byte K-runs, so every wave then reads its MFMA B operands
-//    with conflict-free ds_read_b128 (row stride 144 bytes).
-//  * BK = 64 per stage (K % 128 == 0 is required); A is double-buffered in registers and B
-//    in LDS, so the global loads of stage s+1 are in flight while stage s computes. Loads
-//    are never masked: rows and columns past the tile read valid memory whose results are
-//    never stored.
-//  * SwiGLU: the 256 columns interleave 16-column tiles of W1 and W3 for the same 128
-//    output columns, so each lane holds the gate and the up value of the same output and the
-//    epilogue silu(gate) * up needs no data exchange.
+// One 256-thread block per 256 x 256 output tile, one block per CU; 4 waves stacked along M,
+// wave w owning rows 64w .. 64w+63 and all 256 columns (2 x 8 tiles of
+// v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane).
+//
+// Both operands go from global memory straight into LDS with global_load_lds_dwordx4 (lane l
+// of an instruction writes 16 bytes at the instruction's LDS base + 16 l), one whole 128-byte
+// line per 8 lanes, so the vector L1 only ever sees full-line requests:
+//  * A (activations, 256 rows x 64 K per stage, 128 bytes a row): an instruction fills 8 rows;
+//    16-byte chunk c of row r is stored at chunk c ^ ((r / 2) % 8), which makes the MFMA
+//    operand reads (ds_read_b128: 16 rows x 16 bytes per 16 lanes) conflict-free. A row gather
+//    (token rows of x through the dispatch permutation) is just a per-lane source address.
+//  * B (weights, 64 K-rows x 256 columns per stage, (K, N) row-major, 512 bytes a row): an
+//    instruction fills 2 K-rows; chunk c of K-row k is stored at c ^ (4 (k % 4)), and the MFMA
+//    operands come from transposed reads (ds_read_b64_tr_b16), which turn the N-contiguous
+//    layout into 8 consecutive K values per lane.
+// Two LDS buffers per operand (128 KB): the loads of stage s + 1 run while stage s computes.
+// The loads are issued from inline assembly, so the compiler does not track them; every wait
+// for them is explicit (s_waitcnt vmcnt(0) before the barrier that publishes a stage).
+//  * SwiGLU: the 256 columns interleave 32-column tiles of W1 and W3 for the same 128 output
+//    columns, so each lane holds the gate and the up value of the same output.
 //  * Tile order: expert by expert, in blocks of (that expert's M-tiles) x 8 column tiles with
-//    the M-tiles fastest; blockIdx is remapped so each XCD (blocks b with the same b % 8)
-//    works through a contiguous range of that order. The ~32 tiles an XCD runs at once then
-//    share a few activation row blocks and a few weight column blocks in its own L2.
+//    the M-tiles fastest; each XCD (blocks b with the same b % 8) works through a contiguous
+//    eighth of the real tiles, so the tiles it runs at once share rows and columns in its L2.
 #include "common.hpp"
 #include "tile_schedule.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBM = 256, kBK = 64;
-constexpr int kLds = kBK + 8;  // elements per LDS column (144 bytes)
+constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kTileBlockN = 8;  // column tiles per L2-sharing block of one expert
+constexpr int kTileBlockN = 8;       // column tiles per L2-sharing block of one expert
+constexpr int kSlab = kBK * 256;     // elements of one stage of either operand (32 KB)
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// Global loads as a block-uniform base plus a 32-bit per-lane byte offset, so each load is
-// one instruction with the base in scalar registers (no 64-bit address per lane and load).
-__device__ __forceinline__ uint4 gload(const char* base, uint32_t off) {
-  return *(const uint4*)(base + off);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-__device__ __forceinline__ uint4 select4(bool keep, const uint4& v) {
-  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+// One global_load_lds_dwordx4: 16 bytes per lane from `src` to LDS byte address
+// lds + 16 * lane (lds is wave-uniform). No register receives data, so nothing in the wave
+// depends on it until an explicit s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
 }
 
-struct BLoader {
-  const char* base;  // this expert's weight matrix (block-uniform)
-  uint32_t col_off;  // byte offset of this thread's 8-column block (column 0 if past N)
-  uint32_t row_bytes;
-  int kq;            // 8-row group of K within a stage
-  int64_t K;
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+struct Loader {
+  const char* a[8];  // A source of this lane for instruction j, at K = 0
+  const char* b[2];  // B source of this lane for instructions with j % 2 == q, at K-row 0
+  int64_t b_row_bytes;
 };
 
-// 8 rows (K) x 8 columns (N) of the weight tile for stage k0 (this kernel requires
-// K % 64 == 0). Columns past N read column 0 of the block instead (valid memory; those
-// outputs are never stored), so no load is masked or branched around.
-__device__ __forceinline__ void load_b(const BLoader& bl, int64_t k0, uint4 (&rb)[8]) {
-  const uint32_t o0 = bl.col_off + (uint32_t)(k0 + 8 * bl.kq) * bl.row_bytes;
+__device__ __forceinline__ void load_stage(const Loader& ld, int64_t k0, uint32_t sa, uint32_t sb,
+                                           int wv) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) rb[i] = gload(bl.base, o0 + i * bl.row_bytes);
+  for (int j = 0; j < 8; ++j) dma16(ld.a[j] + k0 * 2, sa + (8 * wv + j) * 1024);
+  const int64_t bk = k0 * ld.b_row_bytes;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sb + (8 * wv + j) * 1024);
 }
 
-// Transposed into LDS: column c of the block gets its 8 K values as one 16-byte run.
-__device__ __forceinline__ void store_b(uint16_t* sb, int cb, int kq, const uint4 (&rb)[8]) {
-  uint32_t w[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w[i][0] = rb[i].x;
-    w[i][1] = rb[i].y;
-    w[i][2] = rb[i].z;
-    w[i][3] = rb[i].w;
-  }
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    // columns 2d (low halves) and 2d+1 (high halves)
-    const uint4 lo = make_uint4(pack_lo(w[0][d], w[1][d]), pack_lo(w[2][d], w[3][d]),
-                                pack_lo(w[4][d], w[5][d]), pack_lo(w[6][d], w[7][d]));
-    const uint4 hi = make_uint4(pack_hi(w[0][d], w[1][d]), pack_hi(w[2][d], w[3][d]),
-                                pack_hi(w[4][d], w[5][d]), pack_hi(w[6][d], w[7][d]));
-    *(uint4*)&sb[(8 * cb + 2 * d) * kLds + 8 * kq] = lo;
-    *(uint4*)&sb[(8 * cb + 2 * d + 1) * kLds + 8 * kq] = hi;
-  }
+// B operand of n-tile c, k-step t: two transposed 8-byte reads (K-rows 16t + 8 (lane/32) + 4h
+// + (lane%16)/4, see the offsets in the kernel) give column lane % 32, K values
+// 16t + 8 (lane / 32) .. +7.
+__device__ __forceinline__ bf16x8 read_b(const char* sb, const uint32_t (&boff)[4], int c, int t) {
+  const char* p = sb + boff[c & 3] + (c & 4) * 64 + t * 16 * 512;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * 512));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// A operands of one stage: 2 m-tiles of 32 rows x 4 k-steps of 16. Rows past the tile read
-// row 0 of A (valid memory; their outputs are never stored).
-__device__ __forceinline__ void load_a(const char* abase, const uint32_t (&aoff)[2], int64_t k0,
-                                       uint4 (&ra)[2][4]) {
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) ra[mi][t] = gload(abase, aoff[mi] + (uint32_t)(k0 + 16 * t) * 2u);
+// A operand of m-tile mi, k-step t: row 64 w + 32 mi + lane % 32, K values 16t + 8 (lane/32)..
+__device__ __forceinline__ bf16x8 read_a(const char* sa, const uint32_t (&aoff)[4], int mi, int t) {
+  return *(const lds_bf16x8*)(sa + aoff[t] + mi * 32 * 128);
 }
 
-__device__ __forceinline__ bf16x8 read_b(const uint16_t* sb, int c, int t, int lane) {
-  return *(const bf16x8*)&sb[(32 * c + (lane & 31)) * kLds + 16 * t + 8 * (lane >> 5)];
-}
-
-template <int NTW>
-__device__ __forceinline__ void read_bs(const uint16_t* sb, int t, int lane, bf16x8 (&b)[NTW]) {
+// One stage: 4 k-steps x (2 x 8) MFMAs. B operands rotate through one register set (the read
+// for k-step t + 1 of n-tile c follows the two MFMAs of k-step t that consume it); A operands
+// of k-step t + 1 are read at the start of k-step t.
+__device__ __forceinline__ void compute_stage(const char* sa, const char* sb,
+                                              const uint32_t (&aoff)[4],
+                                              const uint32_t (&boff)[4], f32x16 (&acc)[2][8]) {
+  bf16x8 b[8], a0 = read_a(sa, aoff, 0, 0), a1 = read_a(sa, aoff, 1, 0);
 #pragma unroll
-  for (int c = 0; c < NTW; ++c) b[c] = read_b(sb, c, t, lane);
-}
-
-template <int NTW>
-__device__ __forceinline__ void mfma_step(const uint4 (&ra)[2][4], int t, const bf16x8 (&b)[NTW],
-                                          f32x16 (&acc)[2][NTW]) {
-  const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[0][t]);
-  const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[1][t]);
+  for (int c = 0; c < 8; ++c) b[c] = read_b(sb, boff, c, 0);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int c = 0; c < NTW; ++c) {
-    acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
-    acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
+  for (int t = 0; t < 4; ++t) {
+    bf16x8 n0 = a0, n1 = a1;
+    if (t < 3) {
+      n0 = read_a(sa, aoff, 0, t + 1);
+      n1 = read_a(sa, aoff, 1, t + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
+      acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
+      if (t < 3) b[c] = read_b(sb, boff, c, t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    a0 = n0;
+    a1 = n1;
   }
 }
 
-// 4 k-steps of 16, each 2 row tiles x NTW column tiles of v_mfma_f32_32x32x16_bf16. The B
-// operands of k-step t+1 are read from LDS while the MFMAs of k-step t run; scheduling
-// fences keep the compiler from sinking those reads next to their uses.
-template <int NTW>
-__device__ __forceinline__ void compute_stage(const uint16_t* sb, const uint4 (&ra)[2][4],
-                                              int lane, f32x16 (&acc)[2][NTW]) {
-  bf16x8 b0[NTW], b1[NTW];
-  read_bs<NTW>(sb, 0, lane, b0);
-  __builtin_amdgcn_sched_barrier(0);
-  read_bs<NTW>(sb, 1, lane, b1);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step<NTW>(ra, 0, b0, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  read_bs<NTW>(sb, 2, lane, b0);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step<NTW>(ra, 1, b1, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  read_bs<NTW>(sb, 3, lane, b1);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step<NTW>(ra, 2, b0, acc);
-  __builtin_amdgcn_sched_barrier(0);
-  mfma_step<NTW>(ra, 3, b1, acc);
-}
-
-// NTW = column tiles of 32 per wave: 8 gives 256 x 256 tiles at one block per CU, 4 gives
-// 256 x 128 tiles with two blocks per CU (each wave hides the other's LDS latency).
-template <int EPI, int NTW>
-__global__ __launch_bounds__(kThreads, 8 / NTW) void gemm_bf16_256_kernel(const GroupedGemm g,
-                                                                          int nt) {
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const GroupedGemm g, int nt) {
   constexpr bool kSwiGLU = EPI == EPI_SWIGLU;
-  constexpr int kBN = 32 * NTW;
-  __shared__ __align__(16) uint16_t sB[2][kBN * kLds];
+  __shared__ __align__(16) uint16_t sA0[kSlab];
+  __shared__ __align__(16) uint16_t sA1[kSlab];
+  __shared__ __align__(16) uint16_t sB0[kSlab];
+  __shared__ __align__(16) uint16_t sB1[kSlab];
 
-  // XCD-aware order: XCD x (= blockIdx % 8) takes the x-th contiguous eighth of the tiles.
   const int b = blockIdx.x;
   int e, row0, rows, n_tile;
   if (!find_tile_2d(g.offsets, g.E, kBM, nt, kTileBlockN, b, e, row0, rows, n_tile)) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = g.K, N = g.N;
   const int64_t n0 = (int64_t)n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output column
   if (n0 >= N) return;
 
-  // A: this lane's 4 rows (one per m-tile) and its K offset inside each 32-step
-  const char* abase = (const char*)g.A;
-  const int koff = 8 * (lane >> 5);
-  uint32_t aoff[2];
+  Loader ld;
+  // A: instruction j of wave w fills tile rows 8 (8w + j) + lane / 8; its 16-byte chunk at
+  // position lane % 8 is logical chunk (lane % 8) ^ ((row / 2) % 8), and (row / 2) % 8 =
+  // 4 (j % 2) + lane / 16 % 4. Rows past the tile read row 0 of the expert block (valid memory;
+  // their outputs are never stored).
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int r = 64 * wv + 32 * mi + (lane & 31);
+  for (int j = 0; j < 8; ++j) {
+    const int r = 8 * (8 * wv + j) + (lane >> 3);
+    const int c = (lane & 7) ^ (4 * (j & 1) + ((lane >> 4) & 3));
     int64_t src = 0;
     if (r < rows) {
       const int64_t gr = row0 + r;
       src = g.a_gather ? (int64_t)(g.a_gather[gr] / g.gather_div) : gr;
+    } else {
+      src = g.a_gather ? (int64_t)(g.a_gather[row0] / g.gather_div) : row0;
     }
-    aoff[mi] = (uint32_t)((src * g.lda + koff) * 2);
+    ld.a[j] = (const char*)g.A + (src * g.lda + 8 * c) * 2;
   }
-
-  // B: thread -> (8-column block cb of the tile columns, 8-row group kq of the stage). With
-  // 128-column tiles the upper 128 threads load a copy of the lower half's blocks (so every
-  // thread issues the same loads and the wait counts stay static) and do not store them.
-  const int cb = tid >> 3, kq = tid & 7;
-  const bool b_loader = cb < kBN / 8;
-  BLoader bl;
-  {
+  // B: instruction j of wave w fills K-rows 16w + 2j + lane / 32; position lane % 32 of the
+  // K-row holds logical chunk (lane % 32) ^ (4 (K-row % 4)), K-row % 4 = 2 (j % 2) + lane / 32.
+  ld.b_row_bytes = N * 2;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = (lane & 31) ^ (4 * ((2 * q + (lane >> 5)) & 3));
     int64_t col;
     const uint16_t* Wm;
-    const int cbl = cb % (kBN / 8);
     if (kSwiGLU) {
-      const int c = cbl >> 2;  // tile column block of 32: even -> W1, odd -> W3
-      Wm = (const uint16_t*)((c & 1) ? g.B1 : g.B0);
-      col = n0 + 32 * (c >> 1) + 8 * (cbl & 3);
+      const int ct = c >> 2;  // n-tile of 32: even -> W1, odd -> W3, same output columns
+      Wm = (const uint16_t*)((ct & 1) ? g.B1 : g.B0);
+      col = n0 + 32 * (ct >> 1) + 8 * (c & 3);
     } else {
       Wm = (const uint16_t*)g.B0;
-      col = n0 + 8 * cbl;
+      col = n0 + 8 * c;
     }
-    bl.base = (const char*)(Wm + (int64_t)e * K * N);
-    bl.col_off = (uint32_t)((col < N ? col : 0) * 2);
-    bl.row_bytes = (uint32_t)(N * 2);
-    bl.K = K;
-    bl.kq = kq;
+    const int krow = 16 * wv + (lane >> 5);
+    ld.b[q] = (const char*)(Wm + (int64_t)e * K * N + (int64_t)krow * N + (col < N ? col : 0));
   }
 
-  f32x16 acc[2][NTW];
+  // Operand read offsets (bytes within a stage buffer).
+  uint32_t aoff[4], boff[4];
+  {
+    const int r = 64 * wv + (lane & 31);  // + 32 mi
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int chunk = (2 * t + (lane >> 5)) ^ ((r >> 1) & 7);
+      aoff[t] = (uint32_t)(r * 128 + chunk * 16);
+    }
+    const int gq = lane >> 4, L = lane & 15;
+    const int krow = 8 * (gq >> 1) + (L >> 2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int chunk = (4 * c + 2 * (gq & 1) + ((L & 3) >> 1)) ^ (4 * (L >> 2));
+      boff[c] = (uint32_t)(krow * 512 + chunk * 16 + 8 * (L & 1));
+    }
+  }
+
+  f32x16 acc[2][8];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int c = 0; c < NTW; ++c)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][c][v] = 0.f;
 
-  const bool active = 64 * wv < rows;  // this wave has rows to store
-  const int nst = (int)(K / kBK);       // even: K % (2 * kBK) == 0 is required
-  uint4 ra0[2][4], ra1[2][4], rb[8];
+  const uint32_t la0 = lds_addr(sA0), la1 = lds_addr(sA1);
+  const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
+  const int nst = (int)(K / kBK);  // even: K % 128 == 0 is required
+  const int64_t last = (int64_t)(nst - 1) * kBK;
 
-  load_a(abase, aoff, 0, ra0);
-  load_b(bl, 0, rb);
-  if (b_loader) store_b(sB[0], cb, kq, rb);
-  __syncthreads();
-
-  // Stage s computes from registers ra(s%2) and LDS buffer s%2 while the loads of stage s+1
-  // are in flight; B of stage s+1 then goes to the other LDS buffer. Every iteration is the
-  // same (no tail, no conditional loads), so each wait covers exactly the operands it needs;
-  // the prefetch past the last stage re-reads the last stage (valid memory) and is unused.
-  // Every wave computes, including waves whose rows are all past the tile (their results are
-  // not stored): a branch around the MFMAs would make the compiler copy accumulators.
+  load_stage(ld, 0, la0, lb0, wv);
   for (int s = 0; s < nst; s += 2) {
-    const int64_t k1 = (int64_t)(s + 1) * kBK;
-    const int64_t k2 = (int64_t)min(s + 2, nst - 1) * kBK;
-    load_a(abase, aoff, k1, ra1);
-    load_b(bl, k1, rb);
-    compute_stage<NTW>(sB[0], ra0, lane, acc);
-    if (b_loader) store_b(sB[1], cb, kq, rb);
-    __syncthreads();
-    load_a(abase, aoff, k2, ra0);
-    load_b(bl, k2, rb);
-    compute_stage<NTW>(sB[1], ra1, lane, acc);
-    if (b_loader) store_b(sB[0], cb, kq, rb);
-    __syncthreads();
+    wait_vm0();
+    block_barrier();
+    load_stage(ld, (int64_t)(s + 1) * kBK, la1, lb1, wv);
+    compute_stage((const char*)sA0, (const char*)sB0, aoff, boff, acc);
+    wait_vm0();
+    block_barrier();
+    load_stage(ld, s + 2 < nst ? (int64_t)(s + 2) * kBK : last, la0, lb0, wv);
+    compute_stage((const char*)sA1, (const char*)sB1, aoff, boff, acc);
   }
+  // The prefetch past the last stage is still in flight: let it land before the wave can end
+  // (the block's LDS must not be written after it is released).
+  wait_vm0();
 
-  if (!active) return;
+  if (64 * wv >= rows) return;
   // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
   uint16_t* C = (uint16_t*)g.C;
 #pragma unroll
@@ -257,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 8 / NTW) void gemm_bf16_256_kernel(const 
       uint16_t* crow = C + (int64_t)(row0 + r) * N;
       if (kSwiGLU) {
 #pragma unroll
-        for (int q = 0; q < NTW / 2; ++q) {
+        for (int q = 0; q < 4; ++q) {
           const int64_t col = n0 + 32 * q + (lane & 31);
           if (col < N) {
             const float gt = acc[mi][2 * q][v], up = acc[mi][2 * q + 1][v];
@@ -266,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 8 / NTW) void gemm_bf16_256_kernel(const 
         }
       } else {
 #pragma unroll
-        for (int c = 0; c < NTW; ++c) {
+        for (int c = 0; c < 8; ++c) {
           const int64_t col = n0 + 32 * c + (lane & 31);
           if (col < N) {
             float val = acc[mi][c][v];
@@ -278,9 +253,9 @@ __global__ __launch_bounds__(kThreads, 8 / NTW) void gemm_bf16_256_kernel(const 
     }
 }
 
-template <int NTW>
-hipError_t launch_ntw(const GroupedGemm& g, hipStream_t s) {
-  constexpr int kBN = 32 * NTW;
+}  // namespace
+
+hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s) {
   const int64_t mt_max = (g.max_rows + kBM - 1) / kBM + g.E;
   const int64_t cols = (g.epilogue == EPI_SWIGLU) ? kBN / 2 : kBN;
   const int64_t nt = (g.N + cols - 1) / cols;
@@ -289,25 +264,16 @@ hipError_t launch_ntw(const GroupedGemm& g, hipStream_t s) {
   const dim3 grid((unsigned)G);
   switch (g.epilogue) {
     case EPI_NONE:
-      hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI_NONE, NTW>), grid, dim3(kThreads), 0, s, g,
-                         (int)nt);
+      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_NONE>, grid, dim3(kThreads), 0, s, g, (int)nt);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI_RELU, NTW>), grid, dim3(kThreads), 0, s, g,
-                         (int)nt);
+      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s, g, (int)nt);
       break;
     default:
-      hipLaunchKernelGGL((gemm_bf16_256_kernel<EPI_SWIGLU, NTW>), grid, dim3(kThreads), 0, s, g,
-                         (int)nt);
+      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s, g, (int)nt);
       break;
   }
   return hipGetLastError();
-}
-
-}  // namespace
-
-hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s) {
-  return launch_ntw<8>(g, s);
 }
 
 }  // namespace moe
