@@ -304,8 +304,9 @@ __device__ __forceinline__ void write_block_partials(const BlockPartials<EPL>& b
       a += s_psum[q][e];
       c += s_cnt[q][e];
     }
-    psum_blk[(int64_t)blockIdx.x * E + e] = a;
-    count_blk[(int64_t)blockIdx.x * E + e] = c;
+    // expert-major: the loss reduction then reads each expert's partials contiguously
+    psum_blk[(int64_t)e * gridDim.x + blockIdx.x] = a;
+    count_blk[(int64_t)e * gridDim.x + blockIdx.x] = c;
   }
 }
 
@@ -339,7 +340,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
     int64_t T, int64_t D, int E, int k, const TIn* __restrict__ x, const TIn* __restrict__ w,
     const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ gates,
     float* __restrict__ logits_out, double* __restrict__ psum_blk,
-    int32_t* __restrict__ count_blk) {
+    int32_t* __restrict__ count_blk, int32_t* __restrict__ ticket,
+    int32_t* __restrict__ uncertified) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *ticket = 0;  // the loss reduction that follows counts its blocks here
+    if (uncertified) *uncertified = 0;  // float32 layers never need a recompute
+  }
   BlockPartials<EPL> bp;
   bp.zero();
   const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
@@ -362,13 +368,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
 // ---- bfloat16 layers ----------------------------------------------------------------------
 
 // wt[e][d] = w[d][e]; wnorm[e] = ||w[:, e]||_2 (float64). One block per expert; the sum of
-// squares is reduced in a fixed order (per-thread, then an LDS tree).
+// squares is reduced in a fixed order (per-thread, then an LDS tree). Also zeroes the
+// counters that the later routing kernels of the call accumulate into.
 __global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
                                                           const uint16_t* __restrict__ w,
                                                           uint16_t* __restrict__ wt,
-                                                          double* __restrict__ wnorm) {
+                                                          double* __restrict__ wnorm,
+                                                          int32_t* __restrict__ ticket,
+                                                          int32_t* __restrict__ uncertified) {
   __shared__ double s_part[256];
   const int e = blockIdx.x;
+  if (e == 0 && threadIdx.x == 0) {
+    *ticket = 0;
+    if (uncertified) *uncertified = 0;
+  }
   double acc = 0.0;
 #pragma unroll 4
   for (int64_t d = threadIdx.x; d < D; d += 256) {
@@ -572,61 +585,66 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
 // aux = E * sum_e (count_e / (T k)) * (sum_t probs[t, e] / T). 1024 threads: thread i sums
 // the blocks b = p (mod P) of expert e = i / P, in block order; the P part sums are then
 // added in order, and the E terms in expert order.
-constexpr int kAuxThreads = 1024;
+constexpr int kAuxThreads = 256;
 
+// Switch loss from the per-block partials (expert-major, nblk per expert): block e sums
+// expert e's probability partials and counts in a fixed order (strided per thread, then a
+// fixed tree), writes P_e and count_e, and takes a ticket; the block with the last ticket
+// forms aux = E * sum_e (count_e / (T k)) * (P_e / T) in expert order and resets the ticket.
+// The result does not depend on block scheduling.
 __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int64_t nblk, int E, int64_t T, int k, const double* __restrict__ psum_blk,
-    const int32_t* __restrict__ count_blk, float* __restrict__ aux,
-    int32_t* __restrict__ counts_out) {
+    const int32_t* __restrict__ count_blk, double* __restrict__ pe, int64_t* __restrict__ ce,
+    int32_t* __restrict__ ticket, float* __restrict__ aux, int32_t* __restrict__ counts_out) {
   __shared__ double s_p[kAuxThreads];
   __shared__ int64_t s_c[kAuxThreads];
-  __shared__ double s_term[kMaxExperts];
-  int NE = 1;
-  while (NE < E) NE <<= 1;
-  const int P = kAuxThreads / NE;
-  const int i = threadIdx.x, p = i % P, e = i / P;
+  __shared__ bool s_last;
+  const int e = blockIdx.x, i = threadIdx.x;
   double pacc = 0.0;
   int64_t cacc = 0;
-  if (e < E) {
-    constexpr int kChunk = 8;  // independent loads in flight
-    for (int64_t b0 = p; b0 < nblk; b0 += (int64_t)P * kChunk) {
-      double pv[kChunk];
-      int cv[kChunk];
-#pragma unroll
-      for (int q = 0; q < kChunk; ++q) {
-        const int64_t b = b0 + (int64_t)q * P;
-        pv[q] = (b < nblk) ? psum_blk[b * E + e] : 0.0;
-        cv[q] = (b < nblk) ? count_blk[b * E + e] : 0;
-      }
-#pragma unroll
-      for (int q = 0; q < kChunk; ++q) {
-        pacc += pv[q];
-        cacc += cv[q];
-      }
-    }
+  const double* pp = psum_blk + (int64_t)e * nblk;
+  const int32_t* cp = count_blk + (int64_t)e * nblk;
+  for (int64_t b = i; b < nblk; b += kAuxThreads) {
+    pacc += pp[b];
+    cacc += cp[b];
   }
   s_p[i] = pacc;
   s_c[i] = cacc;
   __syncthreads();
-  if (i < E) {
-    double Pe = 0.0;
-    int64_t c = 0;
-    for (int q = 0; q < P; ++q) {
-      Pe += s_p[i * P + q];
-      c += s_c[i * P + q];
+  for (int h = kAuxThreads / 2; h >= 1; h >>= 1) {
+    if (i < h) {
+      s_p[i] += s_p[i + h];
+      s_c[i] += s_c[i + h];
     }
-    if (counts_out) counts_out[i] = (int32_t)c;
-    s_term[i] = (T > 0) ? ((double)c / ((double)T * (double)k)) * (Pe / (double)T) : 0.0;
+    __syncthreads();
+  }
+  if (i == 0) {
+    pe[e] = s_p[0];
+    ce[e] = s_c[0];
+    if (counts_out) counts_out[e] = (int32_t)s_c[0];
+    __threadfence();
+    s_last = atomicAdd(ticket, 1) == E - 1;
   }
   __syncthreads();
-  if (i == 0) {
-    double acc = 0.0;
-    for (int q = 0; q < E; ++q) acc += s_term[q];
-    *aux = (float)((double)E * acc);
+  if (!s_last || i != 0) return;
+  __threadfence();
+  double acc = 0.0;
+  for (int q = 0; q < E; ++q) {
+    const double Pe = __builtin_nontemporal_load(&pe[q]);
+    const double c = (double)__builtin_nontemporal_load(&ce[q]);
+    acc += (T > 0) ? (c / ((double)T * (double)k)) * (Pe / (double)T) : 0.0;
   }
+  *aux = (float)((double)E * acc);
+  *ticket = 0;
 }
 
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+// T = 0: aux = 0 and every count 0.
+__global__ void aux_empty_kernel(int E, float* __restrict__ aux, int32_t* __restrict__ counts_out) {
+  if (threadIdx.x == 0) *aux = 0.f;
+  if (counts_out && (int)threadIdx.x < E) counts_out[threadIdx.x] = 0;
+}
 
 // ---- scratch layout -------------------------------------------------------------------------
 
@@ -635,6 +653,9 @@ size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 struct RouteScratch {
   double* psum;
   int32_t* pcnt;
+  double* pe;        // per-expert probability sums (aux reduction)
+  int64_t* ce;       // per-expert counts (aux reduction)
+  int32_t* ticket;   // blocks of the aux reduction done; zeroed by the first routing kernel
   uint16_t* wt;
   double* wnorm;
   float* part;
@@ -654,6 +675,9 @@ RouteScratch route_scratch(const Problem& p, void* base) {
   const int64_t nblk = route_blocks(p);
   r.psum = (double*)take((size_t)nblk * p.E * sizeof(double));
   r.pcnt = (int32_t*)take((size_t)nblk * p.E * sizeof(int32_t));
+  r.pe = (double*)take((size_t)p.E * sizeof(double));
+  r.ce = (int64_t*)take((size_t)p.E * sizeof(int64_t));
+  r.ticket = (int32_t*)take(sizeof(int32_t));
   if (p.dtype == MOE_BF16) {
     const int S = route_splits(p);
     r.wt = (uint16_t*)take((size_t)p.E * p.D * sizeof(uint16_t));
@@ -690,14 +714,16 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
                         void* ws, hipStream_t s) {
   const RouteScratch r = route_scratch(p, ws);
   const int64_t nblk = route_blocks(p);
-  if (uncertified) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, uncertified);
-  if (nblk == 0) return hipGetLastError();
+  if (nblk == 0) {
+    if (uncertified) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, uncertified);
+    return hipGetLastError();
+  }
   const int epl = (p.E + kWave - 1) / kWave;
   if (p.dtype != MOE_BF16) {
 #define MOE_ROUTE_F64(EPLV)                                                                      \
   hipLaunchKernelGGL((route_f64_kernel<float, EPLV>), dim3((unsigned)nblk), dim3(kRouteThreads), \
                      0, s, p.T, p.D, p.E, p.top_k, (const float*)x, (const float*)w_router, bias, \
-                     idx, gates, logits_out, r.psum, r.pcnt)
+                     idx, gates, logits_out, r.psum, r.pcnt, r.ticket, uncertified)
     if (epl <= 1)
       MOE_ROUTE_F64(1);
     else if (epl <= 2)
@@ -711,7 +737,7 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
   int64_t kc = (p.D + S - 1) / S;
   kc = (kc + 31) / 32 * 32;
   hipLaunchKernelGGL(router_prep_kernel, dim3(p.E), dim3(256), 0, s, p.D, p.E,
-                     (const uint16_t*)w_router, r.wt, r.wnorm);
+                     (const uint16_t*)w_router, r.wt, r.wnorm, r.ticket, uncertified);
   const dim3 lgrid((unsigned)((p.T + kLT - 1) / kLT), (unsigned)S);
   const int NT = (p.E + 15) / 16;
   const uint16_t* xb = (const uint16_t*)x;
@@ -747,8 +773,12 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
 hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* counts_out,
                                hipStream_t s) {
   const RouteScratch r = route_scratch(p, ws);
-  hipLaunchKernelGGL(aux_finalize_kernel, dim3(1), dim3(kAuxThreads), 0, s, route_blocks(p), p.E,
-                     p.T, p.top_k, r.psum, r.pcnt, aux, counts_out);
+  if (route_blocks(p) == 0) {  // nothing was routed: aux = 0, counts = 0
+    hipLaunchKernelGGL(aux_empty_kernel, dim3(1), dim3(kMaxExperts), 0, s, p.E, aux, counts_out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(aux_finalize_kernel, dim3(p.E), dim3(kAuxThreads), 0, s, route_blocks(p),
+                     p.E, p.T, p.top_k, r.psum, r.pcnt, r.pe, r.ce, r.ticket, aux, counts_out);
   return hipGetLastError();
 }
 
