@@ -30,6 +30,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -88,86 +90,71 @@ __device__ __forceinline__ double dot8_f64(const uint4& xv, const uint4& wv) {
   return a + b;
 }
 
+// Float64 dot products of one bf16 token row with n rows of the transposed router, CG rows
+// per pass over D (the row of the j-th product is row_of(j)): each lane takes the 16-byte
+// slices c = lane (mod 64) of x and of the CG rows, all loads of a pass in flight at once.
+// Every product of two bf16 values is exact in float64, and so is its conversion, so the
+// sums carry only float64 rounding. put(j, v) receives the wave-uniform j-th sum.
+template <int CG, class RowOf, class Put>
+__device__ __forceinline__ void token_dots_f64(const uint16_t* __restrict__ x,
+                                               const uint16_t* __restrict__ wt, int64_t t,
+                                               int64_t D, int n, RowOf row_of, Put put) {
+  const int lane = lane_id();
+  const uint4* xr = (const uint4*)(x + t * D);
+  const int64_t nc = D / 8;
+  for (int j0 = 0; j0 < n; j0 += CG) {
+    const int nj = min(CG, n - j0);
+    const uint4* wr[CG];
+#pragma unroll
+    for (int jj = 0; jj < CG; ++jj)
+      wr[jj] = (const uint4*)(wt + (int64_t)row_of(j0 + (jj < nj ? jj : 0)) * D);
+    double acc[CG];
+#pragma unroll
+    for (int jj = 0; jj < CG; ++jj) acc[jj] = 0.0;
+    constexpr int kUnroll = CG <= 4 ? 2 : 1;  // loads in flight vs registers
+#pragma unroll kUnroll
+    for (int64_t c = lane; c < nc; c += kWave) {
+      const uint4 xv = xr[c];
+      uint4 wv[CG];
+#pragma unroll
+      for (int jj = 0; jj < CG; ++jj) wv[jj] = wr[jj][c];  // duplicates of row j0 past nj
+#pragma unroll
+      for (int jj = 0; jj < CG; ++jj) acc[jj] += dot8_f64(xv, wv[jj]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < CG; ++jj) {
+      if (jj >= nj) break;
+      put(j0 + jj, wave_sum(acc[jj]));
+    }
+  }
+}
+
 // Exact-product float64 logits of the k chosen experts of one bf16 token (gates need the
 // differences of these to ~1e-7 absolute, which a float32 partial cannot carry when the
-// logits are large). Up to kCG experts per pass over D: each lane takes 16-byte slices
-// c = lane (mod 64) of x and of the kCG weight rows, all loads of a pass in flight at once.
-constexpr int kCG = 4;  // chosen experts per pass over D
-
-template <int EPL>
+// logits are large). CG >= k does it in one pass over D.
+template <int EPL, int CG>
 __device__ __forceinline__ void chosen_logits_f64(const uint16_t* __restrict__ x,
                                                   const uint16_t* __restrict__ wt,
                                                   const float* __restrict__ bias, int64_t t,
                                                   int64_t D, int k, const int my_e[EPL],
                                                   double my_v[EPL]) {
   const int lane = lane_id();
-  const uint4* xr = (const uint4*)(x + t * D);
-  const int64_t nc = D / 8;
-  for (int j0 = 0; j0 < k; j0 += kCG) {
-    const int nj = min(kCG, k - j0);
-    const uint4* wr[kCG];
-    int ev[kCG];
+  auto row_of = [&](int j) {
+    int e = 0;
 #pragma unroll
-    for (int jj = 0; jj < kCG; ++jj) {
-      const int j = j0 + (jj < nj ? jj : 0);
-      int e = 0;
+    for (int i = 0; i < EPL; ++i)
+      if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
+    return e;
+  };
+  auto put = [&](int j, double v) {
+    if (bias) v += (double)bias[row_of(j)];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
-      ev[jj] = e;
-      wr[jj] = (const uint4*)(wt + (int64_t)e * D);
-    }
-    double acc[kCG];
-#pragma unroll
-    for (int jj = 0; jj < kCG; ++jj) acc[jj] = 0.0;
-#pragma unroll 2
-    for (int64_t c = lane; c < nc; c += kWave) {
-      const uint4 xv = xr[c];
-      uint4 wv[kCG];
-#pragma unroll
-      for (int jj = 0; jj < kCG; ++jj) wv[jj] = wr[jj][c];  // duplicates of row j0 past nj
-#pragma unroll
-      for (int jj = 0; jj < kCG; ++jj) acc[jj] += dot8_f64(xv, wv[jj]);
-    }
-#pragma unroll
-    for (int jj = 0; jj < kCG; ++jj) {
-      if (jj >= nj) break;
-      double v = wave_sum(acc[jj]);
-      if (bias) v += (double)bias[ev[jj]];
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (j0 + jj == lane + kWave * i) my_v[i] = v;
-    }
-  }
+    for (int i = 0; i < EPL; ++i)
+      if (j == lane + kWave * i) my_v[i] = v;
+  };
+  token_dots_f64<CG>(x, wt, t, D, k, row_of, put);
 }
 
-// Exact-product float64 logits of all E experts of one bf16 token, computed by a whole
-// 1024-thread block (thread i: expert i / P over the 16-byte slices i % P (mod P)), then
-// summed over the P slices in order. Result in s_out[0..E).
-__device__ __forceinline__ void block_logits_f64(const uint16_t* __restrict__ x,
-                                                 const uint16_t* __restrict__ wt, int64_t t,
-                                                 int64_t D, int E, double* s_red,
-                                                 double* s_out) {
-  int NE = 1;
-  while (NE < E) NE <<= 1;
-  const int P = 1024 / NE;
-  const int i = threadIdx.x, p = i % P, e = i / P;
-  const uint4* xr = (const uint4*)(x + t * D);
-  double acc = 0.0;
-  if (e < E) {
-    const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
-#pragma unroll 4
-    for (int64_t c = p; c < D / 8; c += P) acc += dot8_f64(xr[c], wr[c]);
-  }
-  s_red[i] = acc;
-  __syncthreads();
-  if (i < E) {
-    double v = 0.0;
-    for (int q = 0; q < P; ++q) v += s_red[i * P + q];
-    s_out[i] = v;
-  }
-  __syncthreads();
-}
 
 // k rounds of a wave-wide argmax over the not-yet-chosen experts: larger logit first,
 // equal logits -> smaller expert index. Lane j (+64i) keeps the j-th choice. When
@@ -375,12 +362,12 @@ __global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
                                                           uint16_t* __restrict__ wt,
                                                           double* __restrict__ wnorm,
                                                           int32_t* __restrict__ ticket,
-                                                          int32_t* __restrict__ uncertified) {
+                                                          int32_t* __restrict__ nlist) {
   __shared__ double s_part[256];
   const int e = blockIdx.x;
   if (e == 0 && threadIdx.x == 0) {
     *ticket = 0;
-    if (uncertified) *uncertified = 0;
+    *nlist = 0;
   }
   double acc = 0.0;
 #pragma unroll 4
@@ -483,17 +470,16 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
 
 constexpr int kSelWaves = kRouteTokensPerBlock;  // one token per wave
 constexpr int kSelThreads = kSelWaves * kWave;
+constexpr int kFbThreads = 1024;  // threads per uncertified token in the fallback
 
-template <int EPL>
+template <int EPL, int CG>
 __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     int64_t T, int64_t D, int E, int k, int S, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wt, const double* __restrict__ wnorm,
     const float* __restrict__ part, const float* __restrict__ xsq, const float* __restrict__ bias,
     int32_t* __restrict__ idx, float* __restrict__ gates, float* __restrict__ logits_out,
-    double* __restrict__ psum_blk, int32_t* __restrict__ count_blk, int32_t* __restrict__ nflag) {
-  __shared__ int s_flag[kSelWaves];
-  __shared__ double s_red[kSelThreads];
-  __shared__ double s_lg[kMaxExperts];
+    double* __restrict__ psum_blk, int32_t* __restrict__ count_blk, int32_t* __restrict__ list,
+    int32_t* __restrict__ nlist) {
   const int lane = lane_id(), wv = wave_id();
   const int64_t t = (int64_t)blockIdx.x * kRouteTokensPerBlock + wv;
   const bool valid = t < T;
@@ -550,36 +536,88 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
                      rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30;
     const double gap = topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, true);
     flagged = !(gap > 2.0 * B);
-    if (!flagged) chosen_logits_f64<EPL>(x, wt, bias, t, D, k, my_e, my_v);
-  }
-  if (lane == 0) s_flag[wv] = flagged ? 1 : 0;
-  __syncthreads();
-  // uncertified tokens: the whole block recomputes their logits exactly, one at a time
-  int nfl = 0;
-  for (int w2 = 0; w2 < kSelWaves; ++w2) {
-    if (!s_flag[w2]) continue;  // block-uniform
-    ++nfl;
-    block_logits_f64(x, wt, (int64_t)blockIdx.x * kRouteTokensPerBlock + w2, D, E, s_red, s_lg);
-    if (wv == w2) {
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        lg[i] = (e < E) ? s_lg[e] : 0.0;
-      }
-      add_bias<EPL>(bias, E, lg);
-      topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);  // chosen values are exact already
+    if (flagged) {
+      // uncertified: decided later by route_fallback_kernel from exact logits
+      if (lane == 0) list[atomicAdd(nlist, 1)] = (int32_t)t;
+    } else {
+      chosen_logits_f64<EPL, CG>(x, wt, bias, t, D, k, my_e, my_v);
     }
-    __syncthreads();
   }
   BlockPartials<EPL> bp;
   bp.zero();
   if (valid) {
     write_logits<EPL>(logits_out, t, E, lg);
     finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    // the loss probabilities come from these logits for every token; the counts of an
+    // uncertified token are added by the fallback once its experts are known
+    if (flagged)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) sel[i] = false;
     bp.add(prob, sel);
   }
   write_block_partials<kSelWaves, EPL>(bp, E, psum_blk, count_blk);
-  if (nflag && threadIdx.x == 0 && nfl) atomicAdd(nflag, nfl);
+}
+
+// Uncertified tokens (listed by route_select_kernel), one per 1024-thread block at a time:
+// thread i takes expert i / P and every P-th 16-byte slice of D from slice i % P
+// (P = 1024 / E rounded to a power of two), so the exact-product float64 logits of all E
+// experts come from 1024 concurrent partial sums, added per expert in slice order. Wave 0
+// then takes the top-k and the gates from them and adds the token's counts to its routing
+// block's partials (integer atomics: the totals do not depend on order). Also reports the
+// number of uncertified tokens.
+template <int EPL>
+__global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
+    int64_t D, int E, int k, int64_t nblk, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wt, const float* __restrict__ bias,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ nlist,
+    int32_t* __restrict__ idx, float* __restrict__ gates, float* __restrict__ logits_out,
+    int32_t* __restrict__ count_blk, int32_t* __restrict__ uncertified) {
+  __shared__ double s_red[kFbThreads];
+  __shared__ double s_lg[kMaxExperts];
+  const int n = *nlist;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && uncertified) *uncertified = n;
+  int NE = 1;
+  while (NE < E) NE <<= 1;
+  const int P = kFbThreads / NE;
+  const int i = threadIdx.x, pp = i % P, e = i / P;
+  const int lane = lane_id();
+  for (int slot = blockIdx.x; slot < n; slot += gridDim.x) {
+    const int64_t t = list[slot];
+    const uint4* xr = (const uint4*)(x + t * D);
+    double acc = 0.0;
+    if (e < E) {
+      const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
+#pragma unroll 4
+      for (int64_t c = pp; c < D / 8; c += P) acc += dot8_f64(xr[c], wr[c]);
+    }
+    s_red[i] = acc;
+    __syncthreads();
+    if (i < E) {
+      double v = 0.0;
+      for (int q = 0; q < P; ++q) v += s_red[i * P + q];
+      s_lg[i] = v;
+    }
+    __syncthreads();
+    if (wave_id() == 0) {
+      double lg[EPL], prob[EPL], my_v[EPL];
+      int my_e[EPL];
+      bool sel[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const int ee = lane + kWave * q;
+        lg[q] = (ee < E) ? s_lg[ee] : 0.0;
+      }
+      add_bias<EPL>(bias, E, lg);
+      write_logits<EPL>(logits_out, t, E, lg);
+      topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);
+      finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
+      const int64_t blk = t / kRouteTokensPerBlock;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q)
+        if (sel[q]) atomicAdd(&count_blk[(int64_t)(lane + kWave * q) * nblk + blk], 1);
+    }
+    __syncthreads();  // s_red / s_lg are reused by the next token
+  }
 }
 
 // aux = E * sum_e (count_e / (T k)) * (sum_t probs[t, e] / T). 1024 threads: thread i sums
@@ -656,6 +694,8 @@ struct RouteScratch {
   double* pe;        // per-expert probability sums (aux reduction)
   int64_t* ce;       // per-expert counts (aux reduction)
   int32_t* ticket;   // blocks of the aux reduction done; zeroed by the first routing kernel
+  int32_t* list;     // uncertified tokens (bf16), appended by the select kernel
+  int32_t* nlist;    // their number; zeroed by the first routing kernel
   uint16_t* wt;
   double* wnorm;
   float* part;
@@ -678,6 +718,8 @@ RouteScratch route_scratch(const Problem& p, void* base) {
   r.pe = (double*)take((size_t)p.E * sizeof(double));
   r.ce = (int64_t*)take((size_t)p.E * sizeof(int64_t));
   r.ticket = (int32_t*)take(sizeof(int32_t));
+  r.list = (int32_t*)take((size_t)p.T * sizeof(int32_t));
+  r.nlist = (int32_t*)take(sizeof(int32_t));
   if (p.dtype == MOE_BF16) {
     const int S = route_splits(p);
     r.wt = (uint16_t*)take((size_t)p.E * p.D * sizeof(uint16_t));
@@ -737,7 +779,7 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
   int64_t kc = (p.D + S - 1) / S;
   kc = (kc + 31) / 32 * 32;
   hipLaunchKernelGGL(router_prep_kernel, dim3(p.E), dim3(256), 0, s, p.D, p.E,
-                     (const uint16_t*)w_router, r.wt, r.wnorm, r.ticket, uncertified);
+                     (const uint16_t*)w_router, r.wt, r.wnorm, r.ticket, r.nlist);
   const dim3 lgrid((unsigned)((p.T + kLT - 1) / kLT), (unsigned)S);
   const int NT = (p.E + 15) / 16;
   const uint16_t* xb = (const uint16_t*)x;
@@ -756,17 +798,40 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
   else
     hipLaunchKernelGGL(route_logits_mfma_kernel<16>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
                        xb, r.wt, r.part, r.xsq);
-#define MOE_ROUTE_SELECT(EPLV)                                                                 \
-  hipLaunchKernelGGL((route_select_kernel<EPLV>), dim3((unsigned)nblk), dim3(kSelThreads), 0, s, \
-                     p.T, p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias, idx,     \
-                     gates, logits_out, r.psum, r.pcnt, uncertified)
-  if (epl <= 1)
-    MOE_ROUTE_SELECT(1);
-  else if (epl <= 2)
-    MOE_ROUTE_SELECT(2);
-  else
-    MOE_ROUTE_SELECT(4);
+#define MOE_ROUTE_SELECT(EPLV, CGV)                                                           \
+  hipLaunchKernelGGL((route_select_kernel<EPLV, CGV>), dim3((unsigned)nblk), dim3(kSelThreads), 0, \
+                     s, p.T, p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias, idx,  \
+                     gates, logits_out, r.psum, r.pcnt, r.list, r.nlist)
+#define MOE_ROUTE_SELECT_CG(EPLV)   \
+  if (p.top_k <= 2)                 \
+    MOE_ROUTE_SELECT(EPLV, 2);      \
+  else if (p.top_k <= 4)            \
+    MOE_ROUTE_SELECT(EPLV, 4);      \
+  else                              \
+    MOE_ROUTE_SELECT(EPLV, 8);
+  if (epl <= 1) {
+    MOE_ROUTE_SELECT_CG(1)
+  } else if (epl <= 2) {
+    MOE_ROUTE_SELECT_CG(2)
+  } else {
+    MOE_ROUTE_SELECT_CG(4)
+  }
+#undef MOE_ROUTE_SELECT_CG
 #undef MOE_ROUTE_SELECT
+  // one block per uncertified token, at most 512 blocks (a grid-stride loop covers the rest)
+  const unsigned fgrid = (unsigned)std::min<int64_t>(p.T, 512);
+#define MOE_ROUTE_FALLBACK(EPLV)                                                          \
+  hipLaunchKernelGGL((route_fallback_kernel<EPLV>), dim3(fgrid), dim3(kFbThreads), 0, s, \
+                     p.D, p.E,                                                            \
+                     p.top_k, nblk, xb, r.wt, bias, r.list, r.nlist, idx, gates, logits_out, \
+                     r.pcnt, uncertified)
+  if (epl <= 1)
+    MOE_ROUTE_FALLBACK(1);
+  else if (epl <= 2)
+    MOE_ROUTE_FALLBACK(2);
+  else
+    MOE_ROUTE_FALLBACK(4);
+#undef MOE_ROUTE_FALLBACK
   return hipGetLastError();
 }
 
