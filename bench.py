@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("2a6a9f6f02154555afc3f302237e929073062c35edfad44322cf3e66fbeca349",
-                            2584028.40625, 229376.015625),
+    "mixtral_swiglu_bf16": ("ed0be10a168ed6a3663d90efe8697d53a40dfc6094537e42f707a55442332141",
+                            1842045.703125, 229376.078125),
 }
 
 
