@@ -204,9 +204,14 @@ def moe_forward_timed(p: Problem, x, w_router, router_bias, w1, w3, w2, out, exp
 
 
 class StageEvents:
-    """2 * len(STAGES) HIP events for moe_forward_timed, created with hipEventCreate."""
+    """2 * len(STAGES) HIP event slots for moe_forward_timed, created with hipEventCreate for
+    the stages named in `stages` (default: all) and left NULL for the others."""
 
-    def __init__(self):
+    def __init__(self, stages=None):
+        self.stages = tuple(STAGES if stages is None else stages)
+        unknown = set(self.stages) - set(STAGES)
+        if unknown:
+            raise ValueError(f"unknown stages {sorted(unknown)}")
         # HIP entry points through libmoe.so's own dependency scope, i.e. the one HIP
         # runtime this process has loaded (never a second copy)
         self._hip = lib()
@@ -216,17 +221,22 @@ class StageEvents:
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         n = 2 * len(STAGES)
         self.events = (ctypes.c_void_p * n)()
-        for i in range(n):
-            h = ctypes.c_void_p()
-            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            self.events[i] = h
+        for s, name in enumerate(STAGES):
+            if name not in self.stages:
+                continue
+            for i in (2 * s, 2 * s + 1):
+                h = ctypes.c_void_p()
+                if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                self.events[i] = h
         self._alive = True
 
     def elapsed_ms(self) -> dict:
         """Per-stage device milliseconds; call after the stream has been synchronised."""
         out = {}
         for s, name in enumerate(STAGES):
+            if name not in self.stages:
+                continue
             ms = ctypes.c_float()
             if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.events[2 * s],
                                              self.events[2 * s + 1]) != 0:
@@ -237,7 +247,8 @@ class StageEvents:
     def close(self):
         if self._alive:
             for h in self.events:
-                self._hip.hipEventDestroy(h)
+                if h:
+                    self._hip.hipEventDestroy(h)
             self._alive = False
 
     def __del__(self):

@@ -7,6 +7,7 @@
 using namespace moe;
 
 namespace {
+static_assert(kSplitSlots <= kMaxExperts, "the dispatch scan block zeroes every K-split ticket");
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
@@ -59,6 +60,7 @@ struct Layout {
   size_t blkc, lrank;   // dispatch: (dispatch blocks, E) int32 and (T*k) int32
   size_t perm;          // moe_forward's own permutation, (T*k) int32
   size_t hbuf;          // expert hidden activations, (T*k, DH)
+  size_t gsplit, gctr;  // bf16 GEMM K-split tail: partial tiles and tickets
   size_t ybuf;          // moe_forward's expert outputs, (T*k, D_out)
   size_t route_end, dispatch_end, ffn_end, total;
 };
@@ -79,6 +81,9 @@ Layout layout_of(const Problem& q) {
   L.lrank = take(slots * sizeof(int32_t));
   L.dispatch_end = off;
   L.hbuf = take(q.kind == MOE_EXPERT_LINEAR ? 0 : slots * (size_t)q.DH * es);
+  const bool split = q.dtype == MOE_BF16 && q.T > 0;
+  L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
+  L.gctr = take(split ? (size_t)kSplitSlots * sizeof(int32_t) : 0);
   L.ffn_end = off;
   L.perm = take(slots * sizeof(int32_t));
   L.ybuf = take(slots * (size_t)q.D_out * es);
@@ -100,15 +105,32 @@ moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 void mark(hipEvent_t* ev, int i, hipStream_t s) {
-  if (ev) hipEventRecord(ev[i], s);
+  if (ev && ev[i]) hipEventRecord(ev[i], s);
 }
+hipEvent_t event_at(hipEvent_t* ev, int i) { return ev ? ev[i] : nullptr; }
 
 // The expert FFN over expert-ordered rows; `gather` (nullable) maps rows to token rows of A.
 // `ev` (nullable) receives the stage markers of the up and down GEMMs.
 hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, const int32_t* offsets,
                        const void* w1, const void* w3, const void* w2, void* hbuf, void* y,
-                       hipStream_t s, hipEvent_t* ev) {
+                       void* ws, const Layout& Lw, bool tickets_zeroed, hipStream_t s,
+                       hipEvent_t* ev) {
+  float* split_ws = nullptr;
+  int32_t* split_ctr = nullptr;
+  const int ncu = q.dtype == MOE_BF16 ? device_split_cus() : 0;
+  if (ncu > 0) {
+    split_ws = at<float>(ws, Lw.gsplit);
+    split_ctr = at<int32_t>(ws, Lw.gctr);
+    // both GEMMs leave the tickets zero, so one reset before the first serves both
+    if (!tickets_zeroed) {
+      const hipError_t e0 = launch_zero_tickets(split_ctr, kSplitSlots, s);
+      if (e0 != hipSuccess) return e0;
+    }
+  }
   GroupedGemm g{};
+  g.split_ws = split_ws;
+  g.split_ctr = split_ctr;
+  g.ncu = ncu;
   g.A = A;
   g.lda = q.D;
   g.a_gather = gather;
@@ -124,12 +146,15 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   g.C = linear ? y : hbuf;
   g.N = linear ? q.D_out : q.DH;
   g.epilogue = linear ? EPI_NONE : (q.kind == MOE_EXPERT_SWIGLU ? EPI_SWIGLU : EPI_RELU);
-  mark(ev, 2 * MOE_STAGE_EXPERT_UP, s);
+  // the expert stages' events bracket the GEMM kernels themselves
+  g.ev_start = event_at(ev, 2 * MOE_STAGE_EXPERT_UP);
+  g.ev_stop = event_at(ev, 2 * MOE_STAGE_EXPERT_UP + 1);
   hipError_t err = launch_grouped_gemm(g, s);
-  mark(ev, 2 * MOE_STAGE_EXPERT_UP + 1, s);
-  mark(ev, 2 * MOE_STAGE_EXPERT_DOWN, s);
   if (err == hipSuccess && !linear) {
     GroupedGemm d{};
+    d.split_ws = split_ws;
+    d.split_ctr = split_ctr;
+    d.ncu = ncu;
     d.A = hbuf;
     d.lda = q.DH;
     d.a_gather = nullptr;
@@ -144,9 +169,13 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
     d.max_rows = q.slots();
     d.epilogue = EPI_NONE;
     d.dtype = q.dtype;
+    d.ev_start = event_at(ev, 2 * MOE_STAGE_EXPERT_DOWN);
+    d.ev_stop = event_at(ev, 2 * MOE_STAGE_EXPERT_DOWN + 1);
     err = launch_grouped_gemm(d, s);
+  } else {  // no second GEMM: an empty stage
+    mark(ev, 2 * MOE_STAGE_EXPERT_DOWN, s);
+    mark(ev, 2 * MOE_STAGE_EXPERT_DOWN + 1, s);
   }
-  mark(ev, 2 * MOE_STAGE_EXPERT_DOWN + 1, s);
   return err;
 }
 
@@ -234,7 +263,7 @@ moe_status moe_expert_ffn(const moe_problem* p, const void* x_perm, const int32_
   if (st != MOE_OK) return st;
   if (q.T == 0) return MOE_OK;
   return hip_status(run_experts(q, x_perm, nullptr, expert_offsets, w1, w3, w2,
-                                at<void>(ws, L.hbuf), y_perm, stream, nullptr));
+                                at<void>(ws, L.hbuf), y_perm, ws, L, false, stream, nullptr));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot_row,
@@ -269,13 +298,16 @@ moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_
     err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream);
   mark(ev, 2 * MOE_STAGE_ROUTE + 1, stream);
   mark(ev, 2 * MOE_STAGE_DISPATCH, stream);
+  // the dispatch scan also zeroes the GEMMs' K-split tickets
+  int32_t* tickets = (q.dtype == MOE_BF16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
   if (err == hipSuccess)
     err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
-                          nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream);
+                          nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
+                          tickets, tickets ? kSplitSlots : 0);
   mark(ev, 2 * MOE_STAGE_DISPATCH + 1, stream);
   if (err == hipSuccess)
     err = run_experts(q, x, perm, expert_offsets, w1, w3, w2, at<void>(ws, L.hbuf),
-                      at<void>(ws, L.ybuf), stream, ev);
+                      at<void>(ws, L.ybuf), ws, L, tickets != nullptr, stream, ev);
   mark(ev, 2 * MOE_STAGE_COMBINE, stream);
   if (err == hipSuccess) err = launch_combine(q, at<void>(ws, L.ybuf), slot_row, gates, out, stream);
   mark(ev, 2 * MOE_STAGE_COMBINE + 1, stream);

@@ -77,10 +77,12 @@ hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* 
 
 // Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
 int64_t dispatch_blocks(const Problem& p);
+// `zero` (nullable): nzero <= kMaxExperts int32 that the scan kernel sets to 0 on the way
+// (the GEMM K-split tickets of the same call, which saves a launch).
 hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_row,
                            void* x_perm, int32_t* blk_counts, int32_t* local_rank,
-                           hipStream_t s);
+                           hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 
 // Grouped expert GEMM over expert-ordered rows.
 enum Epilogue { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
@@ -98,10 +100,25 @@ struct GroupedGemm {
   int64_t max_rows;         // upper bound of offsets[E] (grid sizing)
   int epilogue;
   int dtype;
+  // K-split tail (bf16 256x256 kernel only; null split_ws: no split). split_ws holds
+  // kSplitSlots partial tiles of kSplitSlotFloats floats, split_ctr kSplitSlots tickets;
+  // ncu = compute units used to size waves (at most kSplitSlots, a multiple of 8).
+  float* split_ws;
+  int32_t* split_ctr;
+  int ncu;
+  // Optional (null: none): events that bracket the GEMM kernel itself (recorded by its
+  // dispatch where the kernel supports that, else recorded on the stream around it).
+  hipEvent_t ev_start, ev_stop;
 };
+constexpr int kSplitSlots = 256;
+constexpr int64_t kSplitSlotFloats = 256 * 256;
+// Compute units of the current device, capped at kSplitSlots (0 when not a multiple of 8).
+int device_split_cus();
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
-// bf16, 256 x 256 tiles (expert_gemm_bf16.hip).
+// bf16, 256 x 256 tiles (expert_gemm_bf16.hip). The K-split tickets (split_ctr) must be zero
+// on entry; the kernel leaves them zero.
 hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_zero_tickets(int32_t* tickets, int n, hipStream_t s);
 
 // Combine: out[t] = sum_j gates[t,j] * y[slot_row[t*k+j]].
 hipError_t launch_combine(const Problem& p, const void* y, const int32_t* slot_row,

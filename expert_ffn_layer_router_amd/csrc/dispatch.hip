@@ -64,9 +64,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_rank_kernel(
 
 __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
     int64_t nblk, int E, int64_t capacity, int32_t* __restrict__ blk_counts,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ zero,
+    int nzero) {
   __shared__ int s_kept[kMaxExperts];
   const int e = threadIdx.x;
+  if (zero && e < nzero) zero[e] = 0;  // a later kernel's counters (see launch_dispatch)
   if (e < E) {
     int run = 0;
     constexpr int kChunk = 16;  // independent loads in flight
@@ -142,14 +144,15 @@ int64_t dispatch_blocks(const Problem& p) {
 
 hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* slot_row, void* x_perm,
-                           int32_t* blk_counts, int32_t* local_rank, hipStream_t s) {
+                           int32_t* blk_counts, int32_t* local_rank, hipStream_t s,
+                           int32_t* zero, int nzero) {
   const int64_t nblk = dispatch_blocks(p);
   if (nblk > 0) {
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, s, p.T,
                        p.top_k, p.E, idx, blk_counts, local_rank);
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kMaxExperts), 0, s, nblk, p.E,
-                     p.capacity, blk_counts, counts, offsets);
+                     p.capacity, blk_counts, counts, offsets, zero, nzero);
   if (p.T == 0) return hipGetLastError();
   const int64_t es = (p.dtype == MOE_BF16) ? 2 : 4;
   const int64_t row_bytes = p.D * es;

@@ -25,6 +25,8 @@
 //  * Tile order: expert by expert, in blocks of (that expert's M-tiles) x 8 column tiles with
 //    the M-tiles fastest; each XCD (blocks b with the same b % 8) works through a contiguous
 //    eighth of the real tiles, so the tiles it runs at once share rows and columns in its L2.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "tile_schedule.hpp"
 
@@ -35,6 +37,8 @@ constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kTileBlockN = 8;       // column tiles per L2-sharing block of one expert
 constexpr int kSlab = kBK * 256;     // elements of one stage of either operand (32 KB)
+constexpr int kMaxSplit = 4;         // K parts of a tail tile at most
+constexpr int kMinPartStages = 32;   // K stages of a part at least (K >= 2048 per part)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -126,9 +130,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   __shared__ __align__(16) uint16_t sB0[kSlab];
   __shared__ __align__(16) uint16_t sB1[kSlab];
 
+  __shared__ int s_last;
+
+  // Tiles that fill whole waves of the CUs run over all of K. When the count leaves a partial
+  // last wave of r tiles, those tiles are split along K into s parts (r * s <= CUs, each part
+  // an even number of stages), so the tail is one short wave instead of a long, mostly idle
+  // one. Block b runs on XCD b % 8; each XCD takes a contiguous eighth of the whole tiles,
+  // then an eighth of the split parts.
   const int b = blockIdx.x;
+  const TileScan sc = tile_scan(g.offsets, g.E, kBM, nt);
+  const int total = sc.total;
+  const int nst_all = (int)(g.K / kBK);
+  int full = total, r = 0, split = 1;
+  if (g.split_ws && g.ncu >= 8 && total % g.ncu != 0) {
+    full = total / g.ncu * g.ncu;
+    r = total - full;
+    split = min(kMaxSplit, g.ncu / r);
+    // each part needs an even number of stages, and enough of them (kMinPartStages) to pay
+    // for storing and adding its float32 partial
+    while (split > 1 && (nst_all % (2 * split) != 0 || nst_all / split < kMinPartStages)) --split;
+    if (split == 1) full = total;
+  }
+  int L, ks = 0;
+  const int xcd = b & 7, jb = b >> 3;
+  if (split == 1) {
+    const int chunk = (total + 7) >> 3;
+    if (jb >= chunk) return;
+    L = xcd * chunk + jb;
+    if (L >= total) return;
+  } else {
+    const int F8 = full >> 3;  // full is a multiple of the CU count, itself a multiple of 8
+    if (jb < F8) {
+      L = xcd * F8 + jb;
+    } else {
+      const int R8 = (r * split + 7) >> 3;
+      const int u = xcd * R8 + (jb - F8);
+      if (jb - F8 >= R8 || u >= r * split) return;
+      L = full + u / split;
+      ks = u % split;
+    }
+  }
+  const int parts = L >= full ? split : 1;  // K parts of this tile
   int e, row0, rows, n_tile;
-  if (!find_tile_2d(g.offsets, g.E, kBM, nt, kTileBlockN, b, e, row0, rows, n_tile)) return;
+  tile_of(sc, g.offsets, kBM, nt, kTileBlockN, L, e, row0, rows, n_tile);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,75 +246,183 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
 
   const uint32_t la0 = lds_addr(sA0), la1 = lds_addr(sA1);
   const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
-  const int nst = (int)(K / kBK);  // even: K % 128 == 0 is required
-  const int64_t last = (int64_t)(nst - 1) * kBK;
+  const int nst = nst_all / parts;  // even: K % 128 == 0, and parts divides it in pairs
+  const int64_t kbeg = (int64_t)ks * nst * kBK;
+  const int64_t last = kbeg + (int64_t)(nst - 1) * kBK;
 
-  load_stage(ld, 0, la0, lb0, wv);
+  load_stage(ld, kbeg, la0, lb0, wv);
   for (int s = 0; s < nst; s += 2) {
     wait_vm0();
     block_barrier();
-    load_stage(ld, (int64_t)(s + 1) * kBK, la1, lb1, wv);
+    load_stage(ld, kbeg + (int64_t)(s + 1) * kBK, la1, lb1, wv);
     compute_stage((const char*)sA0, (const char*)sB0, aoff, boff, acc);
     wait_vm0();
     block_barrier();
-    load_stage(ld, s + 2 < nst ? (int64_t)(s + 2) * kBK : last, la0, lb0, wv);
+    load_stage(ld, s + 2 < nst ? kbeg + (int64_t)(s + 2) * kBK : last, la0, lb0, wv);
     compute_stage((const char*)sA1, (const char*)sB1, aoff, boff, acc);
   }
   // The prefetch past the last stage is still in flight: let it land before the wave can end
   // (the block's LDS must not be written after it is released).
   wait_vm0();
 
+  // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a time, in
+  // a lane-interleaved layout), then take a ticket; the part that takes the last ticket adds
+  // all parts in part order (its own from registers) while it stores the tile. The sum order
+  // is fixed, so the result does not depend on which part finishes last.
+  float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
+  auto pidx = [&](int mi, int c, int v) -> int64_t {
+    return ((((wv * 2 + mi) * 8 + c) * 4 + (v >> 2)) * 64 + lane) * 4 + (v & 3);
+  };
+  if (parts > 1) {
+    if (64 * wv < rows) {
+      float* mine = slots + (int64_t)ks * kSplitSlotFloats;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            *(float4*)(mine + pidx(mi, c, 4 * v4)) =
+                make_float4(acc[mi][c][4 * v4], acc[mi][c][4 * v4 + 1], acc[mi][c][4 * v4 + 2],
+                            acc[mi][c][4 * v4 + 3]);
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
+  }
   if (64 * wv >= rows) return;
   // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
   uint16_t* C = (uint16_t*)g.C;
+  auto store_tile = [&](auto val) {
 #pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 64 * wv + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r >= rows) continue;
+        uint16_t* crow = C + (int64_t)(row0 + r) * N;
+        if (kSwiGLU) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n0 + 32 * q + (lane & 31);
+            if (col < N) {
+              const float gt = val(mi, 2 * q, v), up = val(mi, 2 * q + 1, v);
+              crow[col] = f32_to_bf16(gt / (1.f + __expf(-gt)) * up);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const int64_t col = n0 + 32 * c + (lane & 31);
+            if (col < N) {
+              float x = val(mi, c, v);
+              if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+              crow[col] = f32_to_bf16(x);
+            }
+          }
+        }
+      }
+  };
+  if (parts == 1) {
+    store_tile([&](int mi, int c, int v) { return acc[mi][c][v]; });
+    return;
+  }
+  // Every part (this one included) has stored its partial: add them in part order, 16
+  // coalesced bytes (4 rows of one column) per lane and part at a time, and store the rows.
+  auto part4 = [&](int mi, int c, int v4) {
+    const int64_t pi = pidx(mi, c, 4 * v4);
+    f32x4 tot = *(const f32x4*)(slots + pi);
+#pragma unroll
+    for (int q = 1; q < kMaxSplit; ++q)
+      if (q < parts) tot += *(const f32x4*)(slots + q * kSplitSlotFloats + pi);
+    return tot;
+  };
   for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = 64 * wv + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= rows) continue;
-      uint16_t* crow = C + (int64_t)(row0 + r) * N;
+    for (int v4 = 0; v4 < 4; ++v4) {
       if (kSwiGLU) {
-#pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const f32x4 gt = part4(mi, 2 * q, v4), up = part4(mi, 2 * q + 1, v4);
           const int64_t col = n0 + 32 * q + (lane & 31);
-          if (col < N) {
-            const float gt = acc[mi][2 * q][v], up = acc[mi][2 * q + 1][v];
-            crow[col] = f32_to_bf16(gt / (1.f + __expf(-gt)) * up);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i;
+            if (r < rows && col < N)
+              C[(int64_t)(row0 + r) * N + col] = f32_to_bf16(gt[i] / (1.f + __expf(-gt[i])) * up[i]);
           }
         }
       } else {
-#pragma unroll
         for (int c = 0; c < 8; ++c) {
+          const f32x4 t = part4(mi, c, v4);
           const int64_t col = n0 + 32 * c + (lane & 31);
-          if (col < N) {
-            float val = acc[mi][c][v];
-            if (EPI == EPI_RELU) val = fmaxf(val, 0.f);
-            crow[col] = f32_to_bf16(val);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i;
+            float x = t[i];
+            if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+            if (r < rows && col < N) C[(int64_t)(row0 + r) * N + col] = f32_to_bf16(x);
           }
         }
       }
     }
 }
 
+__global__ void zero_tickets_kernel(int32_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
 }  // namespace
 
-hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g, hipStream_t s) {
+hipError_t launch_zero_tickets(int32_t* tickets, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_tickets_kernel, dim3(1), dim3(256), 0, s, tickets, n);
+  return hipGetLastError();
+}
+
+int device_split_cus() {
+  static int cache[64] = {0};  // per device: 0 unknown, -1 not usable, else the CU count
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    n = n < kSplitSlots ? n : kSplitSlots;
+    cache[dev] = (n >= 8 && n % 8 == 0) ? n : -1;
+  }
+  return cache[dev] > 0 ? cache[dev] : 0;
+}
+
+hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) {
+  GroupedGemm g = g_in;
+  // A K split needs at least two parts of kMinPartStages stages each; below that the split
+  // path (and its ticket reset) is skipped altogether.
+  if (g.K / kBK < 2 * kMinPartStages) {
+    g.split_ws = nullptr;
+    g.split_ctr = nullptr;
+  }
   const int64_t mt_max = (g.max_rows + kBM - 1) / kBM + g.E;
   const int64_t cols = (g.epilogue == EPI_SWIGLU) ? kBN / 2 : kBN;
   const int64_t nt = (g.N + cols - 1) / cols;
-  int64_t G = mt_max * nt;
+  // every whole tile, plus at most one split part per CU beyond them
+  int64_t G = mt_max * nt + (g.split_ws ? g.ncu + 8 : 0);
   G = (G + 7) / 8 * 8;
   const dim3 grid((unsigned)G);
+  // The start/stop events (if any) are recorded by the kernel's own dispatch, so timing adds
+  // no packets, and no gaps, to the stream.
   switch (g.epilogue) {
     case EPI_NONE:
-      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_NONE>, grid, dim3(kThreads), 0, s, g, (int)nt);
+      hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_NONE>, grid, dim3(kThreads), 0, s,
+                            g.ev_start, g.ev_stop, 0, g, (int)nt);
       break;
     case EPI_RELU:
-      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s, g, (int)nt);
+      hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s,
+                            g.ev_start, g.ev_stop, 0, g, (int)nt);
       break;
     default:
-      hipLaunchKernelGGL(gemm_bf16_256_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s, g, (int)nt);
+      hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s,
+                            g.ev_start, g.ev_stop, 0, g, (int)nt);
       break;
   }
   return hipGetLastError();

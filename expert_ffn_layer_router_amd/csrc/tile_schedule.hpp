@@ -48,24 +48,29 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   return true;
 }
 
-// Maps block b of a grid of at least (real tile count rounded up to 8) blocks to a tile
-// (expert, first row, rows, column tile) of the (M-tiles x nt column tiles) grid of each
-// expert. Experts come in order; within an expert the
-// tiles go in blocks of nb column tiles, and inside a block the M-tiles vary fastest. A
-// block of one expert (its M-tiles x nb column tiles) is about as many tiles as one XCD runs
-// at once, so concurrent blocks share both their activation rows and their weight columns
-// in that XCD's L2. Every wave computes the same answer. Returns false past the last tile.
-__device__ __forceinline__ bool find_tile_2d(const int32_t* __restrict__ offsets, int E, int BM,
-                                             int nt, int nb, int b, int& e_out, int& row0,
-                                             int& rows, int& n_tile) {
+// Tiles of a grouped GEMM laid out as (M-tiles x nt column tiles) per expert, experts in
+// order; within an expert the tiles go in blocks of nb column tiles with the M-tiles fastest.
+// A block of one expert (its M-tiles x nb column tiles) is about as many tiles as one XCD runs
+// at once, so concurrent tiles share both their activation rows and their weight columns in
+// that XCD's L2. tile_scan takes the per-expert tile counts (every wave computes the same);
+// tile_of maps a linear tile id to (expert, first row, rows, column tile).
+struct TileScan {
+  int excl, incl;  // this lane's experts (4 lane, .. 4 lane + 3): first tile id, one past last
+  int total;       // tiles of all experts
+  int tiles[4];
+};
+
+__device__ __forceinline__ TileScan tile_scan(const int32_t* __restrict__ offsets, int E, int BM,
+                                              int nt) {
   const int lane = lane_id();
-  int n[4], tiles[4], mine = 0;
+  TileScan sc;
+  int mine = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 4 * lane + q;
-    n[q] = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-    tiles[q] = ((n[q] + BM - 1) / BM) * nt;
-    mine += tiles[q];
+    const int n = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    sc.tiles[q] = ((n + BM - 1) / BM) * nt;
+    mine += sc.tiles[q];
   }
   int incl = mine;
 #pragma unroll
@@ -73,24 +78,27 @@ __device__ __forceinline__ bool find_tile_2d(const int32_t* __restrict__ offsets
     const int v = __shfl_up(incl, o);
     if (lane >= o) incl += v;
   }
-  const int excl = incl - mine;
-  // Block b runs on XCD b % 8; each XCD takes one contiguous eighth of the real tiles.
-  const int total = __shfl(incl, kWave - 1);
-  const int chunk = (total + 7) >> 3;
-  if ((b >> 3) >= chunk) return false;
-  const int L = (b & 7) * chunk + (b >> 3);
-  const unsigned long long own = __ballot(L >= excl && L < incl);
-  if (own == 0ull) return false;
+  sc.incl = incl;
+  sc.excl = incl - mine;
+  sc.total = __shfl(incl, kWave - 1);
+  return sc;
+}
+
+__device__ __forceinline__ void tile_of(const TileScan& sc, const int32_t* __restrict__ offsets,
+                                        int BM, int nt, int nb, int L, int& e_out, int& row0,
+                                        int& rows, int& n_tile) {
+  const int lane = lane_id();
+  const unsigned long long own = __ballot(L >= sc.excl && L < sc.incl);
   const int owner = __ffsll((long long)own) - 1;
   int e = -1, local = 0;
-  int run = excl;
+  int run = sc.excl;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if (e < 0 && L < run + tiles[q]) {
+    if (e < 0 && L < run + sc.tiles[q]) {
       e = 4 * lane + q;
       local = L - run;
     }
-    run += tiles[q];
+    run += sc.tiles[q];
   }
   e = __shfl(e, owner);
   local = __shfl(local, owner);
@@ -103,7 +111,6 @@ __device__ __forceinline__ bool find_tile_2d(const int32_t* __restrict__ offsets
   e_out = e;
   row0 = offsets[e] + m * BM;
   rows = min(BM, cnt - m * BM);
-  return true;
 }
 
 }  // namespace moe

@@ -167,9 +167,12 @@ enum {
 };
 
 /* moe_forward with per-stage timing: `stage_events` holds 2 * MOE_NUM_STAGES events that the
- * caller created (hipEventCreate); event 2s is recorded on `stream` right before stage s and
- * event 2s+1 right after it, so hipEventElapsedTime(events[2s], events[2s+1]) is the device
- * time of stage s once the stream has reached it. NULL stage_events behaves as moe_forward.
+ * caller created (hipEventCreate), or NULL entries for stages not to be timed. For the two
+ * expert stages the pair brackets the GEMM kernel itself (recorded by the kernel's dispatch,
+ * which adds nothing to the stream); for the other stages event 2s is recorded on `stream`
+ * right before stage s and event 2s+1 right after it (each such record can leave the device
+ * idle for a few microseconds). hipEventElapsedTime(events[2s], events[2s+1]) is then the
+ * device time of stage s. NULL stage_events behaves as moe_forward.
  * (Per-stage device timing of the layer; the work is identical to moe_forward.) */
 moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_router,
                              const float* router_bias, const void* w1, const void* w3,

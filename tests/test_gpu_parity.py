@@ -35,6 +35,10 @@ MID_CASES = {
     "relu_f32_ragged": spec("small_relu_f32", T=333, D=40, DH=70, E=5, top_k=3,
                             capacity_factor=1.3),
     "swiglu_f32": spec("small_relu_f32", T=50, D=12, DH=20, E=6, top_k=2, kind="swiglu"),
+    # long down-projection K with few tiles: the tail tiles are split along K (2 and 4 parts)
+    "swiglu_long_k_split2": spec("mixtral_swiglu_bf16", T=300, D=256, DH=4096, E=4, top_k=2),
+    "relu_long_k_split4": spec("switch_top1_cap_bf16", T=200, D=128, DH=8192, E=2,
+                               capacity_factor=0.0),
 }
 
 
@@ -109,8 +113,11 @@ def test_empty_batch():
     assert (outs["expert_offsets"] == 0).all() and (outs["expert_counts"] == 0).all()
 
 
-def test_deterministic():
-    sp = MID_CASES["swiglu_zipf_cap"]
+@pytest.mark.parametrize("name", ["swiglu_zipf_cap", "relu_long_k_split4"])
+def test_deterministic(name):
+    """Bit-identical results on repeated calls (no order-dependent atomics; the K-split parts
+    are added in part order whichever finishes last)."""
+    sp = MID_CASES[name]
     I = make_inputs(sp, seed=11)
     a, b = run_forward(I), run_forward(I)
     for key in a:
