@@ -139,7 +139,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   // then an eighth of the split parts.
   const int b = blockIdx.x;
   const TileScan sc = tile_scan(g.offsets, g.E, kBM, nt);
-  const int total = sc.total;
+  // every value that steers the loop is wave-uniform; saying so keeps the loop under scalar
+  // control (a divergent trip count would make the compiler copy the accumulators)
+  const int total = __builtin_amdgcn_readfirstlane(sc.total);
   const int nst_all = (int)(g.K / kBK);
   int full = total, r = 0, split = 1;
   if (g.split_ws && g.ncu >= 8 && total % g.ncu != 0) {
@@ -173,6 +175,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   const int parts = L >= full ? split : 1;  // K parts of this tile
   int e, row0, rows, n_tile;
   tile_of(sc, g.offsets, kBM, nt, kTileBlockN, L, e, row0, rows, n_tile);
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -265,36 +271,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   // (the block's LDS must not be written after it is released).
   wait_vm0();
 
-  // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a time, in
-  // a lane-interleaved layout), then take a ticket; the part that takes the last ticket adds
-  // all parts in part order (its own from registers) while it stores the tile. The sum order
-  // is fixed, so the result does not depend on which part finishes last.
-  float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
-  auto pidx = [&](int mi, int c, int v) -> int64_t {
-    return ((((wv * 2 + mi) * 8 + c) * 4 + (v >> 2)) * 64 + lane) * 4 + (v & 3);
-  };
-  if (parts > 1) {
-    if (64 * wv < rows) {
-      float* mine = slots + (int64_t)ks * kSplitSlotFloats;
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4)
-            *(float4*)(mine + pidx(mi, c, 4 * v4)) =
-                make_float4(acc[mi][c][4 * v4], acc[mi][c][4 * v4 + 1], acc[mi][c][4 * v4 + 2],
-                            acc[mi][c][4 * v4 + 3]);
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
-  }
-  if (64 * wv >= rows) return;
   // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
   uint16_t* C = (uint16_t*)g.C;
   auto store_tile = [&](auto val) {
@@ -327,18 +303,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         }
       }
   };
-  if (parts == 1) {
-    store_tile([&](int mi, int c, int v) { return acc[mi][c][v]; });
+  if (parts == 1) {  // a whole tile: store it from the accumulators
+    if (64 * wv < rows) store_tile([&](int mi, int c, int v) { return acc[mi][c][v]; });
     return;
   }
+
+  // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a time, in
+  // a lane-interleaved layout), then take a ticket; the part that takes the last ticket adds
+  // all parts in part order and stores the tile. The sum order is fixed, so the result does
+  // not depend on which part finishes last.
+  float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
+  {
+    if (64 * wv < rows) {
+      float* mine = slots + (int64_t)ks * kSplitSlotFloats;
+      // group (wv, mi, c) of 16 accumulators: 4 KB at a wave-uniform base, lane l's 16-byte
+      // chunk v4 at +1 KB * v4 + 16 l (so every store is base + one lane offset + a constant)
+      const uint32_t lane_off = (uint32_t)lane * 16u;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          char* gb = (char*)mine + (int64_t)((wv * 2 + mi) * 8 + c) * 4096;
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4)
+            *(f32x4*)(gb + v4 * 1024 + lane_off) =
+                f32x4{acc[mi][c][4 * v4], acc[mi][c][4 * v4 + 1], acc[mi][c][4 * v4 + 2],
+                      acc[mi][c][4 * v4 + 3]};
+        }
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
+  }
+  if (64 * wv >= rows) return;
   // Every part (this one included) has stored its partial: add them in part order, 16
   // coalesced bytes (4 rows of one column) per lane and part at a time, and store the rows.
+  const uint32_t lane_off = (uint32_t)lane * 16u;
   auto part4 = [&](int mi, int c, int v4) {
-    const int64_t pi = pidx(mi, c, 4 * v4);
-    f32x4 tot = *(const f32x4*)(slots + pi);
+    const char* gb = (const char*)slots + (int64_t)((wv * 2 + mi) * 8 + c) * 4096 + v4 * 1024;
+    f32x4 tot = *(const f32x4*)(gb + lane_off);
 #pragma unroll
     for (int q = 1; q < kMaxSplit; ++q)
-      if (q < parts) tot += *(const f32x4*)(slots + q * kSplitSlotFloats + pi);
+      if (q < parts) tot += *(const f32x4*)(gb + q * kSplitSlotFloats * 4 + lane_off);
     return tot;
   };
   for (int mi = 0; mi < 2; ++mi)
