@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("ed0be10a168ed6a3663d90efe8697d53a40dfc6094537e42f707a55442332141",
-                            1842045.703125, 229376.078125),
+    "mixtral_swiglu_bf16": ("b1bd779b0a85821576d3f5a874f243db10d6bd6cadfb75b953989892c805aec1",
+                            2110486.410714286, 301952.40178571426),
 }
 
 
