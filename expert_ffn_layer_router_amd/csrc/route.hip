@@ -620,9 +620,6 @@ __global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
   }
 }
 
-// aux = E * sum_e (count_e / (T k)) * (sum_t probs[t, e] / T). 1024 threads: thread i sums
-// the blocks b = p (mod P) of expert e = i / P, in block order; the P part sums are then
-// added in order, and the E terms in expert order.
 constexpr int kAuxThreads = 256;
 
 // Switch loss from the per-block partials (expert-major, nblk per expert): block e sums
