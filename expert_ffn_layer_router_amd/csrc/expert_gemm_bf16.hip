@@ -17,11 +17,16 @@
 //    instruction fills 2 K-rows; chunk c of K-row k is stored at c ^ (4 (k % 4)), and the MFMA
 //    operands come from transposed reads (ds_read_b64_tr_b16), which turn the N-contiguous
 //    layout into 8 consecutive K values per lane.
-// Two LDS buffers per operand (128 KB): the loads of stage s + 1 run while stage s computes.
-// The loads are issued from inline assembly, so the compiler does not track them; every wait
-// for them is explicit (s_waitcnt vmcnt(0) before the barrier that publishes a stage).
+// Two LDS buffers per operand (128 KB). The block synchronises once per stage, before the
+// stage's last k-step: that k-step's operands are already in registers, so its MFMAs cover
+// the reads of the next buffer's first operands and the issue of the loads two stages ahead
+// (into the buffer just finished). The loads are issued from inline assembly, so the compiler
+// does not track them; every wait for them is explicit (s_waitcnt vmcnt(0) before the
+// barrier that publishes a stage).
 //  * SwiGLU: the 256 columns interleave 32-column tiles of W1 and W3 for the same 128 output
 //    columns, so each lane holds the gate and the up value of the same output.
+//  * Epilogue: lanes l and l ^ 1 hold adjacent columns; one swap per pair of rows lets each
+//    lane convert two outputs with one v_cvt_pk_bf16_f32 and store them in 4 bytes.
 //  * Tile order: expert by expert, in blocks of (that expert's M-tiles) x 8 column tiles with
 //    the M-tiles fastest; each XCD (blocks b with the same b % 8) works through a contiguous
 //    eighth of the real tiles, so the tiles it runs at once share rows and columns in its L2.
@@ -59,6 +64,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void wait_vm0_lgkm0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 struct Loader {
@@ -77,49 +83,103 @@ __device__ __forceinline__ void load_stage(const Loader& ld, int64_t k0, uint32_
     dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sb + (8 * wv + j) * 1024);
 }
 
+typedef __attribute__((address_space(3))) const char lds_cchar;
+
+// Per-buffer operand read bases: LDS byte address of the buffer + this lane's offset for each
+// of the 4 slots. They are made opaque to the optimiser, so every read adds its constant part
+// in the instruction's offset field instead of holding one precomputed address per read.
+__device__ __forceinline__ void make_bases(uint32_t lds_a, uint32_t lds_b, const uint32_t (&aoff)[4],
+                                           const uint32_t (&boff)[4], uint32_t (&ab)[4],
+                                           uint32_t (&bb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ab[i] = lds_a + aoff[i];
+    bb[i] = lds_b + boff[i];
+    asm volatile("" : "+v"(ab[i]));
+    asm volatile("" : "+v"(bb[i]));
+  }
+}
+
 // B operand of n-tile c, k-step t: two transposed 8-byte reads (K-rows 16t + 8 (lane/32) + 4h
 // + (lane%16)/4, see the offsets in the kernel) give column lane % 32, K values
 // 16t + 8 (lane / 32) .. +7.
-__device__ __forceinline__ bf16x8 read_b(const char* sb, const uint32_t (&boff)[4], int c, int t) {
-  const char* p = sb + boff[c & 3] + (c & 4) * 64 + t * 16 * 512;
+__device__ __forceinline__ bf16x8 read_b(const uint32_t (&bb)[4], int c, int t) {
+  lds_cchar* p = (lds_cchar*)(uintptr_t)bb[c & 3] + (c & 4) * 64 + t * 16 * 512;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * 512));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // A operand of m-tile mi, k-step t: row 64 w + 32 mi + lane % 32, K values 16t + 8 (lane/32)..
-__device__ __forceinline__ bf16x8 read_a(const char* sa, const uint32_t (&aoff)[4], int mi, int t) {
-  return *(const lds_bf16x8*)(sa + aoff[t] + mi * 32 * 128);
+__device__ __forceinline__ bf16x8 read_a(const uint32_t (&ab)[4], int mi, int t) {
+  return *(const lds_bf16x8*)((lds_cchar*)(uintptr_t)ab[t] + mi * 32 * 128);
 }
 
-// One stage: 4 k-steps x (2 x 8) MFMAs. B operands rotate through one register set (the read
-// for k-step t + 1 of n-tile c follows the two MFMAs of k-step t that consume it); A operands
-// of k-step t + 1 are read at the start of k-step t.
-__device__ __forceinline__ void compute_stage(const char* sa, const char* sb,
-                                              const uint32_t (&aoff)[4],
-                                              const uint32_t (&boff)[4], f32x16 (&acc)[2][8]) {
-  bf16x8 b[8], a0 = read_a(sa, aoff, 0, 0), a1 = read_a(sa, aoff, 1, 0);
+// One stage (4 k-steps x 2 x 8 MFMAs) on the current buffer, with the stage boundary inside it.
+// Operands rotate through registers: the B read for k-step t + 1 of n-tile c follows the two
+// MFMAs of k-step t that consume it, and the A operands of k-step t + 1 are read at the start
+// of k-step t. So k-steps 0..2 bring in all of k-step 3's operands; then every read and this
+// wave's loads of the next buffer are waited for and the block synchronises, and k-step 3 runs
+// from registers while the next buffer's k-step 0 operands are read and, when `load2`, the
+// loads of the stage after next (K offset k2) are issued into the current buffer, which no
+// wave reads any more. The matrix pipe is thus never left waiting for a whole LDS round trip
+// at a stage boundary.
+__device__ __forceinline__ void stage(const uint32_t (&ab)[4], const uint32_t (&bb)[4],
+                                      const uint32_t (&abn)[4], const uint32_t (&bbn)[4],
+                                      f32x16 (&acc)[2][8], bf16x8& a0, bf16x8& a1, bf16x8 (&b)[8],
+                                      const Loader& ld, int64_t k2, bool load2, uint32_t sa,
+                                      uint32_t sb, int wv) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = read_b(sb, boff, c, 0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    bf16x8 n0 = a0, n1 = a1;
-    if (t < 3) {
-      n0 = read_a(sa, aoff, 0, t + 1);
-      n1 = read_a(sa, aoff, 1, t + 1);
-    }
+  for (int t = 0; t < 3; ++t) {
+    const bf16x8 n0 = read_a(ab, 0, t + 1), n1 = read_a(ab, 1, t + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
       acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
-      if (t < 3) b[c] = read_b(sb, boff, c, t + 1);
+      b[c] = read_b(bb, c, t + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     a0 = n0;
     a1 = n1;
   }
+  wait_vm0_lgkm0();
+  block_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  const bf16x8 n0 = read_a(abn, 0, 0), n1 = read_a(abn, 1, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t bk = k2 * ld.b_row_bytes;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
+    acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
+    b[c] = read_b(bbn, c, 0);
+    if (load2) {
+      dma16(ld.a[c] + k2 * 2, sa + (8 * wv + c) * 1024);
+      dma16(ld.b[c & 1] + bk + (int64_t)(2 * c) * ld.b_row_bytes, sb + (8 * wv + c) * 1024);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  a0 = n0;
+  a1 = n1;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to two bfloat16 (round to nearest even, one v_cvt_pk_bf16_f32), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ float silu_f(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
+}
+
+// The value of lane l ^ 1.
+__device__ __forceinline__ float swap_adjacent_lanes(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
 }
 
 template <int EPI>
@@ -254,57 +314,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
   const int nst = nst_all / parts;  // even: K % 128 == 0, and parts divides it in pairs
   const int64_t kbeg = (int64_t)ks * nst * kBK;
-  const int64_t last = kbeg + (int64_t)(nst - 1) * kBK;
 
+  // Stage 0 into buffer 0, stage 1 into buffer 1 while stage 0's first operands are read;
+  // from then on each stage issues the loads of the stage after next (see `stage`).
   load_stage(ld, kbeg, la0, lb0, wv);
-  for (int s = 0; s < nst; s += 2) {
-    wait_vm0();
-    block_barrier();
-    load_stage(ld, kbeg + (int64_t)(s + 1) * kBK, la1, lb1, wv);
-    compute_stage((const char*)sA0, (const char*)sB0, aoff, boff, acc);
-    wait_vm0();
-    block_barrier();
-    load_stage(ld, s + 2 < nst ? kbeg + (int64_t)(s + 2) * kBK : last, la0, lb0, wv);
-    compute_stage((const char*)sA1, (const char*)sB1, aoff, boff, acc);
-  }
-  // The prefetch past the last stage is still in flight: let it land before the wave can end
-  // (the block's LDS must not be written after it is released).
   wait_vm0();
+  block_barrier();
+  load_stage(ld, kbeg + kBK, la1, lb1, wv);
+  uint32_t ab0[4], bb0[4], ab1[4], bb1[4];
+  make_bases(la0, lb0, aoff, boff, ab0, bb0);
+  make_bases(la1, lb1, aoff, boff, ab1, bb1);
+  bf16x8 a0 = read_a(ab0, 0, 0), a1 = read_a(ab0, 1, 0), bq[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) bq[c] = read_b(bb0, c, 0);
+  for (int s = 0; s < nst; s += 2) {
+    stage(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 2) * kBK, s + 2 < nst, la0,
+          lb0, wv);
+    stage(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 3) * kBK, s + 3 < nst, la1,
+          lb1, wv);
+  }
+  // (The last stage's reads of the "next" buffer fetch operands nobody uses; no load is in
+  // flight past the last stage.)
 
   // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
   uint16_t* C = (uint16_t*)g.C;
-  auto store_tile = [&](auto val) {
+  if (parts == 1) {  // a whole tile: store it from the accumulators
+    if (64 * wv >= rows) return;
+    // Lanes l and l ^ 1 hold adjacent columns of the same rows. For each pair of rows
+    // (v0, v0 + 1) they swap one value, so the even lane stores columns (c, c + 1) of row v0
+    // and the odd lane the same two columns of row v0 + 1: one 4-byte store per two outputs.
+    const bool odd = lane & 1;
+    const int lrow = 64 * wv + 4 * (lane >> 5) + (odd ? 1 : 0);
+    const int colp = (lane & 31) & ~1;
+    uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
+    const bool whole = 64 * wv + 64 <= rows && n0 + (kSwiGLU ? kBN / 2 : kBN) <= N;
+    auto put = [&](int mi, int v0, int cq, float x0, float x1) {
+      const float recv = swap_adjacent_lanes(odd ? x0 : x1);
+      const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
+      const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
+      if (whole || (lrow + dr < rows && n0 + cq + colp < N))
+        *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
+    };
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 64 * wv + 32 * mi + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r >= rows) continue;
-        uint16_t* crow = C + (int64_t)(row0 + r) * N;
-        if (kSwiGLU) {
+      for (int q = 0; q < (kSwiGLU ? 4 : 8); ++q)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t col = n0 + 32 * q + (lane & 31);
-            if (col < N) {
-              const float gt = val(mi, 2 * q, v), up = val(mi, 2 * q + 1, v);
-              crow[col] = f32_to_bf16(gt / (1.f + __expf(-gt)) * up);
+        for (int v0 = 0; v0 < 16; v0 += 2) {
+          float x0, x1;
+          if (kSwiGLU) {  // columns 32q.. of the output: gate in n-tile 2q, up in 2q + 1
+            x0 = silu_f(acc[mi][2 * q][v0]) * acc[mi][2 * q + 1][v0];
+            x1 = silu_f(acc[mi][2 * q][v0 + 1]) * acc[mi][2 * q + 1][v0 + 1];
+          } else {
+            x0 = acc[mi][q][v0];
+            x1 = acc[mi][q][v0 + 1];
+            if (EPI == EPI_RELU) {
+              x0 = fmaxf(x0, 0.f);
+              x1 = fmaxf(x1, 0.f);
             }
           }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int64_t col = n0 + 32 * c + (lane & 31);
-            if (col < N) {
-              float x = val(mi, c, v);
-              if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
-              crow[col] = f32_to_bf16(x);
-            }
-          }
+          put(mi, v0, 32 * q, x0, x1);
         }
-      }
-  };
-  if (parts == 1) {  // a whole tile: store it from the accumulators
-    if (64 * wv < rows) store_tile([&](int mi, int c, int v) { return acc[mi][c][v]; });
     return;
   }
 
@@ -361,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
           for (int i = 0; i < 4; ++i) {
             const int r = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i;
             if (r < rows && col < N)
-              C[(int64_t)(row0 + r) * N + col] = f32_to_bf16(gt[i] / (1.f + __expf(-gt[i])) * up[i]);
+              C[(int64_t)(row0 + r) * N + col] = f32_to_bf16(silu_f(gt[i]) * up[i]);
           }
         }
       } else {
