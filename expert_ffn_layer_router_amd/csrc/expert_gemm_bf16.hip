@@ -177,6 +177,15 @@ __device__ __forceinline__ float silu_f(float g) {
   return g * __builtin_amdgcn_rcpf(1.f + __expf(-g));
 }
 
+// An accumulator, read into a VGPR where it is used. (Left to itself the compiler copies all
+// 256 accumulators out of their AGPRs at the end of the K loop, which needs more VGPRs than
+// there are; the spilled ones then cost scratch round trips that also wait for every store.)
+__device__ __forceinline__ float acc_get(float a) {
+  float r;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(a));
+  return r;
+}
+
 // The value of lane l ^ 1.
 __device__ __forceinline__ float swap_adjacent_lanes(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
@@ -363,11 +372,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         for (int v0 = 0; v0 < 16; v0 += 2) {
           float x0, x1;
           if (kSwiGLU) {  // columns 32q.. of the output: gate in n-tile 2q, up in 2q + 1
-            x0 = silu_f(acc[mi][2 * q][v0]) * acc[mi][2 * q + 1][v0];
-            x1 = silu_f(acc[mi][2 * q][v0 + 1]) * acc[mi][2 * q + 1][v0 + 1];
+            x0 = silu_f(acc_get(acc[mi][2 * q][v0])) * acc_get(acc[mi][2 * q + 1][v0]);
+            x1 = silu_f(acc_get(acc[mi][2 * q][v0 + 1])) * acc_get(acc[mi][2 * q + 1][v0 + 1]);
           } else {
-            x0 = acc[mi][q][v0];
-            x1 = acc[mi][q][v0 + 1];
+            x0 = acc_get(acc[mi][q][v0]);
+            x1 = acc_get(acc[mi][q][v0 + 1]);
             if (EPI == EPI_RELU) {
               x0 = fmaxf(x0, 0.f);
               x1 = fmaxf(x1, 0.f);
@@ -397,8 +406,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
 #pragma unroll
           for (int v4 = 0; v4 < 4; ++v4)
             *(f32x4*)(gb + v4 * 1024 + lane_off) =
-                f32x4{acc[mi][c][4 * v4], acc[mi][c][4 * v4 + 1], acc[mi][c][4 * v4 + 2],
-                      acc[mi][c][4 * v4 + 3]};
+                f32x4{acc_get(acc[mi][c][4 * v4]), acc_get(acc[mi][c][4 * v4 + 1]),
+                      acc_get(acc[mi][c][4 * v4 + 2]), acc_get(acc[mi][c][4 * v4 + 3])};
         }
     }
     __threadfence();
