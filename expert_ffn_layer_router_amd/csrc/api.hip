@@ -7,7 +7,6 @@
 using namespace moe;
 
 namespace {
-static_assert(kSplitSlots <= kMaxExperts, "the dispatch scan block zeroes every K-split ticket");
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 size_t elem_size(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
@@ -60,7 +59,7 @@ struct Layout {
   size_t blkc, lrank;   // dispatch: (dispatch blocks, E) int32 and (T*k) int32
   size_t perm;          // moe_forward's own permutation, (T*k) int32
   size_t hbuf;          // expert hidden activations, (T*k, DH)
-  size_t gsplit, gctr;  // bf16 GEMM K-split tail: partial tiles and tickets
+  size_t gsplit, gctr;  // bf16 GEMM: K-split partial tiles; K-split tickets + work queue
   size_t ybuf;          // moe_forward's expert outputs, (T*k, D_out)
   size_t route_end, dispatch_end, ffn_end, total;
 };
@@ -83,7 +82,7 @@ Layout layout_of(const Problem& q) {
   L.hbuf = take(q.kind == MOE_EXPERT_LINEAR ? 0 : slots * (size_t)q.DH * es);
   const bool split = q.dtype == MOE_BF16 && q.T > 0;
   L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
-  L.gctr = take(split ? (size_t)kSplitSlots * sizeof(int32_t) : 0);
+  L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
   L.ffn_end = off;
   L.perm = take(slots * sizeof(int32_t));
   L.ybuf = take(slots * (size_t)q.D_out * es);
@@ -117,13 +116,19 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
                        hipEvent_t* ev) {
   float* split_ws = nullptr;
   int32_t* split_ctr = nullptr;
+  int32_t* queue = nullptr;
   const int ncu = q.dtype == MOE_BF16 ? device_split_cus() : 0;
-  if (ncu > 0) {
-    split_ws = at<float>(ws, Lw.gsplit);
-    split_ctr = at<int32_t>(ws, Lw.gctr);
-    // both GEMMs leave the tickets zero, so one reset before the first serves both
+  if (q.dtype == MOE_BF16 && q.T > 0) {
+    int32_t* ctr = at<int32_t>(ws, Lw.gctr);
+    queue = ctr + kSplitSlots;
+    if (ncu > 0) {
+      split_ws = at<float>(ws, Lw.gsplit);
+      split_ctr = ctr;
+    }
+    // both GEMMs leave the tickets and the queue zero, so one reset before the first serves
+    // both
     if (!tickets_zeroed) {
-      const hipError_t e0 = launch_zero_tickets(split_ctr, kSplitSlots, s);
+      const hipError_t e0 = launch_zero_tickets(ctr, kSplitSlots + kQueueInts, s);
       if (e0 != hipSuccess) return e0;
     }
   }
@@ -131,6 +136,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   g.split_ws = split_ws;
   g.split_ctr = split_ctr;
   g.ncu = ncu;
+  g.queue = queue;
   g.A = A;
   g.lda = q.D;
   g.a_gather = gather;
@@ -155,6 +161,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
     d.split_ws = split_ws;
     d.split_ctr = split_ctr;
     d.ncu = ncu;
+    d.queue = queue;
     d.A = hbuf;
     d.lda = q.DH;
     d.a_gather = nullptr;
@@ -298,12 +305,12 @@ moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_
     err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream);
   mark(ev, 2 * MOE_STAGE_ROUTE + 1, stream);
   mark(ev, 2 * MOE_STAGE_DISPATCH, stream);
-  // the dispatch scan also zeroes the GEMMs' K-split tickets
+  // the dispatch scan also zeroes the GEMMs' K-split tickets and work queue
   int32_t* tickets = (q.dtype == MOE_BF16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
   if (err == hipSuccess)
     err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
                           nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
-                          tickets, tickets ? kSplitSlots : 0);
+                          tickets, tickets ? kSplitSlots + kQueueInts : 0);
   mark(ev, 2 * MOE_STAGE_DISPATCH + 1, stream);
   if (err == hipSuccess)
     err = run_experts(q, x, perm, expert_offsets, w1, w3, w2, at<void>(ws, L.hbuf),

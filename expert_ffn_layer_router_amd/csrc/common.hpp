@@ -77,8 +77,8 @@ hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* 
 
 // Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
 int64_t dispatch_blocks(const Problem& p);
-// `zero` (nullable): nzero <= kMaxExperts int32 that the scan kernel sets to 0 on the way
-// (the GEMM K-split tickets of the same call, which saves a launch).
+// `zero` (nullable): nzero int32 that the scan kernel sets to 0 on the way (the GEMMs'
+// K-split tickets and work queue of the same call, which saves a launch).
 hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_row,
                            void* x_perm, int32_t* blk_counts, int32_t* local_rank,
@@ -106,11 +106,15 @@ struct GroupedGemm {
   float* split_ws;
   int32_t* split_ctr;
   int ncu;
+  // Work queue of the 256 x 256 kernel (kQueueInts int32, zero on entry, left zero): one
+  // counter per XCD and a count of finished blocks. Null: the 256 x 256 kernel is not used.
+  int32_t* queue;
   // Optional (null: none): events that bracket the GEMM kernel itself (recorded by its
   // dispatch where the kernel supports that, else recorded on the stream around it).
   hipEvent_t ev_start, ev_stop;
 };
 constexpr int kSplitSlots = 256;
+constexpr int kQueueInts = 16;
 constexpr int64_t kSplitSlotFloats = 256 * 256;
 // Compute units of the current device, capped at kSplitSlots (0 when not a multiple of 8).
 int device_split_cus();

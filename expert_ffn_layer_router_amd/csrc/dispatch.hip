@@ -68,7 +68,8 @@ __global__ __launch_bounds__(kMaxExperts) void dispatch_scan_kernel(
     int nzero) {
   __shared__ int s_kept[kMaxExperts];
   const int e = threadIdx.x;
-  if (zero && e < nzero) zero[e] = 0;  // a later kernel's counters (see launch_dispatch)
+  if (zero)  // a later kernel's counters (see launch_dispatch)
+    for (int i = e; i < nzero; i += blockDim.x) zero[i] = 0;
   if (e < E) {
     int run = 0;
     constexpr int kChunk = 16;  // independent loads in flight

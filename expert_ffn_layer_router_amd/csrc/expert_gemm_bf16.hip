@@ -198,265 +198,344 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   __shared__ __align__(16) uint16_t sA1[kSlab];
   __shared__ __align__(16) uint16_t sB0[kSlab];
   __shared__ __align__(16) uint16_t sB1[kSlab];
-
+  __shared__ int s_unit[2];  // queue positions of later units, by unit parity
   __shared__ int s_last;
 
-  // Tiles that fill whole waves of the CUs run over all of K. When the count leaves a partial
-  // last wave of r tiles, those tiles are split along K into s parts (r * s <= CUs, each part
-  // an even number of stages), so the tail is one short wave instead of a long, mostly idle
-  // one. Block b runs on XCD b % 8; each XCD takes a contiguous eighth of the whole tiles,
-  // then an eighth of the split parts.
-  const int b = blockIdx.x;
+  // One block per CU (gridDim.x blocks: a multiple of 8, at most kSplitSlots). Tiles that fill
+  // whole waves of the blocks run over all of K. When the count leaves a partial last wave of
+  // r tiles, those tiles are split along K into s parts (r * s <= blocks, each part an even
+  // number of stages), so the tail is one short wave instead of a long, mostly idle one.
+  // Block b runs on XCD b % 8. Each XCD owns a contiguous eighth of the whole tiles, then an
+  // eighth of the split parts, and its blocks take them in order from the XCD's counter, so
+  // the tiles an XCD runs at once are neighbours that share rows and columns in its L2, and a
+  // block that finishes early simply takes the next one.
+  const int b = blockIdx.x, nblk = gridDim.x;
   const TileScan sc = tile_scan(g.offsets, g.E, kBM, nt);
-  // every value that steers the loop is wave-uniform; saying so keeps the loop under scalar
+  // every value that steers the loops is wave-uniform; saying so keeps them under scalar
   // control (a divergent trip count would make the compiler copy the accumulators)
   const int total = __builtin_amdgcn_readfirstlane(sc.total);
+  if (total == 0) return;
   const int nst_all = (int)(g.K / kBK);
   int full = total, r = 0, split = 1;
-  if (g.split_ws && g.ncu >= 8 && total % g.ncu != 0) {
-    full = total / g.ncu * g.ncu;
+  if (g.split_ws && nblk <= kSplitSlots && total % nblk != 0) {
+    full = total / nblk * nblk;
     r = total - full;
-    split = min(kMaxSplit, g.ncu / r);
+    split = min(kMaxSplit, nblk / r);
     // each part needs an even number of stages, and enough of them (kMinPartStages) to pay
     // for storing and adding its float32 partial
     while (split > 1 && (nst_all % (2 * split) != 0 || nst_all / split < kMinPartStages)) --split;
     if (split == 1) full = total;
   }
-  int L, ks = 0;
-  const int xcd = b & 7, jb = b >> 3;
-  if (split == 1) {
-    const int chunk = (total + 7) >> 3;
-    if (jb >= chunk) return;
-    L = xcd * chunk + jb;
-    if (L >= total) return;
-  } else {
-    const int F8 = full >> 3;  // full is a multiple of the CU count, itself a multiple of 8
-    if (jb < F8) {
-      L = xcd * F8 + jb;
-    } else {
-      const int R8 = (r * split + 7) >> 3;
-      const int u = xcd * R8 + (jb - F8);
-      if (jb - F8 >= R8 || u >= r * split) return;
-      L = full + u / split;
-      ks = u % split;
+  const int xcd = b & 7;
+  // Position q of this XCD's queue -> tile L, K part ks. False past the end.
+  auto unit_at = [&](int q, int& L, int& ks) -> bool {
+    ks = 0;
+    L = 0;
+    if (q < 0) return false;
+    if (split == 1) {
+      const int chunk = (total + 7) >> 3;
+      L = xcd * chunk + q;
+      return q < chunk && L < total;
     }
-  }
-  const int parts = L >= full ? split : 1;  // K parts of this tile
-  int e, row0, rows, n_tile;
-  tile_of(sc, g.offsets, kBM, nt, kTileBlockN, L, e, row0, rows, n_tile);
-  e = __builtin_amdgcn_readfirstlane(e);
-  row0 = __builtin_amdgcn_readfirstlane(row0);
-  rows = __builtin_amdgcn_readfirstlane(rows);
-  n_tile = __builtin_amdgcn_readfirstlane(n_tile);
+    const int F8 = full >> 3;
+    if (q < F8) {
+      L = xcd * F8 + q;
+      return true;
+    }
+    const int R8 = (r * split + 7) >> 3;
+    const int u = xcd * R8 + (q - F8);
+    if (q - F8 >= R8 || u >= r * split) return false;
+    L = full + u / split;
+    ks = u % split;
+    return true;
+  };
+  // Queue positions: block (xcd, j) starts with positions j and per + j of its XCD's list; the
+  // XCD's counter hands out the rest from 2 per on, in order.
+  int32_t* const qctr = g.queue + xcd;
+  const int per = nblk >> 3, jb = b >> 3;
+  auto grab = [&]() { return 2 * per + atomicAdd(qctr, 1); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = g.K, N = g.N;
-  const int64_t n0 = (int64_t)n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output column
-  if (n0 >= N) return;
 
-  Loader ld;
+  // Geometry of a unit (all wave-uniform).
+  struct Unit {
+    int L, ks, e, row0, rows, n_tile, parts, nst;
+    int64_t kbeg;
+  };
+  auto geometry = [&](int L, int ks) {
+    Unit u;
+    u.L = L;
+    u.ks = ks;
+    tile_of(sc, g.offsets, kBM, nt, kTileBlockN, L, u.e, u.row0, u.rows, u.n_tile);
+    u.e = __builtin_amdgcn_readfirstlane(u.e);
+    u.row0 = __builtin_amdgcn_readfirstlane(u.row0);
+    u.rows = __builtin_amdgcn_readfirstlane(u.rows);
+    u.n_tile = __builtin_amdgcn_readfirstlane(u.n_tile);
+    u.parts = L >= full ? split : 1;  // K parts of this tile
+    u.nst = nst_all / u.parts;        // even: K % 128 == 0, and parts divide it in pairs
+    u.kbeg = (int64_t)ks * u.nst * kBK;
+    return u;
+  };
+
   // A: instruction j of wave w fills tile rows 8 (8w + j) + lane / 8; its 16-byte chunk at
   // position lane % 8 is logical chunk (lane % 8) ^ ((row / 2) % 8), and (row / 2) % 8 =
   // 4 (j % 2) + lane / 16 % 4. Rows past the tile read row 0 of the expert block (valid memory;
-  // their outputs are never stored).
+  // their outputs are never stored). The source rows of a unit are fetched ahead
+  // (`gather_rows`) and turned into addresses when its loads are about to be issued.
+  auto gather_rows = [&](const Unit& u, int32_t (&src)[8]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 8 * (8 * wv + j) + (lane >> 3);
-    const int c = (lane & 7) ^ (4 * (j & 1) + ((lane >> 4) & 3));
-    int64_t src = 0;
-    if (r < rows) {
-      const int64_t gr = row0 + r;
-      src = g.a_gather ? (int64_t)(g.a_gather[gr] / g.gather_div) : gr;
-    } else {
-      src = g.a_gather ? (int64_t)(g.a_gather[row0] / g.gather_div) : row0;
+    for (int j = 0; j < 8; ++j) {
+      const int rr = 8 * (8 * wv + j) + (lane >> 3);
+      const int64_t gr = u.row0 + (rr < u.rows ? rr : 0);
+      src[j] = g.a_gather ? g.a_gather[gr] / g.gather_div : (int32_t)gr;
     }
-    ld.a[j] = (const char*)g.A + (src * g.lda + 8 * c) * 2;
-  }
-  // B: instruction j of wave w fills K-rows 16w + 2j + lane / 32; position lane % 32 of the
-  // K-row holds logical chunk (lane % 32) ^ (4 (K-row % 4)), K-row % 4 = 2 (j % 2) + lane / 32.
-  ld.b_row_bytes = N * 2;
+  };
+  auto make_loader = [&](const Unit& u, const int32_t (&src)[8]) {
+    Loader ld;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = (lane & 31) ^ (4 * ((2 * q + (lane >> 5)) & 3));
-    int64_t col;
-    const uint16_t* Wm;
-    if (kSwiGLU) {
-      const int ct = c >> 2;  // n-tile of 32: even -> W1, odd -> W3, same output columns
-      Wm = (const uint16_t*)((ct & 1) ? g.B1 : g.B0);
-      col = n0 + 32 * (ct >> 1) + 8 * (c & 3);
-    } else {
-      Wm = (const uint16_t*)g.B0;
-      col = n0 + 8 * c;
+    for (int j = 0; j < 8; ++j) {
+      const int c = (lane & 7) ^ (4 * (j & 1) + ((lane >> 4) & 3));
+      ld.a[j] = (const char*)g.A + ((int64_t)src[j] * g.lda + 8 * c) * 2;
     }
-    const int krow = 16 * wv + (lane >> 5);
-    ld.b[q] = (const char*)(Wm + (int64_t)e * K * N + (int64_t)krow * N + (col < N ? col : 0));
-  }
+    // B: instruction j of wave w fills K-rows 16w + 2j + lane / 32; position lane % 32 of the
+    // K-row holds logical chunk (lane % 32) ^ (4 (K-row % 4)), K-row % 4 = 2 (j % 2) + lane / 32.
+    const int64_t n0 = (int64_t)u.n_tile * (kSwiGLU ? kBN / 2 : kBN);
+    ld.b_row_bytes = N * 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = (lane & 31) ^ (4 * ((2 * q + (lane >> 5)) & 3));
+      int64_t col;
+      const uint16_t* Wm;
+      if (kSwiGLU) {
+        const int ct = c >> 2;  // n-tile of 32: even -> W1, odd -> W3, same output columns
+        Wm = (const uint16_t*)((ct & 1) ? g.B1 : g.B0);
+        col = n0 + 32 * (ct >> 1) + 8 * (c & 3);
+      } else {
+        Wm = (const uint16_t*)g.B0;
+        col = n0 + 8 * c;
+      }
+      const int krow = 16 * wv + (lane >> 5);
+      ld.b[q] = (const char*)(Wm + (int64_t)u.e * K * N + (int64_t)krow * N + (col < N ? col : 0));
+    }
+    return ld;
+  };
 
-  // Operand read offsets (bytes within a stage buffer).
+  // Operand read offsets (bytes within a stage buffer) and the read bases of both buffers.
   uint32_t aoff[4], boff[4];
   {
-    const int r = 64 * wv + (lane & 31);  // + 32 mi
+    const int rr = 64 * wv + (lane & 31);  // + 32 mi
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int chunk = (2 * t + (lane >> 5)) ^ ((r >> 1) & 7);
-      aoff[t] = (uint32_t)(r * 128 + chunk * 16);
+      const int chunk = (2 * t + (lane >> 5)) ^ ((rr >> 1) & 7);
+      aoff[t] = (uint32_t)(rr * 128 + chunk * 16);
     }
-    const int gq = lane >> 4, L = lane & 15;
-    const int krow = 8 * (gq >> 1) + (L >> 2);
+    const int gq = lane >> 4, Lq = lane & 15;
+    const int krow = 8 * (gq >> 1) + (Lq >> 2);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int chunk = (4 * c + 2 * (gq & 1) + ((L & 3) >> 1)) ^ (4 * (L >> 2));
-      boff[c] = (uint32_t)(krow * 512 + chunk * 16 + 8 * (L & 1));
+      const int chunk = (4 * c + 2 * (gq & 1) + ((Lq & 3) >> 1)) ^ (4 * (Lq >> 2));
+      boff[c] = (uint32_t)(krow * 512 + chunk * 16 + 8 * (Lq & 1));
     }
   }
-
-  f32x16 acc[2][8];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][c][v] = 0.f;
-
   const uint32_t la0 = lds_addr(sA0), la1 = lds_addr(sA1);
   const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
-  const int nst = nst_all / parts;  // even: K % 128 == 0, and parts divides it in pairs
-  const int64_t kbeg = (int64_t)ks * nst * kBK;
-
-  // Stage 0 into buffer 0, stage 1 into buffer 1 while stage 0's first operands are read;
-  // from then on each stage issues the loads of the stage after next (see `stage`).
-  load_stage(ld, kbeg, la0, lb0, wv);
-  wait_vm0();
-  block_barrier();
-  load_stage(ld, kbeg + kBK, la1, lb1, wv);
   uint32_t ab0[4], bb0[4], ab1[4], bb1[4];
   make_bases(la0, lb0, aoff, boff, ab0, bb0);
   make_bases(la1, lb1, aoff, boff, ab1, bb1);
-  bf16x8 a0 = read_a(ab0, 0, 0), a1 = read_a(ab0, 1, 0), bq[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) bq[c] = read_b(bb0, c, 0);
-  for (int s = 0; s < nst; s += 2) {
-    stage(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 2) * kBK, s + 2 < nst, la0,
-          lb0, wv);
-    stage(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 3) * kBK, s + 3 < nst, la1,
-          lb1, wv);
-  }
-  // (The last stage's reads of the "next" buffer fetch operands nobody uses; no load is in
-  // flight past the last stage.)
 
-  // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
-  uint16_t* C = (uint16_t*)g.C;
-  if (parts == 1) {  // a whole tile: store it from the accumulators
-    if (64 * wv >= rows) return;
-    // Lanes l and l ^ 1 hold adjacent columns of the same rows. For each pair of rows
-    // (v0, v0 + 1) they swap one value, so the even lane stores columns (c, c + 1) of row v0
-    // and the odd lane the same two columns of row v0 + 1: one 4-byte store per two outputs.
-    const bool odd = lane & 1;
-    const int lrow = 64 * wv + 4 * (lane >> 5) + (odd ? 1 : 0);
-    const int colp = (lane & 31) & ~1;
-    uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
-    const bool whole = 64 * wv + 64 <= rows && n0 + (kSwiGLU ? kBN / 2 : kBN) <= N;
-    auto put = [&](int mi, int v0, int cq, float x0, float x1) {
-      const float recv = swap_adjacent_lanes(odd ? x0 : x1);
-      const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
-      const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
-      if (whole || (lrow + dr < rows && n0 + cq + colp < N))
-        *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
-    };
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int q = 0; q < (kSwiGLU ? 4 : 8); ++q)
-#pragma unroll
-        for (int v0 = 0; v0 < 16; v0 += 2) {
-          float x0, x1;
-          if (kSwiGLU) {  // columns 32q.. of the output: gate in n-tile 2q, up in 2q + 1
-            x0 = silu_f(acc_get(acc[mi][2 * q][v0])) * acc_get(acc[mi][2 * q + 1][v0]);
-            x1 = silu_f(acc_get(acc[mi][2 * q][v0 + 1])) * acc_get(acc[mi][2 * q + 1][v0 + 1]);
-          } else {
-            x0 = acc_get(acc[mi][q][v0]);
-            x1 = acc_get(acc[mi][q][v0 + 1]);
-            if (EPI == EPI_RELU) {
-              x0 = fmaxf(x0, 0.f);
-              x1 = fmaxf(x1, 0.f);
-            }
-          }
-          put(mi, v0, 32 * q, x0, x1);
-        }
-    return;
-  }
+  int L0, ks0;
+  if (unit_at(jb, L0, ks0)) {
+    Unit cu = geometry(L0, ks0);
+    Loader ld;
+    {
+      int32_t src[8];
+      gather_rows(cu, src);
+      ld = make_loader(cu, src);
+    }
+    // Stages 0 and 1 of the first unit; every later unit's first two stages are loaded by the
+    // last two stages of the unit before it (see `stage`), while that unit stores its tile.
+    load_stage(ld, cu.kbeg, la0, lb0, wv);
+    load_stage(ld, cu.kbeg + kBK, la1, lb1, wv);
 
-  // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a time, in
-  // a lane-interleaved layout), then take a ticket; the part that takes the last ticket adds
-  // all parts in part order and stores the tile. The sum order is fixed, so the result does
-  // not depend on which part finishes last.
-  float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
-  {
-    if (64 * wv < rows) {
-      float* mine = slots + (int64_t)ks * kSplitSlotFloats;
-      // group (wv, mi, c) of 16 accumulators: 4 KB at a wave-uniform base, lane l's 16-byte
-      // chunk v4 at +1 KB * v4 + 16 l (so every store is base + one lane offset + a constant)
-      const uint32_t lane_off = (uint32_t)lane * 16u;
+    uint16_t* C = (uint16_t*)g.C;
+    for (int i = 0;; ++i) {
+      int Ln, ksn;
+      // (the first unit's successor is fixed; later ones were published through LDS)
+      const int qn = i == 0 ? per + jb : __builtin_amdgcn_readfirstlane(s_unit[(i + 1) & 1]);
+      const bool has_next = unit_at(qn, Ln, ksn);
+
+      f32x16 acc[2][8];
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          char* gb = (char*)mine + (int64_t)((wv * 2 + mi) * 8 + c) * 4096;
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4)
-            *(f32x4*)(gb + v4 * 1024 + lane_off) =
-                f32x4{acc_get(acc[mi][c][4 * v4]), acc_get(acc[mi][c][4 * v4 + 1]),
-                      acc_get(acc[mi][c][4 * v4 + 2]), acc_get(acc[mi][c][4 * v4 + 3])};
-        }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
-  }
-  if (64 * wv >= rows) return;
-  // Every part (this one included) has stored its partial: add them in part order, 16
-  // coalesced bytes (4 rows of one column) per lane and part at a time, and store the rows.
-  const uint32_t lane_off = (uint32_t)lane * 16u;
-  auto part4 = [&](int mi, int c, int v4) {
-    const char* gb = (const char*)slots + (int64_t)((wv * 2 + mi) * 8 + c) * 4096 + v4 * 1024;
-    f32x4 tot = *(const f32x4*)(gb + lane_off);
+          for (int v = 0; v < 16; ++v) acc[mi][c][v] = 0.f;
+
+      wait_vm0();
+      block_barrier();
+      // The unit after next (taken now so that its atomic is not waited for at this barrier),
+      // and the next unit's source rows: both are in flight while this unit computes.
+      int after_next = -1;
+      if (tid == 0 && has_next) after_next = grab();
+      Unit nx = cu;
+      int32_t nsrc[8];
+      if (has_next) {
+        nx = geometry(Ln, ksn);
+        gather_rows(nx, nsrc);
+      }
+      bf16x8 a0 = read_a(ab0, 0, 0), a1 = read_a(ab0, 1, 0), bq[8];
 #pragma unroll
-    for (int q = 1; q < kMaxSplit; ++q)
-      if (q < parts) tot += *(const f32x4*)(gb + q * kSplitSlotFloats * 4 + lane_off);
-    return tot;
-  };
-  for (int mi = 0; mi < 2; ++mi)
-    for (int v4 = 0; v4 < 4; ++v4) {
-      if (kSwiGLU) {
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 gt = part4(mi, 2 * q, v4), up = part4(mi, 2 * q + 1, v4);
-          const int64_t col = n0 + 32 * q + (lane & 31);
+      for (int c = 0; c < 8; ++c) bq[c] = read_b(bb0, c, 0);
+      const int nst = cu.nst;
+      const int64_t kbeg = cu.kbeg;
+      for (int s = 0; s + 2 < nst; s += 2) {
+        stage(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 2) * kBK, true, la0,
+              lb0, wv);
+        stage(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 3) * kBK, true, la1,
+              lb1, wv);
+      }
+      // Publish the unit after next (its slot was last read before this unit's barriers), then
+      // let the last two stages load the next unit's first two.
+      if (tid == 0) s_unit[i & 1] = after_next;
+      if (has_next) ld = make_loader(nx, nsrc);
+      stage(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, nx.kbeg, has_next, la0, lb0, wv);
+      stage(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, nx.kbeg + kBK, has_next, la1, lb1, wv);
+
+      const int row0 = cu.row0, rows = cu.rows, parts = cu.parts, L = cu.L, ks = cu.ks;
+      const int64_t n0 = (int64_t)cu.n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output column
+      // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
+      if (parts == 1) {
+        if (64 * wv < rows) {  // a whole tile: store it from the accumulators
+          // Lanes l and l ^ 1 hold adjacent columns of the same rows. For each pair of rows
+          // (v0, v0 + 1) they swap one value, so the even lane stores columns (c, c + 1) of row
+          // v0 and the odd lane the same two columns of row v0 + 1: one 4-byte store per two
+          // outputs.
+          const bool odd = lane & 1;
+          const int lrow = 64 * wv + 4 * (lane >> 5) + (odd ? 1 : 0);
+          const int colp = (lane & 31) & ~1;
+          uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
+          const bool whole = 64 * wv + 64 <= rows && n0 + (kSwiGLU ? kBN / 2 : kBN) <= N;
+          auto put = [&](int mi, int v0, int cq, float x0, float x1) {
+            const float recv = swap_adjacent_lanes(odd ? x0 : x1);
+            const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
+            const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
+            if (whole || (lrow + dr < rows && n0 + cq + colp < N))
+              *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
+          };
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i;
-            if (r < rows && col < N)
-              C[(int64_t)(row0 + r) * N + col] = f32_to_bf16(silu_f(gt[i]) * up[i]);
-          }
+          for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int q = 0; q < (kSwiGLU ? 4 : 8); ++q)
+#pragma unroll
+              for (int v0 = 0; v0 < 16; v0 += 2) {
+                float x0, x1;
+                if (kSwiGLU) {  // columns 32q.. of the output: gate in n-tile 2q, up in 2q + 1
+                  x0 = silu_f(acc_get(acc[mi][2 * q][v0])) * acc_get(acc[mi][2 * q + 1][v0]);
+                  x1 = silu_f(acc_get(acc[mi][2 * q][v0 + 1])) *
+                       acc_get(acc[mi][2 * q + 1][v0 + 1]);
+                } else {
+                  x0 = acc_get(acc[mi][q][v0]);
+                  x1 = acc_get(acc[mi][q][v0 + 1]);
+                  if (EPI == EPI_RELU) {
+                    x0 = fmaxf(x0, 0.f);
+                    x1 = fmaxf(x1, 0.f);
+                  }
+                }
+                put(mi, v0, 32 * q, x0, x1);
+              }
         }
       } else {
-        for (int c = 0; c < 8; ++c) {
-          const f32x4 t = part4(mi, c, v4);
-          const int64_t col = n0 + 32 * c + (lane & 31);
+        // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a
+        // time, in a lane-interleaved layout), then take a ticket; the part that takes the last
+        // ticket adds all parts in part order and stores the tile. The sum order is fixed, so
+        // the result does not depend on which part finishes last.
+        float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
+        if (64 * wv < rows) {
+          float* mine = slots + (int64_t)ks * kSplitSlotFloats;
+          // group (wv, mi, c) of 16 accumulators: 4 KB at a wave-uniform base, lane l's 16-byte
+          // chunk v4 at +1 KB * v4 + 16 l (so every store is base + one lane offset + a const)
+          const uint32_t lane_off = (uint32_t)lane * 16u;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i;
-            float x = t[i];
-            if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
-            if (r < rows && col < N) C[(int64_t)(row0 + r) * N + col] = f32_to_bf16(x);
+          for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              char* gb = (char*)mine + (int64_t)((wv * 2 + mi) * 8 + c) * 4096;
+#pragma unroll
+              for (int v4 = 0; v4 < 4; ++v4)
+                *(f32x4*)(gb + v4 * 1024 + lane_off) =
+                    f32x4{acc_get(acc[mi][c][4 * v4]), acc_get(acc[mi][c][4 * v4 + 1]),
+                          acc_get(acc[mi][c][4 * v4 + 2]), acc_get(acc[mi][c][4 * v4 + 3])};
+            }
+        }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
+        __syncthreads();
+        if (s_last) {
+          __threadfence();
+          if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
+          if (64 * wv < rows) {
+            // Every part (this one included) has stored its partial: add them in part order,
+            // 16 coalesced bytes (4 rows of one column) per lane and part at a time, and store
+            // the rows.
+            const uint32_t lane_off = (uint32_t)lane * 16u;
+            auto part4 = [&](int mi, int c, int v4) {
+              const char* gb =
+                  (const char*)slots + (int64_t)((wv * 2 + mi) * 8 + c) * 4096 + v4 * 1024;
+              f32x4 tot = *(const f32x4*)(gb + lane_off);
+#pragma unroll
+              for (int q = 1; q < kMaxSplit; ++q)
+                if (q < parts) tot += *(const f32x4*)(gb + q * kSplitSlotFloats * 4 + lane_off);
+              return tot;
+            };
+            for (int mi = 0; mi < 2; ++mi)
+              for (int v4 = 0; v4 < 4; ++v4) {
+                if (kSwiGLU) {
+                  for (int q = 0; q < 4; ++q) {
+                    const f32x4 gt = part4(mi, 2 * q, v4), up = part4(mi, 2 * q + 1, v4);
+                    const int64_t col = n0 + 32 * q + (lane & 31);
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                      const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
+                      if (rr < rows && col < N)
+                        C[(int64_t)(row0 + rr) * N + col] =
+                            f32_to_bf16(silu_f(gt[i4]) * up[i4]);
+                    }
+                  }
+                } else {
+                  for (int c = 0; c < 8; ++c) {
+                    const f32x4 t = part4(mi, c, v4);
+                    const int64_t col = n0 + 32 * c + (lane & 31);
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                      const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
+                      float x = t[i4];
+                      if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+                      if (rr < rows && col < N) C[(int64_t)(row0 + rr) * N + col] = f32_to_bf16(x);
+                    }
+                  }
+                }
+              }
           }
         }
       }
+      if (!has_next) break;
+      cu = nx;
     }
+  }
+  // The last block to finish resets the queue for the next launch (every block has taken its
+  // last position by then).
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(g.queue + 8, 1) == nblk - 1) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x) g.queue[x] = 0;
+      g.queue[8] = 0;
+    }
+  }
 }
 
 __global__ void zero_tickets_kernel(int32_t* __restrict__ p, int n) {
@@ -494,9 +573,14 @@ hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) 
   const int64_t mt_max = (g.max_rows + kBM - 1) / kBM + g.E;
   const int64_t cols = (g.epilogue == EPI_SWIGLU) ? kBN / 2 : kBN;
   const int64_t nt = (g.N + cols - 1) / cols;
-  // every whole tile, plus at most one split part per CU beyond them
-  int64_t G = mt_max * nt + (g.split_ws ? g.ncu + 8 : 0);
-  G = (G + 7) / 8 * 8;
+  // One block per CU (a multiple of 8, at most kSplitSlots, the split parts' slot count), or
+  // fewer when there are fewer tiles than that. The kernel takes its block count as the
+  // width of a wave of tiles.
+  int64_t G = g.ncu >= 8 ? g.ncu : kSplitSlots;
+  if (G > kSplitSlots) G = kSplitSlots;
+  G = G / 8 * 8;
+  const int64_t tiles_max = (mt_max * nt + 7) / 8 * 8;
+  if (G > tiles_max) G = tiles_max;
   const dim3 grid((unsigned)G);
   // The start/stop events (if any) are recorded by the kernel's own dispatch, so timing adds
   // no packets, and no gaps, to the stream.
