@@ -32,6 +32,8 @@
 //    eighth of the real tiles, so the tiles it runs at once share rows and columns in its L2.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "tile_schedule.hpp"
 
@@ -85,21 +87,6 @@ __device__ __forceinline__ void load_stage(const Loader& ld, int64_t k0, uint32_
 
 typedef __attribute__((address_space(3))) const char lds_cchar;
 
-// Per-buffer operand read bases: LDS byte address of the buffer + this lane's offset for each
-// of the 4 slots. They are made opaque to the optimiser, so every read adds its constant part
-// in the instruction's offset field instead of holding one precomputed address per read.
-__device__ __forceinline__ void make_bases(uint32_t lds_a, uint32_t lds_b, const uint32_t (&aoff)[4],
-                                           const uint32_t (&boff)[4], uint32_t (&ab)[4],
-                                           uint32_t (&bb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ab[i] = lds_a + aoff[i];
-    bb[i] = lds_b + boff[i];
-    asm volatile("" : "+v"(ab[i]));
-    asm volatile("" : "+v"(bb[i]));
-  }
-}
-
 // B operand of n-tile c, k-step t: two transposed 8-byte reads (K-rows 16t + 8 (lane/32) + 4h
 // + (lane%16)/4, see the offsets in the kernel) give column lane % 32, K values
 // 16t + 8 (lane / 32) .. +7.
@@ -115,15 +102,16 @@ __device__ __forceinline__ bf16x8 read_a(const uint32_t (&ab)[4], int mi, int t)
   return *(const lds_bf16x8*)((lds_cchar*)(uintptr_t)ab[t] + mi * 32 * 128);
 }
 
-// One stage (4 k-steps x 2 x 8 MFMAs) on the current buffer, with the stage boundary inside it.
-// Operands rotate through registers: the B read for k-step t + 1 of n-tile c follows the two
-// MFMAs of k-step t that consume it, and the A operands of k-step t + 1 are read at the start
-// of k-step t. So k-steps 0..2 bring in all of k-step 3's operands; then every read and this
-// wave's loads of the next buffer are waited for and the block synchronises, and k-step 3 runs
-// from registers while the next buffer's k-step 0 operands are read and, when `load2`, the
-// loads of the stage after next (K offset k2) are issued into the current buffer, which no
-// wave reads any more. The matrix pipe is thus never left waiting for a whole LDS round trip
-// at a stage boundary.
+// One stage (4 k-steps x 2 x NN MFMAs: this wave's 2 row tiles by its NN column tiles) on the
+// current buffer, with the stage boundary inside it. Operands rotate through registers: the B
+// read for k-step t + 1 of column tile c follows the two MFMAs of k-step t that consume it,
+// and the A operands of k-step t + 1 are read at the start of k-step t. So k-steps 0..2 bring
+// in all of k-step 3's operands; then every read and this wave's loads of the next buffer are
+// waited for and the block synchronises, and k-step 3 runs from registers while the next
+// buffer's k-step 0 operands are read and, when `load2`, the loads of the stage after next
+// (K offset k2) are issued into the current buffer, which no wave reads any more. The matrix
+// pipe is thus never left waiting for a whole LDS round trip at a stage boundary.
+template <int NN>
 __device__ __forceinline__ void stage(const uint32_t (&ab)[4], const uint32_t (&bb)[4],
                                       const uint32_t (&abn)[4], const uint32_t (&bbn)[4],
                                       f32x16 (&acc)[2][8], bf16x8& a0, bf16x8& a1, bf16x8 (&b)[8],
@@ -134,7 +122,7 @@ __device__ __forceinline__ void stage(const uint32_t (&ab)[4], const uint32_t (&
     const bf16x8 n0 = read_a(ab, 0, t + 1), n1 = read_a(ab, 1, t + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < NN; ++c) {
       acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
       acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
       b[c] = read_b(bb, c, t + 1);
@@ -150,18 +138,54 @@ __device__ __forceinline__ void stage(const uint32_t (&ab)[4], const uint32_t (&
   __builtin_amdgcn_sched_barrier(0);
   const int64_t bk = k2 * ld.b_row_bytes;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < NN; ++c) {
     acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
     acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
     b[c] = read_b(bbn, c, 0);
     if (load2) {
-      dma16(ld.a[c] + k2 * 2, sa + (8 * wv + c) * 1024);
-      dma16(ld.b[c & 1] + bk + (int64_t)(2 * c) * ld.b_row_bytes, sb + (8 * wv + c) * 1024);
+#pragma unroll
+      for (int j = c * (8 / NN); j < (c + 1) * (8 / NN); ++j) {
+        dma16(ld.a[j] + k2 * 2, sa + (8 * wv + j) * 1024);
+        dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sb + (8 * wv + j) * 1024);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   a0 = n0;
   a1 = n1;
+}
+
+// Wave layouts of a tile (NN = column tiles of 32 per wave):
+//   NN = 8: wave w computes rows 64 w .. + 63, all 256 columns (any tile);
+//   NN = 4: rows 64 (w % 2) .. + 63, columns 128 (w / 2) .. + 127 (tiles of at most 128 rows);
+//   NN = 2: rows 0 .. 63, columns 64 w .. + 63 (tiles of at most 64 rows).
+// A tile with fewer rows thus costs fewer MFMAs per wave, not idle waves. The read bases of
+// one buffer for this wave: A rows start at the wave's first row; B column tile j of the wave
+// is tile c = first + j of the block, read at bases[c % 4] + 256 bytes * (c / 4).
+template <int NN>
+__device__ __forceinline__ int wave_row0(int wv) {
+  return NN == 8 ? 64 * wv : NN == 4 ? 64 * (wv & 1) : 0;
+}
+template <int NN>
+__device__ __forceinline__ int wave_col_tile0(int wv) {
+  return NN == 8 ? 0 : NN == 4 ? 4 * (wv >> 1) : 2 * wv;
+}
+template <int NN>
+__device__ __forceinline__ void unit_bases(uint32_t lds_a, uint32_t lds_b, const uint32_t (&aoff)[4],
+                                           const uint32_t (&boff)[4], int wv, uint32_t (&ab)[4],
+                                           uint32_t (&bb)[4]) {
+  const uint32_t arow = (uint32_t)wave_row0<NN>(wv) * 128u;
+  const int c0 = wave_col_tile0<NN>(wv);
+  const uint32_t bhi = (uint32_t)(c0 >> 2) * 256u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ab[i] = lds_a + aoff[i] + arow;
+    // column tile c0 + i of the block (only i < NN is read)
+    const int q = (c0 + i) & 3;
+    bb[i] = lds_b + (q == 0 ? boff[0] : q == 1 ? boff[1] : q == 2 ? boff[2] : boff[3]) + bhi;
+    asm volatile("" : "+v"(ab[i]));
+    asm volatile("" : "+v"(bb[i]));
+  }
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -322,10 +346,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     return ld;
   };
 
-  // Operand read offsets (bytes within a stage buffer) and the read bases of both buffers.
+  // Operand read offsets within a stage buffer: A for row lane % 32 (the wave's first row and
+  // the row tile are added as constants), B for the block's column tiles 0..3 (see
+  // `unit_bases`).
   uint32_t aoff[4], boff[4];
   {
-    const int rr = 64 * wv + (lane & 31);  // + 32 mi
+    const int rr = lane & 31;  // + 32 mi
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int chunk = (2 * t + (lane >> 5)) ^ ((rr >> 1) & 7);
@@ -341,9 +367,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   }
   const uint32_t la0 = lds_addr(sA0), la1 = lds_addr(sA1);
   const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
-  uint32_t ab0[4], bb0[4], ab1[4], bb1[4];
-  make_bases(la0, lb0, aoff, boff, ab0, bb0);
-  make_bases(la1, lb1, aoff, boff, ab1, bb1);
 
   int L0, ks0;
   if (unit_at(jb, L0, ks0)) {
@@ -386,142 +409,160 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         nx = geometry(Ln, ksn);
         gather_rows(nx, nsrc);
       }
-      bf16x8 a0 = read_a(ab0, 0, 0), a1 = read_a(ab0, 1, 0), bq[8];
+      // The wave layout follows the tile's rows (K parts always use the full layout, since
+      // their partial tiles are laid out by it).
+      const int shape = (cu.parts > 1 || cu.rows > 128) ? 0 : (cu.rows > 64 ? 1 : 2);
+      auto run = [&](auto nn_tag) {
+        constexpr int NN = decltype(nn_tag)::value;
+        uint32_t ab0[4], bb0[4], ab1[4], bb1[4];
+        unit_bases<NN>(la0, lb0, aoff, boff, wv, ab0, bb0);
+        unit_bases<NN>(la1, lb1, aoff, boff, wv, ab1, bb1);
+        bf16x8 a0 = read_a(ab0, 0, 0), a1 = read_a(ab0, 1, 0), bq[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) bq[c] = read_b(bb0, c, 0);
-      const int nst = cu.nst;
-      const int64_t kbeg = cu.kbeg;
-      for (int s = 0; s + 2 < nst; s += 2) {
-        stage(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 2) * kBK, true, la0,
-              lb0, wv);
-        stage(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 3) * kBK, true, la1,
-              lb1, wv);
-      }
-      // Publish the unit after next (its slot was last read before this unit's barriers), then
-      // let the last two stages load the next unit's first two.
-      if (tid == 0) s_unit[i & 1] = after_next;
-      if (has_next) ld = make_loader(nx, nsrc);
-      stage(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, nx.kbeg, has_next, la0, lb0, wv);
-      stage(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, nx.kbeg + kBK, has_next, la1, lb1, wv);
+        for (int c = 0; c < NN; ++c) bq[c] = read_b(bb0, c, 0);
+        const int nst = cu.nst;
+        const int64_t kbeg = cu.kbeg;
+        for (int s = 0; s + 2 < nst; s += 2) {
+          stage<NN>(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 2) * kBK, true,
+                    la0, lb0, wv);
+          stage<NN>(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 3) * kBK, true,
+                    la1, lb1, wv);
+        }
+        // Publish the unit after next (its slot was last read before this unit's barriers),
+        // then let the last two stages load the next unit's first two.
+        if (tid == 0) s_unit[i & 1] = after_next;
+        if (has_next) ld = make_loader(nx, nsrc);
+        stage<NN>(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, nx.kbeg, has_next, la0, lb0, wv);
+        stage<NN>(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, nx.kbeg + kBK, has_next, la1, lb1, wv);
 
-      const int row0 = cu.row0, rows = cu.rows, parts = cu.parts, L = cu.L, ks = cu.ks;
-      const int64_t n0 = (int64_t)cu.n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output column
-      // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
-      if (parts == 1) {
-        if (64 * wv < rows) {  // a whole tile: store it from the accumulators
-          // Lanes l and l ^ 1 hold adjacent columns of the same rows. For each pair of rows
-          // (v0, v0 + 1) they swap one value, so the even lane stores columns (c, c + 1) of row
-          // v0 and the odd lane the same two columns of row v0 + 1: one 4-byte store per two
-          // outputs.
-          const bool odd = lane & 1;
-          const int lrow = 64 * wv + 4 * (lane >> 5) + (odd ? 1 : 0);
-          const int colp = (lane & 31) & ~1;
-          uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
-          const bool whole = 64 * wv + 64 <= rows && n0 + (kSwiGLU ? kBN / 2 : kBN) <= N;
-          auto put = [&](int mi, int v0, int cq, float x0, float x1) {
-            const float recv = swap_adjacent_lanes(odd ? x0 : x1);
-            const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
-            const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
-            if (whole || (lrow + dr < rows && n0 + cq + colp < N))
-              *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
-          };
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int q = 0; q < (kSwiGLU ? 4 : 8); ++q)
-#pragma unroll
-              for (int v0 = 0; v0 < 16; v0 += 2) {
-                float x0, x1;
-                if (kSwiGLU) {  // columns 32q.. of the output: gate in n-tile 2q, up in 2q + 1
-                  x0 = silu_f(acc_get(acc[mi][2 * q][v0])) * acc_get(acc[mi][2 * q + 1][v0]);
-                  x1 = silu_f(acc_get(acc[mi][2 * q][v0 + 1])) *
-                       acc_get(acc[mi][2 * q + 1][v0 + 1]);
-                } else {
-                  x0 = acc_get(acc[mi][q][v0]);
-                  x1 = acc_get(acc[mi][q][v0 + 1]);
-                  if (EPI == EPI_RELU) {
-                    x0 = fmaxf(x0, 0.f);
-                    x1 = fmaxf(x1, 0.f);
-                  }
-                }
-                put(mi, v0, 32 * q, x0, x1);
-              }
-        }
-      } else {
-        // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a
-        // time, in a lane-interleaved layout), then take a ticket; the part that takes the last
-        // ticket adds all parts in part order and stores the tile. The sum order is fixed, so
-        // the result does not depend on which part finishes last.
-        float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
-        if (64 * wv < rows) {
-          float* mine = slots + (int64_t)ks * kSplitSlotFloats;
-          // group (wv, mi, c) of 16 accumulators: 4 KB at a wave-uniform base, lane l's 16-byte
-          // chunk v4 at +1 KB * v4 + 16 l (so every store is base + one lane offset + a const)
-          const uint32_t lane_off = (uint32_t)lane * 16u;
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              char* gb = (char*)mine + (int64_t)((wv * 2 + mi) * 8 + c) * 4096;
-#pragma unroll
-              for (int v4 = 0; v4 < 4; ++v4)
-                *(f32x4*)(gb + v4 * 1024 + lane_off) =
-                    f32x4{acc_get(acc[mi][c][4 * v4]), acc_get(acc[mi][c][4 * v4 + 1]),
-                          acc_get(acc[mi][c][4 * v4 + 2]), acc_get(acc[mi][c][4 * v4 + 3])};
-            }
-        }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
-        __syncthreads();
-        if (s_last) {
-          __threadfence();
-          if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
-          if (64 * wv < rows) {
-            // Every part (this one included) has stored its partial: add them in part order,
-            // 16 coalesced bytes (4 rows of one column) per lane and part at a time, and store
-            // the rows.
-            const uint32_t lane_off = (uint32_t)lane * 16u;
-            auto part4 = [&](int mi, int c, int v4) {
-              const char* gb =
-                  (const char*)slots + (int64_t)((wv * 2 + mi) * 8 + c) * 4096 + v4 * 1024;
-              f32x4 tot = *(const f32x4*)(gb + lane_off);
-#pragma unroll
-              for (int q = 1; q < kMaxSplit; ++q)
-                if (q < parts) tot += *(const f32x4*)(gb + q * kSplitSlotFloats * 4 + lane_off);
-              return tot;
+        const int row0 = cu.row0, rows = cu.rows, parts = cu.parts, L = cu.L, ks = cu.ks;
+        const int64_t n0 = (int64_t)cu.n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output col
+        const int wr0 = wave_row0<NN>(wv), wc0 = wave_col_tile0<NN>(wv);
+        // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
+        if (parts == 1) {
+          if (wr0 < rows) {  // a whole tile: store this wave's part from the accumulators
+            // Lanes l and l ^ 1 hold adjacent columns of the same rows. For each pair of rows
+            // (v0, v0 + 1) they swap one value, so the even lane stores columns (c, c + 1) of
+            // row v0 and the odd lane the same two columns of row v0 + 1: one 4-byte store per
+            // two outputs.
+            const bool odd = lane & 1;
+            const int lrow = wr0 + 4 * (lane >> 5) + (odd ? 1 : 0);
+            const int colp = (lane & 31) & ~1;
+            uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
+            const int ccol0 = 32 * (kSwiGLU ? wc0 / 2 : wc0);  // first output column of the wave
+            const int ccols = 32 * (kSwiGLU ? NN / 2 : NN);
+            const bool whole = wr0 + 64 <= rows && n0 + ccol0 + ccols <= N;
+            auto put = [&](int mi, int v0, int cq, float x0, float x1) {
+              const float recv = swap_adjacent_lanes(odd ? x0 : x1);
+              const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
+              const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
+              if (whole || (lrow + dr < rows && n0 + cq + colp < N))
+                *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
             };
+#pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-              for (int v4 = 0; v4 < 4; ++v4) {
-                if (kSwiGLU) {
-                  for (int q = 0; q < 4; ++q) {
-                    const f32x4 gt = part4(mi, 2 * q, v4), up = part4(mi, 2 * q + 1, v4);
-                    const int64_t col = n0 + 32 * q + (lane & 31);
 #pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                      const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
-                      if (rr < rows && col < N)
-                        C[(int64_t)(row0 + rr) * N + col] =
-                            f32_to_bf16(silu_f(gt[i4]) * up[i4]);
+              for (int q = 0; q < (kSwiGLU ? NN / 2 : NN); ++q)
+#pragma unroll
+                for (int v0 = 0; v0 < 16; v0 += 2) {
+                  float x0, x1;
+                  if (kSwiGLU) {  // gate in the wave's column tile 2q, up in 2q + 1
+                    x0 = silu_f(acc_get(acc[mi][2 * q][v0])) * acc_get(acc[mi][2 * q + 1][v0]);
+                    x1 = silu_f(acc_get(acc[mi][2 * q][v0 + 1])) *
+                         acc_get(acc[mi][2 * q + 1][v0 + 1]);
+                  } else {
+                    x0 = acc_get(acc[mi][q][v0]);
+                    x1 = acc_get(acc[mi][q][v0 + 1]);
+                    if (EPI == EPI_RELU) {
+                      x0 = fmaxf(x0, 0.f);
+                      x1 = fmaxf(x1, 0.f);
                     }
                   }
-                } else {
-                  for (int c = 0; c < 8; ++c) {
-                    const f32x4 t = part4(mi, c, v4);
-                    const int64_t col = n0 + 32 * c + (lane & 31);
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4) {
-                      const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
-                      float x = t[i4];
-                      if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
-                      if (rr < rows && col < N) C[(int64_t)(row0 + rr) * N + col] = f32_to_bf16(x);
-                    }
-                  }
+                  put(mi, v0, ccol0 + 32 * q, x0, x1);
                 }
+          }
+        } else if constexpr (NN == 8) {
+          // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a
+          // time, in a lane-interleaved layout), then take a ticket; the part that takes the last
+          // ticket adds all parts in part order and stores the tile. The sum order is fixed, so
+          // the result does not depend on which part finishes last.
+          float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
+          if (64 * wv < rows) {
+            float* mine = slots + (int64_t)ks * kSplitSlotFloats;
+            // group (wv, mi, c) of 16 accumulators: 4 KB at a wave-uniform base, lane l's 16-byte
+            // chunk v4 at +1 KB * v4 + 16 l (so every store is base + one lane offset + a const)
+            const uint32_t lane_off = (uint32_t)lane * 16u;
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+              for (int c = 0; c < 8; ++c) {
+                char* gb = (char*)mine + (int64_t)((wv * 2 + mi) * 8 + c) * 4096;
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4)
+                  *(f32x4*)(gb + v4 * 1024 + lane_off) =
+                      f32x4{acc_get(acc[mi][c][4 * v4]), acc_get(acc[mi][c][4 * v4 + 1]),
+                            acc_get(acc[mi][c][4 * v4 + 2]), acc_get(acc[mi][c][4 * v4 + 3])};
               }
           }
+          __threadfence();
+          __syncthreads();
+          if (tid == 0) s_last = atomicAdd(&g.split_ctr[L - full], 1) == parts - 1;
+          __syncthreads();
+          if (s_last) {
+            __threadfence();
+            if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
+            if (64 * wv < rows) {
+              // Every part (this one included) has stored its partial: add them in part order,
+              // 16 coalesced bytes (4 rows of one column) per lane and part at a time, and store
+              // the rows.
+              const uint32_t lane_off = (uint32_t)lane * 16u;
+              auto part4 = [&](int mi, int c, int v4) {
+                const char* gb =
+                    (const char*)slots + (int64_t)((wv * 2 + mi) * 8 + c) * 4096 + v4 * 1024;
+                f32x4 tot = *(const f32x4*)(gb + lane_off);
+#pragma unroll
+                for (int q = 1; q < kMaxSplit; ++q)
+                  if (q < parts) tot += *(const f32x4*)(gb + q * kSplitSlotFloats * 4 + lane_off);
+                return tot;
+              };
+              for (int mi = 0; mi < 2; ++mi)
+                for (int v4 = 0; v4 < 4; ++v4) {
+                  if (kSwiGLU) {
+                    for (int q = 0; q < 4; ++q) {
+                      const f32x4 gt = part4(mi, 2 * q, v4), up = part4(mi, 2 * q + 1, v4);
+                      const int64_t col = n0 + 32 * q + (lane & 31);
+#pragma unroll
+                      for (int i4 = 0; i4 < 4; ++i4) {
+                        const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
+                        if (rr < rows && col < N)
+                          C[(int64_t)(row0 + rr) * N + col] =
+                              f32_to_bf16(silu_f(gt[i4]) * up[i4]);
+                      }
+                    }
+                  } else {
+                    for (int c = 0; c < 8; ++c) {
+                      const f32x4 t = part4(mi, c, v4);
+                      const int64_t col = n0 + 32 * c + (lane & 31);
+#pragma unroll
+                      for (int i4 = 0; i4 < 4; ++i4) {
+                        const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
+                        float x = t[i4];
+                        if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+                        if (rr < rows && col < N) C[(int64_t)(row0 + rr) * N + col] = f32_to_bf16(x);
+                      }
+                    }
+                  }
+                }
+            }
+          }
         }
-      }
+      };
+      if (shape == 0)
+        run(std::integral_constant<int, 8>{});
+      else if (shape == 1)
+        run(std::integral_constant<int, 4>{});
+      else
+        run(std::integral_constant<int, 2>{});
       if (!has_next) break;
       cu = nx;
     }
