@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("b1bd779b0a85821576d3f5a874f243db10d6bd6cadfb75b953989892c805aec1",
-                            2110486.410714286, 301952.40178571426),
+    "mixtral_swiglu_bf16": ("816ecbef5f811f9358fd0c1bcc3d6ff5499a43eef6330333d30a9e5df1b44118",
+                            3106280.785714286, 232146.7767857143),
 }
 
 
