@@ -220,6 +220,49 @@ def test_expert_ffn_stage(kind, dtype):
     assert max_abs_rel(got, ref) <= OUT_TOL[dtype]
 
 
+@pytest.mark.parametrize("kind,D,DH", [("swiglu", 4096, 4096), ("swiglu", 512, 4096),
+                                        ("relu2", 512, 4096)])
+def test_expert_ffn_designed_row_counts(kind, D, DH):
+    """Rows per expert at each edge of the bf16 GEMM's tile row layouts (1, 64, 65, 128, 129,
+    256 and 257 rows, and an expert of two tiles). With D = DH = 4096 the up-projection has
+    9 x 32 = 288 tiles: a whole wave of 256 and a tail of 32 split along K. Two calls on one
+    workspace must give the same bits (the work queue and the split tickets are left ready for
+    the next call)."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    counts = [1, 64, 65, 128, 129, 256, 257, 300]
+    E, R = len(counts), sum(counts)
+    sp = spec("mixtral_swiglu_bf16", T=R, D=D, DH=DH, E=E, top_k=1, kind=kind,
+              capacity_factor=0.0)
+    _say(f"designed row counts {counts}: {kind} D={D} DH={DH}")
+    I = make_inputs(sp, seed=11)
+    p = B.Problem.from_spec(sp)
+    offsets_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    offsets = torch.from_numpy(offsets_np).cuda()
+    x_perm = to_dev(I.x)  # expert-ordered rows: expert e owns rows offsets[e] .. offsets[e+1]
+    d = device_inputs(I)
+    ws = B.alloc_workspace(p)
+    outs = []
+    for _ in range(2):
+        y = torch.zeros((R, sp.D_out), dtype=torch.bfloat16, device="cuda")
+        B.moe_expert_ffn(p, x_perm, offsets, d["w1"], d["w3"], d["w2"], y, ws)
+        torch.cuda.synchronize()
+        outs.append(to_host(y))
+    assert np.array_equal(outs[0], outs[1])  # bf16 values widened exactly to float32
+    xs = I.values("x")
+    ref = np.zeros((R, sp.D_out))
+    for e in range(E):
+        lo, hi = offsets_np[e], offsets_np[e + 1]
+        ref[lo:hi] = oracle.expert_forward(kind, xs[lo:hi], I.values("w1")[e],
+                                           I.values("w2")[e],
+                                           None if I.w3 is None else I.values("w3")[e])
+    # every expert's rows, and each edge row count, within the bar on its own
+    assert max_abs_rel(outs[0], ref) <= OUT_TOL["bf16"]
+    for e in range(E):
+        lo, hi = offsets_np[e], offsets_np[e + 1]
+        assert max_abs_rel(outs[0][lo:hi], ref[lo:hi]) <= OUT_TOL["bf16"], (e, counts[e])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_combine_stage(dtype):
     import torch
