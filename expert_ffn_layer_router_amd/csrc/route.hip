@@ -146,11 +146,15 @@ __device__ __forceinline__ void chosen_logits_f64(const uint16_t* __restrict__ x
       if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
     return e;
   };
+  // the chosen experts' biases, loaded together (lane j holds choice j's)
+  double my_b[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    my_b[i] = (bias && lane + kWave * i < k) ? (double)bias[my_e[i]] : 0.0;
   auto put = [&](int j, double v) {
-    if (bias) v += (double)bias[row_of(j)];
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (j == lane + kWave * i) my_v[i] = v;
+      if (j == lane + kWave * i) my_v[i] = v + my_b[i];
   };
   token_dots_f64<CG>(x, wt, t, D, k, row_of, put);
 }
@@ -483,8 +487,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
   const int lane = lane_id(), wv = wave_id();
   const int64_t t = (int64_t)blockIdx.x * kRouteTokensPerBlock + wv;
   const bool valid = t < T;
-  double wmax = 0.0;
-  for (int e = 0; e < E; ++e) wmax = fmax(wmax, wnorm[e]);
+  double wmax = 0.0;  // max_e |W_e|: one load per lane and a wave max
+  for (int e = lane; e < E; e += kWave) wmax = fmax(wmax, wnorm[e]);
+  wmax = wave_max(wmax);
 
   double lg[EPL], prob[EPL], my_v[EPL];
   int my_e[EPL];
@@ -804,6 +809,8 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
     MOE_ROUTE_SELECT(EPLV, 2);      \
   else if (p.top_k <= 4)            \
     MOE_ROUTE_SELECT(EPLV, 4);      \
+  else if (p.top_k <= 6)            \
+    MOE_ROUTE_SELECT(EPLV, 6);      \
   else                              \
     MOE_ROUTE_SELECT(EPLV, 8);
   if (epl <= 1) {
