@@ -626,11 +626,13 @@ __global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
 }
 
 constexpr int kAuxThreads = 256;
+static_assert(kAuxThreads >= kMaxExperts, "one thread per expert in the final sum");
 
 // Switch loss from the per-block partials (expert-major, nblk per expert): block e sums
 // expert e's probability partials and counts in a fixed order (strided per thread, then a
 // fixed tree), writes P_e and count_e, and takes a ticket; the block with the last ticket
-// forms aux = E * sum_e (count_e / (T k)) * (P_e / T) in expert order and resets the ticket.
+// forms aux = E * sum_e (count_e / (T k)) * (P_e / T) (the E terms added by a fixed tree) and
+// resets the ticket.
 // The result does not depend on block scheduling.
 __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int64_t nblk, int E, int64_t T, int k, const double* __restrict__ psum_blk,
@@ -644,6 +646,7 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
   int64_t cacc = 0;
   const double* pp = psum_blk + (int64_t)e * nblk;
   const int32_t* cp = count_blk + (int64_t)e * nblk;
+#pragma unroll 4
   for (int64_t b = i; b < nblk; b += kAuxThreads) {
     pacc += pp[b];
     cacc += cp[b];
@@ -666,16 +669,25 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     s_last = atomicAdd(ticket, 1) == E - 1;
   }
   __syncthreads();
-  if (!s_last || i != 0) return;
+  if (!s_last) return;
   __threadfence();
-  double acc = 0.0;
-  for (int q = 0; q < E; ++q) {
-    const double Pe = __builtin_nontemporal_load(&pe[q]);
-    const double c = (double)__builtin_nontemporal_load(&ce[q]);
-    acc += (T > 0) ? (c / ((double)T * (double)k)) * (Pe / (double)T) : 0.0;
+  // thread q forms expert q's term; a fixed tree adds them
+  double term = 0.0;
+  if (i < E && T > 0) {
+    const double Pe = __builtin_nontemporal_load(&pe[i]);
+    const double c = (double)__builtin_nontemporal_load(&ce[i]);
+    term = (c / ((double)T * (double)k)) * (Pe / (double)T);
   }
-  *aux = (float)((double)E * acc);
-  *ticket = 0;
+  s_p[i] = term;
+  __syncthreads();
+  for (int h = kAuxThreads / 2; h >= 1; h >>= 1) {
+    if (i < h) s_p[i] += s_p[i + h];
+    __syncthreads();
+  }
+  if (i == 0) {
+    *aux = (float)((double)E * s_p[0]);
+    *ticket = 0;
+  }
 }
 
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
