@@ -250,8 +250,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     while (split > 1 && (nst_all % (2 * split) != 0 || nst_all / split < kMinPartStages)) --split;
     if (split == 1) full = total;
   }
-  const int xcd = b & 7;
-  // Position q of this XCD's queue -> tile L, K part ks. False past the end.
+  const int xcd = b & 7, per = nblk >> 3, jb = b >> 3;
+  // Position q of this XCD's queue -> tile L, K part ks; false past the end. Positions past
+  // the whole tiles stand for this block's own K part (at most one per block, r * s <= blocks),
+  // handed out once: taking parts from the queue instead would let one block take two while
+  // another, still busy with its whole tiles, gets none.
+  bool part_taken = false;
   auto unit_at = [&](int q, int& L, int& ks) -> bool {
     ks = 0;
     L = 0;
@@ -266,9 +270,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       L = xcd * F8 + q;
       return true;
     }
+    if (part_taken) return false;
     const int R8 = (r * split + 7) >> 3;
-    const int u = xcd * R8 + (q - F8);
-    if (q - F8 >= R8 || u >= r * split) return false;
+    const int u = xcd * R8 + jb;
+    if (jb >= R8 || u >= r * split) return false;
+    part_taken = true;
     L = full + u / split;
     ks = u % split;
     return true;
@@ -276,7 +282,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   // Queue positions: block (xcd, j) starts with positions j and per + j of its XCD's list; the
   // XCD's counter hands out the rest from 2 per on, in order.
   int32_t* const qctr = g.queue + xcd;
-  const int per = nblk >> 3, jb = b >> 3;
   auto grab = [&]() { return 2 * per + atomicAdd(qctr, 1); };
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -402,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       // The unit after next (taken now so that its atomic is not waited for at this barrier),
       // and the next unit's source rows: both are in flight while this unit computes.
       int after_next = -1;
-      if (tid == 0 && has_next) after_next = grab();
+      if (tid == 0 && has_next && Ln < full) after_next = grab();  // none after a K part
       Unit nx = cu;
       int32_t nsrc[8];
       if (has_next) {
@@ -439,26 +444,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         const int64_t n0 = (int64_t)cu.n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output col
         const int wr0 = wave_row0<NN>(wv), wc0 = wave_col_tile0<NN>(wv);
         // 32x32 accumulator layout: lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
+        // Output store of this wave's rows: lanes l and l ^ 1 hold adjacent columns of the same
+        // rows. For each pair of rows (v0, v0 + 1) they swap one value, so the even lane stores
+        // columns (c, c + 1) of row v0 and the odd lane the same two columns of row v0 + 1: one
+        // 4-byte store per two outputs. cq is the output column of the lanes' 32-column tile.
+        const bool odd = lane & 1;
+        const int lrow = wr0 + 4 * (lane >> 5) + (odd ? 1 : 0);
+        const int colp = (lane & 31) & ~1;
+        uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
+        const int ccol0 = 32 * (kSwiGLU ? wc0 / 2 : wc0);  // first output column of the wave
+        const int ccols = 32 * (kSwiGLU ? NN / 2 : NN);
+        const bool whole = wr0 + 64 <= rows && n0 + ccol0 + ccols <= N;
+        auto put = [&](int mi, int v0, int cq, float x0, float x1) {
+          const float recv = swap_adjacent_lanes(odd ? x0 : x1);
+          const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
+          const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
+          if (whole || (lrow + dr < rows && n0 + cq + colp < N))
+            *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
+        };
         if (parts == 1) {
           if (wr0 < rows) {  // a whole tile: store this wave's part from the accumulators
-            // Lanes l and l ^ 1 hold adjacent columns of the same rows. For each pair of rows
-            // (v0, v0 + 1) they swap one value, so the even lane stores columns (c, c + 1) of
-            // row v0 and the odd lane the same two columns of row v0 + 1: one 4-byte store per
-            // two outputs.
-            const bool odd = lane & 1;
-            const int lrow = wr0 + 4 * (lane >> 5) + (odd ? 1 : 0);
-            const int colp = (lane & 31) & ~1;
-            uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
-            const int ccol0 = 32 * (kSwiGLU ? wc0 / 2 : wc0);  // first output column of the wave
-            const int ccols = 32 * (kSwiGLU ? NN / 2 : NN);
-            const bool whole = wr0 + 64 <= rows && n0 + ccol0 + ccols <= N;
-            auto put = [&](int mi, int v0, int cq, float x0, float x1) {
-              const float recv = swap_adjacent_lanes(odd ? x0 : x1);
-              const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
-              const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
-              if (whole || (lrow + dr < rows && n0 + cq + colp < N))
-                *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
-            };
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
           // ticket adds all parts in part order and stores the tile. The sum order is fixed, so
           // the result does not depend on which part finishes last.
           float* slots = g.split_ws + (int64_t)(L - full) * parts * kSplitSlotFloats;
-          if (64 * wv < rows) {
+          if (wr0 < rows) {
             float* mine = slots + (int64_t)ks * kSplitSlotFloats;
             // group (wv, mi, c) of 16 accumulators: 4 KB at a wave-uniform base, lane l's 16-byte
             // chunk v4 at +1 KB * v4 + 16 l (so every store is base + one lane offset + a const)
@@ -511,45 +516,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
           if (s_last) {
             __threadfence();
             if (tid == 0) g.split_ctr[L - full] = 0;  // ready for the next launch
-            if (64 * wv < rows) {
+            if (wr0 < rows) {
               // Every part (this one included) has stored its partial: add them in part order,
               // 16 coalesced bytes (4 rows of one column) per lane and part at a time, and store
               // the rows.
               const uint32_t lane_off = (uint32_t)lane * 16u;
-              auto part4 = [&](int mi, int c, int v4) {
-                const char* gb =
-                    (const char*)slots + (int64_t)((wv * 2 + mi) * 8 + c) * 4096 + v4 * 1024;
-                f32x4 tot = *(const f32x4*)(gb + lane_off);
-#pragma unroll
-                for (int q = 1; q < kMaxSplit; ++q)
-                  if (q < parts) tot += *(const f32x4*)(gb + q * kSplitSlotFloats * 4 + lane_off);
-                return tot;
-              };
               for (int mi = 0; mi < 2; ++mi)
                 for (int v4 = 0; v4 < 4; ++v4) {
-                  if (kSwiGLU) {
-                    for (int q = 0; q < 4; ++q) {
-                      const f32x4 gt = part4(mi, 2 * q, v4), up = part4(mi, 2 * q + 1, v4);
-                      const int64_t col = n0 + 32 * q + (lane & 31);
+                  // every part of this row group's 8 column tiles, all loads issued before any
+                  // is used; then added in part order
+                  f32x4 pv[kMaxSplit][8];
 #pragma unroll
-                      for (int i4 = 0; i4 < 4; ++i4) {
-                        const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
-                        if (rr < rows && col < N)
-                          C[(int64_t)(row0 + rr) * N + col] =
-                              f32_to_bf16(silu_f(gt[i4]) * up[i4]);
-                      }
+                  for (int q = 0; q < kMaxSplit; ++q)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                      if (q < parts)
+                        pv[q][c] = *(const f32x4*)((const char*)slots +
+                                                   (int64_t)((wv * 2 + mi) * 8 + c) * 4096 +
+                                                   v4 * 1024 + q * kSplitSlotFloats * 4 + lane_off);
+                  f32x4 t[8];
+#pragma unroll
+                  for (int c = 0; c < 8; ++c) {
+                    t[c] = pv[0][c];
+#pragma unroll
+                    for (int q = 1; q < kMaxSplit; ++q)
+                      if (q < parts) t[c] += pv[q][c];
+                  }
+                  // rows 8 v4 + 4 (lane / 32) + i4 of the lanes' columns: accumulator rows
+                  // v = 4 v4 + i4, stored as the pairs (v, v + 1) like a whole tile
+                  if (kSwiGLU) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                      const f32x4 gt = t[2 * q], up = t[2 * q + 1];
+#pragma unroll
+                      for (int i4 = 0; i4 < 4; i4 += 2)
+                        put(mi, 4 * v4 + i4, 32 * q, silu_f(gt[i4]) * up[i4],
+                            silu_f(gt[i4 + 1]) * up[i4 + 1]);
                     }
                   } else {
-                    for (int c = 0; c < 8; ++c) {
-                      const f32x4 t = part4(mi, c, v4);
-                      const int64_t col = n0 + 32 * c + (lane & 31);
 #pragma unroll
-                      for (int i4 = 0; i4 < 4; ++i4) {
-                        const int rr = 64 * wv + 32 * mi + 8 * v4 + 4 * (lane >> 5) + i4;
-                        float x = t[i4];
-                        if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
-                        if (rr < rows && col < N) C[(int64_t)(row0 + rr) * N + col] = f32_to_bf16(x);
-                      }
+                    for (int c = 0; c < 8; ++c) {
+                      f32x4 x = t[c];
+                      if (EPI == EPI_RELU)
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) x[i4] = fmaxf(x[i4], 0.f);
+#pragma unroll
+                      for (int i4 = 0; i4 < 4; i4 += 2) put(mi, 4 * v4 + i4, 32 * c, x[i4], x[i4 + 1]);
                     }
                   }
                 }
