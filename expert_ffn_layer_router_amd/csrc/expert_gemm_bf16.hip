@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   __shared__ __align__(16) uint16_t sA1[kSlab];
   __shared__ __align__(16) uint16_t sB0[kSlab];
   __shared__ __align__(16) uint16_t sB1[kSlab];
-  __shared__ int s_unit[2];  // queue positions of later units, by unit parity
+  __shared__ int s_unit[2];  // work positions of later units, by unit parity
   __shared__ int s_last;
 
   // One block per CU (gridDim.x blocks: a multiple of 8, at most kSplitSlots). Tiles that fill
@@ -251,26 +251,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     if (split == 1) full = total;
   }
   const int xcd = b & 7, per = nblk >> 3, jb = b >> 3;
-  // Position q of this XCD's queue -> tile L, K part ks; false past the end. Positions past
-  // the whole tiles stand for this block's own K part (at most one per block, r * s <= blocks),
-  // handed out once: taking parts from the queue instead would let one block take two while
-  // another, still busy with its whole tiles, gets none.
+  // Work positions: q * 8 + x stands for entry q of XCD x's list (its eighth of the whole
+  // tiles, or of all tiles when nothing is split); -2: no whole tile is left anywhere; -1:
+  // nothing. Entries j and per + j of its own XCD's list are block (xcd, j)'s first two units;
+  // the XCD's counter hands out the rest of the list from 2 per on, in order, and a block whose
+  // own list is used up takes entries of the other XCDs' lists (so every XCD ends at about the
+  // same time). Each block's K part (at most one, r * s <= blocks) comes last and is its own:
+  // taking parts from a queue would let one block take two while another, still busy with its
+  // whole tiles, gets none.
+  const int chunk = (total + 7) >> 3;  // list length per XCD when nothing is split
+  const int F8 = full >> 3;            // whole tiles per XCD when the tail is split
   bool part_taken = false;
-  auto unit_at = [&](int q, int& L, int& ks) -> bool {
+  auto unit_at = [&](int pos, int& L, int& ks) -> bool {
     ks = 0;
     L = 0;
-    if (q < 0) return false;
-    if (split == 1) {
-      const int chunk = (total + 7) >> 3;
-      L = xcd * chunk + q;
-      return q < chunk && L < total;
+    if (pos >= 0) {
+      const int src = pos & 7, q = pos >> 3;
+      if (split == 1) {
+        L = src * chunk + q;
+        return q < chunk && L < total;
+      }
+      if (q < F8) {
+        L = src * F8 + q;
+        return true;
+      }
+      // an own entry past the whole tiles: this block's K part
+    } else if (pos != -2 || split == 1) {
+      return false;
     }
-    const int F8 = full >> 3;
-    if (q < F8) {
-      L = xcd * F8 + q;
-      return true;
-    }
-    if (part_taken) return false;
+    if (split == 1 || part_taken) return false;
     const int R8 = (r * split + 7) >> 3;
     const int u = xcd * R8 + jb;
     if (jb >= R8 || u >= r * split) return false;
@@ -279,10 +288,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     ks = u % split;
     return true;
   };
-  // Queue positions: block (xcd, j) starts with positions j and per + j of its XCD's list; the
-  // XCD's counter hands out the rest from 2 per on, in order.
-  int32_t* const qctr = g.queue + xcd;
-  auto grab = [&]() { return 2 * per + atomicAdd(qctr, 1); };
+  // The next work position from the counters (own XCD first), for thread 0 only.
+  unsigned done_mask = 0;  // lists this thread has found used up
+  auto grab = [&]() -> int {
+    for (int d = 0; d < 8; ++d) {
+      const int src = (xcd + d) & 7;
+      if (done_mask & (1u << src)) continue;
+      const int q = 2 * per + atomicAdd(g.queue + src, 1);
+      const int lim = split == 1 ? min(chunk, total - src * chunk) : F8;
+      if (q < lim) return q * 8 + src;
+      done_mask |= 1u << src;
+    }
+    return split == 1 ? -1 : -2;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -374,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
 
   int L0, ks0;
-  if (unit_at(jb, L0, ks0)) {
+  if (unit_at(jb * 8 + xcd, L0, ks0)) {
     Unit cu = geometry(L0, ks0);
     Loader ld;
     {
@@ -391,7 +409,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     for (int i = 0;; ++i) {
       int Ln, ksn;
       // (the first unit's successor is fixed; later ones were published through LDS)
-      const int qn = i == 0 ? per + jb : __builtin_amdgcn_readfirstlane(s_unit[(i + 1) & 1]);
+      const int qn =
+          i == 0 ? (per + jb) * 8 + xcd : __builtin_amdgcn_readfirstlane(s_unit[(i + 1) & 1]);
       const bool has_next = unit_at(qn, Ln, ksn);
 
       f32x16 acc[2][8];
