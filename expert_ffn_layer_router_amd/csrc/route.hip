@@ -212,6 +212,92 @@ __device__ __forceinline__ double topk_rounds(int E, int k, const double lg[EPL]
   return min_gap;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  return __longlong_as_double((long long)readlane64((uint64_t)__double_as_longlong(v), l));
+}
+// Wave-wide maximum of a 64-bit key, the same in every lane: within each row of 16 lanes by
+// four DPP exchanges (lanes l ^ 1, l ^ 2, then the mirrored lane of the half row and of the
+// row), then the four row maxima read out.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t m) {
+  uint64_t o;
+  o = dpp64<0xB1>(m);   // quad_perm [1,0,3,2]
+  m = o > m ? o : m;
+  o = dpp64<0x4E>(m);   // quad_perm [2,3,0,1]
+  m = o > m ? o : m;
+  o = dpp64<0x141>(m);  // row_half_mirror
+  m = o > m ? o : m;
+  o = dpp64<0x140>(m);  // row_mirror
+  m = o > m ? o : m;
+  const uint64_t r0 = readlane64(m, 0), r1 = readlane64(m, 16);
+  const uint64_t r2 = readlane64(m, 32), r3 = readlane64(m, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// The same selection as topk_rounds with want_gap, for the certified fast path: each round's
+// argmax runs on 64-bit keys (the logit rounded to float32, mapped to an order-preserving
+// unsigned integer, above the complemented expert index, so equal keys go to the lower index),
+// and the chosen expert's float64 value is read from its lane. Rounding to float32 can only
+// reorder logits that lie within one float32 ulp of each other; the gaps returned are float64
+// differences of the chosen sequence, and the caller's certification threshold includes two
+// float32 ulps of the largest logit, so any such token is sent to the exact path.
+template <int EPL>
+__device__ __forceinline__ double topk_rounds_keys(int E, int k, const double lg[EPL],
+                                                   bool sel[EPL], double my_v[EPL],
+                                                   int my_e[EPL]) {
+  const int lane = lane_id();
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    const uint32_t u = __float_as_uint((float)lg[i]);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[i] = e < E ? (((uint64_t)o << 32) | (0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+    sel[i] = false;
+    my_v[i] = 0.0;
+    my_e[i] = 0;
+  }
+  double prev = 0.0, min_gap = DBL_MAX;
+  const int rounds = k < E ? k + 1 : k;
+  for (int j = 0; j < rounds; ++j) {
+    uint64_t best = 0;
+    double cand = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (!sel[i] && key[i] > best) {
+        best = key[i];
+        cand = lg[i];
+      }
+    const uint64_t w = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)w);
+    const double bv = readlane_f64(cand, e & (kWave - 1));
+    if (j > 0) min_gap = fmin(min_gap, prev - bv);
+    prev = bv;
+    if (j == k) break;  // the extra round only measures the boundary gap
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (e == lane + kWave * i) sel[i] = true;
+      if (j == lane + kWave * i) {
+        my_v[i] = bv;
+        my_e[i] = e;
+      }
+    }
+  }
+  return min_gap;
+}
+
 // Probabilities over all experts (returned in prob[]), and the index/gate rows.
 template <int EPL>
 __device__ __forceinline__ void finish_token(int E, int k, int64_t t, const double lg[EPL],
@@ -539,8 +625,8 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     const double gamma = 32.0 * 0x1p-23;
     const double B = gamma * sqrt(xn2 * (1.0 + (double)D * 0x1p-23)) * wmax * (1.0 + 1e-6) +
                      rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30;
-    const double gap = topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, true);
-    flagged = !(gap > 2.0 * B);
+    const double gap = topk_rounds_keys<EPL>(E, k, lg, sel, my_v, my_e);
+    flagged = !(gap > 2.0 * B + lmax * 0x1p-22);
     if (flagged) {
       // uncertified: decided later by route_fallback_kernel from exact logits
       if (lane == 0) list[atomicAdd(nlist, 1)] = (int32_t)t;
