@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("816ecbef5f811f9358fd0c1bcc3d6ff5499a43eef6330333d30a9e5df1b44118",
-                            3106280.785714286, 232146.7767857143),
+    "mixtral_swiglu_bf16": ("1de685249213cae805e7853fa4ed7d7c4056ccc215020a4341770abc334d3cd2",
+                            3102533.151785714, 237983.49107142858),
 }
 
 
