@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("1de685249213cae805e7853fa4ed7d7c4056ccc215020a4341770abc334d3cd2",
-                            3102533.151785714, 237983.49107142858),
+    "mixtral_swiglu_bf16": ("1e7840997e931cd43cd537a8bb580f1002eeea2e9422b286475f8f32a3696870",
+                            3426028.901785714, 237382.89285714287),
 }
 
 

@@ -7,22 +7,26 @@
 // v_mfma_f32_32x32x16_bf16, 256 fp32 accumulators per lane).
 //
 // Both operands go from global memory straight into LDS with global_load_lds_dwordx4 (lane l
-// of an instruction writes 16 bytes at the instruction's LDS base + 16 l), one whole 128-byte
-// line per 8 lanes, so the vector L1 only ever sees full-line requests:
-//  * A (activations, 256 rows x 64 K per stage, 128 bytes a row): an instruction fills 8 rows;
-//    16-byte chunk c of row r is stored at chunk c ^ ((r / 2) % 8), which makes the MFMA
-//    operand reads (ds_read_b128: 16 rows x 16 bytes per 16 lanes) conflict-free. A row gather
-//    (token rows of x through the dispatch permutation) is just a per-lane source address.
-//  * B (weights, 64 K-rows x 256 columns per stage, (K, N) row-major, 512 bytes a row): an
-//    instruction fills 2 K-rows; chunk c of K-row k is stored at c ^ (4 (k % 4)), and the MFMA
-//    operands come from transposed reads (ds_read_b64_tr_b16), which turn the N-contiguous
-//    layout into 8 consecutive K values per lane.
-// Two LDS buffers per operand (128 KB). The block synchronises once per stage, before the
+// of an instruction writes 16 bytes at the instruction's LDS base + 16 l). A stage is 32 of K:
+//  * A (activations, 256 rows x 32 K, 64 bytes a row): an instruction fills 16 rows; 16-byte
+//    chunk c of row r is stored at chunk c ^ ((r / 4) % 4), which makes the MFMA operand
+//    reads (ds_read_b128: 16 rows x 16 bytes per 16 lanes, 64 banks) conflict-free. A row
+//    gather (token rows of x through the dispatch permutation) is just a per-lane source
+//    address.
+//  * B (weights, 32 K-rows x 256 columns, (K, N) row-major, 512 bytes a row): an instruction
+//    fills 2 K-rows; chunk c of K-row k is stored at c ^ (4 (k % 4)), and the MFMA operands
+//    come from transposed reads (ds_read_b64_tr_b16), which turn the N-contiguous layout into
+//    8 consecutive K values per lane.
+// Four stage buffers (A then B, 32 KB each, 128 KB in all), used in rotation. The loads of a
+// stage are issued four stages before it is computed, so about three stages (96 KB per CU)
+// are in flight while the waves compute. The block synchronises once per stage, before the
 // stage's last k-step: that k-step's operands are already in registers, so its MFMAs cover
-// the reads of the next buffer's first operands and the issue of the loads two stages ahead
-// (into the buffer just finished). The loads are issued from inline assembly, so the compiler
-// does not track them; every wait for them is explicit (s_waitcnt vmcnt(0) before the
-// barrier that publishes a stage).
+// the reads of the next buffer's first operands and the issue of the loads four stages ahead
+// into the buffer just finished. The loads are issued from inline assembly, so the compiler
+// does not track them; every wait for them is explicit and counted: before the barrier that
+// publishes stage s + 1, a wave lets only its loads of the two stages after it stay in
+// flight (s_waitcnt vmcnt(16), 8 loads per wave and stage; vector memory operations
+// complete in issue order).
 //  * SwiGLU: the 256 columns interleave 32-column tiles of W1 and W3 for the same 128 output
 //    columns, so each lane holds the gate and the up value of the same output.
 //  * Epilogue: lanes l and l ^ 1 hold adjacent columns; one swap per pair of rows lets each
@@ -40,12 +44,15 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kThreads = 256;
 constexpr int kTileBlockN = 8;       // column tiles per L2-sharing block of one expert
-constexpr int kSlab = kBK * 256;     // elements of one stage of either operand (32 KB)
+constexpr int kNBuf = 4;             // stage buffers; loads run kNBuf stages ahead
+constexpr uint32_t kHalf = kBK * 256 * 2;  // bytes of one stage of either operand (16 KB)
+constexpr uint32_t kBuf = 2 * kHalf;       // one stage buffer: A then B (32 KB)
+constexpr int kKeep = (kNBuf - 2) * 8;     // own loads a stage wait leaves in flight
 constexpr int kMaxSplit = 4;         // K parts of a tail tile at most
-constexpr int kMinPartStages = 32;   // K stages of a part at least (K >= 2048 per part)
+constexpr int kMinPartStages = 64;   // K stages of a part at least (K >= 2048 per part)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -65,24 +72,45 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
-__device__ __forceinline__ void wait_vm0_lgkm0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// The same for a wave-uniform keep of 0, 8, 16, 24 or 32 loads (a scalar branch to the
+// matching immediate; any other value waits for everything).
+__device__ __forceinline__ void wait_keep(int keep) {
+  switch (keep) {
+    case 8: wait_vm_lgkm0<8>(); break;
+    case 16: wait_vm_lgkm0<16>(); break;
+    case 24: wait_vm_lgkm0<24>(); break;
+    case 32: wait_vm_lgkm0<32>(); break;
+    default: wait_vm_lgkm0<0>(); break;
+  }
+}
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 struct Loader {
-  const char* a[8];  // A source of this lane for instruction j, at K = 0
+  const char* a[4];  // A source of this lane for instruction j, at K = 0
   const char* b[2];  // B source of this lane for instructions with j % 2 == q, at K-row 0
   int64_t b_row_bytes;
 };
 
-__device__ __forceinline__ void load_stage(const Loader& ld, int64_t k0, uint32_t sa, uint32_t sb,
-                                           int wv) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(ld.a[j] + k0 * 2, sa + (8 * wv + j) * 1024);
+// Load d (0..7) of this wave for a stage at K offset k0 into the buffer at LDS byte address
+// sa: even d -> A instruction d / 2 (16 rows), odd d -> B instruction d / 2 (2 K-rows).
+__device__ __forceinline__ void load_one(const Loader& ld, int64_t k0, int64_t bk, uint32_t sa,
+                                         int wv, int d) {
+  const int j = d >> 1;
+  if (d & 1)
+    dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sa + kHalf + (4 * wv + j) * 1024);
+  else
+    dma16(ld.a[j] + k0 * 2, sa + (4 * wv + j) * 1024);
+}
+__device__ __forceinline__ void load_stage(const Loader& ld, int64_t k0, uint32_t sa, int wv) {
   const int64_t bk = k0 * ld.b_row_bytes;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sb + (8 * wv + j) * 1024);
+  for (int d = 0; d < 8; ++d) load_one(ld, k0, bk, sa, wv, d);
 }
 
 typedef __attribute__((address_space(3))) const char lds_cchar;
@@ -98,40 +126,39 @@ __device__ __forceinline__ bf16x8 read_b(const uint32_t (&bb)[4], int c, int t) 
 }
 
 // A operand of m-tile mi, k-step t: row 64 w + 32 mi + lane % 32, K values 16t + 8 (lane/32)..
-__device__ __forceinline__ bf16x8 read_a(const uint32_t (&ab)[4], int mi, int t) {
-  return *(const lds_bf16x8*)((lds_cchar*)(uintptr_t)ab[t] + mi * 32 * 128);
+__device__ __forceinline__ bf16x8 read_a(const uint32_t (&ab)[2], int mi, int t) {
+  return *(const lds_bf16x8*)((lds_cchar*)(uintptr_t)ab[t] + mi * 32 * 64);
 }
 
-// One stage (4 k-steps x 2 x NN MFMAs: this wave's 2 row tiles by its NN column tiles) on the
+// One stage (2 k-steps x 2 x NN MFMAs: this wave's 2 row tiles by its NN column tiles) on the
 // current buffer, with the stage boundary inside it. Operands rotate through registers: the B
-// read for k-step t + 1 of column tile c follows the two MFMAs of k-step t that consume it,
-// and the A operands of k-step t + 1 are read at the start of k-step t. So k-steps 0..2 bring
-// in all of k-step 3's operands; then every read and this wave's loads of the next buffer are
-// waited for and the block synchronises, and k-step 3 runs from registers while the next
-// buffer's k-step 0 operands are read and, when `load2`, the loads of the stage after next
-// (K offset k2) are issued into the current buffer, which no wave reads any more. The matrix
-// pipe is thus never left waiting for a whole LDS round trip at a stage boundary.
+// read for k-step 1 of column tile c follows the two MFMAs of k-step 0 that consume it, and
+// the A operands of k-step 1 are read at the start of k-step 0. Then every LDS read and all
+// but `keep` of this wave's loads (those of the next stage included) are waited for and the
+// block synchronises, and k-step 1 runs from registers while the next buffer's k-step 0
+// operands are read and, when `load2`, the loads of the stage at K offset k2 are issued into
+// the current buffer, which no wave reads any more. The matrix pipe is thus never left
+// waiting for a whole LDS round trip at a stage boundary.
 template <int NN>
-__device__ __forceinline__ void stage(const uint32_t (&ab)[4], const uint32_t (&bb)[4],
-                                      const uint32_t (&abn)[4], const uint32_t (&bbn)[4],
+__device__ __forceinline__ void stage(const uint32_t (&ab)[2], const uint32_t (&bb)[4],
+                                      const uint32_t (&abn)[2], const uint32_t (&bbn)[4],
                                       f32x16 (&acc)[2][8], bf16x8& a0, bf16x8& a1, bf16x8 (&b)[8],
                                       const Loader& ld, int64_t k2, bool load2, uint32_t sa,
-                                      uint32_t sb, int wv) {
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-    const bf16x8 n0 = read_a(ab, 0, t + 1), n1 = read_a(ab, 1, t + 1);
+                                      int wv, int keep) {
+  {
+    const bf16x8 n0 = read_a(ab, 0, 1), n1 = read_a(ab, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < NN; ++c) {
       acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
       acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
-      b[c] = read_b(bb, c, t + 1);
+      b[c] = read_b(bb, c, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     a0 = n0;
     a1 = n1;
   }
-  wait_vm0_lgkm0();
+  wait_keep(keep);
   block_barrier();
   __builtin_amdgcn_sched_barrier(0);
   const bf16x8 n0 = read_a(abn, 0, 0), n1 = read_a(abn, 1, 0);
@@ -144,10 +171,7 @@ __device__ __forceinline__ void stage(const uint32_t (&ab)[4], const uint32_t (&
     b[c] = read_b(bbn, c, 0);
     if (load2) {
 #pragma unroll
-      for (int j = c * (8 / NN); j < (c + 1) * (8 / NN); ++j) {
-        dma16(ld.a[j] + k2 * 2, sa + (8 * wv + j) * 1024);
-        dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sb + (8 * wv + j) * 1024);
-      }
+      for (int d = c * (8 / NN); d < (c + 1) * (8 / NN); ++d) load_one(ld, k2, bk, sa, wv, d);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -171,19 +195,21 @@ __device__ __forceinline__ int wave_col_tile0(int wv) {
   return NN == 8 ? 0 : NN == 4 ? 4 * (wv >> 1) : 2 * wv;
 }
 template <int NN>
-__device__ __forceinline__ void unit_bases(uint32_t lds_a, uint32_t lds_b, const uint32_t (&aoff)[4],
-                                           const uint32_t (&boff)[4], int wv, uint32_t (&ab)[4],
+__device__ __forceinline__ void unit_bases(uint32_t lds_a, uint32_t lds_b, const uint32_t (&aoff)[2],
+                                           const uint32_t (&boff)[4], int wv, uint32_t (&ab)[2],
                                            uint32_t (&bb)[4]) {
-  const uint32_t arow = (uint32_t)wave_row0<NN>(wv) * 128u;
+  const uint32_t arow = (uint32_t)wave_row0<NN>(wv) * 64u;
   const int c0 = wave_col_tile0<NN>(wv);
   const uint32_t bhi = (uint32_t)(c0 >> 2) * 256u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ab[i] = lds_a + aoff[i] + arow;
+    if (i < 2) {
+      ab[i] = lds_a + aoff[i] + arow;
+      asm volatile("" : "+v"(ab[i]));
+    }
     // column tile c0 + i of the block (only i < NN is read)
     const int q = (c0 + i) & 3;
     bb[i] = lds_b + (q == 0 ? boff[0] : q == 1 ? boff[1] : q == 2 ? boff[2] : boff[3]) + bhi;
-    asm volatile("" : "+v"(ab[i]));
     asm volatile("" : "+v"(bb[i]));
   }
 }
@@ -218,10 +244,7 @@ __device__ __forceinline__ float swap_adjacent_lanes(float x) {
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const GroupedGemm g, int nt) {
   constexpr bool kSwiGLU = EPI == EPI_SWIGLU;
-  __shared__ __align__(16) uint16_t sA0[kSlab];
-  __shared__ __align__(16) uint16_t sA1[kSlab];
-  __shared__ __align__(16) uint16_t sB0[kSlab];
-  __shared__ __align__(16) uint16_t sB1[kSlab];
+  __shared__ __align__(16) char sbuf[kNBuf * kBuf];
   __shared__ int s_unit[2];  // work positions of later units, by unit parity
   __shared__ int s_last;
 
@@ -247,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     split = min(kMaxSplit, nblk / r);
     // each part needs an even number of stages, and enough of them (kMinPartStages) to pay
     // for storing and adding its float32 partial
-    while (split > 1 && (nst_all % (2 * split) != 0 || nst_all / split < kMinPartStages)) --split;
+    while (split > 1 && (nst_all % split != 0 || nst_all / split < kMinPartStages)) --split;
     if (split == 1) full = total;
   }
   const int xcd = b & 7, per = nblk >> 3, jb = b >> 3;
@@ -321,32 +344,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     u.rows = __builtin_amdgcn_readfirstlane(u.rows);
     u.n_tile = __builtin_amdgcn_readfirstlane(u.n_tile);
     u.parts = L >= full ? split : 1;  // K parts of this tile
-    u.nst = nst_all / u.parts;        // even: K % 128 == 0, and parts divide it in pairs
+    u.nst = nst_all / u.parts;        // >= 4: K % 128 == 0, and parts have kMinPartStages
     u.kbeg = (int64_t)ks * u.nst * kBK;
     return u;
   };
 
-  // A: instruction j of wave w fills tile rows 8 (8w + j) + lane / 8; its 16-byte chunk at
-  // position lane % 8 is logical chunk (lane % 8) ^ ((row / 2) % 8), and (row / 2) % 8 =
-  // 4 (j % 2) + lane / 16 % 4. Rows past the tile read row 0 of the expert block (valid memory;
-  // their outputs are never stored). The source rows of a unit are fetched ahead
+  // A: instruction j of wave w fills tile rows 16 (4w + j) + lane / 4; its 16-byte chunk at
+  // position lane % 4 is logical chunk (lane % 4) ^ ((row / 4) % 4), and (row / 4) % 4 =
+  // lane / 16 % 4. Rows past the tile read row 0 of the expert block (valid memory; their
+  // outputs are never stored). The source rows of a unit are fetched ahead
   // (`gather_rows`) and turned into addresses when its loads are about to be issued.
-  auto gather_rows = [&](const Unit& u, int32_t (&src)[8]) {
+  auto gather_rows = [&](const Unit& u, int32_t (&src)[4]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = 8 * (8 * wv + j) + (lane >> 3);
+    for (int j = 0; j < 4; ++j) {
+      const int rr = 16 * (4 * wv + j) + (lane >> 2);
       const int64_t gr = u.row0 + (rr < u.rows ? rr : 0);
       src[j] = g.a_gather ? g.a_gather[gr] / g.gather_div : (int32_t)gr;
     }
   };
-  auto make_loader = [&](const Unit& u, const int32_t (&src)[8]) {
+  auto make_loader = [&](const Unit& u, const int32_t (&src)[4]) {
     Loader ld;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = (lane & 7) ^ (4 * (j & 1) + ((lane >> 4) & 3));
+    for (int j = 0; j < 4; ++j) {
+      const int c = (lane & 3) ^ ((lane >> 4) & 3);
       ld.a[j] = (const char*)g.A + ((int64_t)src[j] * g.lda + 8 * c) * 2;
     }
-    // B: instruction j of wave w fills K-rows 16w + 2j + lane / 32; position lane % 32 of the
+    // B: instruction j of wave w fills K-rows 8w + 2j + lane / 32; position lane % 32 of the
     // K-row holds logical chunk (lane % 32) ^ (4 (K-row % 4)), K-row % 4 = 2 (j % 2) + lane / 32.
     const int64_t n0 = (int64_t)u.n_tile * (kSwiGLU ? kBN / 2 : kBN);
     ld.b_row_bytes = N * 2;
@@ -363,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         Wm = (const uint16_t*)g.B0;
         col = n0 + 8 * c;
       }
-      const int krow = 16 * wv + (lane >> 5);
+      const int krow = 8 * wv + (lane >> 5);
       ld.b[q] = (const char*)(Wm + (int64_t)u.e * K * N + (int64_t)krow * N + (col < N ? col : 0));
     }
     return ld;
@@ -372,13 +395,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   // Operand read offsets within a stage buffer: A for row lane % 32 (the wave's first row and
   // the row tile are added as constants), B for the block's column tiles 0..3 (see
   // `unit_bases`).
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[2], boff[4];
   {
     const int rr = lane & 31;  // + 32 mi
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int chunk = (2 * t + (lane >> 5)) ^ ((rr >> 1) & 7);
-      aoff[t] = (uint32_t)(rr * 128 + chunk * 16);
+    for (int t = 0; t < 2; ++t) {
+      const int chunk = (2 * t + (lane >> 5)) ^ ((rr >> 2) & 3);
+      aoff[t] = (uint32_t)(rr * 64 + chunk * 16);
     }
     const int gq = lane >> 4, Lq = lane & 15;
     const int krow = 8 * (gq >> 1) + (Lq >> 2);
@@ -388,22 +411,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       boff[c] = (uint32_t)(krow * 512 + chunk * 16 + 8 * (Lq & 1));
     }
   }
-  const uint32_t la0 = lds_addr(sA0), la1 = lds_addr(sA1);
-  const uint32_t lb0 = lds_addr(sB0), lb1 = lds_addr(sB1);
+  const uint32_t lbase = lds_addr(sbuf);
+
+  uint32_t co = 0;  // buffer offset of the current unit's first stage
 
   int L0, ks0;
   if (unit_at(jb * 8 + xcd, L0, ks0)) {
     Unit cu = geometry(L0, ks0);
     Loader ld;
     {
-      int32_t src[8];
+      int32_t src[4];
       gather_rows(cu, src);
       ld = make_loader(cu, src);
     }
-    // Stages 0 and 1 of the first unit; every later unit's first two stages are loaded by the
-    // last two stages of the unit before it (see `stage`), while that unit stores its tile.
-    load_stage(ld, cu.kbeg, la0, lb0, wv);
-    load_stage(ld, cu.kbeg + kBK, la1, lb1, wv);
+    // The first unit's first kNBuf stages; every later unit's are loaded by the last kNBuf
+    // stages of the unit before it.
+#pragma unroll
+    for (int q = 0; q < kNBuf; ++q) load_stage(ld, cu.kbeg + (int64_t)q * kBK, lbase + q * kBuf, wv);
 
     uint16_t* C = (uint16_t*)g.C;
     for (int i = 0;; ++i) {
@@ -421,14 +445,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[mi][c][v] = 0.f;
 
-      wait_vm0();
-      block_barrier();
+      if (i == 0) {
+        wait_keep((kNBuf - 1) * 8);
+        block_barrier();
+      }
       // The unit after next (taken now so that its atomic is not waited for at this barrier),
       // and the next unit's source rows: both are in flight while this unit computes.
       int after_next = -1;
       if (tid == 0 && has_next && Ln < full) after_next = grab();  // none after a K part
       Unit nx = cu;
-      int32_t nsrc[8];
+      int32_t nsrc[4];
       if (has_next) {
         nx = geometry(Ln, ksn);
         gather_rows(nx, nsrc);
@@ -438,26 +464,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       const int shape = (cu.parts > 1 || cu.rows > 128) ? 0 : (cu.rows > 64 ? 1 : 2);
       auto run = [&](auto nn_tag) {
         constexpr int NN = decltype(nn_tag)::value;
-        uint32_t ab0[4], bb0[4], ab1[4], bb1[4];
-        unit_bases<NN>(la0, lb0, aoff, boff, wv, ab0, bb0);
-        unit_bases<NN>(la1, lb1, aoff, boff, wv, ab1, bb1);
-        bf16x8 a0 = read_a(ab0, 0, 0), a1 = read_a(ab0, 1, 0), bq[8];
+        uint32_t vab[2], vbb[4];  // read bases in buffer 0
+        unit_bases<NN>(lbase, lbase + kHalf, aoff, boff, wv, vab, vbb);
+        uint32_t ab[2], bb[4];
 #pragma unroll
-        for (int c = 0; c < NN; ++c) bq[c] = read_b(bb0, c, 0);
+        for (int t = 0; t < 2; ++t) ab[t] = vab[t] + co;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bb[c] = vbb[c] + co;
+        bf16x8 a0 = read_a(ab, 0, 0), a1 = read_a(ab, 1, 0), bq[8];
+#pragma unroll
+        for (int c = 0; c < NN; ++c) bq[c] = read_b(bb, c, 0);
         const int nst = cu.nst;
         const int64_t kbeg = cu.kbeg;
-        for (int s = 0; s + 2 < nst; s += 2) {
-          stage<NN>(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 2) * kBK, true,
-                    la0, lb0, wv);
-          stage<NN>(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, kbeg + (int64_t)(s + 3) * kBK, true,
-                    la1, lb1, wv);
-        }
+        // One stage on buffer co (the next one is no): loads through loader LDR of the stage
+        // at K offset KL go into buffer co when LOAD; KEEP of this wave's loads may stay in
+        // flight at the stage's barrier. (A macro, not a lambda: captured operand arrays would
+        // live in scratch memory.)
+#define MOE_STAGE(LDR, KL, LOAD, KEEP)                                                      \
+  {                                                                                         \
+    uint32_t no = co + kBuf;                                                                \
+    no = no == kNBuf * kBuf ? 0u : no;                                                      \
+    no = __builtin_amdgcn_readfirstlane(no);                                                \
+    uint32_t abn[2], bbn[4];                                                                \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) abn[t] = vab[t] + no;                     \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) bbn[c] = vbb[c] + no;                     \
+    stage<NN>(ab, bb, abn, bbn, acc, a0, a1, bq, LDR, KL, LOAD, lbase + co, wv, KEEP);      \
+    co = no;                                                                                \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) ab[t] = abn[t];                           \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) bb[c] = bbn[c];                           \
+  }
+        for (int s = 0; s + kNBuf < nst; ++s)
+          MOE_STAGE(ld, kbeg + (int64_t)(s + kNBuf) * kBK, true, kKeep)
         // Publish the unit after next (its slot was last read before this unit's barriers),
-        // then let the last two stages load the next unit's first two.
+        // then let the last kNBuf stages load the next unit's first kNBuf. With no next unit
+        // those stages load nothing, so fewer loads are left to keep in flight.
         if (tid == 0) s_unit[i & 1] = after_next;
         if (has_next) ld = make_loader(nx, nsrc);
-        stage<NN>(ab0, bb0, ab1, bb1, acc, a0, a1, bq, ld, nx.kbeg, has_next, la0, lb0, wv);
-        stage<NN>(ab1, bb1, ab0, bb0, acc, a0, a1, bq, ld, nx.kbeg + kBK, has_next, la1, lb1, wv);
+#pragma unroll 1
+        for (int q = 0; q < kNBuf; ++q) {
+          const int keep = has_next ? kKeep : (kNBuf - 2 - q > 0 ? (kNBuf - 2 - q) * 8 : 0);
+          MOE_STAGE(ld, nx.kbeg + (int64_t)q * kBK, has_next, keep)
+        }
+#undef MOE_STAGE
 
         const int row0 = cu.row0, rows = cu.rows, parts = cu.parts, L = cu.L, ks = cu.ks;
         const int64_t n0 = (int64_t)cu.n_tile * (kSwiGLU ? kBN / 2 : kBN);  // first output col
