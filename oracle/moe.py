@@ -35,6 +35,21 @@ Steps, with the passage each follows:
    a drop -- ML Grind, Algorithm step 3 and "Constraints"; Sparsely-Gated
    Layer, ``moe_forward``.
 
+Router options (Sparsely-Gated Layer, "The one formula" and "The code",
+``router()`` stages (2) and (5); "Hot shards: the load-balancing loss"):
+
+* noise: ``logits + noise * softplus(x @ W_noise)``, with the standard-normal
+  draw ``noise`` (T, E) given as an input so that both sides use the same one;
+  probabilities, top-k and gates are then taken from the noisy logits.
+* ``renormalise=False``: the gates are the chosen experts' probabilities
+  over all E experts, without the division by their sum.
+* importance loss: ``importance_e`` = the sum over tokens of expert e's gate
+  (zero where e was not chosen); the loss is its squared coefficient of
+  variation, (population standard deviation / mean)^2; 0 when T = 0.
+* padded layout (Switch capacity, "Switch: top-1, one loss, and a rate
+  limit": experts run as fixed-size batches): expert e's kept slots at rows
+  ``e * capacity + rank``, the other rows of its batch empty.
+
 Experts: linear ``x @ W`` (ML Grind, Background), two-layer ReLU
 ``relu(x @ Wh) @ Wo`` without biases (Sparsely-Gated Layer ``expert_forward``;
 Bendersky ``FFParams``), and SwiGLU ``(silu(x @ W1) * (x @ W3)) @ W2`` with
@@ -43,7 +58,8 @@ form is the textbook one).
 
 Pins (the ``-m "not gpu"`` tests): the three worked examples of ML Grind, the
 top_k = 1 convention, the token-0 gates printed on the Sparsely-Gated Layer
-page, its capacity/drop table, the k = E and uniform-router closed forms,
+page (renormalised and not), its capacity/drop table and its importance-loss
+values, softplus and noise closed forms, the k = E and uniform-router closed forms,
 identity-weight closed forms of each expert, permutation equivariance, and a
 second, per-token implementation (``moe_forward_per_token``) on tiny random
 inputs. There is no printed worked example of the absolute output values at
@@ -101,6 +117,41 @@ def switch_aux_loss(idx: np.ndarray, probs: np.ndarray, E: int) -> float:
     return float(E * np.sum(f * P))
 
 
+# --- router options: noise, renormalisation, importance loss ----------------------------
+
+def softplus(z):
+    """``log(1 + e^z)``, without overflow (``logaddexp(0, z)``)."""
+    return np.logaddexp(0.0, _f64(z))
+
+
+def noisy_router_logits(x, w_router, bias=None, w_noise=None, noise=None) -> np.ndarray:
+    """Router logits plus ``noise * softplus(x @ W_noise)`` (Sparsely-Gated Layer, "The
+    one formula", the + noise row; ``router()`` stage (2)). ``noise`` is the (T, E)
+    standard-normal draw. Without ``w_noise`` these are the plain logits."""
+    logits = router_logits(x, w_router, bias)
+    if w_noise is None:
+        return logits
+    return logits + _f64(noise) * softplus(_f64(x) @ _f64(w_noise))
+
+
+def gates_from_probs(probs: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """``renormalise=False``: the chosen experts' probabilities over all experts, aligned
+    with ``idx`` (``router()`` without stage (5))."""
+    return np.take_along_axis(_f64(probs), idx, axis=-1)
+
+
+def importance_loss(idx: np.ndarray, gates: np.ndarray, E: int) -> float:
+    """Shazeer's importance loss: CV^2 of the per-expert sums of the gate values
+    (Sparsely-Gated Layer, "Hot shards"; ``importance_loss()``). The dense gate matrix
+    is zero off the chosen experts, so expert e's sum runs over the slots that chose e.
+    Population standard deviation; 0 when no slot was routed."""
+    imp = np.bincount(np.asarray(idx).ravel(), weights=_f64(gates).ravel(), minlength=E)
+    mean = imp.mean()
+    if mean == 0.0:
+        return 0.0
+    return float(imp.std() ** 2 / mean ** 2)
+
+
 # --- dispatch ----------------------------------------------------------------
 
 def capacity_slots(capacity_factor: float, T: int, k: int, E: int) -> Optional[int]:
@@ -140,6 +191,22 @@ def dispatch_from_indices(idx: np.ndarray, E: int, capacity: Optional[int]) -> d
                 dropped=int(T * k - perm.size))
 
 
+def padded_layout(disp: dict, E: int, capacity: int) -> dict:
+    """Capacity-padded rows: expert e's batch is rows ``e*capacity .. (e+1)*capacity-1``,
+    its kept slots first in token order, the rest of the batch empty. Returns
+    ``slot_row_padded`` (T*k,) the padded row of each slot or -1 when dropped, and
+    ``perm_padded`` (E*capacity,) the slot of each row or -1 for an empty row."""
+    slot_row = np.asarray(disp["slot_row"])
+    perm_padded = np.full(E * capacity, -1, dtype=np.int64)
+    for e in range(E):
+        seg = disp["perm"][disp["offsets"][e]:disp["offsets"][e + 1]]
+        perm_padded[e * capacity:e * capacity + seg.size] = seg
+    slot_row_padded = np.full(slot_row.size, -1, dtype=np.int64)
+    rows = np.flatnonzero(perm_padded >= 0)
+    slot_row_padded[perm_padded[rows]] = rows
+    return dict(slot_row_padded=slot_row_padded, perm_padded=perm_padded)
+
+
 # --- experts -----------------------------------------------------------------
 
 def silu(z):
@@ -168,8 +235,9 @@ def _expert_weights(e, w1, w2, w3):
 # --- the layer ----------------------------------------------------------------
 
 def moe_forward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=None,
-                capacity_factor: float = 0.0, tokens: Optional[Sequence[int]] = None) -> dict:
-    """The layer forward, steps 1-7.
+                capacity_factor: float = 0.0, tokens: Optional[Sequence[int]] = None,
+                w_noise=None, noise=None, renormalise: bool = True) -> dict:
+    """The layer forward, steps 1-7, with the router options above.
 
     ``w1``/``w3`` are (E, D, DH) (``w1`` is (E, D, D_out) for a linear expert),
     ``w2`` is (E, DH, D_out). Expert weights are widened to float64 one expert
@@ -183,11 +251,12 @@ def moe_forward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=N
     E = np.asarray(w_router).shape[1]
     if not 1 <= top_k <= E:
         raise ValueError("top_k must satisfy 1 <= top_k <= E")
-    logits = router_logits(x, w_router, bias)
+    logits = noisy_router_logits(x, w_router, bias, w_noise, noise)
     probs = softmax_rows(logits)
     idx = top_k_sorted(logits, top_k)
-    gates = gates_from_logits(logits, idx)
+    gates = gates_from_logits(logits, idx) if renormalise else gates_from_probs(probs, idx)
     aux = switch_aux_loss(idx, probs, E)
+    imp = importance_loss(idx, gates, E)
     cap = capacity_slots(capacity_factor, T, top_k, E)
     disp = dispatch_from_indices(idx, E, cap)
 
@@ -209,7 +278,7 @@ def moe_forward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=N
         # one slot per (token, expert), so no two rows of t repeat here
         out[t] += flat_gates[rows][:, None] * y
     return dict(output=out, expert_indices=idx, gates=gates, aux_loss=aux, logits=logits,
-                probs=probs, capacity=cap, **disp)
+                probs=probs, capacity=cap, importance_loss=imp, **disp)
 
 
 def _expert_one_token(kind: str, xt: np.ndarray, w1, w2=None, w3=None) -> np.ndarray:
@@ -232,8 +301,13 @@ def _expert_one_token(kind: str, xt: np.ndarray, w1, w2=None, w3=None) -> np.nda
     raise ValueError(f"unknown expert kind {kind!r}")
 
 
+def _softplus_scalar(z: float) -> float:
+    return z + math.log1p(math.exp(-z)) if z > 0 else math.log1p(math.exp(z))
+
+
 def moe_forward_per_token(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=None,
-                          capacity_factor: float = 0.0) -> dict:
+                          capacity_factor: float = 0.0, w_noise=None, noise=None,
+                          renormalise: bool = True) -> dict:
     """A second, independent implementation: token by token, plain Python.
 
     The shape of Bendersky's ``moe`` loop ("A Minimal Numpy Implementation")
@@ -250,22 +324,36 @@ def moe_forward_per_token(x, w_router, top_k: int, kind: str, w1, w2=None, w3=No
     rows_idx, rows_gate, rows_prob = [], [], []
     for t in range(T):
         logit = [float(np.dot(x[t], W[:, e])) + float(b[e]) for e in range(E)]
+        if w_noise is not None:
+            Wn, eps = _f64(w_noise), _f64(noise)
+            logit = [logit[e] + float(eps[t, e]) * _softplus_scalar(float(np.dot(x[t], Wn[:, e])))
+                     for e in range(E)]
         order = sorted(range(E), key=lambda e: (-logit[e], e))[:top_k]
         m = max(logit)
         ez = [math.exp(v - m) for v in logit]
         s = sum(ez)
         rows_prob.append([v / s for v in ez])
-        mk = max(logit[e] for e in order)
-        gz = [math.exp(logit[e] - mk) for e in order]
-        gs = sum(gz)
         rows_idx.append(order)
-        rows_gate.append([v / gs for v in gz])
+        if renormalise:
+            mk = max(logit[e] for e in order)
+            gz = [math.exp(logit[e] - mk) for e in order]
+            gs = sum(gz)
+            rows_gate.append([v / gs for v in gz])
+        else:
+            rows_gate.append([rows_prob[t][e] for e in order])
     counts = [0] * E
     for order in rows_idx:
         for e in order:
             counts[e] += 1
     P = [sum(rows_prob[t][e] for t in range(T)) / T for e in range(E)]
     aux = E * sum((counts[e] / (T * top_k)) * P[e] for e in range(E))
+    imp = [0.0] * E
+    for t in range(T):
+        for j, e in enumerate(rows_idx[t]):
+            imp[e] += rows_gate[t][j]
+    mean_imp = sum(imp) / E
+    var_imp = sum((v - mean_imp) ** 2 for v in imp) / E
+    importance = var_imp / mean_imp ** 2 if mean_imp > 0 else 0.0
 
     cap = None
     if capacity_factor and capacity_factor > 0:
@@ -285,6 +373,6 @@ def moe_forward_per_token(x, w_router, top_k: int, kind: str, w1, w2=None, w3=No
                 y = _expert_one_token(kind, x[t], *_expert_weights(e, w1, w2, w3))
                 out[t] += rows_gate[t][j] * y
     return dict(output=out, expert_indices=np.array(rows_idx, dtype=np.int64),
-                gates=np.array(rows_gate), aux_loss=float(aux),
+                gates=np.array(rows_gate), aux_loss=float(aux), importance_loss=float(importance),
                 counts=np.array(counts, dtype=np.int64),
                 kept_mask=np.array(kept, dtype=bool))

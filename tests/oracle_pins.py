@@ -335,18 +335,150 @@ def pin_matches_per_token_implementation():
                 w1 = r_.standard_normal((E, D, DH if kind != "linear" else 3))
                 w3 = r_.standard_normal((E, D, DH)) if kind == "swiglu" else None
                 w2 = r_.standard_normal((E, DH, 3)) if kind != "linear" else None
-                a = O.moe_forward(x, w, k, kind, w1, w2, w3, bias=bias, capacity_factor=cf)
+                opts = {}
+                if r_.random() < 0.5:
+                    opts = dict(w_noise=r_.standard_normal((D, E)),
+                                noise=r_.standard_normal((T, E)))
+                opts["renormalise"] = bool(r_.random() < 0.6)
+                a = O.moe_forward(x, w, k, kind, w1, w2, w3, bias=bias, capacity_factor=cf,
+                                  **opts)
                 b = O.moe_forward_per_token(x, w, k, kind, w1, w2, w3, bias=bias,
-                                            capacity_factor=cf)
+                                            capacity_factor=cf, **opts)
                 assert np.array_equal(a["expert_indices"], b["expert_indices"])
                 assert np.allclose(a["gates"], b["gates"], rtol=1e-13, atol=0)
                 assert abs(a["aux_loss"] - b["aux_loss"]) <= 1e-13 * max(1.0, b["aux_loss"])
+                assert abs(a["importance_loss"] - b["importance_loss"]) <= 1e-12 * max(
+                    1.0, b["importance_loss"])
                 assert np.array_equal(a["counts"], b["counts"])
                 assert np.array_equal(a["slot_row"].reshape(T, k) >= 0, b["kept_mask"])
                 scale = max(1.0, np.abs(b["output"]).max())
                 assert np.abs(a["output"] - b["output"]).max() <= 1e-12 * scale
                 cases += 1
     assert cases >= 30
+
+
+# --- router options on the Sparsely-Gated Layer page: noise, renormalise, importance ----
+
+def pin_importance_loss_page_values():
+    """The page's importance losses: 0.301 for the untouched router, 7.000 collapsed."""
+    g = load("sparsely_gated_importance.txt")
+    T, E, k = g["T"], g["E"], g["top_k"]
+    for name in ("random", "collapsed"):
+        idx = _tokens_with_counts(g[f"{name}_counts"], salt=31)
+        v = O.importance_loss(idx, np.ones((T, k)), E)  # top-1 gates are exactly 1
+        assert round(v, g["decimals"]) == g[f"{name}_importance"]
+    # one expert takes every token: exactly E - 1
+    idx = _tokens_with_counts(g["collapsed_counts"], salt=31)
+    assert abs(O.importance_loss(idx, np.ones((T, k)), E) - (E - 1)) <= 1e-12
+    # the same through the layer: tokens one-hot on their expert, router 10 * I, top-1
+    tok = _tokens_with_counts(g["random_counts"], salt=32)[:, 0]
+    r = O.moe_forward(np.eye(E)[tok], 10.0 * np.eye(E), 1, "linear",
+                      _rng(33).standard_normal((E, E, 2)))
+    assert round(r["importance_loss"], g["decimals"]) == g["random_importance"]
+
+
+def pin_importance_closed_forms():
+    """CV^2 of the per-expert gate sums: 0 for equal sums, E - 1 when one expert has all,
+    invariant to scaling every gate, and built from gate values, not counts."""
+    E = 5
+    idx = np.array([[e, (e + 1) % E] for e in range(E)] * 3)
+    assert abs(O.importance_loss(idx, np.tile([0.7, 0.3], (idx.shape[0], 1)), E)) <= 1e-15
+    # two experts, each chosen twice: sums 0.9 + 0.4 and 0.1 + 0.6 -> mean 1, variance 0.09
+    idx = np.array([[0, 1], [1, 0]])
+    gates = np.array([[0.9, 0.1], [0.6, 0.4]])
+    assert abs(O.importance_loss(idx, gates, 2) - 0.09) <= 1e-14
+    r_ = _rng(34)
+    idx = np.array([r_.permutation(7)[:3] for _ in range(50)])
+    g = r_.random((50, 3)) + 0.05
+    a, b = O.importance_loss(idx, g, 7), O.importance_loss(idx, 3.0 * g, 7)
+    assert abs(a - b) <= 1e-13 * max(a, 1.0)
+    assert abs(O.importance_loss(np.zeros((10, 1), int), r_.random((10, 1)) + 0.1, 6) - 5) <= 1e-12
+    assert O.importance_loss(np.zeros((0, 2), int), np.zeros((0, 2)), 4) == 0.0
+
+
+def pin_token0_unrenormalised_gates():
+    """renormalise=False: token 0's gates are its top-2 probabilities 0.39 and 0.232, summing
+    to 0.622 as printed; with k = E they are all the probabilities, best first."""
+    g = load("sparsely_gated_token0_gates.txt")
+    logits = np.log(np.array(g["probs"], dtype=np.float64))[None, :]
+    probs = O.softmax_rows(logits)
+    idx = O.top_k_sorted(logits, g["top_k"])
+    gates = O.gates_from_probs(probs, idx)
+    assert idx[0].tolist() == g["expert_indices"]
+    assert np.round(gates[0], g["decimals"]).tolist() == g["top_probs"]
+    # the printed probabilities are rounded (they sum to 0.999), so the printed sum holds to
+    # the rounding of two probabilities and of the sum itself
+    half = 0.5 * 10.0 ** -g["decimals"]
+    assert abs(float(gates[0].sum()) - g["top_probs_sum"]) <= 3 * half
+    idx8 = O.top_k_sorted(logits, 8)
+    g8 = O.gates_from_probs(probs, idx8)
+    assert np.allclose(np.sort(g8[0])[::-1], np.sort(probs[0])[::-1], rtol=1e-15, atol=0)
+    # through the layer, top-1: the gate is the winner's probability, not 1
+    x = np.eye(3)
+    r = O.moe_forward(x, np.diag([2.0, 1.0, 0.5]), 1, "linear", np.ones((3, 3, 1)),
+                      renormalise=False)
+    p = O.softmax_rows(np.diag([2.0, 1.0, 0.5]))
+    assert np.allclose(r["gates"][:, 0], p.max(axis=1), rtol=1e-15, atol=0)
+    assert np.allclose(r["output"][:, 0], p.max(axis=1), rtol=1e-15, atol=0)
+
+
+def pin_softplus_identities():
+    """softplus(0) = ln 2, softplus(z) - softplus(-z) = z, softplus(z) -> z and -> e^z."""
+    z = np.array([-30.0, -1.5, -1e-9, 0.0, 1e-9, 2.5, 30.0, 700.0])
+    sp = O.softplus(z)
+    assert sp[3] == math.log(2.0)
+    assert np.allclose(sp - O.softplus(-z), z, rtol=1e-13, atol=1e-15)
+    assert abs(sp[-1] - 700.0) <= 1e-13 * 700.0
+    assert abs(sp[0] - math.exp(-30.0)) <= 1e-12 * math.exp(-30.0)
+    assert (np.diff(sp) > 0).all() and (sp > 0).all()
+
+
+def pin_noise_closed_forms():
+    """Noisy logits = logits + noise * softplus(x @ W_noise): zero noise leaves the logits
+    exactly; W_noise = 0 scales the noise by ln 2; one-hot tokens read one row of W_noise;
+    noise larger than the margin flips the choice (the page's noise-on runs differ)."""
+    r_ = _rng(35)
+    T, D, E = 9, 6, 6  # square W_noise: a transposed read would go unnoticed otherwise
+    x, w, b = r_.standard_normal((T, D)), r_.standard_normal((D, E)), r_.standard_normal(E)
+    wn, eps = r_.standard_normal((D, E)), r_.standard_normal((T, E))
+    base = O.router_logits(x, w, b)
+    assert np.array_equal(O.noisy_router_logits(x, w, b, wn, np.zeros((T, E))), base)
+    assert np.allclose(O.noisy_router_logits(x, w, b, np.zeros((D, E)), eps),
+                       base + eps * math.log(2.0), rtol=0, atol=1e-14)
+    x1 = np.eye(D)[[0, 3, 1, 2]]
+    e1 = r_.standard_normal((4, E))
+    want = np.array([[x1[t] @ w[:, e] + e1[t, e] * math.log1p(math.exp(wn[np.argmax(x1[t]), e]))
+                      for e in range(E)] for t in range(4)])
+    assert np.allclose(O.noisy_router_logits(x1, w, None, wn, e1), want, rtol=1e-14, atol=1e-14)
+    common = dict(w_noise=np.zeros((1, 2)))
+    lay = (np.array([[1.0]]), np.array([[1.0, 0.0]]), 1, "linear", np.ones((2, 1, 1)))
+    assert O.moe_forward(*lay, noise=np.zeros((1, 2)), **common)["expert_indices"].tolist() == [[0]]
+    # 1 - 2 ln 2 < 0: the noise moves expert 0 below expert 1
+    assert O.moe_forward(*lay, noise=np.array([[-2.0, 0.0]]), **common)["expert_indices"].tolist() == [[1]]
+
+
+def pin_padded_layout():
+    """Capacity-padded rows: each kept slot at e * capacity + its rank in the compact
+    layout, the kept rows first in every batch and the rest empty."""
+    r_ = _rng(36)
+    for (T, E, k, cap) in [(60, 8, 3, 13), (45, 5, 1, 4), (10, 4, 4, 2), (12, 3, 2, 0)]:
+        idx = np.array([r_.permutation(E)[:k] for _ in range(T)])
+        d = O.dispatch_from_indices(idx, E, cap)
+        p = O.padded_layout(d, E, cap)
+        assert p["perm_padded"].shape == (E * cap,)
+        flat = idx.reshape(-1)
+        for s_ in range(T * k):
+            if d["slot_row"][s_] < 0:
+                assert p["slot_row_padded"][s_] == -1
+            else:
+                e = flat[s_]
+                assert p["slot_row_padded"][s_] == e * cap + d["slot_row"][s_] - d["offsets"][e]
+        for e in range(E):
+            seg = p["perm_padded"][e * cap:(e + 1) * cap]
+            n = d["kept"][e]
+            assert (seg[:n] >= 0).all() and (seg[n:] == -1).all()
+        rows = np.flatnonzero(p["perm_padded"] >= 0)
+        assert np.array_equal(p["slot_row_padded"][p["perm_padded"][rows]], rows)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

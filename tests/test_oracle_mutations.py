@@ -136,6 +136,47 @@ def _renormalise_after_drop(*a, **kw):
     return dict(r, output=r["output"] * scale[:, None])
 
 
+def _softplus_is_exp(z):
+    return np.exp(np.asarray(z, dtype=np.float64))
+
+
+_orig_noisy = O.noisy_router_logits
+
+
+def _noise_unscaled(x, w_router, bias=None, w_noise=None, noise=None):
+    base = O.router_logits(x, w_router, bias)
+    return base if w_noise is None else base + np.asarray(noise, dtype=np.float64)
+
+
+def _noise_scale_transposed(x, w_router, bias=None, w_noise=None, noise=None):
+    """Reads W_noise's transpose where it is square (x @ W_noise^T)."""
+    if w_noise is not None and np.asarray(w_noise).shape[0] == np.asarray(w_noise).shape[1]:
+        return _orig_noisy(x, w_router, bias, np.asarray(w_noise).T, noise)
+    return _orig_noisy(x, w_router, bias, w_noise, noise)
+
+
+def _importance_sample_std(idx, gates, E):
+    imp = np.bincount(np.asarray(idx).ravel(), weights=np.asarray(gates, float).ravel(),
+                      minlength=E)
+    return 0.0 if imp.mean() == 0 else float(imp.std(ddof=1) ** 2 / imp.mean() ** 2)
+
+
+def _importance_cv_not_squared(idx, gates, E):
+    imp = np.bincount(np.asarray(idx).ravel(), weights=np.asarray(gates, float).ravel(),
+                      minlength=E)
+    return 0.0 if imp.mean() == 0 else float(imp.std() / imp.mean())
+
+
+def _importance_from_counts(idx, gates, E):
+    imp = np.bincount(np.asarray(idx).ravel(), minlength=E).astype(float)
+    return 0.0 if imp.mean() == 0 else float(imp.std() ** 2 / imp.mean() ** 2)
+
+
+def _probs_renormalised_anyway(probs, idx):
+    p = np.take_along_axis(np.asarray(probs, dtype=np.float64), idx, axis=-1)
+    return p / p.sum(axis=-1, keepdims=True)
+
+
 MUTATIONS = {
     "ties_to_higher_index": ("top_k_sorted", _ties_to_higher_index),
     "ascending_top_k": ("top_k_sorted", _ascending),
@@ -152,6 +193,13 @@ MUTATIONS = {
     "relu_is_abs": ("expert_forward", _relu_as_abs),
     "drops_still_contribute": ("moe_forward", _drops_ignored_in_output),
     "gates_renormalised_after_drop": ("moe_forward", _renormalise_after_drop),
+    "softplus_is_exp": ("softplus", _softplus_is_exp),
+    "noise_without_softplus_scale": ("noisy_router_logits", _noise_unscaled),
+    "noise_scale_transposed": ("noisy_router_logits", _noise_scale_transposed),
+    "importance_sample_std": ("importance_loss", _importance_sample_std),
+    "importance_cv_not_squared": ("importance_loss", _importance_cv_not_squared),
+    "importance_from_counts": ("importance_loss", _importance_from_counts),
+    "unrenormalised_gates_renormalised": ("gates_from_probs", _probs_renormalised_anyway),
 }
 
 
