@@ -27,7 +27,8 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16}
 EXPORTED = (
     "moe_status_string", "moe_check_problem", "moe_capacity", "moe_workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-    "moe_forward_timed",
+    "moe_forward_timed", "moe_workspace_size_ex", "moe_route_ex", "moe_dispatch_padded",
+    "moe_expert_ffn_ex", "moe_forward_ex",
 )
 STAGES = ("route", "dispatch", "expert_up", "expert_down", "combine")
 
@@ -41,6 +42,16 @@ class MoeProblem(ctypes.Structure):
     ]
 
 
+class MoeOptions(ctypes.Structure):
+    """``moe_options``: router noise, un-renormalised gates, the padded layout and the
+    importance-loss output (device pointers; all zero = the plain layer)."""
+    _fields_ = [
+        ("w_noise", ctypes.c_void_p), ("noise", ctypes.c_void_p),
+        ("no_renormalise", ctypes.c_int32), ("padded", ctypes.c_int32),
+        ("importance_loss", ctypes.c_void_p),
+    ]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -50,6 +61,7 @@ class MoeError(RuntimeError):
 _lib = None
 _P = ctypes.c_void_p
 _PP = ctypes.POINTER(MoeProblem)
+_PO = ctypes.POINTER(MoeOptions)
 
 
 def lib() -> ctypes.CDLL:
@@ -82,6 +94,20 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.restype = ctypes.c_int
         L.moe_forward_timed.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                         _P, ctypes.c_size_t, _P, _P]
+        L.moe_workspace_size_ex.restype = ctypes.c_size_t
+        L.moe_workspace_size_ex.argtypes = [_PP, _PO]
+        L.moe_route_ex.restype = ctypes.c_int
+        L.moe_route_ex.argtypes = [_PP, _PO, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]
+        L.moe_dispatch_padded.restype = ctypes.c_int
+        L.moe_dispatch_padded.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                          _P]
+        L.moe_expert_ffn_ex.restype = ctypes.c_int
+        L.moe_expert_ffn_ex.argtypes = [_PP, _PO, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                        _P]
+        L.moe_forward_ex.restype = ctypes.c_int
+        L.moe_forward_ex.argtypes = [_PP, _PO, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, ctypes.c_size_t, _P, _P]
         _lib = L
     return _lib
 
@@ -148,6 +174,71 @@ def capacity(p: Problem) -> int:
 
 def workspace_size(p: Problem) -> int:
     return int(lib().moe_workspace_size(ctypes.byref(p.c())))
+
+
+@dataclass
+class Options:
+    """``moe_options`` with torch tensors: w_noise (D, E) and noise (T, E) float32 (both or
+    neither), renormalise, padded, importance_loss (1,) float32 output."""
+
+    w_noise: object = None
+    noise: object = None
+    renormalise: bool = True
+    padded: bool = False
+    importance_loss: object = None
+
+    def c(self) -> MoeOptions:
+        return MoeOptions(_ptr(self.w_noise), _ptr(self.noise), 0 if self.renormalise else 1,
+                          1 if self.padded else 0, _ptr(self.importance_loss))
+
+
+def _opts(o: Optional[Options]):
+    return None if o is None else ctypes.byref(o.c())
+
+
+def workspace_size_ex(p: Problem, o: Optional[Options] = None) -> int:
+    return int(lib().moe_workspace_size_ex(ctypes.byref(p.c()), _opts(o)))
+
+
+def moe_route_ex(p: Problem, o: Optional[Options], x, w_router, router_bias, expert_indices,
+                 gates, aux_loss, expert_counts=None, logits_out=None, uncertified=None,
+                 ws=None, stream=None):
+    _check(lib().moe_route_ex(ctypes.byref(p.c()), _opts(o), _ptr(x), _ptr(w_router),
+                              _ptr(router_bias), _ptr(expert_indices), _ptr(gates),
+                              _ptr(aux_loss), _ptr(expert_counts), _ptr(logits_out),
+                              _ptr(uncertified), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)), "moe_route_ex")
+
+
+def moe_dispatch_padded(p: Problem, expert_indices, x, expert_counts, expert_offsets, perm,
+                        slot_row, x_pad=None, ws=None, stream=None):
+    _check(lib().moe_dispatch_padded(ctypes.byref(p.c()), _ptr(expert_indices), _ptr(x),
+                                     _ptr(expert_counts), _ptr(expert_offsets), _ptr(perm),
+                                     _ptr(slot_row), _ptr(x_pad), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)), "moe_dispatch_padded")
+
+
+def moe_expert_ffn_ex(p: Problem, o: Optional[Options], x_perm, expert_offsets, w1, w3, w2,
+                      y_perm, ws=None, stream=None):
+    _check(lib().moe_expert_ffn_ex(ctypes.byref(p.c()), _opts(o), _ptr(x_perm),
+                                   _ptr(expert_offsets), _ptr(w1), _ptr(w3), _ptr(w2),
+                                   _ptr(y_perm), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream)), "moe_expert_ffn_ex")
+
+
+def moe_forward_ex(p: Problem, o: Optional[Options], x, w_router, router_bias, w1, w3, w2, out,
+                   expert_indices, gates, aux_loss, expert_counts, expert_offsets, slot_row, ws,
+                   stage_events=None, stream=None):
+    """``stage_events``: as in moe_forward_timed, or None."""
+    _check(lib().moe_forward_ex(ctypes.byref(p.c()), _opts(o), _ptr(x), _ptr(w_router),
+                                _ptr(router_bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+                                _ptr(expert_indices), _ptr(gates), _ptr(aux_loss),
+                                _ptr(expert_counts), _ptr(expert_offsets), _ptr(slot_row),
+                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream), stage_events), "moe_forward_ex")
 
 
 def moe_route(p: Problem, x, w_router, router_bias, expert_indices, gates, aux_loss,
@@ -265,9 +356,9 @@ def torch_dtype(p: Problem):
     return torch.bfloat16 if p.dtype == "bf16" else torch.float32
 
 
-def alloc_workspace(p: Problem, device="cuda"):
+def alloc_workspace(p: Problem, device="cuda", o: Optional[Options] = None):
     import torch
-    n = workspace_size(p)
+    n = workspace_size(p) if o is None else workspace_size_ex(p, o)
     # torch's caching allocator hands out blocks aligned to at least 512 bytes
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 

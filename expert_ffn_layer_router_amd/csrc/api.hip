@@ -2,6 +2,8 @@
 // each entry point. Nothing here allocates memory or synchronises with the device.
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 
 using namespace moe;
@@ -53,19 +55,25 @@ Problem internal(const moe_problem* p) {
   return q;
 }
 
-// Byte offsets of every scratch region inside the caller's workspace.
+// Byte offsets of every scratch region inside the caller's workspace. `rows` is the number of
+// expert-ordered rows: T*k, or with the padded layout max(T*k, E*capacity).
 struct Layout {
+  int64_t rows;
   size_t route;         // routing scratch (partials, transposed router, partial logits)
   size_t blkc, lrank;   // dispatch: (dispatch blocks, E) int32 and (T*k) int32
-  size_t perm;          // moe_forward's own permutation, (T*k) int32
-  size_t hbuf;          // expert hidden activations, (T*k, DH)
+  size_t offc;          // padded layout: the compact offsets, (E+1) int32
+  size_t hbuf;          // expert hidden activations, (rows, DH)
   size_t gsplit, gctr;  // bf16 GEMM: K-split partial tiles; K-split tickets + work queue
-  size_t ybuf;          // moe_forward's expert outputs, (T*k, D_out)
+  size_t perm;          // moe_forward's own permutation, (rows) int32
+  size_t xpad;          // padded layout: the padded copy of x, (rows, D)
+  size_t ybuf;          // moe_forward's expert outputs, (rows, D_out)
   size_t route_end, dispatch_end, ffn_end, total;
 };
 
-Layout layout_of(const Problem& q) {
+Layout layout_of(const Problem& q, bool padded = false) {
   Layout L;
+  L.rows = q.slots();
+  if (padded && q.capacity >= 0) L.rows = std::max<int64_t>(L.rows, (int64_t)q.E * q.capacity);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -74,20 +82,40 @@ Layout layout_of(const Problem& q) {
   };
   const size_t es = elem_size(q.dtype);
   const size_t slots = (size_t)q.slots();
+  const size_t rows = (size_t)L.rows;
   L.route = take(route_ws_bytes(q));
   L.route_end = off;
   L.blkc = take((size_t)dispatch_blocks(q) * q.E * sizeof(int32_t));
   L.lrank = take(slots * sizeof(int32_t));
+  L.offc = take(padded ? (size_t)(q.E + 1) * sizeof(int32_t) : 0);
   L.dispatch_end = off;
-  L.hbuf = take(q.kind == MOE_EXPERT_LINEAR ? 0 : slots * (size_t)q.DH * es);
+  L.hbuf = take(q.kind == MOE_EXPERT_LINEAR ? 0 : rows * (size_t)q.DH * es);
   const bool split = q.dtype == MOE_BF16 && q.T > 0;
   L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
   L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
   L.ffn_end = off;
-  L.perm = take(slots * sizeof(int32_t));
-  L.ybuf = take(slots * (size_t)q.D_out * es);
+  L.perm = take(rows * sizeof(int32_t));
+  L.xpad = take(padded ? rows * (size_t)q.D * es : 0);
+  L.ybuf = take(rows * (size_t)q.D_out * es);
   L.total = off;
   return L;
+}
+
+// Options -> internal form. Noise needs both pointers; the padded layout needs a capacity.
+moe_status options_of(const moe_problem* p, const moe_options* o, RouteOpts& ro, bool& padded,
+                      float*& importance) {
+  ro = RouteOpts{};
+  padded = false;
+  importance = nullptr;
+  if (!o) return MOE_OK;
+  if ((o->w_noise == nullptr) != (o->noise == nullptr)) return MOE_ERR_INVALID_ARG;
+  ro.w_noise = o->w_noise;
+  ro.noise = o->noise;
+  ro.renorm = o->no_renormalise == 0;
+  padded = o->padded != 0;
+  if (padded && capacity_of(p) < 0) return MOE_ERR_INVALID_ARG;
+  importance = o->importance_loss;
+  return MOE_OK;
 }
 
 template <typename T>
@@ -114,6 +142,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
                        const void* w1, const void* w3, const void* w2, void* hbuf, void* y,
                        void* ws, const Layout& Lw, bool tickets_zeroed, hipStream_t s,
                        hipEvent_t* ev) {
+  const int64_t max_rows = Lw.rows;  // upper bound of offsets[E]
   float* split_ws = nullptr;
   int32_t* split_ctr = nullptr;
   int32_t* queue = nullptr;
@@ -143,7 +172,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   g.gather_div = q.top_k;
   g.offsets = offsets;
   g.E = q.E;
-  g.max_rows = q.slots();
+  g.max_rows = max_rows;
   g.dtype = q.dtype;
   g.K = q.D;
   g.B0 = w1;
@@ -173,7 +202,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
     d.E = q.E;
     d.K = q.DH;
     d.N = q.D_out;
-    d.max_rows = q.slots();
+    d.max_rows = max_rows;
     d.epilogue = EPI_NONE;
     d.dtype = q.dtype;
     d.ev_start = event_at(ev, 2 * MOE_STAGE_EXPERT_DOWN);
@@ -220,23 +249,47 @@ size_t moe_workspace_size(const moe_problem* p) {
   return layout_of(internal(p)).total;
 }
 
-moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
-                     const float* router_bias, int32_t* expert_indices, float* gates,
-                     float* aux_loss, int32_t* expert_counts, float* logits_out,
-                     int32_t* uncertified, void* ws, size_t ws_bytes, hipStream_t stream) {
+size_t moe_workspace_size_ex(const moe_problem* p, const moe_options* opts) {
+  if (check_problem(p) != MOE_OK) return 0;
+  RouteOpts ro;
+  bool padded;
+  float* importance;
+  if (options_of(p, opts, ro, padded, importance) != MOE_OK) return 0;
+  return layout_of(internal(p), padded).total;
+}
+
+moe_status moe_route_ex(const moe_problem* p, const moe_options* opts, const void* x,
+                        const void* w_router, const float* router_bias, int32_t* expert_indices,
+                        float* gates, float* aux_loss, int32_t* expert_counts,
+                        float* logits_out, int32_t* uncertified, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
   moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  RouteOpts ro;
+  bool padded;
+  float* importance;
+  st = options_of(p, opts, ro, padded, importance);
   if (st != MOE_OK) return st;
   if (!aux_loss) return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !w_router || !expert_indices || !gates)) return MOE_ERR_INVALID_ARG;
   const Problem q = internal(p);
-  const Layout L = layout_of(q);
+  const Layout L = layout_of(q, padded);
   st = check_ws(ws, ws_bytes, L.route_end);
   if (st != MOE_OK) return st;
-  hipError_t err = launch_route(q, x, w_router, router_bias, expert_indices, gates, logits_out,
-                                uncertified, at<void>(ws, L.route), stream);
+  hipError_t err = launch_route(q, x, w_router, router_bias, ro, expert_indices, gates,
+                                logits_out, uncertified, at<void>(ws, L.route), stream);
   if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, expert_counts, stream);
+    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, expert_counts, stream,
+                              expert_indices, gates, importance);
   return hip_status(err);
+}
+
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
+                     const float* router_bias, int32_t* expert_indices, float* gates,
+                     float* aux_loss, int32_t* expert_counts, float* logits_out,
+                     int32_t* uncertified, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_route_ex(p, nullptr, x, w_router, router_bias, expert_indices, gates, aux_loss,
+                      expert_counts, logits_out, uncertified, ws, ws_bytes, stream);
 }
 
 moe_status moe_dispatch(const moe_problem* p, const int32_t* expert_indices, const void* x,
@@ -257,20 +310,53 @@ moe_status moe_dispatch(const moe_problem* p, const int32_t* expert_indices, con
                                     at<int32_t>(ws, L.lrank), stream));
 }
 
+moe_status moe_dispatch_padded(const moe_problem* p, const int32_t* expert_indices,
+                               const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* perm, int32_t* slot_row, void* x_pad, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (capacity_of(p) < 0 || !expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!expert_indices || !slot_row)) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  if ((int64_t)q.E * q.capacity > 0 && !perm) return MOE_ERR_INVALID_ARG;
+  if (x_pad && !x && p->T > 0) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(q, true);
+  st = check_ws(ws, ws_bytes, L.dispatch_end);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_dispatch(q, expert_indices, x, expert_counts,
+                                    at<int32_t>(ws, L.offc), perm, slot_row, x_pad,
+                                    at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
+                                    nullptr, 0, expert_offsets));
+}
+
+moe_status moe_expert_ffn_ex(const moe_problem* p, const moe_options* opts, const void* x_perm,
+                             const int32_t* expert_offsets, const void* w1, const void* w3,
+                             const void* w2, void* y_perm, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  RouteOpts ro;
+  bool padded;
+  float* importance;
+  st = options_of(p, opts, ro, padded, importance);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !weights_ok(p, w1, w3, w2)) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q, padded);
+  if (L.rows > 0 && (!x_perm || !y_perm)) return MOE_ERR_INVALID_ARG;
+  st = check_ws(ws, ws_bytes, L.ffn_end);
+  if (st != MOE_OK) return st;
+  if (L.rows == 0) return MOE_OK;
+  return hip_status(run_experts(q, x_perm, nullptr, expert_offsets, w1, w3, w2,
+                                at<void>(ws, L.hbuf), y_perm, ws, L, false, stream, nullptr));
+}
+
 moe_status moe_expert_ffn(const moe_problem* p, const void* x_perm, const int32_t* expert_offsets,
                           const void* w1, const void* w3, const void* w2, void* y_perm, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_problem(p);
-  if (st != MOE_OK) return st;
-  if (!expert_offsets || !weights_ok(p, w1, w3, w2)) return MOE_ERR_INVALID_ARG;
-  if (p->T > 0 && (!x_perm || !y_perm)) return MOE_ERR_INVALID_ARG;
-  const Problem q = internal(p);
-  const Layout L = layout_of(q);
-  st = check_ws(ws, ws_bytes, L.ffn_end);
-  if (st != MOE_OK) return st;
-  if (q.T == 0) return MOE_OK;
-  return hip_status(run_experts(q, x_perm, nullptr, expert_offsets, w1, w3, w2,
-                                at<void>(ws, L.hbuf), y_perm, ws, L, false, stream, nullptr));
+  return moe_expert_ffn_ex(p, nullptr, x_perm, expert_offsets, w1, w3, w2, y_perm, ws, ws_bytes,
+                           stream);
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* slot_row,
@@ -281,39 +367,60 @@ moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* 
   return hip_status(launch_combine(internal(p), y_perm, slot_row, gates, out, stream));
 }
 
-moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_router,
-                             const float* router_bias, const void* w1, const void* w3,
-                             const void* w2, void* out, int32_t* expert_indices, float* gates,
-                             float* aux_loss, int32_t* expert_counts, int32_t* expert_offsets,
-                             int32_t* slot_row, void* ws, size_t ws_bytes, hipStream_t stream,
-                             hipEvent_t* ev) {
+moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const void* x,
+                          const void* w_router, const float* router_bias, const void* w1,
+                          const void* w3, const void* w2, void* out, int32_t* expert_indices,
+                          float* gates, float* aux_loss, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* slot_row, void* ws, size_t ws_bytes,
+                          hipStream_t stream, hipEvent_t* ev) {
   moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  RouteOpts ro;
+  bool padded;
+  float* importance;
+  st = options_of(p, opts, ro, padded, importance);
   if (st != MOE_OK) return st;
   if (!aux_loss || !expert_counts || !expert_offsets || !weights_ok(p, w1, w3, w2))
     return MOE_ERR_INVALID_ARG;
   if (p->T > 0 && (!x || !w_router || !out || !expert_indices || !gates || !slot_row))
     return MOE_ERR_INVALID_ARG;
   const Problem q = internal(p);
-  const Layout L = layout_of(q);
+  const Layout L = layout_of(q, padded);
   st = check_ws(ws, ws_bytes, L.total);
   if (st != MOE_OK) return st;
   int32_t* perm = at<int32_t>(ws, L.perm);
   mark(ev, 2 * MOE_STAGE_ROUTE, stream);
-  hipError_t err = launch_route(q, x, w_router, router_bias, expert_indices, gates, nullptr,
+  hipError_t err = launch_route(q, x, w_router, router_bias, ro, expert_indices, gates, nullptr,
                                 nullptr, at<void>(ws, L.route), stream);
   if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream);
+    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream,
+                              expert_indices, gates, importance);
   mark(ev, 2 * MOE_STAGE_ROUTE + 1, stream);
   mark(ev, 2 * MOE_STAGE_DISPATCH, stream);
   // the dispatch scan also zeroes the GEMMs' K-split tickets and work queue
   int32_t* tickets = (q.dtype == MOE_BF16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
-  if (err == hipSuccess)
-    err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
-                          nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
-                          tickets, tickets ? kSplitSlots + kQueueInts : 0);
+  const void* A = x;
+  const int32_t* gather = perm;
+  const int32_t* offsets = expert_offsets;
+  if (err == hipSuccess) {
+    if (padded) {
+      // compact offsets into the workspace, the batch starts into expert_offsets, and a
+      // padded copy of x that the first GEMM reads row by row
+      err = launch_dispatch(q, expert_indices, x, expert_counts, at<int32_t>(ws, L.offc), perm,
+                            slot_row, at<void>(ws, L.xpad), at<int32_t>(ws, L.blkc),
+                            at<int32_t>(ws, L.lrank), stream, tickets,
+                            tickets ? kSplitSlots + kQueueInts : 0, expert_offsets);
+      A = at<void>(ws, L.xpad);
+      gather = nullptr;
+    } else {
+      err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
+                            nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
+                            tickets, tickets ? kSplitSlots + kQueueInts : 0);
+    }
+  }
   mark(ev, 2 * MOE_STAGE_DISPATCH + 1, stream);
   if (err == hipSuccess)
-    err = run_experts(q, x, perm, expert_offsets, w1, w3, w2, at<void>(ws, L.hbuf),
+    err = run_experts(q, A, gather, offsets, w1, w3, w2, at<void>(ws, L.hbuf),
                       at<void>(ws, L.ybuf), ws, L, tickets != nullptr, stream, ev);
   mark(ev, 2 * MOE_STAGE_COMBINE, stream);
   if (err == hipSuccess) err = launch_combine(q, at<void>(ws, L.ybuf), slot_row, gates, out, stream);
@@ -321,14 +428,25 @@ moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_
   return hip_status(err);
 }
 
+moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, const void* w1, const void* w3,
+                             const void* w2, void* out, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* slot_row, void* ws, size_t ws_bytes, hipStream_t stream,
+                             hipEvent_t* ev) {
+  return moe_forward_ex(p, nullptr, x, w_router, router_bias, w1, w3, w2, out, expert_indices,
+                        gates, aux_loss, expert_counts, expert_offsets, slot_row, ws, ws_bytes,
+                        stream, ev);
+}
+
 moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router,
                        const float* router_bias, const void* w1, const void* w3, const void* w2,
                        void* out, int32_t* expert_indices, float* gates, float* aux_loss,
                        int32_t* expert_counts, int32_t* expert_offsets, int32_t* slot_row,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
-  return moe_forward_timed(p, x, w_router, router_bias, w1, w3, w2, out, expert_indices, gates,
-                           aux_loss, expert_counts, expert_offsets, slot_row, ws, ws_bytes,
-                           stream, nullptr);
+  return moe_forward_ex(p, nullptr, x, w_router, router_bias, w1, w3, w2, out, expert_indices,
+                        gates, aux_loss, expert_counts, expert_offsets, slot_row, ws, ws_bytes,
+                        stream, nullptr);
 }
 
 }  // extern "C"

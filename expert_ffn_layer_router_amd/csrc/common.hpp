@@ -66,23 +66,37 @@ struct Problem {
 int64_t route_blocks(const Problem& p);
 int route_splits(const Problem& p);
 size_t route_ws_bytes(const Problem& p);
-// `uncertified` (nullable, device) receives the number of tokens whose decision was
+// Router options: noise (w_noise (D, E) in the layer's dtype and the (T, E) float32 draw, or
+// both null) and renormalisation of the gates.
+struct RouteOpts {
+  const void* w_noise = nullptr;
+  const float* noise = nullptr;
+  bool renorm = true;
+};
+// `uncertified` (nullable, device) receives the number of tokens whose logits were
 // recomputed in float64 (always 0 for float32 layers, which are float64 throughout).
 hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
-                        int32_t* idx, float* gates, float* logits_out, int32_t* uncertified,
-                        void* ws, hipStream_t s);
-// Sum of the per-block partials -> aux loss (and the per-expert counts, if asked).
+                        const RouteOpts& o, int32_t* idx, float* gates, float* logits_out,
+                        int32_t* uncertified, void* ws, hipStream_t s);
+// Sum of the per-block partials -> aux loss (and the per-expert counts, if asked). With
+// `importance` (nullable) also the importance loss from the final idx / gates.
 hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* counts_out,
-                               hipStream_t s);
+                               hipStream_t s, const int32_t* idx = nullptr,
+                               const float* gates = nullptr, float* importance = nullptr);
 
 // Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
 int64_t dispatch_blocks(const Problem& p);
 // `zero` (nullable): nzero int32 that the scan kernel sets to 0 on the way (the GEMMs'
 // K-split tickets and work queue of the same call, which saves a launch).
+// `pad_offsets` (nullable; needs a capacity): the capacity-padded layout. perm (E * capacity)
+// and slot_row then index padded rows e * capacity + rank, empty rows get perm -1 and a zero
+// row in x_perm, `offsets` still receives the compact offsets (kept rows) and pad_offsets
+// (E + 1) the batch starts e * capacity.
 hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_row,
                            void* x_perm, int32_t* blk_counts, int32_t* local_rank,
-                           hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
+                           hipStream_t s, int32_t* zero = nullptr, int nzero = 0,
+                           int32_t* pad_offsets = nullptr);
 
 // Grouped expert GEMM over expert-ordered rows.
 enum Epilogue { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };

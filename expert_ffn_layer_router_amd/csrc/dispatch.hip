@@ -15,6 +15,11 @@
 //  3. place: one wave per token. Rank = block base + local rank; kept iff rank < capacity;
 //            row = offsets[e] + rank; perm[row] = slot, slot_row[slot] = row (or -1); the
 //            token's x row is read once and written to each of its kept rows.
+// Capacity-padded layout (Switch: every expert a fixed batch of `capacity` rows): place puts
+// the slot at row e * capacity + rank instead, and a fourth kernel marks each batch's empty
+// rows (perm = -1), zeroes them in the copy, and writes the batch starts e * capacity.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
     int64_t T, int k, int E, int64_t capacity, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ blk_base, const int32_t* __restrict__ local_rank,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ slot_row,
-    const U* __restrict__ x, U* __restrict__ x_perm, int64_t row_units) {
+    const U* __restrict__ x, U* __restrict__ x_perm, int64_t row_units, bool padded) {
   const int lane = lane_id();
   const int64_t t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + wave_id()));
   if (t >= T) return;
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
       if ((unsigned)e < (unsigned)E && lr >= 0) {
         const int r = blk_base[b * E + e] + lr;
         if (capacity < 0 || r < capacity) {
-          row = offsets[e] + r;
+          row = padded ? (int)((int64_t)e * capacity + r) : offsets[e] + r;
           perm[row] = (int32_t)s;
         }
       }
@@ -137,6 +142,29 @@ __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
   }
 }
 
+// Empty rows of the padded batches, one wave per row: row i of batch e is empty when i is not
+// below kept_e = offsets[e + 1] - offsets[e] (the compact offsets of the scan): perm = -1 and,
+// with a copy, a zero row. Thread 0 of block 0 also writes the batch starts e * capacity.
+template <typename U>
+__global__ __launch_bounds__(kThreads) void dispatch_pad_fill_kernel(
+    int E, int64_t capacity, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    U* __restrict__ x_pad, int64_t row_units, int32_t* __restrict__ pad_offsets) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= E; i += kThreads)
+      pad_offsets[i] = (int32_t)((int64_t)i * capacity);
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave_id();
+  if (row >= (int64_t)E * capacity) return;
+  const int e = (int)(row / capacity);
+  const int64_t i = row - (int64_t)e * capacity;
+  if (i < offsets[e + 1] - offsets[e]) return;  // a kept slot's row
+  if (lane_id() == 0) perm[row] = -1;
+  if (x_pad) {
+    U zero;
+    __builtin_memset(&zero, 0, sizeof(U));
+    for (int64_t c = lane_id(); c < row_units; c += kWave) x_pad[row * row_units + c] = zero;
+  }
+}
+
 }  // namespace
 
 int64_t dispatch_blocks(const Problem& p) {
@@ -146,7 +174,8 @@ int64_t dispatch_blocks(const Problem& p) {
 hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* slot_row, void* x_perm,
                            int32_t* blk_counts, int32_t* local_rank, hipStream_t s,
-                           int32_t* zero, int nzero) {
+                           int32_t* zero, int nzero, int32_t* pad_offsets) {
+  const bool padded = pad_offsets != nullptr;
   const int64_t nblk = dispatch_blocks(p);
   if (nblk > 0) {
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3((unsigned)nblk), dim3(kThreads), 0, s, p.T,
@@ -154,23 +183,41 @@ hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x, 
   }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kMaxExperts), 0, s, nblk, p.E,
                      p.capacity, blk_counts, counts, offsets, zero, nzero);
-  if (p.T == 0) return hipGetLastError();
   const int64_t es = (p.dtype == MOE_BF16) ? 2 : 4;
   const int64_t row_bytes = p.D * es;
-  const unsigned grid = (unsigned)((p.T + kWaves - 1) / kWaves);
   const bool al16 = ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
-  if (x_perm && row_bytes % 16 == 0 && al16) {
-    hipLaunchKernelGGL(dispatch_place_kernel<uint4>, dim3(grid), dim3(kThreads), 0, s, p.T,
-                       p.top_k, p.E, p.capacity, idx, blk_counts, local_rank, offsets, perm,
-                       slot_row, (const uint4*)x, (uint4*)x_perm, row_bytes / 16);
-  } else if (x_perm && row_bytes % 4 == 0) {
-    hipLaunchKernelGGL(dispatch_place_kernel<uint32_t>, dim3(grid), dim3(kThreads), 0, s, p.T,
-                       p.top_k, p.E, p.capacity, idx, blk_counts, local_rank, offsets, perm,
-                       slot_row, (const uint32_t*)x, (uint32_t*)x_perm, row_bytes / 4);
-  } else {
-    hipLaunchKernelGGL(dispatch_place_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, p.T,
-                       p.top_k, p.E, p.capacity, idx, blk_counts, local_rank, offsets, perm,
-                       slot_row, (const uint16_t*)x, (uint16_t*)x_perm, row_bytes / 2);
+  const int unit = (x_perm && row_bytes % 16 == 0 && al16) ? 16
+                   : (x_perm && row_bytes % 4 == 0)        ? 4
+                                                           : 2;
+  if (p.T > 0) {
+    const unsigned grid = (unsigned)((p.T + kWaves - 1) / kWaves);
+    if (unit == 16)
+      hipLaunchKernelGGL(dispatch_place_kernel<uint4>, dim3(grid), dim3(kThreads), 0, s, p.T,
+                         p.top_k, p.E, p.capacity, idx, blk_counts, local_rank, offsets, perm,
+                         slot_row, (const uint4*)x, (uint4*)x_perm, row_bytes / 16, padded);
+    else if (unit == 4)
+      hipLaunchKernelGGL(dispatch_place_kernel<uint32_t>, dim3(grid), dim3(kThreads), 0, s, p.T,
+                         p.top_k, p.E, p.capacity, idx, blk_counts, local_rank, offsets, perm,
+                         slot_row, (const uint32_t*)x, (uint32_t*)x_perm, row_bytes / 4, padded);
+    else
+      hipLaunchKernelGGL(dispatch_place_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, p.T,
+                         p.top_k, p.E, p.capacity, idx, blk_counts, local_rank, offsets, perm,
+                         slot_row, (const uint16_t*)x, (uint16_t*)x_perm, row_bytes / 2, padded);
+  }
+  if (padded) {
+    const int64_t rows = (int64_t)p.E * p.capacity;
+    const unsigned grid = (unsigned)std::max<int64_t>(1, (rows + kWaves - 1) / kWaves);
+    if (unit == 16)
+      hipLaunchKernelGGL(dispatch_pad_fill_kernel<uint4>, dim3(grid), dim3(kThreads), 0, s, p.E,
+                         p.capacity, offsets, perm, (uint4*)x_perm, row_bytes / 16, pad_offsets);
+    else if (unit == 4)
+      hipLaunchKernelGGL(dispatch_pad_fill_kernel<uint32_t>, dim3(grid), dim3(kThreads), 0, s,
+                         p.E, p.capacity, offsets, perm, (uint32_t*)x_perm, row_bytes / 4,
+                         pad_offsets);
+    else
+      hipLaunchKernelGGL(dispatch_pad_fill_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s,
+                         p.E, p.capacity, offsets, perm, (uint16_t*)x_perm, row_bytes / 2,
+                         pad_offsets);
   }
   return hipGetLastError();
 }

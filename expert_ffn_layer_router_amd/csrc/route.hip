@@ -26,6 +26,20 @@
 //             the one taken on exact logits. The k chosen logits are then recomputed exactly
 //             (k dot products in float64) and the gates come from those; the probabilities
 //             that feed the loss come from the float64-folded MFMA logits.
+//
+// Router options (Sparsely-Gated Layer page, "The one formula" and "The code", router()
+// stages (2) and (5); "Hot shards"):
+//  * noise: the decision logits are logits + noise[t, e] * softplus(x_t . W_noise[:, e]), the
+//    standard-normal draw given as a (T, E) float32 input. The router product covers the 2E
+//    columns [W | W_noise]; the noise columns' own error bound, propagated through softplus
+//    (1-Lipschitz) and scaled by |noise|, is added to B_t before the certification test, and
+//    the exact recompute of the chosen logits includes their noise terms.
+//  * no renormalisation: the gates are the chosen experts' probabilities over all E experts,
+//    which needs every logit of the token to the gates' accuracy, so every token takes the
+//    exact float64 path of the fallback kernel.
+//  * importance loss: the squared coefficient of variation of the per-expert sums of the
+//    final gates, from per-block partial sums taken in token order and added in a fixed
+//    order, so the result does not depend on scheduling.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -57,6 +71,11 @@ __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
+}
+
+// softplus(z) = log(1 + e^z), in float64 without overflow.
+__device__ __forceinline__ double softplus_f64(double z) {
+  return z > 0.0 ? z + log1p(exp(-z)) : log1p(exp(z));
 }
 
 template <typename TIn, int EPL>
@@ -159,6 +178,44 @@ __device__ __forceinline__ void chosen_logits_f64(const uint16_t* __restrict__ x
   token_dots_f64<CG>(x, wt, t, D, k, row_of, put);
 }
 
+
+// The same with router noise: the chosen logits are x.W_e + b_e + noise[t, e] * softplus(
+// x.W_noise[:, e]), both dot products exact-product float64 (2k rows of wt: the chosen
+// experts' router rows, then their noise rows E + e).
+template <int EPL, int CG>
+__device__ __forceinline__ void chosen_logits_noisy_f64(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wt,
+    const float* __restrict__ bias, const float* __restrict__ noise, int64_t t, int64_t D, int E,
+    int k, const int my_e[EPL], double my_v[EPL]) {
+  const int lane = lane_id();
+  auto expert_of = [&](int j) {
+    int e = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if ((j >> 6) == i) e = __shfl(my_e[i], j & 63);
+    return e;
+  };
+  auto row_of = [&](int j) { return j < k ? expert_of(j) : E + expert_of(j - k); };
+  double my_b[EPL], my_n[EPL], my_g[EPL], my_z[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const bool mine = lane + kWave * i < k;
+    my_b[i] = (bias && mine) ? (double)bias[my_e[i]] : 0.0;
+    my_n[i] = mine ? (double)noise[t * E + my_e[i]] : 0.0;
+    my_g[i] = 0.0;
+    my_z[i] = 0.0;
+  }
+  auto put = [&](int j, double v) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (j == lane + kWave * i) my_g[i] = v;
+      if (j - k == lane + kWave * i) my_z[i] = v;
+    }
+  };
+  token_dots_f64<CG>(x, wt, t, D, 2 * k, row_of, put);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) my_v[i] = my_g[i] + my_b[i] + my_n[i] * softplus_f64(my_z[i]);
+}
 
 // k rounds of a wave-wide argmax over the not-yet-chosen experts: larger logit first,
 // equal logits -> smaller expert index. Lane j (+64i) keeps the j-th choice. When
@@ -298,12 +355,13 @@ __device__ __forceinline__ double topk_rounds_keys(int E, int k, const double lg
   return min_gap;
 }
 
-// Probabilities over all experts (returned in prob[]), and the index/gate rows.
+// Probabilities over all experts (returned in prob[]), and the index/gate rows: the gates are
+// the softmax of the chosen logits my_v when `renorm`, else the chosen experts' probabilities.
 template <int EPL>
 __device__ __forceinline__ void finish_token(int E, int k, int64_t t, const double lg[EPL],
                                              const double my_v[EPL], const int my_e[EPL],
                                              double prob[EPL], int32_t* __restrict__ idx,
-                                             float* __restrict__ gates) {
+                                             float* __restrict__ gates, bool renorm = true) {
   const int lane = lane_id();
   double m = -DBL_MAX;
 #pragma unroll
@@ -319,6 +377,24 @@ __device__ __forceinline__ void finish_token(int E, int k, int64_t t, const doub
   s = wave_sum(s);
 #pragma unroll
   for (int i = 0; i < EPL; ++i) prob[i] /= s;
+  if (!renorm) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int j = lane + kWave * i;
+      // the probability of choice j's expert, read from the lane that holds that expert
+      double pv = 0.0;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const double c = __shfl(prob[q], my_e[i] & (kWave - 1));
+        if ((my_e[i] >> 6) == q) pv = c;
+      }
+      if (j < k) {
+        idx[t * k + j] = my_e[i];
+        gates[t * k + j] = (float)pv;
+      }
+    }
+    return;
+  }
   // gates: softmax over the chosen logits, shifted by the first (largest) of them
   const double v0 = __shfl(my_v[0], 0);
   double ev[EPL];
@@ -415,7 +491,9 @@ __device__ __forceinline__ void write_logits(float* __restrict__ logits_out, int
 template <typename TIn, int EPL>
 __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
     int64_t T, int64_t D, int E, int k, const TIn* __restrict__ x, const TIn* __restrict__ w,
-    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ gates,
+    const float* __restrict__ bias, const TIn* __restrict__ w_noise,
+    const float* __restrict__ noise, bool renorm, int32_t* __restrict__ idx,
+    float* __restrict__ gates,
     float* __restrict__ logits_out, double* __restrict__ psum_blk,
     int32_t* __restrict__ count_blk, int32_t* __restrict__ ticket,
     int32_t* __restrict__ uncertified) {
@@ -434,9 +512,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
     bool sel[EPL];
     logits_f64<TIn, EPL>(x, w, t, D, E, lg);
     add_bias<EPL>(bias, E, lg);
+    if (w_noise) {
+      double z[EPL];
+      logits_f64<TIn, EPL>(x, w_noise, t, D, E, z);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane_id() + kWave * i;
+        if (e < E) lg[i] += (double)noise[t * E + e] * softplus_f64(z[i]);
+      }
+    }
     write_logits<EPL>(logits_out, t, E, lg);
     topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);
-    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates, renorm);
     bp.add(prob, sel);
   }
   write_block_partials<kRouteWaves, EPL>(bp, E, psum_blk, count_blk);
@@ -444,11 +531,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_f64_kernel(
 
 // ---- bfloat16 layers ----------------------------------------------------------------------
 
-// wt[e][d] = w[d][e]; wnorm[e] = ||w[:, e]||_2 (float64). One block per expert; the sum of
-// squares is reduced in a fixed order (per-thread, then an LDS tree). Also zeroes the
-// counters that the later routing kernels of the call accumulate into.
+// wt[r][d] = w[d][r] for rows r < E and w_noise[d][r - E] for rows E .. 2E - 1 (one block
+// per row, gridDim.x rows); wnorm[r] = the row's ||.||_2 (float64). The sum of squares is
+// reduced in a fixed order (per-thread, then an LDS tree). Also zeroes the counters that the
+// later routing kernels of the call accumulate into.
 __global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
                                                           const uint16_t* __restrict__ w,
+                                                          const uint16_t* __restrict__ w_noise,
                                                           uint16_t* __restrict__ wt,
                                                           double* __restrict__ wnorm,
                                                           int32_t* __restrict__ ticket,
@@ -459,10 +548,12 @@ __global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
     *ticket = 0;
     *nlist = 0;
   }
+  const uint16_t* src = e < E ? w : w_noise;
+  const int col = e < E ? e : e - E;
   double acc = 0.0;
 #pragma unroll 4
   for (int64_t d = threadIdx.x; d < D; d += 256) {
-    const uint16_t v = w[d * E + e];
+    const uint16_t v = src[d * E + col];
     wt[(int64_t)e * D + d] = v;
     const double f = (double)bf16_to_f32(v);
     acc = fma(f, f, acc);
@@ -477,9 +568,13 @@ __global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
 }
 
 template <int NT>  // tiles of 16 experts
+// Partial logits of E router rows (wt, (E, D)) over one K split (blockIdx.y): columns
+// col0 .. col0 + E - 1 of `part`, whose token rows are ldp floats apart. xsq (nullable)
+// receives the partial ||x_t||^2.
 __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
     int64_t T, int64_t D, int E, int64_t kc, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ wt, float* __restrict__ part, float* __restrict__ xsq) {
+    const uint16_t* __restrict__ wt, float* __restrict__ part, float* __restrict__ xsq, int ldp,
+    int col0) {
   __shared__ __align__(16) uint16_t sB[NT * 16][kLKB + 8];
   const int lane = lane_id(), wv = wave_id();
   const int64_t t0 = (int64_t)blockIdx.x * kLT + wv * 16;
@@ -553,29 +648,38 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
     for (int v = 0; v < 4; ++v) {
       const int64_t t = t0 + 4 * (lane >> 4) + v;
       const int e = n * 16 + (lane & 15);
-      if (t < T && e < E) part[((int64_t)s * T + t) * E + e] = (float)acc[n][v];
+      if (t < T && e < E) part[((int64_t)s * T + t) * ldp + col0 + e] = (float)acc[n][v];
     }
-  if (lane < 16 && row_ok) xsq[(int64_t)s * T + row] = xs;
+  if (xsq && lane < 16 && row_ok) xsq[(int64_t)s * T + row] = xs;
 }
 
 constexpr int kSelWaves = kRouteTokensPerBlock;  // one token per wave
 constexpr int kSelThreads = kSelWaves * kWave;
 constexpr int kFbThreads = 1024;  // threads per uncertified token in the fallback
 
-template <int EPL, int CG>
+// One wave per token. With NOISE, `part` holds 2E columns per token (the router's, then the
+// noise rows') and `noise` the (T, E) draw. Without `renorm` every token is listed for the
+// exact path (its gates need all E logits exactly); the loss probabilities still come from
+// the folded logits here.
+template <int EPL, int CG, bool NOISE>
 __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     int64_t T, int64_t D, int E, int k, int S, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wt, const double* __restrict__ wnorm,
     const float* __restrict__ part, const float* __restrict__ xsq, const float* __restrict__ bias,
-    int32_t* __restrict__ idx, float* __restrict__ gates, float* __restrict__ logits_out,
-    double* __restrict__ psum_blk, int32_t* __restrict__ count_blk, int32_t* __restrict__ list,
-    int32_t* __restrict__ nlist) {
+    const float* __restrict__ noise, bool renorm, int32_t* __restrict__ idx,
+    float* __restrict__ gates, float* __restrict__ logits_out, double* __restrict__ psum_blk,
+    int32_t* __restrict__ count_blk, int32_t* __restrict__ list, int32_t* __restrict__ nlist) {
   const int lane = lane_id(), wv = wave_id();
   const int64_t t = (int64_t)blockIdx.x * kRouteTokensPerBlock + wv;
   const bool valid = t < T;
-  double wmax = 0.0;  // max_e |W_e|: one load per lane and a wave max
-  for (int e = lane; e < E; e += kWave) wmax = fmax(wmax, wnorm[e]);
+  const int ldp = NOISE ? 2 * E : E;
+  double wmax = 0.0, wmaxn = 0.0;  // max_e |W_e| and max_e |W_noise_e|: a wave max each
+  for (int e = lane; e < E; e += kWave) {
+    wmax = fmax(wmax, wnorm[e]);
+    if (NOISE) wmaxn = fmax(wmaxn, wnorm[E + e]);
+  }
   wmax = wave_max(wmax);
+  if (NOISE) wmaxn = wave_max(wmaxn);
 
   double lg[EPL], prob[EPL], my_v[EPL];
   int my_e[EPL];
@@ -584,12 +688,16 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
 #pragma unroll
   for (int i = 0; i < EPL; ++i) lg[i] = 0.0;
   if (valid) {
-    double rnd = 0.0, xn2 = 0.0, ab[EPL];
+    double rnd = 0.0, rndz = 0.0, xn2 = 0.0, ab[EPL], z[EPL], abz[EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) ab[i] = 0.0;
+    for (int i = 0; i < EPL; ++i) {
+      ab[i] = 0.0;
+      z[i] = 0.0;
+      abz[i] = 0.0;
+    }
     // partials in split order; 4 splits' loads issued together
     for (int s0 = 0; s0 < S; s0 += 4) {
-      float pv[4][EPL], xv[4];
+      float pv[4][EPL], pz[4][EPL], xv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const bool ok = s0 + q < S;
@@ -597,7 +705,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
           const int e = lane + kWave * i;
-          pv[q][i] = (ok && e < E) ? part[((int64_t)(s0 + q) * T + t) * E + e] : 0.f;
+          const float* row = part + ((int64_t)(s0 + q) * T + t) * ldp;
+          pv[q][i] = (ok && e < E) ? row[e] : 0.f;
+          pz[q][i] = (NOISE && ok && e < E) ? row[E + e] : 0.f;
         }
       }
 #pragma unroll
@@ -607,29 +717,63 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
         for (int i = 0; i < EPL; ++i) {
           lg[i] += (double)pv[q][i];
           ab[i] += fabs((double)pv[q][i]);
+          if (NOISE) {
+            z[i] += (double)pz[q][i];
+            abz[i] += fabs((double)pz[q][i]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) rnd = fmax(rnd, ab[i]);
+    for (int i = 0; i < EPL; ++i) {
+      rnd = fmax(rnd, ab[i]);
+      if (NOISE) rndz = fmax(rndz, abz[i]);
+    }
     add_bias<EPL>(bias, E, lg);
-    double lmax = 0.0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane + kWave * i < E) lmax = fmax(lmax, fabs(lg[i]));
     rnd = wave_max(rnd);
-    lmax = wave_max(lmax);
     // |computed - exact| bound: every 32-term MFMA sum within 32 * 2^-23 of its sum of
     // |products|, summed by Cauchy-Schwarz; the float32 sum of squares padded by D * 2^-23;
     // the float32 rounding of each partial; the float64 additions.
     const double gamma = 32.0 * 0x1p-23;
-    const double B = gamma * sqrt(xn2 * (1.0 + (double)D * 0x1p-23)) * wmax * (1.0 + 1e-6) +
-                     rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30;
+    const double xnb = sqrt(xn2 * (1.0 + (double)D * 0x1p-23)) * (1.0 + 1e-6);
+    double bnoise = 0.0;
+    if (NOISE) {
+      rndz = wave_max(rndz);
+      double zmax = 0.0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) zmax = fmax(zmax, fabs(z[i]));
+      zmax = wave_max(zmax);
+      const double Bz = gamma * xnb * wmaxn + rndz * 0x1p-23 + zmax * 0x1p-50 + 1e-30;
+      // noise[t, e] * softplus(z): softplus is 1-Lipschitz, so its error is at most Bz plus
+      // its own float64 evaluation; then the product and the sum round once each
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        if (e < E) {
+          const double n = (double)noise[t * E + e];
+          const double sp = softplus_f64(z[i]);
+          lg[i] += n * sp;
+          bnoise = fmax(bnoise, fabs(n) * (Bz + (sp + 1.0) * 0x1p-50) +
+                                    fabs(n * sp) * 0x1p-52 + fabs(lg[i]) * 0x1p-52);
+        }
+      }
+      bnoise = wave_max(bnoise);
+    }
+    double lmax = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i < E) lmax = fmax(lmax, fabs(lg[i]));
+    lmax = wave_max(lmax);
+    const double B = gamma * xnb * wmax + rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30 + bnoise;
     const double gap = topk_rounds_keys<EPL>(E, k, lg, sel, my_v, my_e);
-    flagged = !(gap > 2.0 * B + lmax * 0x1p-22);
+    flagged = !renorm || !(gap > 2.0 * B + lmax * 0x1p-22);
     if (flagged) {
-      // uncertified: decided later by route_fallback_kernel from exact logits
+      // decided (or, without renormalisation, finished) by route_fallback_kernel from
+      // exact logits
       if (lane == 0) list[atomicAdd(nlist, 1)] = (int32_t)t;
+    } else if (NOISE) {
+      chosen_logits_noisy_f64<EPL, CG>(x, wt, bias, noise, t, D, E, k, my_e, my_v);
     } else {
       chosen_logits_f64<EPL, CG>(x, wt, bias, t, D, k, my_e, my_v);
     }
@@ -639,8 +783,8 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
   if (valid) {
     write_logits<EPL>(logits_out, t, E, lg);
     finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
-    // the loss probabilities come from these logits for every token; the counts of an
-    // uncertified token are added by the fallback once its experts are known
+    // the loss probabilities come from these logits for every token; the counts of a
+    // listed token are added by the fallback once its experts are known
     if (flagged)
 #pragma unroll
       for (int i = 0; i < EPL; ++i) sel[i] = false;
@@ -649,26 +793,29 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
   write_block_partials<kSelWaves, EPL>(bp, E, psum_blk, count_blk);
 }
 
-// Uncertified tokens (listed by route_select_kernel), one per 1024-thread block at a time:
-// thread i takes expert i / P and every P-th 16-byte slice of D from slice i % P
-// (P = 1024 / E rounded to a power of two), so the exact-product float64 logits of all E
-// experts come from 1024 concurrent partial sums, added per expert in slice order. Wave 0
-// then takes the top-k and the gates from them and adds the token's counts to its routing
-// block's partials (integer atomics: the totals do not depend on order). Also reports the
-// number of uncertified tokens.
-template <int EPL>
+// Listed tokens (uncertified, or every token without renormalisation), one per 1024-thread
+// block at a time: thread i takes router row i / P (the E experts' rows, then with noise their
+// E noise rows) and every P-th 16-byte slice of D from slice i % P (P = 1024 / the row count
+// rounded up to a power of two), so the exact-product float64 dot products of all rows come
+// from 1024 concurrent partial sums, added per row in slice order. Wave 0 then forms the
+// logits (plus noise[t, e] * softplus(noise row) with noise), takes the top-k and the gates
+// from them and adds the token's counts to its routing block's partials (integer atomics: the
+// totals do not depend on order). Also reports the number of listed tokens.
+template <int EPL, bool NOISE>
 __global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
     int64_t D, int E, int k, int64_t nblk, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wt, const float* __restrict__ bias,
-    const int32_t* __restrict__ list, const int32_t* __restrict__ nlist,
-    int32_t* __restrict__ idx, float* __restrict__ gates, float* __restrict__ logits_out,
-    int32_t* __restrict__ count_blk, int32_t* __restrict__ uncertified) {
+    const float* __restrict__ noise, bool renorm, const int32_t* __restrict__ list,
+    const int32_t* __restrict__ nlist, int32_t* __restrict__ idx, float* __restrict__ gates,
+    float* __restrict__ logits_out, int32_t* __restrict__ count_blk,
+    int32_t* __restrict__ uncertified) {
   __shared__ double s_red[kFbThreads];
-  __shared__ double s_lg[kMaxExperts];
+  __shared__ double s_lg[2 * kMaxExperts];
   const int n = *nlist;
   if (blockIdx.x == 0 && threadIdx.x == 0 && uncertified) *uncertified = n;
+  const int rows = NOISE ? 2 * E : E;
   int NE = 1;
-  while (NE < E) NE <<= 1;
+  while (NE < rows) NE <<= 1;
   const int P = kFbThreads / NE;
   const int i = threadIdx.x, pp = i % P, e = i / P;
   const int lane = lane_id();
@@ -676,14 +823,14 @@ __global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
     const int64_t t = list[slot];
     const uint4* xr = (const uint4*)(x + t * D);
     double acc = 0.0;
-    if (e < E) {
+    if (e < rows) {
       const uint4* wr = (const uint4*)(wt + (int64_t)e * D);
 #pragma unroll 4
       for (int64_t c = pp; c < D / 8; c += P) acc += dot8_f64(xr[c], wr[c]);
     }
     s_red[i] = acc;
     __syncthreads();
-    if (i < E) {
+    if (i < rows) {
       double v = 0.0;
       for (int q = 0; q < P; ++q) v += s_red[i * P + q];
       s_lg[i] = v;
@@ -699,15 +846,49 @@ __global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
         lg[q] = (ee < E) ? s_lg[ee] : 0.0;
       }
       add_bias<EPL>(bias, E, lg);
+      if (NOISE) {
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+          const int ee = lane + kWave * q;
+          if (ee < E) lg[q] += (double)noise[t * E + ee] * softplus_f64(s_lg[E + ee]);
+        }
+      }
       write_logits<EPL>(logits_out, t, E, lg);
       topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);
-      finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
+      finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates, renorm);
       const int64_t blk = t / kRouteTokensPerBlock;
 #pragma unroll
       for (int q = 0; q < EPL; ++q)
         if (sel[q]) atomicAdd(&count_blk[(int64_t)(lane + kWave * q) * nblk + blk], 1);
     }
     __syncthreads();  // s_red / s_lg are reused by the next token
+  }
+}
+
+// Importance partials: block b (one wave) adds the final gates of its kRouteTokensPerBlock
+// tokens per expert, token by token and choice by choice, and writes them expert-major like
+// the probability partials.
+template <int EPL>
+__global__ __launch_bounds__(kWave) void importance_partials_kernel(
+    int64_t T, int E, int k, const int32_t* __restrict__ idx, const float* __restrict__ gates,
+    double* __restrict__ imp_blk) {
+  const int lane = lane_id();
+  double acc[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) acc[i] = 0.0;
+  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokensPerBlock;
+  const int64_t t1 = min(T, t0 + kRouteTokensPerBlock);
+  for (int64_t s = t0 * k; s < t1 * k; ++s) {
+    const int e = idx[s];
+    const double g = (double)gates[s];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (e == lane + kWave * i) acc[i] += g;
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) imp_blk[(int64_t)e * gridDim.x + blockIdx.x] = acc[i];
   }
 }
 
@@ -718,38 +899,48 @@ static_assert(kAuxThreads >= kMaxExperts, "one thread per expert in the final su
 // expert e's probability partials and counts in a fixed order (strided per thread, then a
 // fixed tree), writes P_e and count_e, and takes a ticket; the block with the last ticket
 // forms aux = E * sum_e (count_e / (T k)) * (P_e / T) (the E terms added by a fixed tree) and
-// resets the ticket.
+// resets the ticket. With importance partials (imp_blk non-null) each block also sums expert
+// e's gate partials, and the last block forms the importance loss, the squared coefficient of
+// variation of those E sums (population variance over the squared mean, both fixed trees;
+// 0 when nothing was routed).
 // The result does not depend on block scheduling.
 __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     int64_t nblk, int E, int64_t T, int k, const double* __restrict__ psum_blk,
     const int32_t* __restrict__ count_blk, double* __restrict__ pe, int64_t* __restrict__ ce,
-    int32_t* __restrict__ ticket, float* __restrict__ aux, int32_t* __restrict__ counts_out) {
+    int32_t* __restrict__ ticket, float* __restrict__ aux, int32_t* __restrict__ counts_out,
+    const double* __restrict__ imp_blk, double* __restrict__ ie, float* __restrict__ importance) {
   __shared__ double s_p[kAuxThreads];
+  __shared__ double s_g[kAuxThreads];
   __shared__ int64_t s_c[kAuxThreads];
   __shared__ bool s_last;
   const int e = blockIdx.x, i = threadIdx.x;
-  double pacc = 0.0;
+  double pacc = 0.0, gacc = 0.0;
   int64_t cacc = 0;
   const double* pp = psum_blk + (int64_t)e * nblk;
   const int32_t* cp = count_blk + (int64_t)e * nblk;
+  const double* gp = imp_blk ? imp_blk + (int64_t)e * nblk : nullptr;
 #pragma unroll 4
   for (int64_t b = i; b < nblk; b += kAuxThreads) {
     pacc += pp[b];
     cacc += cp[b];
+    if (gp) gacc += gp[b];
   }
   s_p[i] = pacc;
   s_c[i] = cacc;
+  s_g[i] = gacc;
   __syncthreads();
   for (int h = kAuxThreads / 2; h >= 1; h >>= 1) {
     if (i < h) {
       s_p[i] += s_p[i + h];
       s_c[i] += s_c[i + h];
+      s_g[i] += s_g[i + h];
     }
     __syncthreads();
   }
   if (i == 0) {
     pe[e] = s_p[0];
     ce[e] = s_c[0];
+    if (imp_blk) ie[e] = s_g[0];
     if (counts_out) counts_out[e] = (int32_t)s_c[0];
     __threadfence();
     s_last = atomicAdd(ticket, 1) == E - 1;
@@ -770,17 +961,37 @@ __global__ __launch_bounds__(kAuxThreads) void aux_finalize_kernel(
     if (i < h) s_p[i] += s_p[i + h];
     __syncthreads();
   }
-  if (i == 0) {
-    *aux = (float)((double)E * s_p[0]);
-    *ticket = 0;
+  if (i == 0) *aux = (float)((double)E * s_p[0]);
+  if (imp_blk) {
+    // importance: the mean of the E sums, then the mean squared deviation from it
+    const double g = i < E ? __builtin_nontemporal_load(&ie[i]) : 0.0;
+    __syncthreads();
+    s_g[i] = g;
+    __syncthreads();
+    for (int h = kAuxThreads / 2; h >= 1; h >>= 1) {
+      if (i < h) s_g[i] += s_g[i + h];
+      __syncthreads();
+    }
+    const double mean = s_g[0] / (double)E;
+    __syncthreads();
+    s_g[i] = i < E ? (g - mean) * (g - mean) : 0.0;
+    __syncthreads();
+    for (int h = kAuxThreads / 2; h >= 1; h >>= 1) {
+      if (i < h) s_g[i] += s_g[i + h];
+      __syncthreads();
+    }
+    if (i == 0) *importance = mean > 0.0 ? (float)((s_g[0] / (double)E) / (mean * mean)) : 0.f;
   }
+  if (i == 0) *ticket = 0;
 }
 
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
-// T = 0: aux = 0 and every count 0.
-__global__ void aux_empty_kernel(int E, float* __restrict__ aux, int32_t* __restrict__ counts_out) {
+// T = 0: aux = 0 (and the importance loss, if asked), every count 0.
+__global__ void aux_empty_kernel(int E, float* __restrict__ aux, int32_t* __restrict__ counts_out,
+                                 float* __restrict__ importance) {
   if (threadIdx.x == 0) *aux = 0.f;
+  if (threadIdx.x == 0 && importance) *importance = 0.f;
   if (counts_out && (int)threadIdx.x < E) counts_out[threadIdx.x] = 0;
 }
 
@@ -796,9 +1007,11 @@ struct RouteScratch {
   int32_t* ticket;   // blocks of the aux reduction done; zeroed by the first routing kernel
   int32_t* list;     // uncertified tokens (bf16), appended by the select kernel
   int32_t* nlist;    // their number; zeroed by the first routing kernel
-  uint16_t* wt;
-  double* wnorm;
-  float* part;
+  double* imp;       // importance partials (nblk per expert) and ...
+  double* ie;        // ... per-expert gate sums
+  uint16_t* wt;      // (2E, D): the router's rows, then the noise rows (when there is noise)
+  double* wnorm;     // (2E)
+  float* part;       // (S, T, 2E) partial logits, router columns then noise columns
   float* xsq;
   size_t bytes;
 };
@@ -820,11 +1033,13 @@ RouteScratch route_scratch(const Problem& p, void* base) {
   r.ticket = (int32_t*)take(sizeof(int32_t));
   r.list = (int32_t*)take((size_t)p.T * sizeof(int32_t));
   r.nlist = (int32_t*)take(sizeof(int32_t));
-  if (p.dtype == MOE_BF16) {
+  r.imp = (double*)take((size_t)nblk * p.E * sizeof(double));
+  r.ie = (double*)take((size_t)p.E * sizeof(double));
+  if (p.dtype == MOE_BF16) {  // sized for router noise (2E rows) either way
     const int S = route_splits(p);
-    r.wt = (uint16_t*)take((size_t)p.E * p.D * sizeof(uint16_t));
-    r.wnorm = (double*)take((size_t)p.E * sizeof(double));
-    r.part = (float*)take((size_t)S * p.T * p.E * sizeof(float));
+    r.wt = (uint16_t*)take((size_t)2 * p.E * p.D * sizeof(uint16_t));
+    r.wnorm = (double*)take((size_t)2 * p.E * sizeof(double));
+    r.part = (float*)take((size_t)S * p.T * 2 * p.E * sizeof(float));
     r.xsq = (float*)take((size_t)S * p.T * sizeof(float));
   }
   r.bytes = off;
@@ -852,8 +1067,8 @@ int route_splits(const Problem& p) {
 size_t route_ws_bytes(const Problem& p) { return route_scratch(p, nullptr).bytes; }
 
 hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
-                        int32_t* idx, float* gates, float* logits_out, int32_t* uncertified,
-                        void* ws, hipStream_t s) {
+                        const RouteOpts& o, int32_t* idx, float* gates, float* logits_out,
+                        int32_t* uncertified, void* ws, hipStream_t s) {
   const RouteScratch r = route_scratch(p, ws);
   const int64_t nblk = route_blocks(p);
   if (nblk == 0) {
@@ -861,11 +1076,13 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
     return hipGetLastError();
   }
   const int epl = (p.E + kWave - 1) / kWave;
+  const bool noisy = o.w_noise != nullptr;
   if (p.dtype != MOE_BF16) {
 #define MOE_ROUTE_F64(EPLV)                                                                      \
   hipLaunchKernelGGL((route_f64_kernel<float, EPLV>), dim3((unsigned)nblk), dim3(kRouteThreads), \
                      0, s, p.T, p.D, p.E, p.top_k, (const float*)x, (const float*)w_router, bias, \
-                     idx, gates, logits_out, r.psum, r.pcnt, r.ticket, uncertified)
+                     (const float*)o.w_noise, o.noise, o.renorm, idx, gates, logits_out, r.psum, \
+                     r.pcnt, r.ticket, uncertified)
     if (epl <= 1)
       MOE_ROUTE_F64(1);
     else if (epl <= 2)
@@ -878,74 +1095,115 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
   const int S = route_splits(p);
   int64_t kc = (p.D + S - 1) / S;
   kc = (kc + 31) / 32 * 32;
-  hipLaunchKernelGGL(router_prep_kernel, dim3(p.E), dim3(256), 0, s, p.D, p.E,
-                     (const uint16_t*)w_router, r.wt, r.wnorm, r.ticket, r.nlist);
+  const int rows = noisy ? 2 * p.E : p.E;  // router rows, then noise rows
+  hipLaunchKernelGGL(router_prep_kernel, dim3(rows), dim3(256), 0, s, p.D, p.E,
+                     (const uint16_t*)w_router, (const uint16_t*)o.w_noise, r.wt, r.wnorm,
+                     r.ticket, r.nlist);
   const dim3 lgrid((unsigned)((p.T + kLT - 1) / kLT), (unsigned)S);
-  const int NT = (p.E + 15) / 16;
   const uint16_t* xb = (const uint16_t*)x;
-  if (NT <= 1)
-    hipLaunchKernelGGL(route_logits_mfma_kernel<1>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
-                       xb, r.wt, r.part, r.xsq);
-  else if (NT <= 2)
-    hipLaunchKernelGGL(route_logits_mfma_kernel<2>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
-                       xb, r.wt, r.part, r.xsq);
-  else if (NT <= 4)
-    hipLaunchKernelGGL(route_logits_mfma_kernel<4>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
-                       xb, r.wt, r.part, r.xsq);
-  else if (NT <= 8)
-    hipLaunchKernelGGL(route_logits_mfma_kernel<8>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
-                       xb, r.wt, r.part, r.xsq);
-  else
-    hipLaunchKernelGGL(route_logits_mfma_kernel<16>, lgrid, dim3(256), 0, s, p.T, p.D, p.E, kc,
-                       xb, r.wt, r.part, r.xsq);
-#define MOE_ROUTE_SELECT(EPLV, CGV)                                                           \
-  hipLaunchKernelGGL((route_select_kernel<EPLV, CGV>), dim3((unsigned)nblk), dim3(kSelThreads), 0, \
-                     s, p.T, p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias, idx,  \
-                     gates, logits_out, r.psum, r.pcnt, r.list, r.nlist)
-#define MOE_ROUTE_SELECT_CG(EPLV)   \
-  if (p.top_k <= 2)                 \
-    MOE_ROUTE_SELECT(EPLV, 2);      \
-  else if (p.top_k <= 4)            \
-    MOE_ROUTE_SELECT(EPLV, 4);      \
-  else if (p.top_k <= 6)            \
-    MOE_ROUTE_SELECT(EPLV, 6);      \
-  else                              \
-    MOE_ROUTE_SELECT(EPLV, 8);
-  if (epl <= 1) {
-    MOE_ROUTE_SELECT_CG(1)
-  } else if (epl <= 2) {
-    MOE_ROUTE_SELECT_CG(2)
+  // the router product: all rows in one pass when they fit 16 tiles of 16, else the router
+  // rows and the noise rows in two passes (the second without the ||x||^2 partials)
+  auto logits = [&](int nrows, const uint16_t* w, float* xsq, int col0) {
+    const int NT = (nrows + 15) / 16;
+    if (NT <= 1)
+      hipLaunchKernelGGL(route_logits_mfma_kernel<1>, lgrid, dim3(256), 0, s, p.T, p.D, nrows,
+                         kc, xb, w, r.part, xsq, rows, col0);
+    else if (NT <= 2)
+      hipLaunchKernelGGL(route_logits_mfma_kernel<2>, lgrid, dim3(256), 0, s, p.T, p.D, nrows,
+                         kc, xb, w, r.part, xsq, rows, col0);
+    else if (NT <= 4)
+      hipLaunchKernelGGL(route_logits_mfma_kernel<4>, lgrid, dim3(256), 0, s, p.T, p.D, nrows,
+                         kc, xb, w, r.part, xsq, rows, col0);
+    else if (NT <= 8)
+      hipLaunchKernelGGL(route_logits_mfma_kernel<8>, lgrid, dim3(256), 0, s, p.T, p.D, nrows,
+                         kc, xb, w, r.part, xsq, rows, col0);
+    else
+      hipLaunchKernelGGL(route_logits_mfma_kernel<16>, lgrid, dim3(256), 0, s, p.T, p.D, nrows,
+                         kc, xb, w, r.part, xsq, rows, col0);
+  };
+  if (rows <= 256) {
+    logits(rows, r.wt, r.xsq, 0);
   } else {
-    MOE_ROUTE_SELECT_CG(4)
+    logits(p.E, r.wt, r.xsq, 0);
+    logits(p.E, r.wt + (int64_t)p.E * p.D, nullptr, p.E);
   }
+#define MOE_ROUTE_SELECT(EPLV, CGV, NZ)                                                          \
+  hipLaunchKernelGGL((route_select_kernel<EPLV, CGV, NZ>), dim3((unsigned)nblk), dim3(kSelThreads), \
+                     0, s, p.T, p.D, p.E, p.top_k, S, xb, r.wt, r.wnorm, r.part, r.xsq, bias,       \
+                     o.noise, o.renorm, idx, gates, logits_out, r.psum, r.pcnt, r.list, r.nlist)
+#define MOE_ROUTE_SELECT_CG(EPLV, NZ) \
+  if (p.top_k <= 2)                   \
+    MOE_ROUTE_SELECT(EPLV, 2, NZ);    \
+  else if (p.top_k <= 4)              \
+    MOE_ROUTE_SELECT(EPLV, 4, NZ);    \
+  else if (p.top_k <= 6)              \
+    MOE_ROUTE_SELECT(EPLV, 6, NZ);    \
+  else                                \
+    MOE_ROUTE_SELECT(EPLV, 8, NZ);
+#define MOE_ROUTE_SELECT_EPL(NZ) \
+  if (epl <= 1) {                \
+    MOE_ROUTE_SELECT_CG(1, NZ)   \
+  } else if (epl <= 2) {         \
+    MOE_ROUTE_SELECT_CG(2, NZ)   \
+  } else {                       \
+    MOE_ROUTE_SELECT_CG(4, NZ)   \
+  }
+  if (noisy) {
+    MOE_ROUTE_SELECT_EPL(true)
+  } else {
+    MOE_ROUTE_SELECT_EPL(false)
+  }
+#undef MOE_ROUTE_SELECT_EPL
 #undef MOE_ROUTE_SELECT_CG
 #undef MOE_ROUTE_SELECT
-  // one block per uncertified token, at most 512 blocks (a grid-stride loop covers the rest)
+  // one block per listed token, at most 512 blocks (a grid-stride loop covers the rest)
   const unsigned fgrid = (unsigned)std::min<int64_t>(p.T, 512);
-#define MOE_ROUTE_FALLBACK(EPLV)                                                          \
-  hipLaunchKernelGGL((route_fallback_kernel<EPLV>), dim3(fgrid), dim3(kFbThreads), 0, s, \
-                     p.D, p.E,                                                            \
-                     p.top_k, nblk, xb, r.wt, bias, r.list, r.nlist, idx, gates, logits_out, \
-                     r.pcnt, uncertified)
-  if (epl <= 1)
-    MOE_ROUTE_FALLBACK(1);
-  else if (epl <= 2)
-    MOE_ROUTE_FALLBACK(2);
-  else
-    MOE_ROUTE_FALLBACK(4);
+#define MOE_ROUTE_FALLBACK(EPLV, NZ)                                                           \
+  hipLaunchKernelGGL((route_fallback_kernel<EPLV, NZ>), dim3(fgrid), dim3(kFbThreads), 0, s, \
+                     p.D, p.E, p.top_k, nblk, xb, r.wt, bias, o.noise, o.renorm, r.list,      \
+                     r.nlist, idx, gates, logits_out, r.pcnt, uncertified)
+#define MOE_ROUTE_FALLBACK_EPL(NZ) \
+  if (epl <= 1)                    \
+    MOE_ROUTE_FALLBACK(1, NZ);     \
+  else if (epl <= 2)               \
+    MOE_ROUTE_FALLBACK(2, NZ);     \
+  else                             \
+    MOE_ROUTE_FALLBACK(4, NZ);
+  if (noisy) {
+    MOE_ROUTE_FALLBACK_EPL(true)
+  } else {
+    MOE_ROUTE_FALLBACK_EPL(false)
+  }
+#undef MOE_ROUTE_FALLBACK_EPL
 #undef MOE_ROUTE_FALLBACK
   return hipGetLastError();
 }
 
 hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* counts_out,
-                               hipStream_t s) {
+                               hipStream_t s, const int32_t* idx, const float* gates,
+                               float* importance) {
   const RouteScratch r = route_scratch(p, ws);
-  if (route_blocks(p) == 0) {  // nothing was routed: aux = 0, counts = 0
-    hipLaunchKernelGGL(aux_empty_kernel, dim3(1), dim3(kMaxExperts), 0, s, p.E, aux, counts_out);
+  const int64_t nblk = route_blocks(p);
+  if (nblk == 0) {  // nothing was routed: aux = 0, counts = 0, importance loss 0
+    hipLaunchKernelGGL(aux_empty_kernel, dim3(1), dim3(kMaxExperts), 0, s, p.E, aux, counts_out,
+                       importance);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(aux_finalize_kernel, dim3(p.E), dim3(kAuxThreads), 0, s, route_blocks(p),
-                     p.E, p.T, p.top_k, r.psum, r.pcnt, r.pe, r.ce, r.ticket, aux, counts_out);
+  if (importance) {
+    const int epl = (p.E + kWave - 1) / kWave;
+    if (epl <= 1)
+      hipLaunchKernelGGL(importance_partials_kernel<1>, dim3((unsigned)nblk), dim3(kWave), 0, s,
+                         p.T, p.E, p.top_k, idx, gates, r.imp);
+    else if (epl <= 2)
+      hipLaunchKernelGGL(importance_partials_kernel<2>, dim3((unsigned)nblk), dim3(kWave), 0, s,
+                         p.T, p.E, p.top_k, idx, gates, r.imp);
+    else
+      hipLaunchKernelGGL(importance_partials_kernel<4>, dim3((unsigned)nblk), dim3(kWave), 0, s,
+                         p.T, p.E, p.top_k, idx, gates, r.imp);
+  }
+  hipLaunchKernelGGL(aux_finalize_kernel, dim3(p.E), dim3(kAuxThreads), 0, s, nblk, p.E, p.T,
+                     p.top_k, r.psum, r.pcnt, r.pe, r.ce, r.ticket, aux, counts_out,
+                     importance ? r.imp : nullptr, r.ie, importance);
   return hipGetLastError();
 }
 

@@ -181,6 +181,80 @@ moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_
                              int32_t* slot_row, void* ws, size_t ws_bytes, hipStream_t stream,
                              hipEvent_t* stage_events);
 
+/* ---- Router options and the capacity-padded layout --------------------------------------
+ * Options of the router on the page "Mixture of Experts: the Sparsely-Gated Layer" and of the
+ * Switch layer's fixed-size expert batches (host struct; NULL or all zero = the layer above:
+ * no noise, renormalised gates, compact expert rows, no importance loss).
+ *   w_noise, noise: router noise ("The one formula", the + noise row; router() stage (2) in
+ *     "The code"). w_noise (D, E) in p->dtype; noise (T, E) float32, the standard-normal draw,
+ *     supplied by the caller (the library draws nothing, so every call is deterministic). The
+ *     decision logits become logits + noise[t, e] * softplus(x_t . w_noise[:, e]), and the
+ *     probabilities, top-k, gates and both losses use them. Both NULL or both set.
+ *   no_renormalise: nonzero = the gates are the chosen experts' probabilities over all E
+ *     experts (router(..., renormalise=False): stage (5) skipped), so a gate row sums to at
+ *     most 1. Every token's logits are then recomputed exactly in float64 (these gates need
+ *     all E of them to the gates' accuracy), and `uncertified` counts every token.
+ *   padded: nonzero = expert batches padded to the capacity ("Switch: top-1, one loss, and a
+ *     rate limit": experts run as fixed-size batches); needs capacity_factor > 0. Expert e's
+ *     kept slots take rows e * capacity + rank (rank in token order) and the rest of its batch
+ *     is zero rows, which the expert GEMMs compute anyway (the padding cost the page names).
+ *   importance_loss: device float32 (1), or NULL: Shazeer's importance loss ("Hot shards: the
+ *     load-balancing loss", importance_loss()), the squared coefficient of variation
+ *     (population standard deviation over the mean) of the per-expert sums of the gates;
+ *     0 when T = 0. Deterministic (fixed-order sums). */
+typedef struct moe_options {
+  const void* w_noise;
+  const float* noise;
+  int32_t no_renormalise;
+  int32_t padded;
+  float* importance_loss;
+} moe_options;
+
+/* Bytes of workspace that the *_ex entry points need with these options (opts may be NULL;
+ * then equal to moe_workspace_size). Host only; 0 for an invalid problem or options
+ * (padded without a capacity). */
+size_t moe_workspace_size_ex(const moe_problem* p, const moe_options* opts);
+
+/* moe_route with options (opts->padded plays no part here). Errors as moe_route, plus
+ * MOE_ERR_INVALID_ARG when exactly one of w_noise and noise is set. */
+moe_status moe_route_ex(const moe_problem* p, const moe_options* opts, const void* x,
+                        const void* w_router, const float* router_bias, int32_t* expert_indices,
+                        float* gates, float* aux_loss, int32_t* expert_counts,
+                        float* logits_out, int32_t* uncertified, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Dispatch into the capacity-padded layout (Sparsely-Gated Layer page, "Switch: top-1, one
+ * loss, and a rate limit"; first come, first served as in moe_dispatch). Needs
+ * capacity_factor > 0 (else MOE_ERR_INVALID_ARG); with capacity 0 every slot is dropped.
+ *   expert_indices, x as in moe_dispatch. Outputs: expert_counts (E) int32 before capacity;
+ *   expert_offsets (E+1) int32, the batch starts e * capacity (what moe_expert_ffn_ex takes);
+ *   perm (E * capacity) int32, the slot of each padded row or -1 for an empty row; slot_row
+ *   (T*top_k) int32, the padded row of each slot or -1 when dropped; x_pad (E * capacity, D)
+ *   in p->dtype, each kept slot's token row and zero rows elsewhere, or NULL to skip the copy.
+ *   Workspace: moe_workspace_size_ex with padded set. */
+moe_status moe_dispatch_padded(const moe_problem* p, const int32_t* expert_indices,
+                               const void* x, int32_t* expert_counts, int32_t* expert_offsets,
+                               int32_t* perm, int32_t* slot_row, void* x_pad, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* moe_expert_ffn over a padded layout: as moe_expert_ffn, except that expert_offsets[E] may
+ * be up to max(T * top_k, E * capacity) rows (x_perm and y_perm sized for that many) when
+ * opts->padded; the workspace is moe_workspace_size_ex's. */
+moe_status moe_expert_ffn_ex(const moe_problem* p, const moe_options* opts, const void* x_perm,
+                             const int32_t* expert_offsets, const void* w1, const void* w3,
+                             const void* w2, void* y_perm, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* moe_forward_timed with options (stage_events may be NULL). With opts->padded,
+ * expert_offsets receives the batch starts e * capacity and slot_row the padded rows, as in
+ * moe_dispatch_padded, and the dispatch stage includes the padded copy of x. */
+moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const void* x,
+                          const void* w_router, const float* router_bias, const void* w1,
+                          const void* w3, const void* w2, void* out, int32_t* expert_indices,
+                          float* gates, float* aux_loss, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* slot_row, void* ws, size_t ws_bytes,
+                          hipStream_t stream, hipEvent_t* stage_events);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -13,7 +13,9 @@ Sources (web pages; cited by title and section):
   the primary definition.
 * "Mixture of Experts: the Sparsely-Gated Layer" (paperfordummies, Shazeer 2017
   with Switch 2021): capacity and first-come-first-served dropping, the optional
-  router bias, the two-layer ReLU expert, the FLOP accounting.
+  router bias, the two-layer ReLU expert, the FLOP accounting, and the router
+  options: noise, gates without renormalisation, Shazeer's importance loss and
+  the capacity-padded expert batches.
 * "Sparsely-gated Mixture of Experts (MoE)" (Eli Bendersky): the per-token
   formulation (section "A Minimal Numpy Implementation"), the D, DH, NEXP,
   TOPK naming.
@@ -27,11 +29,16 @@ from .moe import (  # noqa: F401
     dispatch_from_indices,
     expert_forward,
     gates_from_logits,
+    gates_from_probs,
+    importance_loss,
     moe_forward,
     moe_forward_per_token,
+    noisy_router_logits,
+    padded_layout,
     router_logits,
     silu,
     softmax_rows,
+    softplus,
     switch_aux_loss,
     top_k_sorted,
 )

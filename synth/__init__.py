@@ -13,5 +13,7 @@ from .inputs import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_inputs,
+    RouterNoise,
+    make_router_noise,
     spec,
 )

@@ -149,7 +149,7 @@ class LayerInputs:
         return a
 
 
-X_ID, ROUTER_ID, BIAS_ID, W1_ID, W3_ID, W2_ID = range(6)
+X_ID, ROUTER_ID, BIAS_ID, W1_ID, W3_ID, W2_ID, NOISE_W_ID, NOISE_ID = range(8)
 
 
 def _rng(seed: int, tensor: int, expert: int = 0) -> np.random.Generator:
@@ -211,3 +211,29 @@ def make_inputs(sp: LayerSpec, seed: int = 0, router_zero: bool = False) -> Laye
         raise ValueError(f"unknown expert kind {sp.kind!r}")
     w2 = _draw_experts(seed, W2_ID, sp.E, (sp.DH, sp.D_out), _std(sp.w2_std, sp.DH), sp.dtype)
     return LayerInputs(sp, x, w_router, bias, w1, w3, w2)
+
+
+@dataclass
+class RouterNoise:
+    """Router-noise inputs: ``w_noise`` (D, E) stored like the layer's tensors (uint16 bf16 bit
+    patterns or float32) and ``noise`` (T, E) float32 standard-normal draws."""
+
+    w_noise: np.ndarray
+    noise: np.ndarray
+
+    def w_values(self) -> np.ndarray:
+        """float32 array holding exactly the stored values of ``w_noise``."""
+        if self.w_noise.dtype == np.uint16:
+            return bf16_bits_to_f32(self.w_noise)
+        return self.w_noise
+
+
+def make_router_noise(sp: LayerSpec, seed: int = 0, w_std: Std = "fanin",
+                      noise_scale: float = 1.0) -> RouterNoise:
+    """The noise weights (N(0, w_std), fan-in by default, so x . W_noise is about unit scale)
+    and the (T, E) standard-normal draw, times ``noise_scale`` (0 gives an all-zero draw), from
+    their own seeded streams."""
+    w_noise = _draw(_rng(seed, NOISE_W_ID), (sp.D, sp.E), _std(w_std, sp.D), sp.dtype)
+    noise = _rng(seed, NOISE_ID).standard_normal((sp.T, sp.E), dtype=np.float32)
+    noise *= np.float32(noise_scale)
+    return RouterNoise(w_noise, noise)

@@ -162,3 +162,47 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", tmp_path / "libmoe.so")
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+# --- moe_options (host checks only; every call below returns before any launch) ---------
+
+def test_workspace_size_ex():
+    p = P(capacity_factor=2.0)
+    assert B.workspace_size_ex(p, None) == B.workspace_size(p)
+    L = B.lib()
+    opts = B.MoeOptions(None, None, 1, 0, None)
+    assert L.moe_workspace_size_ex(ctypes.byref(p.c()), ctypes.byref(opts)) == B.workspace_size(p)
+    # the padded layout needs room for E * capacity rows (> T * k at capacity factor 2)
+    padded = B.MoeOptions(None, None, 0, 1, None)
+    assert L.moe_workspace_size_ex(ctypes.byref(p.c()), ctypes.byref(padded)) > B.workspace_size(p)
+    # ... and a capacity
+    assert L.moe_workspace_size_ex(ctypes.byref(P().c()), ctypes.byref(padded)) == 0
+    # noise weights without the draw (or the reverse) are not options
+    half = B.MoeOptions(0x1000, None, 0, 0, None)
+    assert L.moe_workspace_size_ex(ctypes.byref(p.c()), ctypes.byref(half)) == 0
+
+
+def test_option_entry_points_reject_bad_options_before_launching():
+    L = B.lib()
+    p = P()
+    pc = ctypes.byref(p.c())
+    fake = 0x1000  # never dereferenced: the checks fail first
+    half = ctypes.byref(B.MoeOptions(fake, None, 0, 0, None))
+    st = L.moe_route_ex(pc, half, fake, fake, None, fake, fake, fake, None, None, None, fake,
+                        1 << 30, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    padded_nocap = ctypes.byref(B.MoeOptions(None, None, 0, 1, None))
+    st = L.moe_forward_ex(pc, padded_nocap, fake, fake, None, fake, fake, fake, fake, fake, fake,
+                          fake, fake, fake, fake, fake, 1 << 30, None, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    # padded dispatch without a capacity
+    st = L.moe_dispatch_padded(pc, fake, fake, fake, fake, fake, fake, None, fake, 1 << 30, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    # a workspace too small for the padded layout
+    pcap = P(capacity_factor=2.0)
+    need = B.workspace_size_ex(pcap, None)
+    padded = ctypes.byref(B.MoeOptions(None, None, 0, 1, None))
+    st = L.moe_forward_ex(ctypes.byref(pcap.c()), padded, fake, fake, None, fake, fake, fake, fake,
+                          fake, fake, fake, fake, fake, fake, 1 << 20, need, None, None)
+    assert st == B.MOE_ERR_WORKSPACE
+
