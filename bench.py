@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("1e7840997e931cd43cd537a8bb580f1002eeea2e9422b286475f8f32a3696870",
-                            3426028.901785714, 237382.89285714287),
+    "mixtral_swiglu_bf16": ("466cbbc79fd656a03a2cfb7636587895f3d65905642418dc2490b69ce1dc9833",
+                            3448114.8214285714, 237126.8392857143),
 }
 
 
@@ -93,9 +93,11 @@ def device_tensor(a):
     return torch.from_numpy(a).cuda()
 
 
-def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4) -> dict:
-    """The oracle as it stands, on the first `tokens` tokens of the same inputs, repeated
-    until at least `min_seconds` of wall time (at most `max_passes` passes)."""
+def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4, N=None,
+                 renormalise: bool = True) -> dict:
+    """The oracle as it stands, on the first `tokens` tokens of the same inputs (and router
+    options), repeated until at least `min_seconds` of wall time (at most `max_passes`
+    passes)."""
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -105,7 +107,10 @@ def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4)
     passes, t0 = 0, time.perf_counter()
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.moe_forward(x, wr, sp.top_k, sp.kind, w1, w2, w3, bias=I.bias,
-                           capacity_factor=sp.capacity_factor)
+                           capacity_factor=sp.capacity_factor,
+                           w_noise=None if N is None else N.w_values(),
+                           noise=None if N is None else N.noise[:tokens],
+                           renormalise=renormalise)
         passes += 1
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -130,6 +135,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--router-noise", action="store_true",
+                    help="noisy router: + noise * softplus(x @ W_noise), seeded draw")
+    ap.add_argument("--no-renormalise", action="store_true",
+                    help="gates = the chosen experts' probabilities")
+    ap.add_argument("--padded", action="store_true",
+                    help="capacity-padded expert batches (needs a capacity factor)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -146,7 +157,7 @@ def main() -> int:
 
     from expert_ffn_layer_router_amd import accounting as A
     from expert_ffn_layer_router_amd import binding as B
-    from synth import make_inputs, spec
+    from synth import make_inputs, make_router_noise, spec
 
     sp = spec(args.config)
     log(f"[bench] generating {sp.name} inputs (seed {args.seed})")
@@ -154,14 +165,34 @@ def main() -> int:
     p = B.Problem.from_spec(sp)
     dev = {n: device_tensor(getattr(I, n)) for n in ("x", "w_router", "bias", "w1", "w3", "w2")}
     outs = B.alloc_outputs(p)
-    ws = B.alloc_workspace(p)
+    options = args.router_noise or args.no_renormalise or args.padded
+    N, opts, importance = None, None, None
+    if options:
+        if args.padded and not sp.capacity_factor > 0:
+            print("--padded needs a layer with a capacity factor", file=sys.stderr)
+            return 2
+        if args.router_noise:
+            N = make_router_noise(sp, seed=args.seed)
+        importance = torch.zeros(1, dtype=torch.float32, device="cuda")
+        opts = B.Options(w_noise=None if N is None else device_tensor(N.w_noise),
+                         noise=None if N is None else device_tensor(N.noise),
+                         renormalise=not args.no_renormalise, padded=args.padded,
+                         importance_loss=importance)
+    ws = B.alloc_workspace(p, o=opts)
     torch.cuda.synchronize()
 
     def step(ev=None):
-        B.moe_forward_timed(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"],
-                            dev["w2"], outs["out"], outs["expert_indices"], outs["gates"],
-                            outs["aux_loss"], outs["expert_counts"], outs["expert_offsets"],
-                            outs["slot_row"], ws, None if ev is None else ev.events)
+        if opts is None:
+            B.moe_forward_timed(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"],
+                                dev["w2"], outs["out"], outs["expert_indices"], outs["gates"],
+                                outs["aux_loss"], outs["expert_counts"], outs["expert_offsets"],
+                                outs["slot_row"], ws, None if ev is None else ev.events)
+        else:
+            B.moe_forward_ex(p, opts, dev["x"], dev["w_router"], dev["bias"], dev["w1"],
+                             dev["w3"], dev["w2"], outs["out"], outs["expert_indices"],
+                             outs["gates"], outs["aux_loss"], outs["expert_counts"],
+                             outs["expert_offsets"], outs["slot_row"], ws,
+                             None if ev is None else ev.events)
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -194,9 +225,9 @@ def main() -> int:
     for e in extra:
         e.close()
 
-    offsets = outs["expert_offsets"].cpu().numpy()
-    R = int(offsets[-1])
     T, D, DH, Do, E, k = sp.T, sp.D, sp.DH, sp.D_out, sp.E, sp.top_k
+    R = int((outs["slot_row"] >= 0).sum().cpu())  # kept slots (either layout)
+    rows = E * B.capacity(p) if args.padded else R  # rows the expert GEMMs run over
     es = 2 if sp.dtype == "bf16" else 4
     peak_tf = BF16_PEAK_TFLOPS if sp.dtype == "bf16" else FP32_PEAK_TFLOPS
     used_tokens = int(np.count_nonzero((outs["slot_row"].view(T, k) >= 0).any(dim=1).cpu()))
@@ -210,6 +241,8 @@ def main() -> int:
         up_flops, down_flops = up_mult * D * DH * R, 2 * DH * Do * R
         up_w = (2 if sp.kind == "swiglu" else 1) * E * D * DH * es
     route_b = A.route_bytes(T, D, E, k, es)
+    if N is not None:
+        route_b += A.route_noise_bytes(T, D, E, es)
     combine_b = A.combine_bytes(T, k, R, Do, es)
 
     def tf(fl, ms_):
@@ -223,7 +256,10 @@ def main() -> int:
         "route": {"us": stage_ms["route"] * 1e3, "GB/s": gbs(route_b, stage_ms["route"]),
                   "hbm_frac": gbs(route_b, stage_ms["route"]) / HBM_PEAK_GBS,
                   "algorithmic_bytes": route_b},
-        "dispatch": {"us": stage_ms["dispatch"] * 1e3},
+        "dispatch": {"us": stage_ms["dispatch"] * 1e3} if not args.padded else {
+            "us": stage_ms["dispatch"] * 1e3,
+            "GB/s": gbs(A.padded_permute_bytes(used_tokens, rows, D, es), stage_ms["dispatch"]),
+            "algorithmic_bytes": A.padded_permute_bytes(used_tokens, rows, D, es)},
         "expert_up": {"us": stage_ms["expert_up"] * 1e3, "TFLOP/s": up_tf,
                       "mfma_frac": up_tf / peak_tf, "algorithmic_flops": up_flops},
         "expert_down": {"us": stage_ms["expert_down"] * 1e3,
@@ -247,21 +283,30 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if sp.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0, sigma) inputs and random-init weights)",
-        "config": {"workload": sp.description, "T": T, "D": D, "DH": DH, "E": E, "top_k": k,
+        "config": {"workload": sp.description + "".join(
+                       s_ for s_, on in ((", router noise", N is not None),
+                                         (", gates not renormalised", args.no_renormalise),
+                                         (", capacity-padded expert batches", args.padded))
+                       if on),
+                   "T": T, "D": D, "DH": DH, "E": E, "top_k": k,
                    "expert": sp.kind, "capacity_factor": sp.capacity_factor,
-                   "kept_slots": R, "dropped_slots": T * k - R, "used_tokens": used_tokens},
+                   "kept_slots": R, "dropped_slots": T * k - R, "used_tokens": used_tokens,
+                   "expert_rows": rows},
         "roofline": {"kernel": "expert up-projection grouped GEMM (stage expert_up)",
                      "bound": "mfma", "achieved": up_tf, "peak": peak_tf, "unit": "TFLOP/s",
-                     "frac": up_tf / peak_tf, "traffic": measured_traffic(sp.name),
+                     "frac": up_tf / peak_tf,
+                     "traffic": None if options else measured_traffic(sp.name),
                      "algorithmic_flops_per_launch": up_flops,
                      "launch_us": stage_ms["expert_up"] * 1e3,
                      "weight_bytes": up_w},
         "stages": stages,
     }
+    if importance is not None:
+        result["importance_loss"] = float(importance.cpu()[0])
     if not args.no_cpu_baseline:
         n = min(args.cpu_baseline_tokens, T) if args.cpu_baseline_tokens > 0 else T
         log(f"[bench] CPU oracle baseline on {n} tokens")
-        result["cpu_baseline"] = cpu_baseline(I, n)
+        result["cpu_baseline"] = cpu_baseline(I, n, N=N, renormalise=not args.no_renormalise)
     print(json.dumps(result), flush=True)
     return 0
 

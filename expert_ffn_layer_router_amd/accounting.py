@@ -52,6 +52,17 @@ def route_bytes(T: int, D: int, E: int, k: int, act_bytes: int) -> int:
     return T * D * act_bytes + D * E * act_bytes + T * k * 8
 
 
+def route_noise_bytes(T: int, D: int, E: int, act_bytes: int) -> int:
+    """Router noise adds a read of W_noise (D, E) and of the (T, E) float32 draw."""
+    return D * E * act_bytes + T * E * 4
+
+
+def padded_permute_bytes(used_tokens: int, rows: int, D: int, act_bytes: int) -> int:
+    """The padded copy: each used x row read once, all E * capacity rows written (kept rows
+    and zero rows)."""
+    return used_tokens * D * act_bytes + rows * D * act_bytes
+
+
 def permute_bytes(used_tokens: int, R: int, D: int, act_bytes: int) -> int:
     """Read each used x row once, write R expert-ordered rows."""
     return used_tokens * D * act_bytes + R * D * act_bytes
