@@ -27,16 +27,19 @@ stated in ``moe.py``'s header ("parity unpinned").
 from .moe import (  # noqa: F401
     capacity_slots,
     dispatch_from_indices,
+    expert_backward,
     expert_forward,
     gates_from_logits,
     gates_from_probs,
     importance_loss,
+    moe_backward,
     moe_forward,
     moe_forward_per_token,
     noisy_router_logits,
     padded_layout,
     router_logits,
     silu,
+    silu_grad,
     softmax_rows,
     softplus,
     switch_aux_loss,

@@ -35,6 +35,12 @@ Steps, with the passage each follows:
    a drop -- ML Grind, Algorithm step 3 and "Constraints"; Sparsely-Gated
    Layer, ``moe_forward``.
 
+Backward (``moe_backward``): the gradients of ``sum(out * dout) + d_aux * aux``
+with respect to x, the router and the experts, by the chain rule through the steps
+above in reverse; the decisions are piecewise constant, so the gradient flows through
+the gates and through P in the Switch loss, and f (a count) has none (Sparsely-Gated
+Layer, "Hot shards"). Pinned by central finite differences of ``moe_forward``.
+
 Router options (Sparsely-Gated Layer, "The one formula" and "The code",
 ``router()`` stages (2) and (5); "Hot shards: the load-balancing loss"):
 
@@ -279,6 +285,99 @@ def moe_forward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=N
         out[t] += flat_gates[rows][:, None] * y
     return dict(output=out, expert_indices=idx, gates=gates, aux_loss=aux, logits=logits,
                 probs=probs, capacity=cap, importance_loss=imp, **disp)
+
+
+# --- backward -------------------------------------------------------------------------
+
+def silu_grad(z):
+    """d silu / dz = sigma(z) * (1 + z * (1 - sigma(z)))."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-z))
+    return sig * (1.0 + z * (1.0 - sig))
+
+
+def expert_backward(kind: str, xr: np.ndarray, dy: np.ndarray, w1, w2=None, w3=None) -> dict:
+    """Gradients of one expert on its rows: given dL/dy for y = expert(x), returns dL/dx
+    and dL/dW for each of its matrices (chain rule through the forms of expert_forward;
+    relu'(0) is taken as 0)."""
+    xr, dy = _f64(xr), _f64(dy)
+    if kind == "linear":
+        W = _f64(w1)
+        return dict(dx=dy @ W.T, dw1=xr.T @ dy)
+    W1, W2 = _f64(w1), _f64(w2)
+    a = xr @ W1
+    if kind == "relu2":
+        h = np.maximum(a, 0.0)
+        dh = dy @ W2.T
+        da = dh * (a > 0.0)
+        return dict(dx=da @ W1.T, dw1=xr.T @ da, dw2=h.T @ dy)
+    if kind == "swiglu":
+        W3 = _f64(w3)
+        b = xr @ W3
+        h = silu(a) * b
+        dh = dy @ W2.T
+        da = dh * b * silu_grad(a)
+        db = dh * silu(a)
+        return dict(dx=da @ W1.T + db @ W3.T, dw1=xr.T @ da, dw3=xr.T @ db, dw2=h.T @ dy)
+    raise ValueError(f"unknown expert kind {kind!r}")
+
+
+def moe_backward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=None,
+                 capacity_factor: float = 0.0, dout=None, d_aux: float = 0.0) -> dict:
+    """Gradients of L = sum(out * dout) + d_aux * aux_loss with respect to x, the router
+    (weights and bias) and every expert matrix, for the layer of moe_forward (no router
+    noise, renormalised gates).
+
+    The routing decisions (top-k and the drop set) are piecewise constant, so the gradient
+    flows through the gates and through P in the Switch loss; f (a count) has none
+    (Sparsely-Gated Layer, "Hot shards": a count has no gradient, a probability does).
+    In reverse order: the combine gives dL/dgate = <dout_t, y_e(x_t)> for a kept slot (0 for
+    a dropped one) and dL/dy = gate * dout_t; each expert's backward on its kept rows; the
+    gates' softmax over the k chosen logits; the loss through P_e = mean_t probs[t, e] and
+    the full softmax; the router product logits = x @ W_router + bias."""
+    r = moe_forward(x, w_router, top_k, kind, w1, w2, w3, bias=bias,
+                    capacity_factor=capacity_factor)
+    x = _f64(x)
+    T, D = x.shape
+    E = np.asarray(w_router).shape[1]
+    dout = _f64(dout)
+    idx, gates, probs = r["expert_indices"], r["gates"], r["probs"]
+    dgates = np.zeros_like(gates)
+    dx = np.zeros_like(x)
+    dw1 = np.zeros(np.asarray(w1).shape)
+    dw2 = None if w2 is None else np.zeros(np.asarray(w2).shape)
+    dw3 = None if w3 is None else np.zeros(np.asarray(w3).shape)
+    flat_gates = gates.reshape(-1)
+    for e in range(E):
+        rows = r["perm"][r["offsets"][e]:r["offsets"][e + 1]]  # kept slot ids of e
+        if rows.size == 0:
+            continue
+        t = rows // top_k
+        we = _expert_weights(e, w1, w2, w3)
+        y = expert_forward(kind, x[t], *we)
+        dgates.reshape(-1)[rows] = np.einsum("rd,rd->r", dout[t], y)
+        g = expert_backward(kind, x[t], flat_gates[rows][:, None] * dout[t], *we)
+        np.add.at(dx, t, g["dx"])
+        dw1[e] += g["dw1"]
+        if dw2 is not None:
+            dw2[e] += g["dw2"]
+        if dw3 is not None:
+            dw3[e] += g["dw3"]
+    # gates = softmax(chosen logits): dl_c = g_c * (dg_c - sum_c' g_c' dg_c')
+    dl = np.zeros((T, E))
+    dl_chosen = gates * (dgates - (gates * dgates).sum(axis=1, keepdims=True))
+    np.add.at(dl, (np.arange(T)[:, None].repeat(top_k, 1), idx), dl_chosen)
+    # aux = E * sum_e f_e * P_e with P_e = mean_t probs[t, e]: dL/dprobs[t, e] = d_aux E f_e / T
+    if T > 0:
+        f = np.bincount(idx.ravel(), minlength=E) / (T * top_k)
+        a = d_aux * E * f / T
+        dl += probs * (a[None, :] - (probs * a[None, :]).sum(axis=1, keepdims=True))
+    dw_router = x.T @ dl
+    dbias = dl.sum(axis=0)
+    dx += dl @ _f64(w_router).T
+    return dict(dx=dx, dw_router=dw_router, dbias=dbias, dw1=dw1, dw2=dw2, dw3=dw3,
+                dgates=dgates, dlogits=dl, forward=r)
 
 
 def _expert_one_token(kind: str, xt: np.ndarray, w1, w2=None, w3=None) -> np.ndarray:

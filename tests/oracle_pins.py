@@ -481,4 +481,111 @@ def pin_padded_layout():
         assert np.array_equal(p["slot_row_padded"][p["perm_padded"][rows]], rows)
 
 
+# --- backward: the analytic gradients against finite differences of the forward ---------
+
+def _loss(args, kw, dout, d_aux):
+    r = O.moe_forward(*args, **kw)
+    return float(np.sum(r["output"] * dout) + d_aux * r["aux_loss"])
+
+
+def _fd_case(kind, T, D, DH, E, k, cf, with_bias, salt):
+    r_ = _rng(salt)
+    x = r_.standard_normal((T, D))
+    w = r_.standard_normal((D, E)) * 1.5
+    bias = r_.standard_normal(E) if with_bias else None
+    if kind == "linear":
+        w1, w2, w3 = r_.standard_normal((E, D, 3)), None, None
+    else:
+        w1 = r_.standard_normal((E, D, DH))
+        w3 = r_.standard_normal((E, D, DH)) if kind == "swiglu" else None
+        w2 = r_.standard_normal((E, DH, 3))
+    return x, w, bias, w1, w2, w3
+
+
+def pin_backward_matches_finite_differences():
+    """moe_backward against central differences of L = sum(out * dout) + d_aux * aux, for
+    every expert kind, k in {1, 2, E}, with and without capacity and bias. Each case first
+    checks that its routing margins (and ReLU pre-activations) are far from a kink, so the
+    perturbation cannot change a decision."""
+    h = 1e-5
+    cases = 0
+    for kind in ("linear", "relu2", "swiglu"):
+        for (k, cf, with_bias) in [(1, 0.0, True), (2, 0.0, False), (2, 0.8, True), (4, 0.0, True)]:
+            for salt in range(40, 60):
+                T, D, DH, E = 6, 4, 3, 4
+                x, w, bias, w1, w2, w3 = _fd_case(kind, T, D, DH, E, k, cf, with_bias, salt)
+                lg = O.router_logits(x, w, bias)
+                srt = np.sort(lg, axis=1)[:, ::-1]
+                if k < E and np.min(srt[:, k - 1] - srt[:, k]) < 1e-2:
+                    continue  # a near tie: pick another draw
+                if kind == "relu2" and np.min(np.abs(np.einsum("td,edh->teh", x, w1))) < 1e-3:
+                    continue
+                break
+            else:
+                raise AssertionError("no draw with clear margins")
+            r_ = _rng(salt + 100)
+            dout = r_.standard_normal((T, 3))
+            d_aux = 0.7
+            g = O.moe_backward(x, w, k, kind, w1, w2, w3, bias=bias, capacity_factor=cf,
+                               dout=dout, d_aux=d_aux)
+            params = dict(x=x, w=w, w1=w1)
+            if bias is not None:
+                params["bias"] = bias
+            if w2 is not None:
+                params["w2"] = w2
+            if w3 is not None:
+                params["w3"] = w3
+            grads = dict(x=g["dx"], w=g["dw_router"], bias=g["dbias"], w1=g["dw1"],
+                         w2=g["dw2"], w3=g["dw3"])
+
+            def call(pp):
+                return _loss((pp["x"], pp["w"], k, kind, pp["w1"], pp.get("w2"), pp.get("w3")),
+                             dict(bias=pp.get("bias"), capacity_factor=cf), dout, d_aux)
+
+            scale = max(1.0, max(np.abs(v).max() for v in grads.values() if v is not None))
+            for name, val in params.items():
+                num = np.zeros_like(val)
+                for i in np.ndindex(val.shape):
+                    pp = {n: v.copy() for n, v in params.items()}
+                    pp[name][i] += h
+                    up = call(pp)
+                    pp[name][i] -= 2 * h
+                    dn = call(pp)
+                    num[i] = (up - dn) / (2 * h)
+                assert np.abs(num - grads[name]).max() <= 1e-6 * scale, (kind, k, cf, name)
+            cases += 1
+    assert cases == 12
+
+
+def pin_backward_closed_forms():
+    """Gradient closed forms: with k = E the Switch loss is 1 for any router, so its
+    gradient is zero; top-1 gates are identically 1, so without the loss the router gets no
+    gradient; linear experts with k = E and no capacity give dW_e = sum_t p_te x_t^T dout_t
+    and dx_t = sum_e p_te dout_t W_e^T plus the router term."""
+    r_ = _rng(60)
+    T, D, E = 7, 5, 4
+    x, w = r_.standard_normal((T, D)), r_.standard_normal((D, E))
+    we = r_.standard_normal((E, D, 3))
+    g = O.moe_backward(x, w, E, "linear", we, dout=np.zeros((T, 3)), d_aux=1.3)
+    assert np.abs(g["dlogits"]).max() <= 1e-14 and np.abs(g["dw_router"]).max() <= 1e-13
+    g = O.moe_backward(x, w, 1, "linear", we, dout=r_.standard_normal((T, 3)), d_aux=0.0)
+    assert np.abs(g["dw_router"]).max() == 0.0 and np.abs(g["dbias"]).max() == 0.0
+    dout = r_.standard_normal((T, 3))
+    g = O.moe_backward(x, w, E, "linear", we, dout=dout, d_aux=0.0)
+    p = O.softmax_rows(O.router_logits(x, w))
+    for e in range(E):
+        want = (x * p[:, e:e + 1]).T @ dout
+        assert np.allclose(g["dw1"][e], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_silu_grad():
+    """silu'(0) = 1/2, the asymptotes 1 and 0, and central differences of silu."""
+    assert O.silu_grad(0.0) == 0.5
+    assert abs(O.silu_grad(40.0) - 1.0) <= 1e-12 and abs(O.silu_grad(-40.0)) <= 1e-12
+    z = np.linspace(-6, 6, 49)
+    h = 1e-6
+    num = (O.silu(z + h) - O.silu(z - h)) / (2 * h)
+    assert np.abs(num - O.silu_grad(z)).max() <= 1e-8
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

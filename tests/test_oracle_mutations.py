@@ -177,6 +177,31 @@ def _probs_renormalised_anyway(probs, idx):
     return p / p.sum(axis=-1, keepdims=True)
 
 
+def _silu_grad_sigma_only(z):
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+_orig_backward = O.moe_backward
+
+
+def _backward_without_loss_term(*a, **kw):
+    kw["d_aux"] = 0.0
+    return _orig_backward(*a, **kw)
+
+
+_orig_expert_backward = O.expert_backward
+
+
+def _expert_backward_w2_untransposed(kind, xr, dy, w1, w2=None, w3=None):
+    """Uses dy @ W2 instead of dy @ W2^T for dL/dh where the shapes allow it."""
+    if w2 is not None and np.asarray(w2).shape[0] == np.asarray(w2).shape[1]:
+        return _orig_expert_backward(kind, xr, dy, w1, np.asarray(w2).T, w3)
+    g = _orig_expert_backward(kind, xr, dy, w1, w2, w3)
+    g["dx"] = -g["dx"]
+    return g
+
+
 MUTATIONS = {
     "ties_to_higher_index": ("top_k_sorted", _ties_to_higher_index),
     "ascending_top_k": ("top_k_sorted", _ascending),
@@ -200,6 +225,9 @@ MUTATIONS = {
     "importance_cv_not_squared": ("importance_loss", _importance_cv_not_squared),
     "importance_from_counts": ("importance_loss", _importance_from_counts),
     "unrenormalised_gates_renormalised": ("gates_from_probs", _probs_renormalised_anyway),
+    "silu_grad_sigma_only": ("silu_grad", _silu_grad_sigma_only),
+    "backward_without_loss_term": ("moe_backward", _backward_without_loss_term),
+    "expert_backward_wrong_dh": ("expert_backward", _expert_backward_w2_untransposed),
 }
 
 
