@@ -28,7 +28,7 @@ EXPORTED = (
     "moe_status_string", "moe_check_problem", "moe_capacity", "moe_workspace_size",
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_forward_timed", "moe_workspace_size_ex", "moe_route_ex", "moe_dispatch_padded",
-    "moe_expert_ffn_ex", "moe_forward_ex",
+    "moe_expert_ffn_ex", "moe_forward_ex", "moe_backward_workspace_size", "moe_backward",
 )
 STAGES = ("route", "dispatch", "expert_up", "expert_down", "combine")
 
@@ -105,6 +105,11 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn_ex.restype = ctypes.c_int
         L.moe_expert_ffn_ex.argtypes = [_PP, _PO, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                         _P]
+        L.moe_backward_workspace_size.restype = ctypes.c_size_t
+        L.moe_backward_workspace_size.argtypes = [_PP]
+        L.moe_backward.restype = ctypes.c_int
+        L.moe_backward.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                   _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_forward_ex.restype = ctypes.c_int
         L.moe_forward_ex.argtypes = [_PP, _PO, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, ctypes.c_size_t, _P, _P]
@@ -239,6 +244,19 @@ def moe_forward_ex(p: Problem, o: Optional[Options], x, w_router, router_bias, w
                                 _ptr(expert_counts), _ptr(expert_offsets), _ptr(slot_row),
                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(stream), stage_events), "moe_forward_ex")
+
+
+def backward_workspace_size(p: Problem) -> int:
+    return int(lib().moe_backward_workspace_size(ctypes.byref(p.c())))
+
+
+def moe_backward(p: Problem, x, w_router, router_bias, w1, w3, w2, dout, d_aux: float, dx,
+                 dw_router, dbias, dw1, dw3, dw2, ws, stream=None):
+    _check(lib().moe_backward(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                              _ptr(w1), _ptr(w3), _ptr(w2), _ptr(dout), float(d_aux), _ptr(dx),
+                              _ptr(dw_router), _ptr(dbias), _ptr(dw1), _ptr(dw3), _ptr(dw2),
+                              _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)), "moe_backward")
 
 
 def moe_route(p: Problem, x, w_router, router_bias, expert_indices, gates, aux_loss,

@@ -449,4 +449,28 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_router
                         stream, nullptr);
 }
 
+size_t moe_backward_workspace_size(const moe_problem* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return backward_ws_bytes(internal(p));
+}
+
+moe_status moe_backward(const moe_problem* p, const void* x, const void* w_router,
+                        const float* router_bias, const void* w1, const void* w3, const void* w2,
+                        const void* dout, float d_aux, void* dx, float* dw_router, float* dbias,
+                        void* dw1, void* dw3, void* dw2, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!weights_ok(p, w1, w3, w2) || !(d_aux == d_aux)) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !w_router || !dout || !dx || !dw_router || !dw1)) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && p->kind == MOE_EXPERT_SWIGLU && !dw3) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && p->kind != MOE_EXPERT_LINEAR && !dw2) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  st = check_ws(ws, ws_bytes, backward_ws_bytes(q));
+  if (st != MOE_OK) return st;
+  if (q.T == 0) return MOE_OK;
+  return hip_status(launch_backward(q, x, w_router, router_bias, w1, w3, w2, dout, d_aux, dx,
+                                    dw_router, dbias, dw1, dw3, dw2, ws, stream));
+}
+
 }  // extern "C"

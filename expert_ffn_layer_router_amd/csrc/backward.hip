@@ -1,0 +1,746 @@
+// Backward of the layer: the gradients of L = sum(out * dout) + d_aux * aux_loss with respect
+// to x, the router (weights, bias) and every expert matrix. The routing decisions (top-k, the
+// drop set) are piecewise constant, so the gradient flows through the gates and through P in
+// the Switch loss; f, a count, has none ("Mixture of Experts: the Sparsely-Gated Layer", Hot
+// shards: a count has no gradient, a probability does). In reverse order of the forward:
+//  * combine:  dgate[t, j] = <dout[t], y[row]> for a kept slot (0 for a dropped one),
+//              dy[row] = gate[t, j] * dout[t];
+//  * experts:  dh = dy W2^T, then through the activation (ReLU: relu'(0) = 0; SwiGLU:
+//              silu'(a) = s (1 + a (1 - s)), s = sigmoid(a)); dx_rows = da W1^T (+ db W3^T);
+//              dW2 = h^T dy, dW1 = x^T da (, dW3 = x^T db), each over the expert's kept rows;
+//  * gates:    softmax over the k chosen logits: dl_c = g_c (dg_c - sum_c' g_c' dg_c');
+//  * loss:     aux = E sum_e f_e P_e, P_e = mean_t p[t, e]: dL/dp[t, e] = d_aux E f_e / T, then
+//              through the full softmax: dl[t, e] += p[t, e] (a_e - sum_j p[t, j] a_j);
+//  * router:   dW_router = x^T dl, dbias = sum_t dl, dx += dl W_router^T.
+// The forward quantities it needs (decisions, gates, logits, the experts' pre-activations and
+// outputs) are recomputed with the forward's own kernels, so the call needs only the inputs
+// and dout. Every reduction runs in a fixed order, so the result does not depend on
+// scheduling.
+//
+// GEMM shapes that the forward does not have get their own kernels (bf16: 128 x 128 tiles,
+// 2 x 2 waves of 64 x 64, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//  * NT, dgrad: C[r, n] = sum_k A[r, k] W_e[n, k] over each expert's rows r (the tile
+//    schedule from the offsets, as in the forward); the weights are read as (E, N, K), i.e.
+//    the forward's (in, out) matrices used transposed. Two (A, W) pairs can share one K loop
+//    (da W1^T + db W3^T).
+//  * TN, wgrad: C_e[m, n] = sum over expert e's rows r of A[r, m] B[r, n]; K is the expert's
+//    row count. Both operands are row-major with m / n contiguous, so both are transposed on
+//    their way into LDS (4 rows x 8 columns per thread, repacked in registers). A's rows can
+//    be gathered (token rows of x through the permutation).
+#include <algorithm>
+
+#include "common.hpp"
+#include "tile_schedule.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLds = kBK + 8;  // padded row stride (elements) of the LDS tiles
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+
+struct BwdGemm {
+  const void* A0;        // NT: (rows, K) row-major; TN: (rows, M) row-major (gathered)
+  const void* A1;        // NT: second A (same shape), or null
+  const void* W0;        // NT: (E, N, K) row-major
+  const void* W1;        // NT: second W, or null
+  const void* B;         // TN: (rows, N) row-major
+  const int32_t* gather; // TN: A row of r is gather[r] / gather_div (null: r)
+  int gather_div;
+  const int32_t* offsets;
+  int E;
+  int64_t K, M, N;       // NT: K and N (M = rows); TN: M and N (K = rows of the expert)
+  int64_t lda;           // row stride of A (elements)
+  void* C;               // NT: (rows, N); TN: (E, M, N)
+  int64_t max_rows;
+};
+
+template <typename OutT>
+__device__ __forceinline__ void store_out(OutT* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, int64_t i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, int64_t i, float v) {
+  p[i] = f32_to_bf16(v);
+}
+
+// 4 x 8 block (4 rows of 8 contiguous columns) -> LDS as 8 columns of 4 consecutive rows:
+// the transposed layout the MFMA operand wants (K values contiguous per column).
+__device__ __forceinline__ void store_transposed(const uint4 (&r)[4], uint16_t* s, int col8,
+                                                 int krow4) {
+  const uint32_t w0[4] = {r[0].x, r[0].y, r[0].z, r[0].w};
+  const uint32_t w1[4] = {r[1].x, r[1].y, r[1].z, r[1].w};
+  const uint32_t w2[4] = {r[2].x, r[2].y, r[2].z, r[2].w};
+  const uint32_t w3[4] = {r[3].x, r[3].y, r[3].z, r[3].w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t lo01 = lo16(w0[wi]) | (lo16(w1[wi]) << 16);
+    const uint32_t lo23 = lo16(w2[wi]) | (lo16(w3[wi]) << 16);
+    const uint32_t hi01 = hi16(w0[wi]) | (hi16(w1[wi]) << 16);
+    const uint32_t hi23 = hi16(w2[wi]) | (hi16(w3[wi]) << 16);
+    *(uint2*)&s[(8 * col8 + 2 * wi) * kLds + 4 * krow4] = make_uint2(lo01, lo23);
+    *(uint2*)&s[(8 * col8 + 2 * wi + 1) * kLds + 4 * krow4] = make_uint2(hi01, hi23);
+  }
+}
+
+// One 64-deep slice of MFMAs on the LDS tiles (2 x 2 tiles of 32 x 32 per wave).
+__device__ __forceinline__ void mfma_slice(const uint16_t* sA, const uint16_t* sB,
+                                           f32x16 (&acc)[2][2], int wm, int wn, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < kBK; kk += 16) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+      a[mi] = *(const bf16x8*)&sA[(wm * 64 + mi * 32 + (lane & 31)) * kLds + kk + (lane >> 5) * 8];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+      b[ni] = *(const bf16x8*)&sB[(wn * 64 + ni * 32 + (lane & 31)) * kLds + kk + (lane >> 5) * 8];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+// NT (dgrad): grid (M-tiles of all experts, N-tiles). NSEG pairs (A_s, W_s) over the same K.
+template <int NSEG, typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void nt_bf16_kernel(const BwdGemm g) {
+  __shared__ __align__(16) uint16_t sA[kBM * kLds];
+  __shared__ __align__(16) uint16_t sB[kBN * kLds];
+  int e, row0, rows;
+  if (!find_tile(g.offsets, g.E, kBM, (int)blockIdx.x, e, row0, rows)) return;
+  const int64_t K = g.K, N = g.N;
+  const int64_t n0 = (int64_t)blockIdx.y * kBN;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int wm = wv >> 1, wn = wv & 1;
+  const int kc = (tid & 7) * 8;  // this thread's 8 K-values within the slice
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    const uint16_t* A = (const uint16_t*)(sg ? g.A1 : g.A0);
+    const uint16_t* W = (const uint16_t*)(sg ? g.W1 : g.W0) + (int64_t)e * N * K;
+    const uint16_t* a_src[4];
+    const uint16_t* w_src[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = (tid >> 3) + 32 * p;
+      a_src[p] = r < rows ? A + (int64_t)(row0 + r) * g.lda : nullptr;
+      w_src[p] = n0 + r < N ? W + (n0 + r) * K : nullptr;
+    }
+    uint4 ra[4], rb[4];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const bool ok = k0 + kc < K;  // K % 8 == 0: a vector is all in or all out
+        ra[p] = (ok && a_src[p]) ? *(const uint4*)(a_src[p] + k0 + kc) : zero;
+        rb[p] = (ok && w_src[p]) ? *(const uint4*)(w_src[p] + k0 + kc) : zero;
+      }
+    };
+    load(0);
+    for (int64_t k0 = 0; k0 < K; k0 += kBK) {
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *(uint4*)&sA[((tid >> 3) + 32 * p) * kLds + kc] = ra[p];
+        *(uint4*)&sB[((tid >> 3) + 32 * p) * kLds + kc] = rb[p];
+      }
+      __syncthreads();
+      if (k0 + kBK < K) load(k0 + kBK);
+      mfma_slice(sA, sB, acc, wm, wn, lane);
+    }
+  }
+  OutT* C = (OutT*)g.C;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wm * 64 + mi * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int64_t col = n0 + wn * 64 + ni * 32 + (lane & 31);
+        if (r < rows && col < N) store_out<OutT>(C, (int64_t)(row0 + r) * N + col, acc[mi][ni][v]);
+      }
+}
+
+// TN (wgrad): grid (M-tiles, N-tiles, experts); K runs over the expert's rows.
+template <typename OutT>
+__global__ __launch_bounds__(kThreads, 2) void tn_bf16_kernel(const BwdGemm g) {
+  __shared__ __align__(16) uint16_t sA[kBM * kLds];
+  __shared__ __align__(16) uint16_t sB[kBN * kLds];
+  const int e = blockIdx.z;
+  const int64_t r0 = g.offsets[e], r1 = g.offsets[e + 1];
+  const int64_t M = g.M, N = g.N;
+  const int64_t m0 = (int64_t)blockIdx.x * kBM, n0 = (int64_t)blockIdx.y * kBN;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int wm = wv >> 1, wn = wv & 1;
+  const int kq = tid >> 4, c8 = tid & 15;  // 4 rows from 4 kq, 8 columns from 8 c8
+  const int64_t am = m0 + 8 * c8, bn = n0 + 8 * c8;
+  const bool a_ok = am < M, b_ok = bn < N;  // M, N % 8 == 0
+  const uint16_t* A = (const uint16_t*)g.A0;
+  const uint16_t* Bm = (const uint16_t*)g.B;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  uint4 ra[4], rb[4];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + k0 + 4 * kq + i;
+      const bool ok = r < r1;
+      int64_t src = r;
+      if (ok && g.gather) src = g.gather[r] / g.gather_div;
+      ra[i] = (ok && a_ok) ? *(const uint4*)(A + src * g.lda + am) : zero;
+      rb[i] = (ok && b_ok) ? *(const uint4*)(Bm + r * N + bn) : zero;
+    }
+  };
+  const int64_t K = r1 - r0;
+  if (K > 0) load(0);
+  for (int64_t k0 = 0; k0 < K; k0 += kBK) {
+    __syncthreads();
+    store_transposed(ra, sA, c8, kq);
+    store_transposed(rb, sB, c8, kq);
+    __syncthreads();
+    if (k0 + kBK < K) load(k0 + kBK);
+    mfma_slice(sA, sB, acc, wm, wn, lane);
+  }
+  OutT* C = (OutT*)g.C + (int64_t)e * M * N;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 64 + mi * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int64_t n = n0 + wn * 64 + ni * 32 + (lane & 31);
+        if (m < M && n < N) store_out<OutT>(C, m * N + n, acc[mi][ni][v]);
+      }
+}
+
+// float32 layers: one thread per output element, K in order (the fp32 layers are small).
+template <int NSEG>
+__global__ __launch_bounds__(kThreads) void nt_f32_kernel(const BwdGemm g) {
+  int e, row0, rows;
+  if (!find_tile(g.offsets, g.E, 16, (int)blockIdx.x, e, row0, rows)) return;
+  const int r = threadIdx.x / 16;
+  const int64_t n = (int64_t)blockIdx.y * 16 + (threadIdx.x % 16);
+  if (r >= rows || n >= g.N) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int sg = 0; sg < NSEG; ++sg) {
+    const float* a = (const float*)(sg ? g.A1 : g.A0) + (int64_t)(row0 + r) * g.lda;
+    const float* w = (const float*)(sg ? g.W1 : g.W0) + ((int64_t)e * g.N + n) * g.K;
+    for (int64_t k = 0; k < g.K; ++k) acc = fmaf(a[k], w[k], acc);
+  }
+  ((float*)g.C)[(int64_t)(row0 + r) * g.N + n] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void tn_f32_kernel(const BwdGemm g) {
+  const int e = blockIdx.z;
+  const int64_t m = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
+  const int64_t n = (int64_t)blockIdx.y * 16 + threadIdx.x % 16;
+  if (m >= g.M || n >= g.N) return;
+  float acc = 0.f;
+  for (int64_t r = g.offsets[e]; r < g.offsets[e + 1]; ++r) {
+    const int64_t src = g.gather ? g.gather[r] / g.gather_div : r;
+    acc = fmaf(((const float*)g.A0)[src * g.lda + m], ((const float*)g.B)[r * g.N + n], acc);
+  }
+  ((float*)g.C)[((int64_t)e * g.M + m) * g.N + n] = acc;
+}
+
+// ---- elementwise and reduction kernels ------------------------------------------------------
+
+// h = act(a, b) over the kept rows (rows from offsets[E] on are left alone).
+template <typename TIn>
+__global__ void act_forward_kernel(int64_t DH, int kind, const int32_t* __restrict__ offsets, int E,
+                                   const TIn* __restrict__ a, const TIn* __restrict__ b,
+                                   TIn* __restrict__ h) {
+  const int64_t n = (int64_t)offsets[E] * DH;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float av = load_as_f32(a, i);
+    float v;
+    if (kind == MOE_EXPERT_SWIGLU) {
+      v = av / (1.f + __expf(-av)) * load_as_f32(b, i);
+    } else {
+      v = fmaxf(av, 0.f);
+    }
+    store_from_f32(h, i, v);
+  }
+}
+
+// da (and db) from dh, a, b: SwiGLU da = dh b s (1 + a (1 - s)), db = dh a s; ReLU da = dh
+// (a > 0).
+template <typename TIn>
+__global__ void act_backward_kernel(int64_t DH, int kind, const int32_t* __restrict__ offsets,
+                                    int E, const TIn* __restrict__ a, const TIn* __restrict__ b,
+                                    const TIn* __restrict__ dh, TIn* __restrict__ da,
+                                    TIn* __restrict__ db) {
+  const int64_t n = (int64_t)offsets[E] * DH;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float av = load_as_f32(a, i), g = load_as_f32(dh, i);
+    if (kind == MOE_EXPERT_SWIGLU) {
+      const float bv = load_as_f32(b, i);
+      const float s = 1.f / (1.f + __expf(-av));
+      store_from_f32(da, i, g * bv * s * (1.f + av * (1.f - s)));
+      store_from_f32(db, i, g * av * s);
+    } else {
+      store_from_f32(da, i, av > 0.f ? g : 0.f);
+    }
+  }
+}
+
+// Combine backward, one wave per token: for each of its slots j, dgate = <dout_t, y[row]>
+// (float64 sum, lanes over columns then a fixed butterfly) and dy[row] = gate * dout_t, or
+// dgate = 0 for a dropped slot.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void combine_backward_kernel(
+    int64_t T, int k, int64_t Dout, const TIn* __restrict__ dout, const TIn* __restrict__ y,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ gates,
+    TIn* __restrict__ dy, float* __restrict__ dgates) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int64_t s = t * k + j;
+    const int row = slot_row[s];
+    double acc = 0.0;
+    if (row >= 0) {
+      const float g = gates[s];
+      for (int64_t c = lane; c < Dout; c += kWave) {
+        const float d = load_as_f32(dout, t * Dout + c);
+        acc += (double)d * (double)load_as_f32(y, (int64_t)row * Dout + c);
+        store_from_f32(dy, (int64_t)row * Dout + c, g * d);
+      }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) dgates[s] = (float)acc;
+  }
+}
+
+// Router backward, one wave per token (lane l holds experts l + 64 i): probabilities from the
+// float32 logits (float64 softmax), then dl over the chosen experts from the gates' softmax and
+// over all experts from the loss term.
+template <int EPL>
+__global__ __launch_bounds__(kThreads) void router_backward_kernel(
+    int64_t T, int E, int k, float d_aux, const float* __restrict__ logits,
+    const int32_t* __restrict__ idx, const float* __restrict__ gates,
+    const float* __restrict__ dgates, const int32_t* __restrict__ counts, float* __restrict__ dl) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (t >= T) return;
+  double p[EPL], a[EPL], d[EPL];
+  double m = -1e300;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    p[i] = e < E ? (double)logits[t * E + e] : -1e300;
+    m = fmax(m, p[i]);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    p[i] = e < E ? exp(p[i] - m) : 0.0;
+    s += p[i];
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  // loss term: a_e = d_aux * E * f_e / T with f_e = count_e / (T k)
+  double pa = 0.0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    p[i] /= s;
+    a[i] = e < E ? (double)d_aux * (double)E * ((double)counts[e] / ((double)T * k)) / (double)T
+                 : 0.0;
+    pa += p[i] * a[i];
+    d[i] = 0.0;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) pa += __shfl_xor(pa, o);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) d[i] = p[i] * (a[i] - pa);
+  // gates' softmax: dl_c = g_c (dg_c - sum g dg), added at the chosen experts
+  double sg = 0.0;
+  for (int j = 0; j < k; ++j) sg += (double)gates[t * k + j] * (double)dgates[t * k + j];
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    const double v = (double)gates[t * k + j] * ((double)dgates[t * k + j] - sg);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (e == lane + kWave * i) d[i] += v;
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) dl[t * E + e] = (float)d[i];
+  }
+}
+
+// dbias[e] = sum_t dl[t, e]: one block per expert, strided partial sums then a fixed tree.
+__global__ __launch_bounds__(256) void dbias_kernel(int64_t T, int E, const float* __restrict__ dl,
+                                                    float* __restrict__ dbias) {
+  __shared__ double s_part[256];
+  const int e = blockIdx.x;
+  double acc = 0.0;
+  for (int64_t t = threadIdx.x; t < T; t += 256) acc += (double)dl[t * E + e];
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if ((int)threadIdx.x < h) s_part[threadIdx.x] += s_part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dbias[e] = (float)s_part[0];
+}
+
+// dW_router[d, e] = sum_t x[t, d] dl[t, e]: block (64 columns d) x (16 experts), thread
+// (d, 4 experts), t in order.
+template <typename TIn>
+__global__ __launch_bounds__(256) void dw_router_kernel(int64_t T, int64_t D, int E,
+                                                        const TIn* __restrict__ x,
+                                                        const float* __restrict__ dl,
+                                                        float* __restrict__ dw) {
+  const int64_t d = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  const int e0 = blockIdx.y * 16 + 4 * (threadIdx.x >> 6);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (d < D) {
+    for (int64_t t = 0; t < T; ++t) {
+      const float xv = load_as_f32(x, t * D + d);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (e0 + q < E) acc[q] = fmaf(xv, dl[t * E + e0 + q], acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (e0 + q < E) dw[d * E + e0 + q] = acc[q];
+  }
+}
+
+// dx[t] = sum over the token's kept slots of dx_rows[row] (float32, ascending j) plus
+// sum_e dl[t, e] W_router[:, e]; one wave per token.
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void dx_kernel(int64_t T, int64_t D, int E, int k,
+                                                      const float* __restrict__ dxr,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ dl,
+                                                      const TIn* __restrict__ w_router,
+                                                      TIn* __restrict__ dx) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (t >= T) return;
+  for (int64_t c = lane; c < D; c += kWave) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int row = slot_row[t * k + j];
+      if (row >= 0) acc += dxr[(int64_t)row * D + c];
+    }
+    for (int e = 0; e < E; ++e) acc = fmaf(dl[t * E + e], load_as_f32(w_router, c * E + e), acc);
+    store_from_f32(dx, t * D + c, acc);
+  }
+}
+
+size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace
+
+// ---- scratch layout and the launch sequence ----------------------------------------------------
+
+struct BwdLayout {
+  size_t route, idx, gates, logits, aux, counts, offsets, perm, slot_row, blkc, lrank;
+  size_t a, b, h, y, dy, dh, da, db, dxr, dgates, dl, gsplit, gctr, total;
+};
+
+static BwdLayout bwd_layout(const Problem& q) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = a256(off + n);
+    return o;
+  };
+  const size_t es = q.dtype == MOE_BF16 ? 2 : 4;
+  const size_t R = (size_t)q.slots(), T = (size_t)q.T, E = (size_t)q.E;
+  const size_t DH = (size_t)(q.kind == MOE_EXPERT_LINEAR ? 0 : q.DH);
+  L.route = take(route_ws_bytes(q));
+  L.idx = take(R * 4);
+  L.gates = take(R * 4);
+  L.logits = take(T * E * 4);
+  L.aux = take(4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(R * 4);
+  L.slot_row = take(R * 4);
+  L.blkc = take((size_t)dispatch_blocks(q) * E * 4);
+  L.lrank = take(R * 4);
+  L.a = take(R * DH * es);
+  L.b = take(q.kind == MOE_EXPERT_SWIGLU ? R * DH * es : 0);
+  L.h = take(R * DH * es);
+  L.y = take(R * (size_t)q.D_out * es);
+  L.dy = take(R * (size_t)q.D_out * es);
+  L.dh = take(R * DH * es);
+  L.da = take(R * DH * es);
+  L.db = take(q.kind == MOE_EXPERT_SWIGLU ? R * DH * es : 0);
+  L.dxr = take(R * (size_t)q.D * 4);
+  L.dgates = take(R * 4);
+  L.dl = take(T * E * 4);
+  const bool split = q.dtype == MOE_BF16 && q.T > 0;
+  L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
+  L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
+  L.total = off;
+  return L;
+}
+
+size_t backward_ws_bytes(const Problem& q) { return bwd_layout(q).total; }
+
+namespace {
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+hipError_t nt(const Problem& q, const void* A0, const void* A1, const void* W0, const void* W1,
+              int64_t K, int64_t N, const int32_t* offsets, void* C, bool c_f32, hipStream_t s) {
+  BwdGemm g{};
+  g.A0 = A0;
+  g.A1 = A1;
+  g.W0 = W0;
+  g.W1 = W1;
+  g.offsets = offsets;
+  g.E = q.E;
+  g.K = K;
+  g.N = N;
+  g.lda = K;
+  g.C = C;
+  g.max_rows = q.slots();
+  if (q.dtype == MOE_BF16) {
+    const dim3 grid((unsigned)((g.max_rows + kBM - 1) / kBM + q.E), (unsigned)((N + kBN - 1) / kBN));
+    if (A1 && c_f32) hipLaunchKernelGGL((nt_bf16_kernel<2, float>), grid, dim3(kThreads), 0, s, g);
+    else if (A1) hipLaunchKernelGGL((nt_bf16_kernel<2, uint16_t>), grid, dim3(kThreads), 0, s, g);
+    else if (c_f32) hipLaunchKernelGGL((nt_bf16_kernel<1, float>), grid, dim3(kThreads), 0, s, g);
+    else hipLaunchKernelGGL((nt_bf16_kernel<1, uint16_t>), grid, dim3(kThreads), 0, s, g);
+  } else {
+    const dim3 grid((unsigned)((g.max_rows + 15) / 16 + q.E), (unsigned)((N + 15) / 16));
+    if (A1) hipLaunchKernelGGL(nt_f32_kernel<2>, grid, dim3(kThreads), 0, s, g);
+    else hipLaunchKernelGGL(nt_f32_kernel<1>, grid, dim3(kThreads), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t tn(const Problem& q, const void* A, int64_t lda, const int32_t* gather, int gather_div,
+              const void* B, int64_t M, int64_t N, const int32_t* offsets, void* C, hipStream_t s) {
+  BwdGemm g{};
+  g.A0 = A;
+  g.lda = lda;
+  g.gather = gather;
+  g.gather_div = gather_div;
+  g.B = B;
+  g.M = M;
+  g.N = N;
+  g.offsets = offsets;
+  g.E = q.E;
+  g.C = C;
+  if (q.dtype == MOE_BF16) {
+    const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((N + kBN - 1) / kBN), (unsigned)q.E);
+    hipLaunchKernelGGL(tn_bf16_kernel<uint16_t>, grid, dim3(kThreads), 0, s, g);
+  } else {
+    const dim3 grid((unsigned)((M + 15) / 16), (unsigned)((N + 15) / 16), (unsigned)q.E);
+    hipLaunchKernelGGL(tn_f32_kernel, grid, dim3(kThreads), 0, s, g);
+  }
+  return hipGetLastError();
+}
+
+// The forward GEMM A_rows -> C without an epilogue (to recompute pre-activations / outputs).
+hipError_t fwd_gemm(const Problem& q, const void* A, int64_t lda, const int32_t* gather,
+                    const void* W, int64_t K, int64_t N, const int32_t* offsets, void* C,
+                    float* split_ws, int32_t* split_ctr, int32_t* queue, int ncu, hipStream_t s) {
+  GroupedGemm g{};
+  g.A = A;
+  g.lda = lda;
+  g.a_gather = gather;
+  g.gather_div = q.top_k;
+  g.B0 = W;
+  g.B1 = nullptr;
+  g.C = C;
+  g.offsets = offsets;
+  g.E = q.E;
+  g.K = K;
+  g.N = N;
+  g.max_rows = q.slots();
+  g.epilogue = EPI_NONE;
+  g.dtype = q.dtype;
+  g.split_ws = split_ws;
+  g.split_ctr = split_ctr;
+  g.ncu = ncu;
+  g.queue = queue;
+  return launch_grouped_gemm(g, s);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Problem& q, const void* x, const void* w_router, const float* bias,
+                           const void* w1, const void* w3, const void* w2, const void* dout,
+                           float d_aux, void* dx, float* dw_router, float* dbias, void* dw1,
+                           void* dw3, void* dw2, void* ws, hipStream_t s) {
+  const BwdLayout L = bwd_layout(q);
+  const bool bf16 = q.dtype == MOE_BF16;
+  const bool linear = q.kind == MOE_EXPERT_LINEAR, swiglu = q.kind == MOE_EXPERT_SWIGLU;
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* gates = at<float>(ws, L.gates);
+  float* logits = at<float>(ws, L.logits);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* offsets = at<int32_t>(ws, L.offsets);
+  int32_t* perm = at<int32_t>(ws, L.perm);
+  int32_t* slot_row = at<int32_t>(ws, L.slot_row);
+  // 1. decisions, gates and logits, exactly as the forward takes them
+  hipError_t err = launch_route(q, x, w_router, bias, RouteOpts{}, idx, gates, logits, nullptr,
+                                at<void>(ws, L.route), s);
+  if (err == hipSuccess)
+    err = launch_aux_finalize(q, at<void>(ws, L.route), at<float>(ws, L.aux), nullptr, s);
+  // 2. dispatch (counts, offsets, permutation, slot rows); the scan also clears the GEMMs'
+  //    split tickets and work queue
+  float* split_ws = nullptr;
+  int32_t* split_ctr = nullptr;
+  int32_t* queue = nullptr;
+  const int ncu = bf16 ? device_split_cus() : 0;
+  if (bf16 && q.T > 0) {
+    int32_t* ctr = at<int32_t>(ws, L.gctr);
+    queue = ctr + kSplitSlots;
+    if (ncu > 0) {
+      split_ws = at<float>(ws, L.gsplit);
+      split_ctr = ctr;
+    }
+  }
+  if (err == hipSuccess)
+    err = launch_dispatch(q, idx, x, counts, offsets, perm, slot_row, nullptr,
+                          at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), s,
+                          queue ? at<int32_t>(ws, L.gctr) : nullptr,
+                          queue ? kSplitSlots + kQueueInts : 0);
+  if (q.T == 0) {
+    return err;  // nothing routed: the caller's outputs are empty or left as they are
+  }
+  const int64_t D = q.D, DH = q.DH, Do = q.D_out;
+  void* a = at<void>(ws, L.a);
+  void* b = at<void>(ws, L.b);
+  void* h = at<void>(ws, L.h);
+  void* y = at<void>(ws, L.y);
+  void* dy = at<void>(ws, L.dy);
+  void* dh = at<void>(ws, L.dh);
+  void* da = at<void>(ws, L.da);
+  void* db = at<void>(ws, L.db);
+  float* dxr = at<float>(ws, L.dxr);
+  float* dgates = at<float>(ws, L.dgates);
+  float* dl = at<float>(ws, L.dl);
+  const unsigned ew_grid = 2048;
+  // 3. the experts' forward quantities on the kept rows
+  if (linear) {
+    if (err == hipSuccess)
+      err = fwd_gemm(q, x, D, perm, w1, D, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
+  } else {
+    if (err == hipSuccess)
+      err = fwd_gemm(q, x, D, perm, w1, D, DH, offsets, a, split_ws, split_ctr, queue, ncu, s);
+    if (err == hipSuccess && swiglu)
+      err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_ctr, queue, ncu, s);
+    if (err == hipSuccess) {
+      if (bf16)
+        hipLaunchKernelGGL(act_forward_kernel<uint16_t>, dim3(ew_grid), dim3(256), 0, s, DH,
+                           q.kind, offsets, q.E, (const uint16_t*)a, (const uint16_t*)b,
+                           (uint16_t*)h);
+      else
+        hipLaunchKernelGGL(act_forward_kernel<float>, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
+                           offsets, q.E, (const float*)a, (const float*)b, (float*)h);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess)
+      err = fwd_gemm(q, h, DH, nullptr, w2, DH, Do, offsets, y, split_ws, split_ctr, queue, ncu,
+                     s);
+  }
+  // 4. combine backward: dy rows and dgates
+  if (err == hipSuccess) {
+    const unsigned grid = (unsigned)((q.T + 3) / 4);
+    if (bf16)
+      hipLaunchKernelGGL(combine_backward_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, q.T,
+                         q.top_k, Do, (const uint16_t*)dout, (const uint16_t*)y, slot_row, gates,
+                         (uint16_t*)dy, dgates);
+    else
+      hipLaunchKernelGGL(combine_backward_kernel<float>, dim3(grid), dim3(kThreads), 0, s, q.T,
+                         q.top_k, Do, (const float*)dout, (const float*)y, slot_row, gates,
+                         (float*)dy, dgates);
+    err = hipGetLastError();
+  }
+  // 5. experts backward
+  if (linear) {
+    if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, dy, D, Do, offsets, dw1, s);
+    if (err == hipSuccess) err = nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr, true, s);
+  } else {
+    if (err == hipSuccess) err = nt(q, dy, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s);
+    if (err == hipSuccess) err = tn(q, h, DH, nullptr, 1, dy, DH, Do, offsets, dw2, s);
+    if (err == hipSuccess) {
+      if (bf16)
+        hipLaunchKernelGGL(act_backward_kernel<uint16_t>, dim3(ew_grid), dim3(256), 0, s, DH,
+                           q.kind, offsets, q.E, (const uint16_t*)a, (const uint16_t*)b,
+                           (const uint16_t*)dh, (uint16_t*)da, (uint16_t*)db);
+      else
+        hipLaunchKernelGGL(act_backward_kernel<float>, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
+                           offsets, q.E, (const float*)a, (const float*)b, (const float*)dh,
+                           (float*)da, (float*)db);
+      err = hipGetLastError();
+    }
+    if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, da, D, DH, offsets, dw1, s);
+    if (err == hipSuccess && swiglu) err = tn(q, x, D, perm, q.top_k, db, D, DH, offsets, dw3, s);
+    if (err == hipSuccess)
+      err = nt(q, da, swiglu ? db : nullptr, w1, swiglu ? w3 : nullptr, DH, D, offsets, dxr, true,
+               s);
+  }
+  // 6. router backward, the router's gradients, and dx
+  if (err == hipSuccess) {
+    const unsigned grid = (unsigned)((q.T + 3) / 4);
+    const int epl = (q.E + kWave - 1) / kWave;
+    if (epl <= 1)
+      hipLaunchKernelGGL(router_backward_kernel<1>, dim3(grid), dim3(kThreads), 0, s, q.T, q.E,
+                         q.top_k, d_aux, logits, idx, gates, dgates, counts, dl);
+    else if (epl <= 2)
+      hipLaunchKernelGGL(router_backward_kernel<2>, dim3(grid), dim3(kThreads), 0, s, q.T, q.E,
+                         q.top_k, d_aux, logits, idx, gates, dgates, counts, dl);
+    else
+      hipLaunchKernelGGL(router_backward_kernel<4>, dim3(grid), dim3(kThreads), 0, s, q.T, q.E,
+                         q.top_k, d_aux, logits, idx, gates, dgates, counts, dl);
+    if (dbias) hipLaunchKernelGGL(dbias_kernel, dim3(q.E), dim3(256), 0, s, q.T, q.E, dl, dbias);
+    const dim3 wgrid((unsigned)((D + 63) / 64), (unsigned)((q.E + 15) / 16));
+    if (bf16) {
+      hipLaunchKernelGGL(dw_router_kernel<uint16_t>, wgrid, dim3(256), 0, s, q.T, D, q.E,
+                         (const uint16_t*)x, dl, dw_router);
+      hipLaunchKernelGGL(dx_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
+                         q.top_k, dxr, slot_row, dl, (const uint16_t*)w_router, (uint16_t*)dx);
+    } else {
+      hipLaunchKernelGGL(dw_router_kernel<float>, wgrid, dim3(256), 0, s, q.T, D, q.E,
+                         (const float*)x, dl, dw_router);
+      hipLaunchKernelGGL(dx_kernel<float>, dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
+                         q.top_k, dxr, slot_row, dl, (const float*)w_router, (float*)dx);
+    }
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace moe

@@ -98,6 +98,13 @@ hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
                            hipStream_t s, int32_t* zero = nullptr, int nzero = 0,
                            int32_t* pad_offsets = nullptr);
 
+// Backward of the layer (backward.hip): workspace bytes and the launch sequence.
+size_t backward_ws_bytes(const Problem& q);
+hipError_t launch_backward(const Problem& q, const void* x, const void* w_router, const float* bias,
+                           const void* w1, const void* w3, const void* w2, const void* dout,
+                           float d_aux, void* dx, float* dw_router, float* dbias, void* dw1,
+                           void* dw3, void* dw2, void* ws, hipStream_t s);
+
 // Grouped expert GEMM over expert-ordered rows.
 enum Epilogue { EPI_NONE = 0, EPI_RELU = 1, EPI_SWIGLU = 2 };
 struct GroupedGemm {

@@ -255,6 +255,29 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
                           int32_t* expert_offsets, int32_t* slot_row, void* ws, size_t ws_bytes,
                           hipStream_t stream, hipEvent_t* stage_events);
 
+/* ---- Backward -------------------------------------------------------------------------------
+ * Gradients of L = sum(out * dout) + d_aux * aux_loss for the layer of moe_forward (no router
+ * noise, renormalised gates), by the chain rule through its steps in reverse. The routing
+ * decisions and the drop set are piecewise constant, so the gradient flows through the gates
+ * and through P in the Switch loss; f, a count, has none (Sparsely-Gated Layer page, "Hot
+ * shards": a count has no gradient, a probability does). relu'(0) is taken as 0; silu'(z) =
+ * s (1 + z (1 - s)) with s = sigmoid(z).
+ *   Inputs: x, w_router, router_bias (nullable), w1, w3, w2 as in moe_forward; dout (T, D_out)
+ *   in p->dtype; d_aux (host) the weight of the Switch loss in L.
+ *   Outputs (overwritten): dx (T, D) and dw1, dw3 (SwiGLU only, else NULL), dw2 (not LINEAR,
+ *   else NULL) in p->dtype with the weights' shapes; dw_router (D, E) float32; dbias (E)
+ *   float32 or NULL. An expert that kept no token gets a zero gradient.
+ *   The call recomputes the forward quantities it needs (routing, dispatch, the experts'
+ *   pre-activations and outputs) with the forward's kernels; it needs no saved state.
+ *   Workspace: moe_backward_workspace_size bytes. With T = 0 nothing is written. */
+size_t moe_backward_workspace_size(const moe_problem* p);
+
+moe_status moe_backward(const moe_problem* p, const void* x, const void* w_router,
+                        const float* router_bias, const void* w1, const void* w3, const void* w2,
+                        const void* dout, float d_aux, void* dx, float* dw_router, float* dbias,
+                        void* dw1, void* dw3, void* dw2, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -324,7 +324,8 @@ def expert_backward(kind: str, xr: np.ndarray, dy: np.ndarray, w1, w2=None, w3=N
 
 
 def moe_backward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=None,
-                 capacity_factor: float = 0.0, dout=None, d_aux: float = 0.0) -> dict:
+                 capacity_factor: float = 0.0, dout=None, d_aux: float = 0.0,
+                 tokens: Optional[Sequence[int]] = None) -> dict:
     """Gradients of L = sum(out * dout) + d_aux * aux_loss with respect to x, the router
     (weights and bias) and every expert matrix, for the layer of moe_forward (no router
     noise, renormalised gates).
@@ -335,9 +336,13 @@ def moe_backward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=
     In reverse order: the combine gives dL/dgate = <dout_t, y_e(x_t)> for a kept slot (0 for
     a dropped one) and dL/dy = gate * dout_t; each expert's backward on its kept rows; the
     gates' softmax over the k chosen logits; the loss through P_e = mean_t probs[t, e] and
-    the full softmax; the router product logits = x @ W_router + bias."""
+    the full softmax; the router product logits = x @ W_router + bias.
+
+    ``tokens`` restricts the work to those tokens' rows: their dx, dgates and dlogits rows
+    are exact (routing, drops and f still cover every token) and every other row is zero;
+    the weight gradients then hold only those tokens' share."""
     r = moe_forward(x, w_router, top_k, kind, w1, w2, w3, bias=bias,
-                    capacity_factor=capacity_factor)
+                    capacity_factor=capacity_factor, tokens=tokens)
     x = _f64(x)
     T, D = x.shape
     E = np.asarray(w_router).shape[1]
@@ -349,8 +354,13 @@ def moe_backward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=
     dw2 = None if w2 is None else np.zeros(np.asarray(w2).shape)
     dw3 = None if w3 is None else np.zeros(np.asarray(w3).shape)
     flat_gates = gates.reshape(-1)
+    want = np.ones(T, dtype=bool)
+    if tokens is not None:
+        want = np.zeros(T, dtype=bool)
+        want[np.asarray(tokens, dtype=np.int64)] = True
     for e in range(E):
         rows = r["perm"][r["offsets"][e]:r["offsets"][e + 1]]  # kept slot ids of e
+        rows = rows[want[rows // top_k]]
         if rows.size == 0:
             continue
         t = rows // top_k
@@ -373,6 +383,7 @@ def moe_backward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=
         f = np.bincount(idx.ravel(), minlength=E) / (T * top_k)
         a = d_aux * E * f / T
         dl += probs * (a[None, :] - (probs * a[None, :]).sum(axis=1, keepdims=True))
+    dl[~want] = 0.0
     dw_router = x.T @ dl
     dbias = dl.sum(axis=0)
     dx += dl @ _f64(w_router).T

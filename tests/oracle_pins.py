@@ -578,6 +578,26 @@ def pin_backward_closed_forms():
         assert np.allclose(g["dw1"][e], want, rtol=1e-12, atol=1e-12)
 
 
+def pin_backward_token_subset():
+    """Restricted to a token subset, the backward gives those tokens' dx, dgates and dlogits
+    rows exactly as the full one (the routing, drops and loss counts still cover all)."""
+    r_ = _rng(61)
+    T, D, DH, E, k = 12, 5, 4, 4, 2
+    x, w = r_.standard_normal((T, D)), r_.standard_normal((D, E))
+    w1, w3, w2 = (r_.standard_normal((E, D, DH)), r_.standard_normal((E, D, DH)),
+                  r_.standard_normal((E, DH, 3)))
+    dout = r_.standard_normal((T, 3))
+    full = O.moe_backward(x, w, k, "swiglu", w1, w2, w3, capacity_factor=0.7, dout=dout,
+                          d_aux=0.4)
+    sub = [0, 3, 4, 10]
+    part = O.moe_backward(x, w, k, "swiglu", w1, w2, w3, capacity_factor=0.7, dout=dout,
+                          d_aux=0.4, tokens=sub)
+    for name in ("dx", "dgates", "dlogits"):
+        assert np.allclose(part[name][sub], full[name][sub], rtol=1e-13, atol=1e-13), name
+        rest = np.setdiff1d(np.arange(T), sub)
+        assert (part[name][rest] == 0).all(), name
+
+
 def pin_silu_grad():
     """silu'(0) = 1/2, the asymptotes 1 and 0, and central differences of silu."""
     assert O.silu_grad(0.0) == 0.5
