@@ -141,6 +141,8 @@ def main() -> int:
                     help="gates = the chosen experts' probabilities")
     ap.add_argument("--padded", action="store_true",
                     help="capacity-padded expert batches (needs a capacity factor)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + moe_backward per step (a training step of the layer)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -179,7 +181,37 @@ def main() -> int:
                          renormalise=not args.no_renormalise, padded=args.padded,
                          importance_loss=importance)
     ws = B.alloc_workspace(p, o=opts)
+    bwd = None
+    if args.backward:
+        if options:
+            print("--backward runs the plain layer (no router options)", file=sys.stderr)
+            return 2
+        dt = torch.bfloat16 if sp.dtype == "bf16" else torch.float32
+        gen = torch.Generator(device="cuda").manual_seed(args.seed + 1)
+        bwd = dict(
+            dout=torch.randn((sp.T, sp.D_out), generator=gen, device="cuda").to(dt),
+            dx=torch.empty((sp.T, sp.D), dtype=dt, device="cuda"),
+            dwr=torch.empty((sp.D, sp.E), dtype=torch.float32, device="cuda"),
+            db=torch.empty((sp.E,), dtype=torch.float32, device="cuda"),
+            dw1=torch.empty_like(dev["w1"]),
+            dw3=None if dev["w3"] is None else torch.empty_like(dev["w3"]),
+            dw2=None if dev["w2"] is None else torch.empty_like(dev["w2"]),
+            ws=torch.empty(max(B.backward_workspace_size(p), 1), dtype=torch.uint8,
+                           device="cuda"),
+            ev=[], )
     torch.cuda.synchronize()
+
+    def backward_step(timed=False):
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        B.moe_backward(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"], dev["w2"],
+                       bwd["dout"], 0.01, bwd["dx"], bwd["dwr"], bwd["db"], bwd["dw1"],
+                       bwd["dw3"], bwd["dw2"], bwd["ws"])
+        if timed:
+            e1.record()
+            bwd["ev"].append((e0, e1))
 
     def step(ev=None):
         if opts is None:
@@ -197,6 +229,8 @@ def main() -> int:
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
+        if bwd is not None:
+            backward_step()
     torch.cuda.synchronize()
     # Timed steps: the up-projection GEMM (the roofline kernel) carries events recorded by its
     # own kernel dispatch, so it is timed live in these steps at the least cost to the stream.
@@ -208,6 +242,8 @@ def main() -> int:
     start.record()
     for i in range(args.steps):
         step(events[i])
+        if bwd is not None:
+            backward_step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
@@ -219,6 +255,8 @@ def main() -> int:
     extra = [B.StageEvents() for _ in range(min(args.steps, 5))]
     for e in extra:
         step(e)
+        if bwd is not None:
+            backward_step(timed=True)
     torch.cuda.synchronize()
     for k in ("route", "dispatch", "expert_down", "combine"):
         stage_ms[k] = float(np.mean([e.elapsed_ms()[k] for e in extra]))
@@ -303,6 +341,16 @@ def main() -> int:
     }
     if importance is not None:
         result["importance_loss"] = float(importance.cpu()[0])
+    if bwd is not None:
+        bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd["ev"]]))
+        bwd_flops = 2 * (up_flops + down_flops)  # dgrad + wgrad of every expert GEMM
+        result["metric"] = "MoE layer forward+backward tokens/s at 1 MI355X"
+        result["config"]["workload"] += ", forward and backward"
+        stages["backward"] = {"us": bwd_ms * 1e3, "TFLOP/s": tf(bwd_flops, bwd_ms),
+                              "mfma_frac": tf(bwd_flops, bwd_ms) / peak_tf,
+                              "algorithmic_flops": bwd_flops,
+                              "note": "dgrad + wgrad of the expert GEMMs; the recomputed "
+                                      "forward inside the call is not counted"}
     if not args.no_cpu_baseline:
         n = min(args.cpu_baseline_tokens, T) if args.cpu_baseline_tokens > 0 else T
         log(f"[bench] CPU oracle baseline on {n} tokens")

@@ -436,11 +436,12 @@ __global__ __launch_bounds__(256) void dw_router_kernel(int64_t T, int64_t D, in
   }
 }
 
-// dx[t] = sum over the token's kept slots of dx_rows[row] (float32, ascending j) plus
-// sum_e dl[t, e] W_router[:, e]; one wave per token.
-template <typename TIn>
+// dx[t] = sum over the token's kept slots of the dx rows (dxr1, plus dxr2 when non-null;
+// float32 sums, ascending j) plus sum_e dl[t, e] W_router[:, e]; one wave per token.
+template <typename TIn, typename TR>
 __global__ __launch_bounds__(kThreads) void dx_kernel(int64_t T, int64_t D, int E, int k,
-                                                      const float* __restrict__ dxr,
+                                                      const TR* __restrict__ dxr1,
+                                                      const TR* __restrict__ dxr2,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ dl,
                                                       const TIn* __restrict__ w_router,
@@ -452,7 +453,10 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(int64_t T, int64_t D, int 
     float acc = 0.f;
     for (int j = 0; j < k; ++j) {
       const int row = slot_row[t * k + j];
-      if (row >= 0) acc += dxr[(int64_t)row * D + c];
+      if (row >= 0) {
+        acc += load_as_f32(dxr1, (int64_t)row * D + c);
+        if (dxr2) acc += load_as_f32(dxr2, (int64_t)row * D + c);
+      }
     }
     for (int e = 0; e < E; ++e) acc = fmaf(dl[t * E + e], load_as_f32(w_router, c * E + e), acc);
     store_from_f32(dx, t * D + c, acc);
@@ -519,8 +523,40 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+struct GemmRes {
+  float* split_ws;
+  int32_t* split_ctr;
+  int32_t* queue;
+  int ncu;
+};
+
 hipError_t nt(const Problem& q, const void* A0, const void* A1, const void* W0, const void* W1,
-              int64_t K, int64_t N, const int32_t* offsets, void* C, bool c_f32, hipStream_t s) {
+              int64_t K, int64_t N, const int32_t* offsets, void* C, bool c_f32, hipStream_t s,
+              const GemmRes& res) {
+  if (q.dtype == MOE_BF16 && !A1 && !c_f32 && K % 128 == 0 && res.queue) {
+    // the forward's 256 x 256 pipeline, reading the weight K-major
+    GroupedGemm f{};
+    f.A = A0;
+    f.lda = K;
+    f.a_gather = nullptr;
+    f.gather_div = 1;
+    f.B0 = W0;
+    f.B1 = nullptr;
+    f.C = C;
+    f.offsets = offsets;
+    f.E = q.E;
+    f.K = K;
+    f.N = N;
+    f.max_rows = q.slots();
+    f.epilogue = EPI_NONE;
+    f.dtype = q.dtype;
+    f.split_ws = res.split_ws;
+    f.split_ctr = res.split_ctr;
+    f.queue = res.queue;
+    f.ncu = res.ncu;
+    f.b_kmajor = true;
+    return launch_grouped_gemm(f, s);
+  }
   BwdGemm g{};
   g.A0 = A0;
   g.A1 = A1;
@@ -631,6 +667,7 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
       split_ctr = ctr;
     }
   }
+  const GemmRes res{split_ws, split_ctr, queue, ncu};
   if (err == hipSuccess)
     err = launch_dispatch(q, idx, x, counts, offsets, perm, slot_row, nullptr,
                           at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), s,
@@ -648,7 +685,11 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   void* dh = at<void>(ws, L.dh);
   void* da = at<void>(ws, L.da);
   void* db = at<void>(ws, L.db);
+  // dx rows: float32 for float32 layers (both halves in one product); two bf16 halves
+  // (da W1^T and db W3^T) for bf16 layers, added in the dx kernel
   float* dxr = at<float>(ws, L.dxr);
+  uint16_t* dxr1 = at<uint16_t>(ws, L.dxr);
+  uint16_t* dxr2 = dxr1 + (size_t)q.slots() * q.D;
   float* dgates = at<float>(ws, L.dgates);
   float* dl = at<float>(ws, L.dl);
   const unsigned ew_grid = 2048;
@@ -691,9 +732,11 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   // 5. experts backward
   if (linear) {
     if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, dy, D, Do, offsets, dw1, s);
-    if (err == hipSuccess) err = nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr, true, s);
+    if (err == hipSuccess)
+      err = bf16 ? nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr1, false, s, res)
+                 : nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr, true, s, res);
   } else {
-    if (err == hipSuccess) err = nt(q, dy, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s);
+    if (err == hipSuccess) err = nt(q, dy, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s, res);
     if (err == hipSuccess) err = tn(q, h, DH, nullptr, 1, dy, DH, Do, offsets, dw2, s);
     if (err == hipSuccess) {
       if (bf16)
@@ -708,9 +751,14 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
     }
     if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, da, D, DH, offsets, dw1, s);
     if (err == hipSuccess && swiglu) err = tn(q, x, D, perm, q.top_k, db, D, DH, offsets, dw3, s);
-    if (err == hipSuccess)
+    if (bf16) {
+      if (err == hipSuccess) err = nt(q, da, nullptr, w1, nullptr, DH, D, offsets, dxr1, false, s, res);
+      if (err == hipSuccess && swiglu)
+        err = nt(q, db, nullptr, w3, nullptr, DH, D, offsets, dxr2, false, s, res);
+    } else if (err == hipSuccess) {
       err = nt(q, da, swiglu ? db : nullptr, w1, swiglu ? w3 : nullptr, DH, D, offsets, dxr, true,
-               s);
+               s, res);
+    }
   }
   // 6. router backward, the router's gradients, and dx
   if (err == hipSuccess) {
@@ -730,13 +778,16 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
     if (bf16) {
       hipLaunchKernelGGL(dw_router_kernel<uint16_t>, wgrid, dim3(256), 0, s, q.T, D, q.E,
                          (const uint16_t*)x, dl, dw_router);
-      hipLaunchKernelGGL(dx_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
-                         q.top_k, dxr, slot_row, dl, (const uint16_t*)w_router, (uint16_t*)dx);
+      hipLaunchKernelGGL((dx_kernel<uint16_t, uint16_t>), dim3(grid), dim3(kThreads), 0, s, q.T, D,
+                         q.E, q.top_k, (const uint16_t*)dxr1,
+                         (const uint16_t*)(swiglu ? dxr2 : nullptr), slot_row, dl,
+                         (const uint16_t*)w_router, (uint16_t*)dx);
     } else {
       hipLaunchKernelGGL(dw_router_kernel<float>, wgrid, dim3(256), 0, s, q.T, D, q.E,
                          (const float*)x, dl, dw_router);
-      hipLaunchKernelGGL(dx_kernel<float>, dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
-                         q.top_k, dxr, slot_row, dl, (const float*)w_router, (float*)dx);
+      hipLaunchKernelGGL((dx_kernel<float, float>), dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
+                         q.top_k, (const float*)dxr, (const float*)nullptr, slot_row, dl,
+                         (const float*)w_router, (float*)dx);
     }
     err = hipGetLastError();
   }

@@ -133,6 +133,9 @@ struct GroupedGemm {
   // Optional (null: none): events that bracket the GEMM kernel itself (recorded by its
   // dispatch where the kernel supports that, else recorded on the stream around it).
   hipEvent_t ev_start, ev_stop;
+  // B0 stored K-major, (E, N, K) row-major (a forward weight used transposed, for the
+  // backward's dgrad). Only with EPI_NONE and the 256 x 256 kernel (bf16, K % 128 == 0).
+  bool b_kmajor;
 };
 constexpr int kSplitSlots = 256;
 constexpr int kQueueInts = 16;

@@ -260,7 +260,9 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const GroupedGemm g)
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {
   if (g.max_rows <= 0 || g.N <= 0) return hipSuccess;
   // the 256 x 256 kernel needs K % 128 == 0; other bf16 shapes take the 128 x 128 kernel
-  if (g.dtype == MOE_BF16 && g.K % 128 == 0 && g.queue) return launch_grouped_gemm_bf16_256(g, s);
+  const bool k256 = g.dtype == MOE_BF16 && g.K % 128 == 0 && g.queue;
+  if (g.b_kmajor && (!k256 || g.epilogue != EPI_NONE)) return hipErrorInvalidValue;
+  if (k256) return launch_grouped_gemm_bf16_256(g, s);
   if (g.ev_start) hipEventRecord(g.ev_start, s);
   if (g.dtype == MOE_BF16) {
     const int64_t mt = (g.max_rows + kBM - 1) / kBM + g.E;

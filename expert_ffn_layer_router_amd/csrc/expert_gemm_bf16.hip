@@ -93,24 +93,34 @@ __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "
 
 struct Loader {
   const char* a[4];  // A source of this lane for instruction j, at K = 0
+  const char* bt[4]; // K-major B (the transposed-weight mode): like a[], rows are columns
   const char* b[2];  // B source of this lane for instructions with j % 2 == q, at K-row 0
   int64_t b_row_bytes;
 };
 
 // Load d (0..7) of this wave for a stage at K offset k0 into the buffer at LDS byte address
 // sa: even d -> A instruction d / 2 (16 rows), odd d -> B instruction d / 2 (2 K-rows).
+// With BT (B stored K-major, (N, K) per expert), B's stage is laid out and loaded exactly like
+// A's: 256 columns x 32 K, 64 bytes a column, an instruction fills 16 columns.
+template <bool BT>
 __device__ __forceinline__ void load_one(const Loader& ld, int64_t k0, int64_t bk, uint32_t sa,
                                          int wv, int d) {
   const int j = d >> 1;
-  if (d & 1)
-    dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes, sa + kHalf + (4 * wv + j) * 1024);
-  else
+  if (d & 1) {
+    if (BT)
+      dma16(ld.bt[j] + k0 * 2, sa + kHalf + (4 * wv + j) * 1024);
+    else
+      dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes,
+            sa + kHalf + (4 * wv + j) * 1024);
+  } else {
     dma16(ld.a[j] + k0 * 2, sa + (4 * wv + j) * 1024);
+  }
 }
+template <bool BT>
 __device__ __forceinline__ void load_stage(const Loader& ld, int64_t k0, uint32_t sa, int wv) {
   const int64_t bk = k0 * ld.b_row_bytes;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) load_one(ld, k0, bk, sa, wv, d);
+  for (int d = 0; d < 8; ++d) load_one<BT>(ld, k0, bk, sa, wv, d);
 }
 
 typedef __attribute__((address_space(3))) const char lds_cchar;
@@ -123,6 +133,15 @@ __device__ __forceinline__ bf16x8 read_b(const uint32_t (&bb)[4], int c, int t) 
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * 512));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// K-major B operand (BT) of column tile c, k-step t: read like A, from bases bb[t].
+__device__ __forceinline__ bf16x8 read_bt(const uint32_t (&bb)[4], int c, int t) {
+  return *(const lds_bf16x8*)((lds_cchar*)(uintptr_t)bb[t] + c * 32 * 64);
+}
+template <bool BT>
+__device__ __forceinline__ bf16x8 read_b_any(const uint32_t (&bb)[4], int c, int t) {
+  return BT ? read_bt(bb, c, t) : read_b(bb, c, t);
 }
 
 // A operand of m-tile mi, k-step t: row 64 w + 32 mi + lane % 32, K values 16t + 8 (lane/32)..
@@ -139,7 +158,7 @@ __device__ __forceinline__ bf16x8 read_a(const uint32_t (&ab)[2], int mi, int t)
 // operands are read and, when `load2`, the loads of the stage at K offset k2 are issued into
 // the current buffer, which no wave reads any more. The matrix pipe is thus never left
 // waiting for a whole LDS round trip at a stage boundary.
-template <int NN>
+template <int NN, bool BT>
 __device__ __forceinline__ void stage(const uint32_t (&ab)[2], const uint32_t (&bb)[4],
                                       const uint32_t (&abn)[2], const uint32_t (&bbn)[4],
                                       f32x16 (&acc)[2][8], bf16x8& a0, bf16x8& a1, bf16x8 (&b)[8],
@@ -152,7 +171,7 @@ __device__ __forceinline__ void stage(const uint32_t (&ab)[2], const uint32_t (&
     for (int c = 0; c < NN; ++c) {
       acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
       acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
-      b[c] = read_b(bb, c, 1);
+      b[c] = read_b_any<BT>(bb, c, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     a0 = n0;
@@ -168,10 +187,10 @@ __device__ __forceinline__ void stage(const uint32_t (&ab)[2], const uint32_t (&
   for (int c = 0; c < NN; ++c) {
     acc[0][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b[c], acc[0][c], 0, 0, 0);
     acc[1][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b[c], acc[1][c], 0, 0, 0);
-    b[c] = read_b(bbn, c, 0);
+    b[c] = read_b_any<BT>(bbn, c, 0);
     if (load2) {
 #pragma unroll
-      for (int d = c * (8 / NN); d < (c + 1) * (8 / NN); ++d) load_one(ld, k2, bk, sa, wv, d);
+      for (int d = c * (8 / NN); d < (c + 1) * (8 / NN); ++d) load_one<BT>(ld, k2, bk, sa, wv, d);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -194,7 +213,7 @@ template <int NN>
 __device__ __forceinline__ int wave_col_tile0(int wv) {
   return NN == 8 ? 0 : NN == 4 ? 4 * (wv >> 1) : 2 * wv;
 }
-template <int NN>
+template <int NN, bool BT>
 __device__ __forceinline__ void unit_bases(uint32_t lds_a, uint32_t lds_b, const uint32_t (&aoff)[2],
                                            const uint32_t (&boff)[4], int wv, uint32_t (&ab)[2],
                                            uint32_t (&bb)[4]) {
@@ -211,6 +230,13 @@ __device__ __forceinline__ void unit_bases(uint32_t lds_a, uint32_t lds_b, const
     const int q = (c0 + i) & 3;
     bb[i] = lds_b + (q == 0 ? boff[0] : q == 1 ? boff[1] : q == 2 ? boff[2] : boff[3]) + bhi;
     asm volatile("" : "+v"(bb[i]));
+  }
+  if (BT) {  // K-major B: A's offsets, from the wave's first column tile (32 columns of 64 B)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bb[t] = lds_b + aoff[t] + (uint32_t)c0 * 32u * 64u;
+      asm volatile("" : "+v"(bb[t]));
+    }
   }
 }
 
@@ -241,9 +267,10 @@ __device__ __forceinline__ float swap_adjacent_lanes(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
 }
 
-template <int EPI>
+template <int EPI, bool BT = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const GroupedGemm g, int nt) {
   constexpr bool kSwiGLU = EPI == EPI_SWIGLU;
+  static_assert(!BT || EPI == EPI_NONE, "the K-major B mode has no epilogue");
   __shared__ __align__(16) char sbuf[kNBuf * kBuf];
   __shared__ int s_unit[2];  // work positions of later units, by unit parity
   __shared__ int s_last;
@@ -389,6 +416,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       const int krow = 8 * wv + (lane >> 5);
       ld.b[q] = (const char*)(Wm + (int64_t)u.e * K * N + (int64_t)krow * N + (col < N ? col : 0));
     }
+    if (BT) {
+      // K-major B ((N, K) per expert): instruction j of wave w fills columns 16 (4w + j) +
+      // lane / 4 like A's rows (columns past N read column 0; their outputs are never stored)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t col = n0 + 16 * (4 * wv + j) + (lane >> 2);
+        const int c = (lane & 3) ^ ((lane >> 4) & 3);
+        ld.bt[j] = (const char*)((const uint16_t*)g.B0 +
+                                 ((int64_t)u.e * N + (col < N ? col : 0)) * K + 8 * c);
+      }
+    }
     return ld;
   };
 
@@ -427,7 +465,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     // The first unit's first kNBuf stages; every later unit's are loaded by the last kNBuf
     // stages of the unit before it.
 #pragma unroll
-    for (int q = 0; q < kNBuf; ++q) load_stage(ld, cu.kbeg + (int64_t)q * kBK, lbase + q * kBuf, wv);
+    for (int q = 0; q < kNBuf; ++q)
+      load_stage<BT>(ld, cu.kbeg + (int64_t)q * kBK, lbase + q * kBuf, wv);
 
     uint16_t* C = (uint16_t*)g.C;
     for (int i = 0;; ++i) {
@@ -465,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       auto run = [&](auto nn_tag) {
         constexpr int NN = decltype(nn_tag)::value;
         uint32_t vab[2], vbb[4];  // read bases in buffer 0
-        unit_bases<NN>(lbase, lbase + kHalf, aoff, boff, wv, vab, vbb);
+        unit_bases<NN, BT>(lbase, lbase + kHalf, aoff, boff, wv, vab, vbb);
         uint32_t ab[2], bb[4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) ab[t] = vab[t] + co;
@@ -473,7 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         for (int c = 0; c < 4; ++c) bb[c] = vbb[c] + co;
         bf16x8 a0 = read_a(ab, 0, 0), a1 = read_a(ab, 1, 0), bq[8];
 #pragma unroll
-        for (int c = 0; c < NN; ++c) bq[c] = read_b(bb, c, 0);
+        for (int c = 0; c < NN; ++c) bq[c] = read_b_any<BT>(bb, c, 0);
         const int nst = cu.nst;
         const int64_t kbeg = cu.kbeg;
         // One stage on buffer co (the next one is no): loads through loader LDR of the stage
@@ -488,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     uint32_t abn[2], bbn[4];                                                                \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) abn[t] = vab[t] + no;                     \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) bbn[c] = vbb[c] + no;                     \
-    stage<NN>(ab, bb, abn, bbn, acc, a0, a1, bq, LDR, KL, LOAD, lbase + co, wv, KEEP);      \
+    stage<NN, BT>(ab, bb, abn, bbn, acc, a0, a1, bq, LDR, KL, LOAD, lbase + co, wv, KEEP);  \
     co = no;                                                                                \
     _Pragma("unroll") for (int t = 0; t < 2; ++t) ab[t] = abn[t];                           \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) bb[c] = bbn[c];                           \
@@ -704,6 +743,11 @@ hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) 
   const dim3 grid((unsigned)G);
   // The start/stop events (if any) are recorded by the kernel's own dispatch, so timing adds
   // no packets, and no gaps, to the stream.
+  if (g.b_kmajor) {
+    hipExtLaunchKernelGGL((gemm_bf16_256_kernel<EPI_NONE, true>), grid, dim3(kThreads), 0, s,
+                          g.ev_start, g.ev_stop, 0, g, (int)nt);
+    return hipGetLastError();
+  }
   switch (g.epilogue) {
     case EPI_NONE:
       hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_NONE>, grid, dim3(kThreads), 0, s,
