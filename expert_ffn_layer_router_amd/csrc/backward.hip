@@ -413,27 +413,140 @@ __global__ __launch_bounds__(256) void dbias_kernel(int64_t T, int E, const floa
   if (threadIdx.x == 0) dbias[e] = (float)s_part[0];
 }
 
-// dW_router[d, e] = sum_t x[t, d] dl[t, e]: block (64 columns d) x (16 experts), thread
-// (d, 4 experts), t in order.
+// dW_router[d, e] = sum_t x[t, d] dl[t, e] in two fixed-order levels: block (256 columns d,
+// 8 experts, token chunk c) sums its chunk's tokens in order into part[c, d, e]; then
+// dw_router_reduce adds the chunks in order.
 template <typename TIn>
-__global__ __launch_bounds__(256) void dw_router_kernel(int64_t T, int64_t D, int E,
-                                                        const TIn* __restrict__ x,
-                                                        const float* __restrict__ dl,
-                                                        float* __restrict__ dw) {
-  const int64_t d = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
-  const int e0 = blockIdx.y * 16 + 4 * (threadIdx.x >> 6);
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (d < D) {
-    for (int64_t t = 0; t < T; ++t) {
-      const float xv = load_as_f32(x, t * D + d);
+__global__ __launch_bounds__(256) void dw_router_partial_kernel(int64_t T, int64_t D, int E,
+                                                                int64_t tc,
+                                                                const TIn* __restrict__ x,
+                                                                const float* __restrict__ dl,
+                                                                float* __restrict__ part) {
+  const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int e0 = blockIdx.y * 8;
+  const int64_t c = blockIdx.z, t0 = c * tc, t1 = min(T, t0 + tc);
+  if (d >= D) return;
+  float acc[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (e0 + q < E) acc[q] = fmaf(xv, dl[t * E + e0 + q], acc[q]);
-    }
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int64_t t = t0; t < t1; ++t) {
+    const float xv = load_as_f32(x, t * D + d);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (e0 + q < E) dw[d * E + e0 + q] = acc[q];
+    for (int q = 0; q < 8; ++q)
+      if (e0 + q < E) acc[q] = fmaf(xv, dl[t * E + e0 + q], acc[q]);
   }
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (e0 + q < E) part[(c * D + d) * E + e0 + q] = acc[q];
+}
+__global__ __launch_bounds__(256) void dw_router_reduce_kernel(int64_t n, int nch,
+                                                               const float* __restrict__ part,
+                                                               float* __restrict__ dw) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float acc = 0.f;
+    for (int c = 0; c < nch; ++c) acc += part[(int64_t)c * n + i];
+    dw[i] = acc;
+  }
+}
+
+// ---- operands of the K-grouped weight-gradient products ----------------------------------------
+// dW_e = A_e^T B_e over expert e's kept rows. The 256 x 256 kernel's K-grouped mode takes A_e^T
+// stored K-contiguous: the experts' transposed operands side by side in one (M, lda) matrix,
+// expert e in columns kg_off[e] .. kg_off[e + 1] (its kept-row count rounded up to a multiple
+// of 128, at least 128), zero past its own rows. B_e is read in place: rows offsets[e] ..
+// offsets[e] + (kg_off[e + 1] - kg_off[e]) of the compact (rows, N) buffer, the rows past the
+// expert's own multiplying those zeros (so they must be finite: the 128 rows after the last
+// kept row are cleared).
+constexpr int kKgAlign = 128;
+
+// kg_off (E + 1) from the compact offsets, and the group row offsets e * M1 and e * M2.
+__global__ __launch_bounds__(256) void kg_prep_kernel(int E, const int32_t* __restrict__ offsets,
+                                                      int64_t M1, int64_t M2,
+                                                      int32_t* __restrict__ kg_off,
+                                                      int32_t* __restrict__ grow1,
+                                                      int32_t* __restrict__ grow2) {
+  for (int e = threadIdx.x; e <= E; e += 256) {
+    grow1[e] = (int32_t)(e * M1);
+    grow2[e] = (int32_t)(e * M2);
+  }
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+      kg_off[e] = acc;
+      const int32_t n = offsets[e + 1] - offsets[e];
+      acc += n <= 0 ? kKgAlign : (n + kKgAlign - 1) / kKgAlign * kKgAlign;
+    }
+    kg_off[E] = acc;
+  }
+}
+
+// kg_map[j] = the compact row of column j of the transposed operand, or -1 (a zero column).
+__global__ __launch_bounds__(256) void kg_map_kernel(int64_t ncols, int E,
+                                                     const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ kg_off,
+                                                     int32_t* __restrict__ kg_map) {
+  const int32_t total = kg_off[E];
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < ncols;
+       j += (int64_t)gridDim.x * 256) {
+    int32_t r = -1;
+    if (j < total) {
+      int lo = 0, hi = E - 1;  // the last e with kg_off[e] <= j
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (kg_off[mid] <= j) lo = mid;
+        else hi = mid - 1;
+      }
+      const int32_t i = (int32_t)j - kg_off[lo];
+      if (i < offsets[lo + 1] - offsets[lo]) r = offsets[lo] + i;
+    }
+    kg_map[j] = r;
+  }
+}
+
+// AT[m, j] = src[row(j), m] (row(j) = kg_map[j], through gather[.] / gather_div when given;
+// zero for kg_map[j] < 0), for the columns j < kg_off[E]. 64 x 64 tiles through LDS; bf16,
+// M % 8 == 0.
+__global__ __launch_bounds__(256) void kg_transpose_kernel(int64_t M, int64_t lda, int E,
+                                                           const int32_t* __restrict__ kg_off,
+                                                           const int32_t* __restrict__ kg_map,
+                                                           const uint16_t* __restrict__ src,
+                                                           const int32_t* __restrict__ gather,
+                                                           int gather_div,
+                                                           uint16_t* __restrict__ at) {
+  __shared__ __align__(16) uint16_t tile[64][64 + 8];
+  const int64_t j0 = (int64_t)blockIdx.x * 64, m0 = (int64_t)blockIdx.y * 64;
+  if (j0 >= kg_off[E]) return;  // kg_off[E] is a multiple of 128: tiles are all in or all out
+  const int t = threadIdx.x;
+  {
+    const int jj = t >> 2, mc = (t & 3) * 16;
+    const int32_t r = kg_map[j0 + jj];
+    const int64_t srow = r < 0 ? -1 : (gather ? gather[r] / gather_div : r);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t m = m0 + mc + 8 * h;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (srow >= 0 && m < M) v = *(const uint4*)(src + srow * M + m);
+      *(uint4*)&tile[jj][mc + 8 * h] = v;
+    }
+  }
+  __syncthreads();
+  const int mm = t >> 2, jc = (t & 3) * 16;
+  if (m0 + mm >= M) return;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    w[i] = (uint32_t)tile[jc + 2 * i][mm] | ((uint32_t)tile[jc + 2 * i + 1][mm] << 16);
+  uint4* dst = (uint4*)(at + (m0 + mm) * lda + j0 + jc);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Clear rows offsets[E] .. + kKgAlign of a (rows, N) bf16 buffer (N % 8 == 0).
+__global__ __launch_bounds__(256) void kg_clear_tail_kernel(int E, const int32_t* __restrict__ offsets,
+                                                            int64_t N, uint16_t* __restrict__ buf) {
+  const int64_t base = (int64_t)offsets[E] * N, n8 = (int64_t)kKgAlign * N / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
+    *(uint4*)(buf + base + 8 * i) = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // dx[t] = sum over the token's kept slots of the dx rows (dxr1, plus dxr2 when non-null;
@@ -471,8 +584,19 @@ size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct BwdLayout {
   size_t route, idx, gates, logits, aux, counts, offsets, perm, slot_row, blkc, lrank;
-  size_t a, b, h, y, dy, dh, da, db, dxr, dgates, dl, gsplit, gctr, total;
+  size_t a, b, h, y, dy, dh, da, db, dxr, dgates, dl, gsplit, gctr;
+  size_t dwr_part, kg_off, kg_grow1, kg_grow2, kg_map, kg_at;
+  int dwr_chunks;
+  int64_t dwr_tc, kg_lda;
+  bool kg;
+  size_t total;
 };
+
+// Token chunks of the router-weight gradient's first level.
+static int dwr_chunks_of(int64_t T) {
+  const int64_t n = (T + 127) / 128;
+  return (int)(n < 1 ? 1 : (n > 32 ? 32 : n));
+}
 
 static BwdLayout bwd_layout(const Problem& q) {
   BwdLayout L;
@@ -500,16 +624,32 @@ static BwdLayout bwd_layout(const Problem& q) {
   L.b = take(q.kind == MOE_EXPERT_SWIGLU ? R * DH * es : 0);
   L.h = take(R * DH * es);
   L.y = take(R * (size_t)q.D_out * es);
-  L.dy = take(R * (size_t)q.D_out * es);
+  // the K-grouped weight gradients (bf16): B operands get kKgAlign spare rows
+  const int64_t Mmax = std::max<int64_t>(q.D, q.kind == MOE_EXPERT_LINEAR ? 0 : q.DH);
+  L.kg = q.dtype == MOE_BF16 && q.T > 0 && q.D % 8 == 0 && q.D_out % 8 == 0 &&
+         (q.kind == MOE_EXPERT_LINEAR || q.DH % 8 == 0) &&
+         (int64_t)q.E * (Mmax + 1) < ((int64_t)1 << 31) &&
+         (int64_t)R + (int64_t)kKgAlign * (E + 1) < ((int64_t)1 << 31);
+  const size_t spare = L.kg ? kKgAlign : 0;
+  L.kg_lda = L.kg ? ((int64_t)R + kKgAlign * (int64_t)E + kKgAlign - 1) / kKgAlign * kKgAlign : 0;
+  L.dy = take((R + spare) * (size_t)q.D_out * es);
   L.dh = take(R * DH * es);
-  L.da = take(R * DH * es);
-  L.db = take(q.kind == MOE_EXPERT_SWIGLU ? R * DH * es : 0);
+  L.da = take((R + spare) * DH * es);
+  L.db = take(q.kind == MOE_EXPERT_SWIGLU ? (R + spare) * DH * es : 0);
   L.dxr = take(R * (size_t)q.D * 4);
   L.dgates = take(R * 4);
   L.dl = take(T * E * 4);
   const bool split = q.dtype == MOE_BF16 && q.T > 0;
   L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
   L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
+  L.dwr_chunks = dwr_chunks_of(q.T);
+  L.dwr_tc = (q.T + L.dwr_chunks - 1) / L.dwr_chunks;
+  L.dwr_part = take((size_t)L.dwr_chunks * (size_t)q.D * E * 4);
+  L.kg_off = take(L.kg ? (E + 1) * 4 : 0);
+  L.kg_grow1 = take(L.kg ? (E + 1) * 4 : 0);
+  L.kg_grow2 = take(L.kg ? (E + 1) * 4 : 0);
+  L.kg_map = take(L.kg ? (size_t)L.kg_lda * 4 : 0);
+  L.kg_at = take(L.kg ? (size_t)Mmax * (size_t)L.kg_lda * 2 : 0);
   L.total = off;
   return L;
 }
@@ -606,6 +746,56 @@ hipError_t tn(const Problem& q, const void* A, int64_t lda, const int32_t* gathe
   return hipGetLastError();
 }
 
+// Weight gradient dW_e = A_e^T B_e through the K-grouped 256 x 256 kernel: kg_transpose
+// writes the transposed operand (src's kept rows, (rows, M), gathered when `gather`), kg_gemm
+// multiplies it with B; tn_kg does both.
+hipError_t kg_transpose(const Problem& q, const BwdLayout& L, void* ws, const void* src,
+                        const int32_t* gather, int gather_div, int64_t M, hipStream_t s) {
+  const dim3 tgrid((unsigned)(L.kg_lda / 64), (unsigned)((M + 63) / 64));
+  hipLaunchKernelGGL(kg_transpose_kernel, tgrid, dim3(256), 0, s, M, L.kg_lda, q.E,
+                     (const int32_t*)at<int32_t>(ws, L.kg_off),
+                     (const int32_t*)at<int32_t>(ws, L.kg_map), (const uint16_t*)src, gather,
+                     gather_div, at<uint16_t>(ws, L.kg_at));
+  return hipGetLastError();
+}
+
+hipError_t kg_gemm(const Problem& q, const BwdLayout& L, void* ws, int64_t M,
+                   const int32_t* grow, const void* B, int64_t N, const int32_t* offsets, void* C,
+                   const GemmRes& res, hipStream_t s) {
+  GroupedGemm f{};
+  f.A = at<uint16_t>(ws, L.kg_at);
+  f.lda = L.kg_lda;
+  f.a_gather = nullptr;
+  f.gather_div = 1;
+  f.B0 = B;
+  f.B1 = nullptr;
+  f.C = C;
+  f.offsets = grow;
+  f.E = q.E;
+  f.K = kKgAlign;
+  f.N = N;
+  f.max_rows = (int64_t)q.E * M;
+  f.epilogue = EPI_NONE;
+  f.dtype = q.dtype;
+  f.split_ws = nullptr;
+  f.split_ctr = nullptr;
+  f.queue = res.queue;
+  f.ncu = res.ncu;
+  f.k_grouped = true;
+  f.k_offsets = at<int32_t>(ws, L.kg_off);
+  f.b_offsets = offsets;
+  f.group_rows = M;
+  return launch_grouped_gemm(f, s);
+}
+
+hipError_t tn_kg(const Problem& q, const BwdLayout& L, void* ws, const void* src,
+                 const int32_t* gather, int gather_div, int64_t M, const int32_t* grow,
+                 const void* B, int64_t N, const int32_t* offsets, void* C, const GemmRes& res,
+                 hipStream_t s) {
+  hipError_t err = kg_transpose(q, L, ws, src, gather, gather_div, M, s);
+  return err == hipSuccess ? kg_gemm(q, L, ws, M, grow, B, N, offsets, C, res, s) : err;
+}
+
 // The forward GEMM A_rows -> C without an epilogue (to recompute pre-activations / outputs).
 hipError_t fwd_gemm(const Problem& q, const void* A, int64_t lda, const int32_t* gather,
                     const void* W, int64_t K, int64_t N, const int32_t* offsets, void* C,
@@ -693,6 +883,25 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   float* dgates = at<float>(ws, L.dgates);
   float* dl = at<float>(ws, L.dl);
   const unsigned ew_grid = 2048;
+  // K-grouped weight gradients: per-expert K ranges, group rows, the column map
+  const bool kg = L.kg && queue != nullptr;
+  int32_t* grow1 = at<int32_t>(ws, L.kg_grow1);  // e * D
+  int32_t* grow2 = at<int32_t>(ws, L.kg_grow2);  // e * DH
+  if (kg && err == hipSuccess) {
+    hipLaunchKernelGGL(kg_prep_kernel, dim3(1), dim3(256), 0, s, q.E, (const int32_t*)offsets, D,
+                       linear ? (int64_t)0 : DH, at<int32_t>(ws, L.kg_off), grow1, grow2);
+    hipLaunchKernelGGL(kg_map_kernel, dim3((unsigned)std::min<int64_t>((L.kg_lda + 255) / 256, 4096)),
+                       dim3(256), 0, s, L.kg_lda, q.E, (const int32_t*)offsets,
+                       (const int32_t*)at<int32_t>(ws, L.kg_off), at<int32_t>(ws, L.kg_map));
+    err = hipGetLastError();
+  }
+  auto clear_tail = [&](void* buf, int64_t N) {
+    if (kg && err == hipSuccess) {
+      hipLaunchKernelGGL(kg_clear_tail_kernel, dim3(64), dim3(256), 0, s, q.E,
+                         (const int32_t*)offsets, N, (uint16_t*)buf);
+      err = hipGetLastError();
+    }
+  };
   // 3. the experts' forward quantities on the kept rows
   if (linear) {
     if (err == hipSuccess)
@@ -730,14 +939,19 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
     err = hipGetLastError();
   }
   // 5. experts backward
+  clear_tail(dy, Do);
   if (linear) {
-    if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, dy, D, Do, offsets, dw1, s);
+    if (err == hipSuccess)
+      err = kg ? tn_kg(q, L, ws, x, perm, q.top_k, D, grow1, dy, Do, offsets, dw1, res, s)
+               : tn(q, x, D, perm, q.top_k, dy, D, Do, offsets, dw1, s);
     if (err == hipSuccess)
       err = bf16 ? nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr1, false, s, res)
                  : nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr, true, s, res);
   } else {
     if (err == hipSuccess) err = nt(q, dy, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s, res);
-    if (err == hipSuccess) err = tn(q, h, DH, nullptr, 1, dy, DH, Do, offsets, dw2, s);
+    if (err == hipSuccess)
+      err = kg ? tn_kg(q, L, ws, h, nullptr, 1, DH, grow2, dy, Do, offsets, dw2, res, s)
+               : tn(q, h, DH, nullptr, 1, dy, DH, Do, offsets, dw2, s);
     if (err == hipSuccess) {
       if (bf16)
         hipLaunchKernelGGL(act_backward_kernel<uint16_t>, dim3(ew_grid), dim3(256), 0, s, DH,
@@ -749,8 +963,18 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
                            (float*)da, (float*)db);
       err = hipGetLastError();
     }
-    if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, da, D, DH, offsets, dw1, s);
-    if (err == hipSuccess && swiglu) err = tn(q, x, D, perm, q.top_k, db, D, DH, offsets, dw3, s);
+    clear_tail(da, DH);
+    if (swiglu) clear_tail(db, DH);
+    if (kg) {
+      // one transposed operand (the gathered x) for both products
+      if (err == hipSuccess)
+        err = tn_kg(q, L, ws, x, perm, q.top_k, D, grow1, da, DH, offsets, dw1, res, s);
+      if (err == hipSuccess && swiglu)
+        err = kg_gemm(q, L, ws, D, grow1, db, DH, offsets, dw3, res, s);
+    } else {
+      if (err == hipSuccess) err = tn(q, x, D, perm, q.top_k, da, D, DH, offsets, dw1, s);
+      if (err == hipSuccess && swiglu) err = tn(q, x, D, perm, q.top_k, db, D, DH, offsets, dw3, s);
+    }
     if (bf16) {
       if (err == hipSuccess) err = nt(q, da, nullptr, w1, nullptr, DH, D, offsets, dxr1, false, s, res);
       if (err == hipSuccess && swiglu)
@@ -774,17 +998,24 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
       hipLaunchKernelGGL(router_backward_kernel<4>, dim3(grid), dim3(kThreads), 0, s, q.T, q.E,
                          q.top_k, d_aux, logits, idx, gates, dgates, counts, dl);
     if (dbias) hipLaunchKernelGGL(dbias_kernel, dim3(q.E), dim3(256), 0, s, q.T, q.E, dl, dbias);
-    const dim3 wgrid((unsigned)((D + 63) / 64), (unsigned)((q.E + 15) / 16));
+    const dim3 wgrid((unsigned)((D + 255) / 256), (unsigned)((q.E + 7) / 8), (unsigned)L.dwr_chunks);
+    float* part = at<float>(ws, L.dwr_part);
+    const int64_t nw = D * q.E;
+    const unsigned rgrid = (unsigned)std::min<int64_t>((nw + 255) / 256, 2048);
     if (bf16) {
-      hipLaunchKernelGGL(dw_router_kernel<uint16_t>, wgrid, dim3(256), 0, s, q.T, D, q.E,
-                         (const uint16_t*)x, dl, dw_router);
+      hipLaunchKernelGGL(dw_router_partial_kernel<uint16_t>, wgrid, dim3(256), 0, s, q.T, D, q.E,
+                         L.dwr_tc, (const uint16_t*)x, dl, part);
+      hipLaunchKernelGGL(dw_router_reduce_kernel, dim3(rgrid), dim3(256), 0, s, nw, L.dwr_chunks,
+                         (const float*)part, dw_router);
       hipLaunchKernelGGL((dx_kernel<uint16_t, uint16_t>), dim3(grid), dim3(kThreads), 0, s, q.T, D,
                          q.E, q.top_k, (const uint16_t*)dxr1,
                          (const uint16_t*)(swiglu ? dxr2 : nullptr), slot_row, dl,
                          (const uint16_t*)w_router, (uint16_t*)dx);
     } else {
-      hipLaunchKernelGGL(dw_router_kernel<float>, wgrid, dim3(256), 0, s, q.T, D, q.E,
-                         (const float*)x, dl, dw_router);
+      hipLaunchKernelGGL(dw_router_partial_kernel<float>, wgrid, dim3(256), 0, s, q.T, D, q.E,
+                         L.dwr_tc, (const float*)x, dl, part);
+      hipLaunchKernelGGL(dw_router_reduce_kernel, dim3(rgrid), dim3(256), 0, s, nw, L.dwr_chunks,
+                         (const float*)part, dw_router);
       hipLaunchKernelGGL((dx_kernel<float, float>), dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
                          q.top_k, (const float*)dxr, (const float*)nullptr, slot_row, dl,
                          (const float*)w_router, (float*)dx);

@@ -136,6 +136,17 @@ struct GroupedGemm {
   // B0 stored K-major, (E, N, K) row-major (a forward weight used transposed, for the
   // backward's dgrad). Only with EPI_NONE and the 256 x 256 kernel (bf16, K % 128 == 0).
   bool b_kmajor;
+  // K-grouped (the backward's wgrad, C_g = A_g^T B_g for each group g): group g owns output
+  // rows offsets[g] .. offsets[g + 1] (offsets[g] = g * M, M = group_rows), and its K range is
+  // k_offsets[g] .. k_offsets[g + 1] (multiples of 128, at least 128 wide). A holds the groups'
+  // transposed operands side by side, (M, lda) row-major: row m of group g starts at column
+  // k_offsets[g]. B's K-row i of group g is row b_offsets[g] + i of B0 ((rows, N) row-major);
+  // every K-row read must be in bounds and finite, and the A columns past a group's own
+  // K-rows zero. Only with EPI_NONE, no split, and the 256 x 256 kernel.
+  bool k_grouped;
+  const int32_t* k_offsets;
+  const int32_t* b_offsets;
+  int64_t group_rows;
 };
 constexpr int kSplitSlots = 256;
 constexpr int kQueueInts = 16;

@@ -260,6 +260,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const GroupedGemm g)
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {
   if (g.max_rows <= 0 || g.N <= 0) return hipSuccess;
   // the 256 x 256 kernel needs K % 128 == 0; other bf16 shapes take the 128 x 128 kernel
+  if (g.k_grouped)  // only the 256 x 256 kernel has this mode
+    return (g.dtype == MOE_BF16 && g.queue && g.epilogue == EPI_NONE && !g.b_kmajor)
+               ? launch_grouped_gemm_bf16_256(g, s)
+               : hipErrorInvalidValue;
   const bool k256 = g.dtype == MOE_BF16 && g.K % 128 == 0 && g.queue;
   if (g.b_kmajor && (!k256 || g.epilogue != EPI_NONE)) return hipErrorInvalidValue;
   if (k256) return launch_grouped_gemm_bf16_256(g, s);

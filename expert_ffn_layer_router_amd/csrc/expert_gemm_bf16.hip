@@ -267,10 +267,11 @@ __device__ __forceinline__ float swap_adjacent_lanes(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
 }
 
-template <int EPI, bool BT = false>
+template <int EPI, bool BT = false, bool KG = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const GroupedGemm g, int nt) {
   constexpr bool kSwiGLU = EPI == EPI_SWIGLU;
   static_assert(!BT || EPI == EPI_NONE, "the K-major B mode has no epilogue");
+  static_assert(!KG || (EPI == EPI_NONE && !BT), "the K-grouped mode has no epilogue");
   __shared__ __align__(16) char sbuf[kNBuf * kBuf];
   __shared__ int s_unit[2];  // work positions of later units, by unit parity
   __shared__ int s_last;
@@ -360,6 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   struct Unit {
     int L, ks, e, row0, rows, n_tile, parts, nst;
     int64_t kbeg;
+    int64_t acol, brow;  // K-grouped: the group's first A column and first B row
   };
   auto geometry = [&](int L, int ks) {
     Unit u;
@@ -373,6 +375,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     u.parts = L >= full ? split : 1;  // K parts of this tile
     u.nst = nst_all / u.parts;        // >= 4: K % 128 == 0, and parts have kMinPartStages
     u.kbeg = (int64_t)ks * u.nst * kBK;
+    u.acol = 0;
+    u.brow = 0;
+    if (KG) {  // the group's own K range (a multiple of 128, never empty); nothing is split
+      const int k0 = __builtin_amdgcn_readfirstlane(g.k_offsets[u.e]);
+      const int k1 = __builtin_amdgcn_readfirstlane(g.k_offsets[u.e + 1]);
+      u.nst = (k1 - k0) / kBK;
+      u.kbeg = 0;
+      u.acol = k0;
+      u.brow = __builtin_amdgcn_readfirstlane(g.b_offsets[u.e]);
+    }
     return u;
   };
 
@@ -386,7 +398,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     for (int j = 0; j < 4; ++j) {
       const int rr = 16 * (4 * wv + j) + (lane >> 2);
       const int64_t gr = u.row0 + (rr < u.rows ? rr : 0);
-      src[j] = g.a_gather ? g.a_gather[gr] / g.gather_div : (int32_t)gr;
+      if (KG)  // row m of the group's transposed operand
+        src[j] = (int32_t)(gr - (int64_t)u.e * g.group_rows);
+      else
+        src[j] = g.a_gather ? g.a_gather[gr] / g.gather_div : (int32_t)gr;
     }
   };
   auto make_loader = [&](const Unit& u, const int32_t (&src)[4]) {
@@ -394,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = (lane & 3) ^ ((lane >> 4) & 3);
-      ld.a[j] = (const char*)g.A + ((int64_t)src[j] * g.lda + 8 * c) * 2;
+      ld.a[j] = (const char*)g.A + ((int64_t)src[j] * g.lda + u.acol + 8 * c) * 2;
     }
     // B: instruction j of wave w fills K-rows 8w + 2j + lane / 32; position lane % 32 of the
     // K-row holds logical chunk (lane % 32) ^ (4 (K-row % 4)), K-row % 4 = 2 (j % 2) + lane / 32.
@@ -414,7 +429,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         col = n0 + 8 * c;
       }
       const int krow = 8 * wv + (lane >> 5);
-      ld.b[q] = (const char*)(Wm + (int64_t)u.e * K * N + (int64_t)krow * N + (col < N ? col : 0));
+      const int64_t brow0 = KG ? u.brow * N : (int64_t)u.e * K * N;
+      ld.b[q] = (const char*)(Wm + brow0 + (int64_t)krow * N + (col < N ? col : 0));
     }
     if (BT) {
       // K-major B ((N, K) per expert): instruction j of wave w fills columns 16 (4w + j) +
@@ -724,8 +740,8 @@ int device_split_cus() {
 hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) {
   GroupedGemm g = g_in;
   // A K split needs at least two parts of kMinPartStages stages each; below that the split
-  // path (and its ticket reset) is skipped altogether.
-  if (g.K / kBK < 2 * kMinPartStages) {
+  // path (and its ticket reset) is skipped altogether. K-grouped products are never split.
+  if (g.k_grouped || g.K / kBK < 2 * kMinPartStages) {
     g.split_ws = nullptr;
     g.split_ctr = nullptr;
   }
@@ -746,6 +762,11 @@ hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) 
   if (g.b_kmajor) {
     hipExtLaunchKernelGGL((gemm_bf16_256_kernel<EPI_NONE, true>), grid, dim3(kThreads), 0, s,
                           g.ev_start, g.ev_stop, 0, g, (int)nt);
+    return hipGetLastError();
+  }
+  if (g.k_grouped) {
+    hipExtLaunchKernelGGL((gemm_bf16_256_kernel<EPI_NONE, false, true>), grid, dim3(kThreads), 0,
+                          s, g.ev_start, g.ev_stop, 0, g, (int)nt);
     return hipGetLastError();
   }
   switch (g.epilogue) {
