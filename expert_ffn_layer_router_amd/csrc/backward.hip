@@ -576,6 +576,120 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(int64_t T, int64_t D, int 
   }
 }
 
+// bf16 versions of the three kernels above, 8 elements a lane (16-byte loads and stores), for
+// DH % 8 == 0 (activations) and D % 8 == 0, E % 8 == 0 (dx). Same arithmetic, same order.
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(256) void act_forward_bf16x8_kernel(int64_t DH, int kind,
+                                                                 const int32_t* __restrict__ offsets,
+                                                                 int E, const uint4* __restrict__ a,
+                                                                 const uint4* __restrict__ b,
+                                                                 uint4* __restrict__ h) {
+  const int64_t n = (int64_t)offsets[E] * DH / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float av[8], v[8];
+    unpack8(a[i], av);
+    if (kind == MOE_EXPERT_SWIGLU) {
+      float bv[8];
+      unpack8(b[i], bv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = av[q] / (1.f + __expf(-av[q])) * bv[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = fmaxf(av[q], 0.f);
+    }
+    h[i] = pack8(v);
+  }
+}
+
+__global__ __launch_bounds__(256) void act_backward_bf16x8_kernel(
+    int64_t DH, int kind, const int32_t* __restrict__ offsets, int E, const uint4* __restrict__ a,
+    const uint4* __restrict__ b, const uint4* __restrict__ dh, uint4* __restrict__ da,
+    uint4* __restrict__ db) {
+  const int64_t n = (int64_t)offsets[E] * DH / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float av[8], g[8], ra[8];
+    unpack8(a[i], av);
+    unpack8(dh[i], g);
+    if (kind == MOE_EXPERT_SWIGLU) {
+      float bv[8], rb[8];
+      unpack8(b[i], bv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float sg = 1.f / (1.f + __expf(-av[q]));
+        ra[q] = g[q] * bv[q] * sg * (1.f + av[q] * (1.f - sg));
+        rb[q] = g[q] * av[q] * sg;
+      }
+      db[i] = pack8(rb);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ra[q] = av[q] > 0.f ? g[q] : 0.f;
+    }
+    da[i] = pack8(ra);
+  }
+}
+
+// One wave per token; lane l handles columns 8 (l + 64 i) .. + 7.
+__global__ __launch_bounds__(kThreads) void dx_bf16x8_kernel(int64_t T, int64_t D, int E, int k,
+                                                             const uint16_t* __restrict__ dxr1,
+                                                             const uint16_t* __restrict__ dxr2,
+                                                             const int32_t* __restrict__ slot_row,
+                                                             const float* __restrict__ dl,
+                                                             const uint16_t* __restrict__ w_router,
+                                                             uint16_t* __restrict__ dx) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (t >= T) return;
+  for (int64_t c = 8 * lane; c < D; c += 8 * kWave) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int row = slot_row[t * k + j];
+      if (row >= 0) {
+        float v[8];
+        unpack8(*(const uint4*)(dxr1 + (int64_t)row * D + c), v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += v[q];
+        if (dxr2) {
+          unpack8(*(const uint4*)(dxr2 + (int64_t)row * D + c), v);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] += v[q];
+        }
+      }
+    }
+    for (int e0 = 0; e0 < E; e0 += 8) {
+      float d8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d8[i] = dl[t * E + e0 + i];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float w[8];
+        unpack8(*(const uint4*)(w_router + (c + q) * E + e0), w);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[q] = fmaf(d8[i], w[i], acc[q]);
+      }
+    }
+    *(uint4*)(dx + t * D + c) = pack8(acc);
+  }
+}
+
 size_t a256(size_t v) { return (v + 255) & ~size_t(255); }
 
 }  // namespace
@@ -912,7 +1026,10 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
     if (err == hipSuccess && swiglu)
       err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_ctr, queue, ncu, s);
     if (err == hipSuccess) {
-      if (bf16)
+      if (bf16 && DH % 8 == 0)
+        hipLaunchKernelGGL(act_forward_bf16x8_kernel, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
+                           offsets, q.E, (const uint4*)a, (const uint4*)b, (uint4*)h);
+      else if (bf16)
         hipLaunchKernelGGL(act_forward_kernel<uint16_t>, dim3(ew_grid), dim3(256), 0, s, DH,
                            q.kind, offsets, q.E, (const uint16_t*)a, (const uint16_t*)b,
                            (uint16_t*)h);
@@ -953,7 +1070,11 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
       err = kg ? tn_kg(q, L, ws, h, nullptr, 1, DH, grow2, dy, Do, offsets, dw2, res, s)
                : tn(q, h, DH, nullptr, 1, dy, DH, Do, offsets, dw2, s);
     if (err == hipSuccess) {
-      if (bf16)
+      if (bf16 && DH % 8 == 0)
+        hipLaunchKernelGGL(act_backward_bf16x8_kernel, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
+                           offsets, q.E, (const uint4*)a, (const uint4*)b, (const uint4*)dh,
+                           (uint4*)da, (uint4*)db);
+      else if (bf16)
         hipLaunchKernelGGL(act_backward_kernel<uint16_t>, dim3(ew_grid), dim3(256), 0, s, DH,
                            q.kind, offsets, q.E, (const uint16_t*)a, (const uint16_t*)b,
                            (const uint16_t*)dh, (uint16_t*)da, (uint16_t*)db);
@@ -1007,10 +1128,16 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
                          L.dwr_tc, (const uint16_t*)x, dl, part);
       hipLaunchKernelGGL(dw_router_reduce_kernel, dim3(rgrid), dim3(256), 0, s, nw, L.dwr_chunks,
                          (const float*)part, dw_router);
-      hipLaunchKernelGGL((dx_kernel<uint16_t, uint16_t>), dim3(grid), dim3(kThreads), 0, s, q.T, D,
-                         q.E, q.top_k, (const uint16_t*)dxr1,
-                         (const uint16_t*)(swiglu ? dxr2 : nullptr), slot_row, dl,
-                         (const uint16_t*)w_router, (uint16_t*)dx);
+      if (D % 8 == 0 && q.E % 8 == 0 && (uintptr_t)w_router % 16 == 0 && (uintptr_t)dx % 16 == 0)
+        hipLaunchKernelGGL(dx_bf16x8_kernel, dim3(grid), dim3(kThreads), 0, s, q.T, D, q.E,
+                           q.top_k, (const uint16_t*)dxr1,
+                           (const uint16_t*)(swiglu ? dxr2 : nullptr), slot_row, dl,
+                           (const uint16_t*)w_router, (uint16_t*)dx);
+      else
+        hipLaunchKernelGGL((dx_kernel<uint16_t, uint16_t>), dim3(grid), dim3(kThreads), 0, s, q.T,
+                           D, q.E, q.top_k, (const uint16_t*)dxr1,
+                           (const uint16_t*)(swiglu ? dxr2 : nullptr), slot_row, dl,
+                           (const uint16_t*)w_router, (uint16_t*)dx);
     } else {
       hipLaunchKernelGGL(dw_router_partial_kernel<float>, wgrid, dim3(256), 0, s, q.T, D, q.E,
                          L.dwr_tc, (const float*)x, dl, part);
