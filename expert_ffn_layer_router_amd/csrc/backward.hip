@@ -1,8 +1,9 @@
 // Backward of the layer: the gradients of L = sum(out * dout) + d_aux * aux_loss with respect
 // to x, the router (weights, bias) and every expert matrix. The routing decisions (top-k, the
 // drop set) are piecewise constant, so the gradient flows through the gates and through P in
-// the Switch loss; f, a count, has none ("Mixture of Experts: the Sparsely-Gated Layer", Hot
-// shards: a count has no gradient, a probability does). In reverse order of the forward:
+// the Switch loss; f, a count, is a step function of the logits and has none ("Mixture-of-
+// Experts (MoE) Routing", the load-balancing step; "Mixture of Experts: the Sparsely-Gated
+// Layer", Hot shards). In reverse order of the forward:
 //  * combine:  dgate[t, j] = <dout[t], y[row]> for a kept slot (0 for a dropped one),
 //              dy[row] = gate[t, j] * dout[t];
 //  * experts:  dh = dy W2^T, then through the activation (ReLU: relu'(0) = 0; SwiGLU:

@@ -259,9 +259,9 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
  * Gradients of L = sum(out * dout) + d_aux * aux_loss for the layer of moe_forward (no router
  * noise, renormalised gates), by the chain rule through its steps in reverse. The routing
  * decisions and the drop set are piecewise constant, so the gradient flows through the gates
- * and through P in the Switch loss; f, a count, has none (Sparsely-Gated Layer page, "Hot
- * shards": a count has no gradient, a probability does). relu'(0) is taken as 0; silu'(z) =
- * s (1 + z (1 - s)) with s = sigmoid(z).
+ * and through P in the Switch loss; f, a count, is a step function of the logits and has none
+ * (ML Grind page, the load-balancing step; Sparsely-Gated Layer page, Hot shards). relu'(0)
+ * is taken as 0; silu'(z) = s (1 + z (1 - s)) with s = sigmoid(z).
  *   Inputs: x, w_router, router_bias (nullable), w1, w3, w2 as in moe_forward; dout (T, D_out)
  *   in p->dtype; d_aux (host) the weight of the Switch loss in L.
  *   Outputs (overwritten): dx (T, D) and dw1, dw3 (SwiGLU only, else NULL), dw2 (not LINEAR,

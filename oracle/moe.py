@@ -332,7 +332,8 @@ def moe_backward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=
 
     The routing decisions (top-k and the drop set) are piecewise constant, so the gradient
     flows through the gates and through P in the Switch loss; f (a count) has none
-    (Sparsely-Gated Layer, "Hot shards": a count has no gradient, a probability does).
+    (f_e is a step function of the logits, so only P_e carries gradient: ML Grind, the
+    load-balancing step; Sparsely-Gated Layer, Hot shards).
     In reverse order: the combine gives dL/dgate = <dout_t, y_e(x_t)> for a kept slot (0 for
     a dropped one) and dL/dy = gate * dout_t; each expert's backward on its kept rows; the
     gates' softmax over the k chosen logits; the loss through P_e = mean_t probs[t, e] and
