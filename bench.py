@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("466cbbc79fd656a03a2cfb7636587895f3d65905642418dc2490b69ce1dc9833",
-                            3448114.8214285714, 237126.8392857143),
+    "mixtral_swiglu_bf16": ("dfbf0879053eef0a4f4ddd740370d5c199bba565a1cd35cc31bd8346e1a3dedf",
+                            3441784.5714285714, 237637.125),
 }
 
 
