@@ -85,6 +85,11 @@ CASES = {
     "linear_bf16": spec("tiny_linear_f32", T=300, D=128, D_out=200, E=4, dtype="bf16"),
     "relu_256_experts": spec("switch_top1_cap_bf16", T=600, D=64, DH=64, E=256, top_k=8,
                              capacity_factor=0.0),
+    # degenerate routings: one expert (every gate 1, the loss constant), and k = E (the
+    # dense layer: nothing is chosen, the loss is constant 1)
+    "single_expert_bf16": spec("mixtral_swiglu_bf16", T=300, D=128, DH=256, E=1, top_k=1),
+    "dense_k_equals_e_bf16": spec("mixtral_swiglu_bf16", T=260, D=128, DH=128, E=4, top_k=4),
+    "dense_k_equals_e_f32": spec("small_relu_f32", T=40, D=16, DH=24, E=3, top_k=3),
 }
 
 
@@ -151,3 +156,30 @@ def test_backward_full_size_sampled_tokens():
     err = max_abs_rel(g["dx"][tokens], r["dx"][tokens])
     _say(f"  dx on {len(tokens)} sampled tokens: max-abs-rel {err:.2e}")
     assert err <= GRAD_TOL["bf16"]
+
+
+def test_backward_with_no_tokens():
+    """T = 0: the call succeeds and writes nothing."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("mixtral_swiglu_bf16", T=0, D=128, DH=256)
+    p = B.Problem.from_spec(sp)
+    dev = "cuda"
+    bf = torch.bfloat16
+    x = torch.empty((0, sp.D), dtype=bf, device=dev)
+    wr = torch.zeros((sp.D, sp.E), dtype=bf, device=dev)
+    w1 = torch.zeros((sp.E, sp.D, sp.DH), dtype=bf, device=dev)
+    w3 = torch.zeros_like(w1)
+    w2 = torch.zeros((sp.E, sp.DH, sp.D_out), dtype=bf, device=dev)
+    dout = torch.empty((0, sp.D_out), dtype=bf, device=dev)
+    dx = torch.empty((0, sp.D), dtype=bf, device=dev)
+    dwr = torch.full((sp.D, sp.E), 7.0, dtype=torch.float32, device=dev)
+    db = torch.full((sp.E,), 7.0, dtype=torch.float32, device=dev)
+    dw1 = torch.full(w1.shape, 7.0, dtype=bf, device=dev)
+    dw3 = torch.full(w3.shape, 7.0, dtype=bf, device=dev)
+    dw2 = torch.full(w2.shape, 7.0, dtype=bf, device=dev)
+    ws = torch.empty(max(B.backward_workspace_size(p), 1), dtype=torch.uint8, device=dev)
+    B.moe_backward(p, x, wr, None, w1, w3, w2, dout, 0.5, dx, dwr, db, dw1, dw3, dw2, ws)
+    torch.cuda.synchronize()
+    for t in (dwr, db, dw1, dw3, dw2):
+        assert bool((t == 7.0).all())
