@@ -143,6 +143,9 @@ def main() -> int:
                     help="capacity-padded expert batches (needs a capacity factor)")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + moe_backward per step (a training step of the layer)")
+    ap.add_argument("--train", action="store_true",
+                    help="time moe_forward_train + moe_backward_saved per step (the training "
+                         "step that keeps the forward's state instead of recomputing it)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -182,6 +185,9 @@ def main() -> int:
                          importance_loss=importance)
     ws = B.alloc_workspace(p, o=opts)
     bwd = None
+    train = args.train
+    if train:
+        args.backward = True
     if args.backward:
         if options:
             print("--backward runs the plain layer (no router options)", file=sys.stderr)
@@ -198,17 +204,39 @@ def main() -> int:
             dw2=None if dev["w2"] is None else torch.empty_like(dev["w2"]),
             ws=torch.empty(max(B.backward_workspace_size(p), 1), dtype=torch.uint8,
                            device="cuda"),
-            ev=[], )
+            ev=[], fev=[],
+            saved=torch.empty(max(B.saved_size(p), 1), dtype=torch.uint8, device="cuda")
+            if train else None)
     torch.cuda.synchronize()
+
+    def forward_train(timed=False):
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        B.moe_forward_train(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"],
+                            dev["w2"], outs["out"], outs["expert_indices"], outs["gates"],
+                            outs["aux_loss"], outs["expert_counts"], outs["expert_offsets"],
+                            outs["slot_row"], bwd["saved"], ws)
+        if timed:
+            e1.record()
+            bwd["fev"].append((e0, e1))
 
     def backward_step(timed=False):
         if timed:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-        B.moe_backward(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"], dev["w2"],
-                       bwd["dout"], 0.01, bwd["dx"], bwd["dwr"], bwd["db"], bwd["dw1"],
-                       bwd["dw3"], bwd["dw2"], bwd["ws"])
+        if train:
+            B.moe_backward_saved(p, dev["x"], dev["w_router"], dev["w1"], dev["w3"], dev["w2"],
+                                 outs["expert_indices"], outs["gates"], outs["expert_counts"],
+                                 outs["expert_offsets"], outs["slot_row"], bwd["saved"],
+                                 bwd["dout"], 0.01, bwd["dx"], bwd["dwr"], bwd["db"],
+                                 bwd["dw1"], bwd["dw3"], bwd["dw2"], bwd["ws"])
+        else:
+            B.moe_backward(p, dev["x"], dev["w_router"], dev["bias"], dev["w1"], dev["w3"],
+                           dev["w2"], bwd["dout"], 0.01, bwd["dx"], bwd["dwr"], bwd["db"],
+                           bwd["dw1"], bwd["dw3"], bwd["dw2"], bwd["ws"])
         if timed:
             e1.record()
             bwd["ev"].append((e0, e1))
@@ -228,7 +256,7 @@ def main() -> int:
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        step()
+        forward_train() if train else step()
         if bwd is not None:
             backward_step()
     torch.cuda.synchronize()
@@ -241,13 +269,16 @@ def main() -> int:
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(events[i])
+        # (the training forward records no stage events: its GEMM figures come from the
+        # stage-timing steps below, which run the plain forward)
+        forward_train() if train else step(events[i])
         if bwd is not None:
             backward_step()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    stage_ms = {k: float(np.mean([e.elapsed_ms()[k] for e in events])) for k in gemm_stages}
+    stage_ms = {} if train else {k: float(np.mean([e.elapsed_ms()[k] for e in events]))
+                                 for k in gemm_stages}
     for e in events:
         e.close()
     # The other stages' times come from a few further steps with an event pair around every
@@ -255,10 +286,12 @@ def main() -> int:
     extra = [B.StageEvents() for _ in range(min(args.steps, 5))]
     for e in extra:
         step(e)
+        if train:
+            forward_train(timed=True)
         if bwd is not None:
             backward_step(timed=True)
     torch.cuda.synchronize()
-    for k in ("route", "dispatch", "expert_down", "combine"):
+    for k in (("expert_up",) if train else ()) + ("route", "dispatch", "expert_down", "combine"):
         stage_ms[k] = float(np.mean([e.elapsed_ms()[k] for e in extra]))
     for e in extra:
         e.close()
@@ -345,12 +378,21 @@ def main() -> int:
         bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd["ev"]]))
         bwd_flops = 2 * (up_flops + down_flops)  # dgrad + wgrad of every expert GEMM
         result["metric"] = "MoE layer forward+backward tokens/s at 1 MI355X"
-        result["config"]["workload"] += ", forward and backward"
+        result["config"]["workload"] += (", training forward and backward from its saved state"
+                                         if train else ", forward and backward")
         stages["backward"] = {"us": bwd_ms * 1e3, "TFLOP/s": tf(bwd_flops, bwd_ms),
                               "mfma_frac": tf(bwd_flops, bwd_ms) / peak_tf,
                               "algorithmic_flops": bwd_flops,
-                              "note": "dgrad + wgrad of the expert GEMMs; the recomputed "
-                                      "forward inside the call is not counted"}
+                              "note": ("dgrad + wgrad of the expert GEMMs, from the training "
+                                       "forward's saved state (moe_backward_saved)") if train else
+                                      ("dgrad + wgrad of the expert GEMMs; the recomputed "
+                                       "forward inside the call is not counted")}
+        if train:
+            fwd_ms = float(np.mean([a.elapsed_time(b) for a, b in bwd["fev"]]))
+            stages["forward_train"] = {"us": fwd_ms * 1e3,
+                                       "note": "moe_forward_train: the forward that also keeps "
+                                               "the pre-activations, h, y, logits and perm"}
+            result["roofline"]["kernel"] += ", timed in plain forward steps beside the timed ones"
     if not args.no_cpu_baseline:
         n = min(args.cpu_baseline_tokens, T) if args.cpu_baseline_tokens > 0 else T
         log(f"[bench] CPU oracle baseline on {n} tokens")

@@ -29,6 +29,7 @@ EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_forward_timed", "moe_workspace_size_ex", "moe_route_ex", "moe_dispatch_padded",
     "moe_expert_ffn_ex", "moe_forward_ex", "moe_backward_workspace_size", "moe_backward",
+    "moe_saved_size", "moe_forward_train", "moe_backward_saved",
 )
 STAGES = ("route", "dispatch", "expert_up", "expert_down", "combine")
 
@@ -110,6 +111,15 @@ def lib() -> ctypes.CDLL:
         L.moe_backward.restype = ctypes.c_int
         L.moe_backward.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                    _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.moe_saved_size.restype = ctypes.c_size_t
+        L.moe_saved_size.argtypes = [_PP]
+        L.moe_forward_train.restype = ctypes.c_int
+        L.moe_forward_train.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, ctypes.c_size_t, _P, ctypes.c_size_t, _P]
+        L.moe_backward_saved.restype = ctypes.c_int
+        L.moe_backward_saved.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P, ctypes.c_float, _P, _P, _P, _P, _P,
+                                         _P, _P, ctypes.c_size_t, _P]
         L.moe_forward_ex.restype = ctypes.c_int
         L.moe_forward_ex.argtypes = [_PP, _PO, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      _P, _P, ctypes.c_size_t, _P, _P]
@@ -257,6 +267,37 @@ def moe_backward(p: Problem, x, w_router, router_bias, w1, w3, w2, dout, d_aux: 
                               _ptr(dw_router), _ptr(dbias), _ptr(dw1), _ptr(dw3), _ptr(dw2),
                               _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                               _stream(stream)), "moe_backward")
+
+
+def saved_size(p: Problem) -> int:
+    return int(lib().moe_saved_size(ctypes.byref(p.c())))
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_forward_train(p: Problem, x, w_router, router_bias, w1, w3, w2, out, expert_indices,
+                      gates, aux_loss, expert_counts, expert_offsets, slot_row, saved, ws,
+                      stream=None):
+    _check(lib().moe_forward_train(ctypes.byref(p.c()), _ptr(x), _ptr(w_router),
+                                   _ptr(router_bias), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(out),
+                                   _ptr(expert_indices), _ptr(gates), _ptr(aux_loss),
+                                   _ptr(expert_counts), _ptr(expert_offsets), _ptr(slot_row),
+                                   _ptr(saved), _nbytes(saved), _ptr(ws), _nbytes(ws),
+                                   _stream(stream)), "moe_forward_train")
+
+
+def moe_backward_saved(p: Problem, x, w_router, w1, w3, w2, expert_indices, gates,
+                       expert_counts, expert_offsets, slot_row, saved, dout, d_aux: float, dx,
+                       dw_router, dbias, dw1, dw3, dw2, ws, stream=None):
+    _check(lib().moe_backward_saved(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(w1),
+                                    _ptr(w3), _ptr(w2), _ptr(expert_indices), _ptr(gates),
+                                    _ptr(expert_counts), _ptr(expert_offsets), _ptr(slot_row),
+                                    _ptr(saved), _nbytes(saved), _ptr(dout), float(d_aux),
+                                    _ptr(dx), _ptr(dw_router), _ptr(dbias), _ptr(dw1), _ptr(dw3),
+                                    _ptr(dw2), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_backward_saved")
 
 
 def moe_route(p: Problem, x, w_router, router_bias, expert_indices, gates, aux_loss,

@@ -473,4 +473,78 @@ moe_status moe_backward(const moe_problem* p, const void* x, const void* w_route
                                     dw_router, dbias, dw1, dw3, dw2, ws, stream));
 }
 
+size_t moe_saved_size(const moe_problem* p) {
+  if (check_problem(p) != MOE_OK) return 0;
+  return saved_layout(internal(p)).total;
+}
+
+moe_status moe_forward_train(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, const void* w1, const void* w3,
+                             const void* w2, void* out, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* slot_row, void* saved, size_t saved_bytes, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!aux_loss || !expert_counts || !expert_offsets || !weights_ok(p, w1, w3, w2))
+    return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !w_router || !out || !expert_indices || !gates || !slot_row))
+    return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  const SavedLayout S = saved_layout(q);
+  st = check_ws(saved, saved_bytes, p->T > 0 ? S.total : 0);
+  if (st != MOE_OK) return st;
+  char* sv = (char*)saved;
+  int32_t* perm = p->T > 0 ? (int32_t*)(sv + S.perm) : at<int32_t>(ws, L.perm);
+  hipError_t err = launch_route(q, x, w_router, router_bias, RouteOpts{}, expert_indices, gates,
+                                p->T > 0 ? (float*)(sv + S.logits) : nullptr, nullptr,
+                                at<void>(ws, L.route), stream);
+  if (err == hipSuccess)
+    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream);
+  // the dispatch scan also zeroes the GEMMs' K-split tickets and work queue
+  int32_t* tickets = (q.dtype == MOE_BF16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
+  if (err == hipSuccess)
+    err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
+                          nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
+                          tickets, tickets ? kSplitSlots + kQueueInts : 0);
+  if (err != hipSuccess || q.T == 0) return hip_status(err);
+  const int ncu = tickets ? device_split_cus() : 0;
+  err = run_experts_saving(q, x, perm, expert_offsets, w1, w3, w2, sv + S.a, sv + S.b, sv + S.h,
+                           sv + S.y, (tickets && ncu > 0) ? at<float>(ws, L.gsplit) : nullptr,
+                           (tickets && ncu > 0) ? tickets : nullptr,
+                           tickets ? tickets + kSplitSlots : nullptr, ncu, stream);
+  if (err == hipSuccess) err = launch_combine(q, sv + S.y, slot_row, gates, out, stream);
+  return hip_status(err);
+}
+
+moe_status moe_backward_saved(const moe_problem* p, const void* x, const void* w_router,
+                              const void* w1, const void* w3, const void* w2,
+                              const int32_t* expert_indices, const float* gates,
+                              const int32_t* expert_counts, const int32_t* expert_offsets,
+                              const int32_t* slot_row, const void* saved, size_t saved_bytes,
+                              const void* dout, float d_aux, void* dx, float* dw_router,
+                              float* dbias, void* dw1, void* dw3, void* dw2, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!weights_ok(p, w1, w3, w2) || !(d_aux == d_aux)) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !w_router || !dout || !dx || !dw_router || !dw1 || !expert_indices ||
+                   !gates || !expert_counts || !expert_offsets || !slot_row))
+    return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && p->kind == MOE_EXPERT_SWIGLU && !dw3) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && p->kind != MOE_EXPERT_LINEAR && !dw2) return MOE_ERR_INVALID_ARG;
+  const Problem q = internal(p);
+  st = check_ws(ws, ws_bytes, backward_ws_bytes(q));
+  if (st != MOE_OK) return st;
+  st = check_ws(saved, saved_bytes, p->T > 0 ? saved_layout(q).total : 0);
+  if (st != MOE_OK) return st;
+  if (q.T == 0) return MOE_OK;
+  return hip_status(launch_backward_saved(q, expert_indices, gates, expert_counts, expert_offsets,
+                                          slot_row, saved, x, w_router, w1, w3, w2, dout, d_aux,
+                                          dx, dw_router, dbias, dw1, dw3, dw2, ws, stream));
+}
+
 }  // extern "C"

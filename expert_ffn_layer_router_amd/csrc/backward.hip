@@ -267,24 +267,6 @@ __global__ __launch_bounds__(kThreads) void tn_f32_kernel(const BwdGemm g) {
 // ---- elementwise and reduction kernels ------------------------------------------------------
 
 // h = act(a, b) over the kept rows (rows from offsets[E] on are left alone).
-template <typename TIn>
-__global__ void act_forward_kernel(int64_t DH, int kind, const int32_t* __restrict__ offsets, int E,
-                                   const TIn* __restrict__ a, const TIn* __restrict__ b,
-                                   TIn* __restrict__ h) {
-  const int64_t n = (int64_t)offsets[E] * DH;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const float av = load_as_f32(a, i);
-    float v;
-    if (kind == MOE_EXPERT_SWIGLU) {
-      v = av / (1.f + __expf(-av)) * load_as_f32(b, i);
-    } else {
-      v = fmaxf(av, 0.f);
-    }
-    store_from_f32(h, i, v);
-  }
-}
-
 // da (and db) from dh, a, b: SwiGLU da = dh b s (1 + a (1 - s)), db = dh a s; ReLU da = dh
 // (a > 0).
 template <typename TIn>
@@ -595,29 +577,6 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ __launch_bounds__(256) void act_forward_bf16x8_kernel(int64_t DH, int kind,
-                                                                 const int32_t* __restrict__ offsets,
-                                                                 int E, const uint4* __restrict__ a,
-                                                                 const uint4* __restrict__ b,
-                                                                 uint4* __restrict__ h) {
-  const int64_t n = (int64_t)offsets[E] * DH / 8;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float av[8], v[8];
-    unpack8(a[i], av);
-    if (kind == MOE_EXPERT_SWIGLU) {
-      float bv[8];
-      unpack8(b[i], bv);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = av[q] / (1.f + __expf(-av[q])) * bv[q];
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = fmaxf(av[q], 0.f);
-    }
-    h[i] = pack8(v);
-  }
-}
-
 __global__ __launch_bounds__(256) void act_backward_bf16x8_kernel(
     int64_t DH, int kind, const int32_t* __restrict__ offsets, int E, const uint4* __restrict__ a,
     const uint4* __restrict__ b, const uint4* __restrict__ dh, uint4* __restrict__ da,
@@ -770,6 +729,27 @@ static BwdLayout bwd_layout(const Problem& q) {
 }
 
 size_t backward_ws_bytes(const Problem& q) { return bwd_layout(q).total; }
+
+SavedLayout saved_layout(const Problem& q) {
+  SavedLayout S;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = a256(off + n);
+    return o;
+  };
+  const size_t es = q.dtype == MOE_BF16 ? 2 : 4;
+  const size_t R = (size_t)q.slots();
+  const size_t DH = (size_t)(q.kind == MOE_EXPERT_LINEAR ? 0 : q.DH);
+  S.logits = take((size_t)q.T * q.E * 4);
+  S.perm = take(R * 4);
+  S.a = take(R * DH * es);
+  S.b = take(q.kind == MOE_EXPERT_SWIGLU ? R * DH * es : 0);
+  S.h = take(R * DH * es);
+  S.y = take(R * (size_t)q.D_out * es);
+  S.total = off;
+  return S;
+}
 
 namespace {
 
@@ -937,7 +917,76 @@ hipError_t fwd_gemm(const Problem& q, const void* A, int64_t lda, const int32_t*
   return launch_grouped_gemm(g, s);
 }
 
+// The forward quantities the backward needs, by pointer: from the recompute inside
+// moe_backward, or from a training forward's saved state.
+struct BwdInputs {
+  const int32_t* idx;
+  const float* gates;
+  const float* logits;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* slot_row;
+  const void* a;
+  const void* b;
+  const void* h;
+  const void* y;
+};
+
+hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
+                         const void* w_router, const void* w1, const void* w3, const void* w2,
+                         const void* dout, float d_aux, void* dx, float* dw_router, float* dbias,
+                         void* dw1, void* dw3, void* dw2, void* ws, bool tickets_zeroed,
+                         hipStream_t s);
+
 }  // namespace
+
+hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* perm,
+                              const int32_t* offsets, const void* w1, const void* w3,
+                              const void* w2, void* a, void* b, void* h, void* y,
+                              float* split_ws, int32_t* split_ctr, int32_t* queue, int ncu,
+                              hipStream_t s) {
+  const int64_t D = q.D, DH = q.DH, Do = q.D_out;
+  if (q.kind == MOE_EXPERT_LINEAR)
+    return fwd_gemm(q, x, D, perm, w1, D, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
+  const bool swiglu = q.kind == MOE_EXPERT_SWIGLU;
+  GroupedGemm g{};
+  g.A = x;
+  g.lda = D;
+  g.a_gather = perm;
+  g.gather_div = q.top_k;
+  g.B0 = w1;
+  g.B1 = swiglu ? w3 : nullptr;
+  g.C = h;
+  g.offsets = offsets;
+  g.E = q.E;
+  g.K = D;
+  g.N = DH;
+  g.max_rows = q.slots();
+  g.epilogue = swiglu ? EPI_SWIGLU : EPI_RELU;
+  g.dtype = q.dtype;
+  g.split_ws = split_ws;
+  g.split_ctr = split_ctr;
+  g.ncu = ncu;
+  g.queue = queue;
+  // the 256 x 256 kernel stores the pre-activations beside h; elsewhere they take products of
+  // their own (the same accumulation, so the same values)
+  const bool saving = q.dtype == MOE_BF16 && D % 128 == 0 && queue != nullptr;
+  if (saving) {
+    g.pre_a = a;
+    g.pre_b = swiglu ? b : nullptr;
+  }
+  hipError_t err = launch_grouped_gemm(g, s);
+  if (!saving) {
+    if (err == hipSuccess)
+      err = fwd_gemm(q, x, D, perm, w1, D, DH, offsets, a, split_ws, split_ctr, queue, ncu, s);
+    if (err == hipSuccess && swiglu)
+      err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_ctr, queue, ncu, s);
+  }
+  if (err == hipSuccess)
+    err = fwd_gemm(q, h, DH, nullptr, w2, DH, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
+  return err;
+}
 
 hipError_t launch_backward(const Problem& q, const void* x, const void* w_router, const float* bias,
                            const void* w1, const void* w3, const void* w2, const void* dout,
@@ -945,7 +994,6 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
                            void* dw3, void* dw2, void* ws, hipStream_t s) {
   const BwdLayout L = bwd_layout(q);
   const bool bf16 = q.dtype == MOE_BF16;
-  const bool linear = q.kind == MOE_EXPERT_LINEAR, swiglu = q.kind == MOE_EXPERT_SWIGLU;
   int32_t* idx = at<int32_t>(ws, L.idx);
   float* gates = at<float>(ws, L.gates);
   float* logits = at<float>(ws, L.logits);
@@ -960,6 +1008,61 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
     err = launch_aux_finalize(q, at<void>(ws, L.route), at<float>(ws, L.aux), nullptr, s);
   // 2. dispatch (counts, offsets, permutation, slot rows); the scan also clears the GEMMs'
   //    split tickets and work queue
+  int32_t* tickets = (bf16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
+  if (err == hipSuccess)
+    err = launch_dispatch(q, idx, x, counts, offsets, perm, slot_row, nullptr,
+                          at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), s, tickets,
+                          tickets ? kSplitSlots + kQueueInts : 0);
+  if (q.T == 0 || err != hipSuccess) return err;
+  // 3. the experts' forward quantities on the kept rows, as a training forward keeps them
+  const int ncu = bf16 ? device_split_cus() : 0;
+  int32_t* queue = tickets ? tickets + kSplitSlots : nullptr;
+  err = run_experts_saving(q, x, perm, offsets, w1, w3, w2, at<void>(ws, L.a), at<void>(ws, L.b),
+                           at<void>(ws, L.h), at<void>(ws, L.y),
+                           (tickets && ncu > 0) ? at<float>(ws, L.gsplit) : nullptr,
+                           (tickets && ncu > 0) ? tickets : nullptr, queue, ncu, s);
+  if (err != hipSuccess) return err;
+  const BwdInputs in{idx, gates, logits, counts, offsets, perm, slot_row,
+                     at<void>(ws, L.a), at<void>(ws, L.b), at<void>(ws, L.h), at<void>(ws, L.y)};
+  return backward_from(q, in, x, w_router, w1, w3, w2, dout, d_aux, dx, dw_router, dbias, dw1,
+                       dw3, dw2, ws, true, s);
+}
+
+hipError_t launch_backward_saved(const Problem& q, const int32_t* idx, const float* gates,
+                                 const int32_t* counts, const int32_t* offsets,
+                                 const int32_t* slot_row, const void* saved, const void* x,
+                                 const void* w_router, const void* w1, const void* w3,
+                                 const void* w2, const void* dout, float d_aux, void* dx,
+                                 float* dw_router, float* dbias, void* dw1, void* dw3, void* dw2,
+                                 void* ws, hipStream_t s) {
+  if (q.T == 0) return hipSuccess;
+  const SavedLayout S = saved_layout(q);
+  const char* sv = (const char*)saved;
+  const BwdInputs in{idx, gates, (const float*)(sv + S.logits), counts, offsets,
+                     (const int32_t*)(sv + S.perm), slot_row, sv + S.a, sv + S.b, sv + S.h,
+                     sv + S.y};
+  return backward_from(q, in, x, w_router, w1, w3, w2, dout, d_aux, dx, dw_router, dbias, dw1,
+                       dw3, dw2, ws, false, s);
+}
+
+namespace {
+
+hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
+                         const void* w_router, const void* w1, const void* w3, const void* w2,
+                         const void* dout, float d_aux, void* dx, float* dw_router, float* dbias,
+                         void* dw1, void* dw3, void* dw2, void* ws, bool tickets_zeroed,
+                         hipStream_t s) {
+  const BwdLayout L = bwd_layout(q);
+  const bool bf16 = q.dtype == MOE_BF16;
+  const bool linear = q.kind == MOE_EXPERT_LINEAR, swiglu = q.kind == MOE_EXPERT_SWIGLU;
+  const int32_t* idx = in.idx;
+  const float* gates = in.gates;
+  const float* logits = in.logits;
+  const int32_t* counts = in.counts;
+  const int32_t* offsets = in.offsets;
+  const int32_t* perm = in.perm;
+  const int32_t* slot_row = in.slot_row;
+  hipError_t err = hipSuccess;
   float* split_ws = nullptr;
   int32_t* split_ctr = nullptr;
   int32_t* queue = nullptr;
@@ -973,19 +1076,15 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
     }
   }
   const GemmRes res{split_ws, split_ctr, queue, ncu};
-  if (err == hipSuccess)
-    err = launch_dispatch(q, idx, x, counts, offsets, perm, slot_row, nullptr,
-                          at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), s,
-                          queue ? at<int32_t>(ws, L.gctr) : nullptr,
-                          queue ? kSplitSlots + kQueueInts : 0);
-  if (q.T == 0) {
-    return err;  // nothing routed: the caller's outputs are empty or left as they are
-  }
+  if (q.T == 0) return hipSuccess;  // nothing routed: the caller's outputs are left as they are
+  // the GEMMs' split tickets and work queue start at zero (the recompute's dispatch cleared
+  // them; a saved forward's workspace is another buffer)
+  if (queue && !tickets_zeroed) err = launch_zero_tickets(at<int32_t>(ws, L.gctr), kSplitSlots + kQueueInts, s);
   const int64_t D = q.D, DH = q.DH, Do = q.D_out;
-  void* a = at<void>(ws, L.a);
-  void* b = at<void>(ws, L.b);
-  void* h = at<void>(ws, L.h);
-  void* y = at<void>(ws, L.y);
+  const void* a = in.a;
+  const void* b = in.b;
+  const void* h = in.h;
+  const void* y = in.y;
   void* dy = at<void>(ws, L.dy);
   void* dh = at<void>(ws, L.dh);
   void* da = at<void>(ws, L.da);
@@ -1017,32 +1116,6 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
       err = hipGetLastError();
     }
   };
-  // 3. the experts' forward quantities on the kept rows
-  if (linear) {
-    if (err == hipSuccess)
-      err = fwd_gemm(q, x, D, perm, w1, D, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
-  } else {
-    if (err == hipSuccess)
-      err = fwd_gemm(q, x, D, perm, w1, D, DH, offsets, a, split_ws, split_ctr, queue, ncu, s);
-    if (err == hipSuccess && swiglu)
-      err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_ctr, queue, ncu, s);
-    if (err == hipSuccess) {
-      if (bf16 && DH % 8 == 0)
-        hipLaunchKernelGGL(act_forward_bf16x8_kernel, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
-                           offsets, q.E, (const uint4*)a, (const uint4*)b, (uint4*)h);
-      else if (bf16)
-        hipLaunchKernelGGL(act_forward_kernel<uint16_t>, dim3(ew_grid), dim3(256), 0, s, DH,
-                           q.kind, offsets, q.E, (const uint16_t*)a, (const uint16_t*)b,
-                           (uint16_t*)h);
-      else
-        hipLaunchKernelGGL(act_forward_kernel<float>, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
-                           offsets, q.E, (const float*)a, (const float*)b, (float*)h);
-      err = hipGetLastError();
-    }
-    if (err == hipSuccess)
-      err = fwd_gemm(q, h, DH, nullptr, w2, DH, Do, offsets, y, split_ws, split_ctr, queue, ncu,
-                     s);
-  }
   // 4. combine backward: dy rows and dgates
   if (err == hipSuccess) {
     const unsigned grid = (unsigned)((q.T + 3) / 4);
@@ -1152,5 +1225,7 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   }
   return err;
 }
+
+}  // namespace
 
 }  // namespace moe

@@ -99,6 +99,27 @@ hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
                            int32_t* pad_offsets = nullptr);
 
 // Backward of the layer (backward.hip): workspace bytes and the launch sequence.
+// A training forward's saved state (byte offsets in the caller's buffer, 256-byte aligned):
+// the float32 logits (T, E), the permutation (T*k), and per expert row (T*k rows, p's dtype)
+// the pre-activations a (ReLU, SwiGLU) and b (SwiGLU), the hidden h and the expert outputs y.
+struct SavedLayout {
+  size_t logits, perm, a, b, h, y, total;
+};
+SavedLayout saved_layout(const Problem& q);
+// The experts' forward on the kept rows (row r reads token row perm[r] / top_k of x), keeping
+// a, b, h and y; the same kernels serve the training forward and the backward's recompute.
+hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* perm,
+                              const int32_t* offsets, const void* w1, const void* w3,
+                              const void* w2, void* a, void* b, void* h, void* y,
+                              float* split_ws, int32_t* split_ctr, int32_t* queue, int ncu,
+                              hipStream_t s);
+hipError_t launch_backward_saved(const Problem& q, const int32_t* idx, const float* gates,
+                                 const int32_t* counts, const int32_t* offsets,
+                                 const int32_t* slot_row, const void* saved, const void* x,
+                                 const void* w_router, const void* w1, const void* w3,
+                                 const void* w2, const void* dout, float d_aux, void* dx,
+                                 float* dw_router, float* dbias, void* dw1, void* dw3, void* dw2,
+                                 void* ws, hipStream_t s);
 size_t backward_ws_bytes(const Problem& q);
 hipError_t launch_backward(const Problem& q, const void* x, const void* w_router, const float* bias,
                            const void* w1, const void* w3, const void* w2, const void* dout,
@@ -147,6 +168,11 @@ struct GroupedGemm {
   const int32_t* k_offsets;
   const int32_t* b_offsets;
   int64_t group_rows;
+  // Optional (null: not stored; 256 x 256 kernel only): the pre-activations of an EPI_RELU or
+  // EPI_SWIGLU product, in C's layout and type: pre_a = A B0 (before the ReLU, or the SwiGLU
+  // gate input), pre_b = A B1 (SwiGLU only).
+  void* pre_a;
+  void* pre_b;
 };
 constexpr int kSplitSlots = 256;
 constexpr int kQueueInts = 16;

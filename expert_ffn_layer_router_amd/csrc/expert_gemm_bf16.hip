@@ -573,17 +573,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         const bool odd = lane & 1;
         const int lrow = wr0 + 4 * (lane >> 5) + (odd ? 1 : 0);
         const int colp = (lane & 31) & ~1;
-        uint16_t* lp = C + (int64_t)(row0 + lrow) * N + n0 + colp;
+        const int64_t lofs = (int64_t)(row0 + lrow) * N + n0 + colp;
+        uint16_t* lp = C + lofs;
+        // optional stores of the pre-activations (the up GEMM's x W1 and x W3), same layout as C
+        uint16_t* const pa = (uint16_t*)g.pre_a;
+        uint16_t* const pb = (uint16_t*)g.pre_b;
         const int ccol0 = 32 * (kSwiGLU ? wc0 / 2 : wc0);  // first output column of the wave
         const int ccols = 32 * (kSwiGLU ? NN / 2 : NN);
         const bool whole = wr0 + 64 <= rows && n0 + ccol0 + ccols <= N;
-        auto put = [&](int mi, int v0, int cq, float x0, float x1) {
+        auto put_at = [&](uint16_t* base, int mi, int v0, int cq, float x0, float x1) {
           const float recv = swap_adjacent_lanes(odd ? x0 : x1);
           const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
           const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
           if (whole || (lrow + dr < rows && n0 + cq + colp < N))
-            *(uint32_t*)(lp + (int64_t)dr * N + cq) = pk;
+            *(uint32_t*)(base + lofs + (int64_t)dr * N + cq) = pk;
         };
+        auto put = [&](int mi, int v0, int cq, float x0, float x1) { put_at(C, mi, v0, cq, x0, x1); };
         if (parts == 1) {
           if (wr0 < rows) {  // a whole tile: store this wave's part from the accumulators
 #pragma unroll
@@ -594,13 +599,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
                 for (int v0 = 0; v0 < 16; v0 += 2) {
                   float x0, x1;
                   if (kSwiGLU) {  // gate in the wave's column tile 2q, up in 2q + 1
-                    x0 = silu_f(acc_get(acc[mi][2 * q][v0])) * acc_get(acc[mi][2 * q + 1][v0]);
-                    x1 = silu_f(acc_get(acc[mi][2 * q][v0 + 1])) *
-                         acc_get(acc[mi][2 * q + 1][v0 + 1]);
+                    const float g0 = acc_get(acc[mi][2 * q][v0]);
+                    const float g1 = acc_get(acc[mi][2 * q][v0 + 1]);
+                    const float u0 = acc_get(acc[mi][2 * q + 1][v0]);
+                    const float u1 = acc_get(acc[mi][2 * q + 1][v0 + 1]);
+                    x0 = silu_f(g0) * u0;
+                    x1 = silu_f(g1) * u1;
+                    if (pa) {
+                      put_at(pa, mi, v0, ccol0 + 32 * q, g0, g1);
+                      put_at(pb, mi, v0, ccol0 + 32 * q, u0, u1);
+                    }
                   } else {
                     x0 = acc_get(acc[mi][q][v0]);
                     x1 = acc_get(acc[mi][q][v0 + 1]);
                     if (EPI == EPI_RELU) {
+                      if (pa) put_at(pa, mi, v0, ccol0 + 32 * q, x0, x1);
                       x0 = fmaxf(x0, 0.f);
                       x1 = fmaxf(x1, 0.f);
                     }
@@ -671,17 +684,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
                     for (int q = 0; q < 4; ++q) {
                       const f32x4 gt = t[2 * q], up = t[2 * q + 1];
 #pragma unroll
-                      for (int i4 = 0; i4 < 4; i4 += 2)
+                      for (int i4 = 0; i4 < 4; i4 += 2) {
                         put(mi, 4 * v4 + i4, 32 * q, silu_f(gt[i4]) * up[i4],
                             silu_f(gt[i4 + 1]) * up[i4 + 1]);
+                        if (pa) {
+                          put_at(pa, mi, 4 * v4 + i4, 32 * q, gt[i4], gt[i4 + 1]);
+                          put_at(pb, mi, 4 * v4 + i4, 32 * q, up[i4], up[i4 + 1]);
+                        }
+                      }
                     }
                   } else {
 #pragma unroll
                     for (int c = 0; c < 8; ++c) {
                       f32x4 x = t[c];
-                      if (EPI == EPI_RELU)
+                      if (EPI == EPI_RELU) {
+                        if (pa)
+#pragma unroll
+                          for (int i4 = 0; i4 < 4; i4 += 2)
+                            put_at(pa, mi, 4 * v4 + i4, 32 * c, x[i4], x[i4 + 1]);
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) x[i4] = fmaxf(x[i4], 0.f);
+                      }
 #pragma unroll
                       for (int i4 = 0; i4 < 4; i4 += 2) put(mi, 4 * v4 + i4, 32 * c, x[i4], x[i4 + 1]);
                     }

@@ -278,6 +278,38 @@ moe_status moe_backward(const moe_problem* p, const void* x, const void* w_route
                         void* dw1, void* dw3, void* dw2, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ---- Training forward and the backward from its saved state ------------------------------
+ * The backward above recomputes what it needs; a training step can instead keep it from the
+ * forward. moe_forward_train is moe_forward (no router options) that also writes, into the
+ * caller's `saved` buffer (moe_saved_size bytes, 256-byte aligned, device memory): the float32
+ * router logits (T, E), the permutation of the kept slots, and for every kept row the
+ * pre-activations x W1 (ReLU, SwiGLU) and x W3 (SwiGLU), the hidden activation and the
+ * expert output, in p->dtype. The values are the ones moe_backward recomputes (the same
+ * kernels), so moe_backward_saved, given that buffer and the forward's expert_indices, gates,
+ * expert_counts, expert_offsets and slot_row, returns bit for bit what moe_backward returns
+ * for the same inputs and dout. The caller owns `saved`, must not change it in between, and
+ * sizes the workspaces with moe_workspace_size (forward) and moe_backward_workspace_size.
+ * Errors as for moe_forward / moe_backward, plus MOE_ERR_WORKSPACE for a missing, short or
+ * misaligned `saved` (T > 0). The gradients are the ones moe_backward defines (same passages
+ * of the ML Grind and Sparsely-Gated Layer pages). */
+size_t moe_saved_size(const moe_problem* p);
+
+moe_status moe_forward_train(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, const void* w1, const void* w3,
+                             const void* w2, void* out, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* slot_row, void* saved, size_t saved_bytes, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+moe_status moe_backward_saved(const moe_problem* p, const void* x, const void* w_router,
+                              const void* w1, const void* w3, const void* w2,
+                              const int32_t* expert_indices, const float* gates,
+                              const int32_t* expert_counts, const int32_t* expert_offsets,
+                              const int32_t* slot_row, const void* saved, size_t saved_bytes,
+                              const void* dout, float d_aux, void* dx, float* dw_router,
+                              float* dbias, void* dw1, void* dw3, void* dw2, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -183,3 +183,65 @@ def test_backward_with_no_tokens():
     torch.cuda.synchronize()
     for t in (dwr, db, dw1, dw3, dw2):
         assert bool((t == 7.0).all())
+
+
+# --- the training forward and the backward from its saved state -----------------------------
+
+SAVED_CASES = {
+    "swiglu_e8_k2": CASES["swiglu_e8_k2"],
+    "swiglu_zipf_cap": CASES["swiglu_zipf_cap"],
+    "relu_top1_cap": CASES["relu_top1_cap"],
+    "linear_bf16": CASES["linear_bf16"],
+    "swiglu_f32": CASES["swiglu_f32"],
+    "relu_f32_ragged_cap": CASES["relu_f32_ragged_cap"],
+    # bf16 with D not a multiple of 128: the 128 x 128 GEMM, pre-activations by products of
+    # their own
+    "swiglu_bf16_d200": spec("mixtral_swiglu_bf16", T=300, D=200, DH=136, E=4, top_k=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SAVED_CASES))
+def test_training_forward_and_saved_backward_match(name):
+    """moe_forward_train returns exactly what moe_forward returns, and moe_backward_saved
+    (from its saved state) exactly what moe_backward returns."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = SAVED_CASES[name]
+    _say(f"[gpu] training forward + saved backward {name} {sp}")
+    I = make_inputs(sp, seed=23)
+    p = B.Problem.from_spec(sp)
+    d = device_inputs(I)
+    ref = B.forward(p, d["x"], d["w_router"], d["bias"], d["w1"], d["w3"], d["w2"])
+    outs = B.alloc_outputs(p)
+    saved = torch.empty(max(B.saved_size(p), 1), dtype=torch.uint8, device="cuda")
+    ws = B.alloc_workspace(p)
+    B.moe_forward_train(p, d["x"], d["w_router"], d["bias"], d["w1"], d["w3"], d["w2"],
+                        outs["out"], outs["expert_indices"], outs["gates"], outs["aux_loss"],
+                        outs["expert_counts"], outs["expert_offsets"], outs["slot_row"], saved,
+                        ws)
+    torch.cuda.synchronize()
+    for k in ("out", "expert_indices", "gates", "aux_loss", "expert_counts", "expert_offsets",
+              "slot_row"):
+        assert np.array_equal(to_host(outs[k]), to_host(ref[k])), k
+    stored, _ = _dout(sp)
+    want = run_backward(I, stored, 0.37)
+    dt = torch.bfloat16 if sp.dtype == "bf16" else torch.float32
+    dx = torch.full((sp.T, sp.D), 7.0, dtype=dt, device="cuda")
+    dwr = torch.full((sp.D, sp.E), 7.0, dtype=torch.float32, device="cuda")
+    db = torch.full((sp.E,), 7.0, dtype=torch.float32, device="cuda")
+    dw1 = torch.full(d["w1"].shape, 7.0, dtype=dt, device="cuda")
+    dw3 = None if d["w3"] is None else torch.full(d["w3"].shape, 7.0, dtype=dt, device="cuda")
+    dw2 = None if d["w2"] is None else torch.full(d["w2"].shape, 7.0, dtype=dt, device="cuda")
+    bws = torch.empty(max(B.backward_workspace_size(p), 1), dtype=torch.uint8, device="cuda")
+    B.moe_backward_saved(p, d["x"], d["w_router"], d["w1"], d["w3"], d["w2"],
+                         outs["expert_indices"], outs["gates"], outs["expert_counts"],
+                         outs["expert_offsets"], outs["slot_row"], saved, to_dev(stored), 0.37,
+                         dx, dwr, db, dw1, dw3, dw2, bws)
+    torch.cuda.synchronize()
+    got = dict(dx=to_host(dx), dw_router=to_host(dwr), dbias=to_host(db), dw1=to_host(dw1))
+    if dw3 is not None:
+        got["dw3"] = to_host(dw3)
+    if dw2 is not None:
+        got["dw2"] = to_host(dw2)
+    for k in want:
+        assert np.array_equal(got[k], want[k]), k
