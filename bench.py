@@ -43,8 +43,8 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("dfbf0879053eef0a4f4ddd740370d5c199bba565a1cd35cc31bd8346e1a3dedf",
-                            3441784.5714285714, 237637.125),
+    "mixtral_swiglu_bf16": ("2e0c7c0e1ccb066c47bd33c989376a2dcc779772d9b549c6f3b9675e17ddf4c2",
+                            3366065.0089285714, 236435.5982142857),
 }
 
 

@@ -266,7 +266,9 @@ hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s) {
                : hipErrorInvalidValue;
   const bool k256 = g.dtype == MOE_BF16 && g.K % 128 == 0 && g.queue;
   if (g.b_kmajor && (!k256 || g.epilogue != EPI_NONE)) return hipErrorInvalidValue;
-  if ((g.pre_a || g.pre_b) && !k256) return hipErrorInvalidValue;
+  if ((g.pre_a || g.pre_b) &&
+      (!k256 || g.epilogue == EPI_NONE || !g.pre_a || (g.epilogue == EPI_SWIGLU) != (g.pre_b != nullptr)))
+    return hipErrorInvalidValue;
   if (k256) return launch_grouped_gemm_bf16_256(g, s);
   if (g.ev_start) hipEventRecord(g.ev_start, s);
   if (g.dtype == MOE_BF16) {

@@ -38,6 +38,8 @@
 
 #include <type_traits>
 
+#include <limits.h>
+
 #include "common.hpp"
 #include "tile_schedule.hpp"
 
@@ -46,6 +48,7 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kThreads = 256;
+constexpr int kTileBlockM = 4;       // M-tiles per L2-sharing block of one group (wgrad)
 constexpr int kTileBlockN = 8;       // column tiles per L2-sharing block of one expert
 constexpr int kNBuf = 4;             // stage buffers; loads run kNBuf stages ahead
 constexpr uint32_t kHalf = kBK * 256 * 2;  // bytes of one stage of either operand (16 KB)
@@ -267,11 +270,12 @@ __device__ __forceinline__ float swap_adjacent_lanes(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, true));
 }
 
-template <int EPI, bool BT = false, bool KG = false>
+template <int EPI, bool BT = false, bool KG = false, bool SAVE = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const GroupedGemm g, int nt) {
   constexpr bool kSwiGLU = EPI == EPI_SWIGLU;
   static_assert(!BT || EPI == EPI_NONE, "the K-major B mode has no epilogue");
   static_assert(!KG || (EPI == EPI_NONE && !BT), "the K-grouped mode has no epilogue");
+  static_assert(!SAVE || EPI != EPI_NONE, "only an activation has pre-activations to store");
   __shared__ __align__(16) char sbuf[kNBuf * kBuf];
   __shared__ int s_unit[2];  // work positions of later units, by unit parity
   __shared__ int s_last;
@@ -367,7 +371,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     Unit u;
     u.L = L;
     u.ks = ks;
-    tile_of(sc, g.offsets, kBM, nt, kTileBlockN, L, u.e, u.row0, u.rows, u.n_tile);
+    // M-blocks for the weight gradients (16 to 56 M-tiles a group, all whole); the forward's
+    // experts have a few M-tiles, the last often ragged, and keep them in one block
+    tile_of(sc, g.offsets, kBM, nt, KG ? kTileBlockM : INT_MAX, kTileBlockN, L, u.e, u.row0,
+            u.rows, u.n_tile);
     u.e = __builtin_amdgcn_readfirstlane(u.e);
     u.row0 = __builtin_amdgcn_readfirstlane(u.row0);
     u.rows = __builtin_amdgcn_readfirstlane(u.rows);
@@ -605,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
                     const float u1 = acc_get(acc[mi][2 * q + 1][v0 + 1]);
                     x0 = silu_f(g0) * u0;
                     x1 = silu_f(g1) * u1;
-                    if (pa) {
+                    if constexpr (SAVE) {
                       put_at(pa, mi, v0, ccol0 + 32 * q, g0, g1);
                       put_at(pb, mi, v0, ccol0 + 32 * q, u0, u1);
                     }
@@ -613,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
                     x0 = acc_get(acc[mi][q][v0]);
                     x1 = acc_get(acc[mi][q][v0 + 1]);
                     if (EPI == EPI_RELU) {
-                      if (pa) put_at(pa, mi, v0, ccol0 + 32 * q, x0, x1);
+                      if constexpr (SAVE) put_at(pa, mi, v0, ccol0 + 32 * q, x0, x1);
                       x0 = fmaxf(x0, 0.f);
                       x1 = fmaxf(x1, 0.f);
                     }
@@ -687,7 +694,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
                       for (int i4 = 0; i4 < 4; i4 += 2) {
                         put(mi, 4 * v4 + i4, 32 * q, silu_f(gt[i4]) * up[i4],
                             silu_f(gt[i4 + 1]) * up[i4 + 1]);
-                        if (pa) {
+                        if constexpr (SAVE) {
                           put_at(pa, mi, 4 * v4 + i4, 32 * q, gt[i4], gt[i4 + 1]);
                           put_at(pb, mi, 4 * v4 + i4, 32 * q, up[i4], up[i4 + 1]);
                         }
@@ -698,7 +705,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
                     for (int c = 0; c < 8; ++c) {
                       f32x4 x = t[c];
                       if (EPI == EPI_RELU) {
-                        if (pa)
+                        if constexpr (SAVE)
 #pragma unroll
                           for (int i4 = 0; i4 < 4; i4 += 2)
                             put_at(pa, mi, 4 * v4 + i4, 32 * c, x[i4], x[i4 + 1]);
@@ -798,12 +805,20 @@ hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) 
                             g.ev_start, g.ev_stop, 0, g, (int)nt);
       break;
     case EPI_RELU:
-      hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s,
-                            g.ev_start, g.ev_stop, 0, g, (int)nt);
+      if (g.pre_a)
+        hipExtLaunchKernelGGL((gemm_bf16_256_kernel<EPI_RELU, false, false, true>), grid,
+                              dim3(kThreads), 0, s, g.ev_start, g.ev_stop, 0, g, (int)nt);
+      else
+        hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_RELU>, grid, dim3(kThreads), 0, s,
+                              g.ev_start, g.ev_stop, 0, g, (int)nt);
       break;
     default:
-      hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s,
-                            g.ev_start, g.ev_stop, 0, g, (int)nt);
+      if (g.pre_a)
+        hipExtLaunchKernelGGL((gemm_bf16_256_kernel<EPI_SWIGLU, false, false, true>), grid,
+                              dim3(kThreads), 0, s, g.ev_start, g.ev_stop, 0, g, (int)nt);
+      else
+        hipExtLaunchKernelGGL(gemm_bf16_256_kernel<EPI_SWIGLU>, grid, dim3(kThreads), 0, s,
+                              g.ev_start, g.ev_stop, 0, g, (int)nt);
       break;
   }
   return hipGetLastError();

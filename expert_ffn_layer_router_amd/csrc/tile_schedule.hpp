@@ -49,10 +49,10 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 }
 
 // Tiles of a grouped GEMM laid out as (M-tiles x nt column tiles) per expert, experts in
-// order; within an expert the tiles go in blocks of nb column tiles with the M-tiles fastest.
-// A block of one expert (its M-tiles x nb column tiles) is about as many tiles as one XCD runs
-// at once, so concurrent tiles share both their activation rows and their weight columns in
-// that XCD's L2. tile_scan takes the per-expert tile counts (every wave computes the same);
+// order; within an expert the tiles go in blocks of at most mb M-tiles by nb column tiles
+// (M-blocks outer, then column blocks, then the M-tiles fastest). A block (mb x nb tiles) is
+// about as many tiles as one XCD runs at once, so concurrent tiles share both their row
+// panels and their column panels in that XCD's L2, however many M-tiles the expert has. tile_scan takes the per-expert tile counts (every wave computes the same);
 // tile_of maps a linear tile id to (expert, first row, rows, column tile).
 struct TileScan {
   int excl, incl;  // this lane's experts (4 lane, .. 4 lane + 3): first tile id, one past last
@@ -85,8 +85,8 @@ __device__ __forceinline__ TileScan tile_scan(const int32_t* __restrict__ offset
 }
 
 __device__ __forceinline__ void tile_of(const TileScan& sc, const int32_t* __restrict__ offsets,
-                                        int BM, int nt, int nb, int L, int& e_out, int& row0,
-                                        int& rows, int& n_tile) {
+                                        int BM, int nt, int mb, int nb, int L, int& e_out,
+                                        int& row0, int& rows, int& n_tile) {
   const int lane = lane_id();
   const unsigned long long own = __ballot(L >= sc.excl && L < sc.incl);
   const int owner = __ffsll((long long)own) - 1;
@@ -104,10 +104,14 @@ __device__ __forceinline__ void tile_of(const TileScan& sc, const int32_t* __res
   local = __shfl(local, owner);
   const int cnt = offsets[e + 1] - offsets[e];
   const int tm = (cnt + BM - 1) / BM;  // M-tiles of this expert
-  const int blk = local / (tm * nb);
-  const int within = local - blk * tm * nb;
-  const int m = within % tm;
-  n_tile = blk * nb + within / tm;
+  const int mbe = min(mb, tm);           // (so mbe * nt <= tm * nt, the expert's tiles)
+  const int mblk = local / (mbe * nt);   // every M-block but the last has mbe M-tiles
+  const int mj = min(mbe, tm - mblk * mbe);
+  const int rem = local - mblk * mbe * nt;
+  const int blk = rem / (mj * nb);
+  const int within = rem - blk * mj * nb;
+  const int m = mblk * mbe + within % mj;
+  n_tile = blk * nb + within / mj;
   e_out = e;
   row0 = offsets[e] + m * BM;
   rows = min(BM, cnt - m * BM);
