@@ -206,3 +206,51 @@ def test_option_entry_points_reject_bad_options_before_launching():
                           fake, fake, fake, fake, fake, fake, 1 << 20, need, None, None)
     assert st == B.MOE_ERR_WORKSPACE
 
+
+
+def test_backward_and_training_entry_points_check_before_launching():
+    """moe_backward, moe_forward_train and moe_backward_saved report bad arguments from host
+    checks alone (no device is touched)."""
+    lib = B.lib()
+    fake = 1 << 20  # never dereferenced
+    big = 1 << 40
+    p = P()
+    pp = ctypes.byref(p.c())
+    # moe_backward: a NaN loss weight; SwiGLU without dw2; a short workspace
+    assert lib.moe_backward(pp, fake, fake, None, fake, fake, fake, fake, float("nan"), fake,
+                            fake, None, fake, fake, fake, fake, big, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_backward(pp, fake, fake, None, fake, fake, fake, fake, 0.5, fake, fake, None,
+                            fake, fake, None, fake, big, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_backward(pp, fake, fake, None, fake, fake, fake, fake, 0.5, fake, fake, None,
+                            fake, fake, fake, fake, 16, None) == B.MOE_ERR_WORKSPACE
+    # moe_forward_train: no aux_loss; a short, a misaligned and a missing saved buffer
+    assert lib.moe_forward_train(pp, fake, fake, None, fake, fake, fake, fake, fake, fake, None,
+                                 fake, fake, fake, fake, big, fake, big,
+                                 None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_train(pp, fake, fake, None, fake, fake, fake, fake, fake, fake, fake,
+                                 fake, fake, fake, fake, 16, fake, big,
+                                 None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_train(pp, fake, fake, None, fake, fake, fake, fake, fake, fake, fake,
+                                 fake, fake, fake, fake + 8, big, fake, big,
+                                 None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_train(pp, fake, fake, None, fake, fake, fake, fake, fake, fake, fake,
+                                 fake, fake, fake, None, 0, fake, big,
+                                 None) == B.MOE_ERR_WORKSPACE
+    # moe_backward_saved: no expert_counts; a short saved buffer
+    assert lib.moe_backward_saved(pp, fake, fake, fake, fake, fake, fake, fake, None, fake, fake,
+                                  fake, big, fake, 0.5, fake, fake, None, fake, fake, fake, fake,
+                                  big, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_backward_saved(pp, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                                  fake, 16, fake, 0.5, fake, fake, None, fake, fake, fake, fake,
+                                  big, None) == B.MOE_ERR_WORKSPACE
+
+
+def test_saved_size():
+    """The saved state holds the logits, the permutation and a, b, h, y per slot row."""
+    p = P(T=64, D=32, DH=48, D_out=32, E=8, top_k=2)
+    R = 64 * 2
+    need = 64 * 8 * 4 + R * 4 + 3 * R * 48 * 2 + R * 32 * 2
+    got = B.saved_size(p)
+    assert need <= got <= need + 6 * 256
+    assert B.saved_size(P(kind="relu2")) < got  # no b
+    assert B.saved_size(P(top_k=0)) == 0
