@@ -41,6 +41,24 @@ constexpr int kLds = kBK + 8;  // padded row stride (elements) of the LDS tiles
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xffffu; }
+
+// 8 bf16 (one 16-byte vector) to float32 and back (round to nearest even).
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 
 struct BwdGemm {
@@ -318,6 +336,39 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
   }
 }
 
+// bf16 version of combine_backward, 8 columns a lane (Dout % 8 == 0): lane l takes columns
+// 8 (l + 64 i) .. + 7, its float64 partial in column order, then the same butterfly.
+__global__ __launch_bounds__(kThreads) void combine_backward_bf16x8_kernel(
+    int64_t T, int k, int64_t Dout, const uint16_t* __restrict__ dout,
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ slot_row,
+    const float* __restrict__ gates, uint16_t* __restrict__ dy, float* __restrict__ dgates) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int64_t s = t * k + j;
+    const int row = slot_row[s];
+    double acc = 0.0;
+    if (row >= 0) {
+      const float g = gates[s];
+      for (int64_t c = 8 * lane; c < Dout; c += 8 * kWave) {
+        float d[8], yv[8], o[8];
+        unpack8(*(const uint4*)(dout + t * Dout + c), d);
+        unpack8(*(const uint4*)(y + (int64_t)row * Dout + c), yv);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          acc += (double)d[q] * (double)yv[q];
+          o[q] = g * d[q];
+        }
+        *(uint4*)(dy + (int64_t)row * Dout + c) = pack8(o);
+      }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) dgates[s] = (float)acc;
+  }
+}
+
 // Router backward, one wave per token (lane l holds experts l + 64 i): probabilities from the
 // float32 logits (float64 softmax), then dl over the chosen experts from the gates' softmax and
 // over all experts from the loss term.
@@ -397,27 +448,44 @@ __global__ __launch_bounds__(256) void dbias_kernel(int64_t T, int E, const floa
 }
 
 // dW_router[d, e] = sum_t x[t, d] dl[t, e] in two fixed-order levels: block (256 columns d,
-// 8 experts, token chunk c) sums its chunk's tokens in order into part[c, d, e]; then
-// dw_router_reduce adds the chunks in order.
+// 8 experts, token chunk c of at most kDwrMaxChunk tokens) sums its chunk's tokens in order
+// into part[c, d, e], with the chunk's dl rows staged in LDS; then dw_router_reduce adds the
+// chunks in order.
+constexpr int kDwrMaxChunk = 64;
 template <typename TIn>
 __global__ __launch_bounds__(256) void dw_router_partial_kernel(int64_t T, int64_t D, int E,
                                                                 int64_t tc,
                                                                 const TIn* __restrict__ x,
                                                                 const float* __restrict__ dl,
                                                                 float* __restrict__ part) {
+  __shared__ float s_dl[kDwrMaxChunk][8];
   const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = d < D;
   const int e0 = blockIdx.y * 8;
   const int64_t c = blockIdx.z, t0 = c * tc, t1 = min(T, t0 + tc);
-  if (d >= D) return;
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int64_t t = t0; t < t1; ++t) {
-    const float xv = load_as_f32(x, t * D + d);
+  // the chunk's tokens in order, kDwrMaxChunk dl rows in LDS at a time
+  for (int64_t b0 = t0; b0 < t1; b0 += kDwrMaxChunk) {
+    __syncthreads();  // the previous rows are no longer read
+    for (int i = threadIdx.x; i < kDwrMaxChunk * 8; i += 256) {
+      const int64_t t = b0 + i / 8;
+      const int e = e0 + i % 8;
+      s_dl[i / 8][i % 8] = (t < t1 && e < E) ? dl[t * E + e] : 0.f;
+    }
+    __syncthreads();
+    const int n = (int)min<int64_t>(kDwrMaxChunk, t1 - b0);
+    if (valid) {
+#pragma unroll 8
+      for (int i = 0; i < n; ++i) {
+        const float xv = load_as_f32(x, (b0 + i) * D + d);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (e0 + q < E) acc[q] = fmaf(xv, dl[t * E + e0 + q], acc[q]);
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(xv, s_dl[i][q], acc[q]);
+      }
+    }
   }
+  if (!valid) return;
 #pragma unroll
   for (int q = 0; q < 8; ++q)
     if (e0 + q < E) part[(c * D + d) * E + e0 + q] = acc[q];
@@ -427,7 +495,15 @@ __global__ __launch_bounds__(256) void dw_router_reduce_kernel(int64_t n, int nc
                                                                float* __restrict__ dw) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     float acc = 0.f;
-    for (int c = 0; c < nch; ++c) acc += part[(int64_t)c * n + i];
+    int c = 0;
+    for (; c + 8 <= nch; c += 8) {  // 8 loads in flight, added in chunk order
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = part[(int64_t)(c + q) * n + i];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += v[q];
+    }
+    for (; c < nch; ++c) acc += part[(int64_t)c * n + i];
     dw[i] = acc;
   }
 }
@@ -561,21 +637,6 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(int64_t T, int64_t D, int 
 
 // bf16 versions of the three kernels above, 8 elements a lane (16-byte loads and stores), for
 // DH % 8 == 0 (activations) and D % 8 == 0, E % 8 == 0 (dx). Same arithmetic, same order.
-__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(w[i] << 16);
-    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-__device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 __global__ __launch_bounds__(256) void act_backward_bf16x8_kernel(
     int64_t DH, int kind, const int32_t* __restrict__ offsets, int E, const uint4* __restrict__ a,
@@ -667,9 +728,13 @@ struct BwdLayout {
 };
 
 // Token chunks of the router-weight gradient's first level.
-static int dwr_chunks_of(int64_t T) {
-  const int64_t n = (T + 127) / 128;
-  return (int)(n < 1 ? 1 : (n > 32 ? 32 : n));
+// Token chunks of 32 (more, longer ones when the partials, chunks x D x E floats, would pass
+// 64 MB), at most 256.
+static int dwr_chunks_of(const Problem& q) {
+  int64_t n = (q.T + 31) / 32;
+  const int64_t per = std::max<int64_t>(1, (int64_t)q.D * q.E * 4);
+  n = std::min<int64_t>(n, std::max<int64_t>(1, ((int64_t)64 << 20) / per));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(n, 256));
 }
 
 static BwdLayout bwd_layout(const Problem& q) {
@@ -716,7 +781,7 @@ static BwdLayout bwd_layout(const Problem& q) {
   const bool split = q.dtype == MOE_BF16 && q.T > 0;
   L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
   L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
-  L.dwr_chunks = dwr_chunks_of(q.T);
+  L.dwr_chunks = dwr_chunks_of(q);
   L.dwr_tc = (q.T + L.dwr_chunks - 1) / L.dwr_chunks;
   L.dwr_part = take((size_t)L.dwr_chunks * (size_t)q.D * E * 4);
   L.kg_off = take(L.kg ? (E + 1) * 4 : 0);
@@ -1119,7 +1184,11 @@ hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
   // 4. combine backward: dy rows and dgates
   if (err == hipSuccess) {
     const unsigned grid = (unsigned)((q.T + 3) / 4);
-    if (bf16)
+    if (bf16 && Do % 8 == 0 && (uintptr_t)dout % 16 == 0)
+      hipLaunchKernelGGL(combine_backward_bf16x8_kernel, dim3(grid), dim3(kThreads), 0, s, q.T,
+                         q.top_k, Do, (const uint16_t*)dout, (const uint16_t*)y, slot_row, gates,
+                         (uint16_t*)dy, dgates);
+    else if (bf16)
       hipLaunchKernelGGL(combine_backward_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, q.T,
                          q.top_k, Do, (const uint16_t*)dout, (const uint16_t*)y, slot_row, gates,
                          (uint16_t*)dy, dgates);
