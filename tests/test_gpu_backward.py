@@ -245,3 +245,38 @@ def test_training_forward_and_saved_backward_match(name):
         got["dw2"] = to_host(dw2)
     for k in want:
         assert np.array_equal(got[k], want[k]), k
+
+
+def test_training_pair_with_no_tokens():
+    """T = 0: the training forward needs no saved buffer and writes zero counts and loss; the
+    saved backward writes nothing."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("mixtral_swiglu_bf16", T=0, D=128, DH=256)
+    p = B.Problem.from_spec(sp)
+    bf = torch.bfloat16
+    x = torch.empty((0, sp.D), dtype=bf, device="cuda")
+    wr = torch.zeros((sp.D, sp.E), dtype=bf, device="cuda")
+    w1 = torch.zeros((sp.E, sp.D, sp.DH), dtype=bf, device="cuda")
+    w3 = torch.zeros_like(w1)
+    w2 = torch.zeros((sp.E, sp.DH, sp.D_out), dtype=bf, device="cuda")
+    outs = B.alloc_outputs(p)
+    outs["aux_loss"].fill_(5.0)
+    outs["expert_counts"].fill_(5)
+    ws = B.alloc_workspace(p)
+    B.moe_forward_train(p, x, wr, None, w1, w3, w2, outs["out"], outs["expert_indices"],
+                        outs["gates"], outs["aux_loss"], outs["expert_counts"],
+                        outs["expert_offsets"], outs["slot_row"], None, ws)
+    torch.cuda.synchronize()
+    assert float(outs["aux_loss"].cpu()[0]) == 0.0
+    assert (to_host(outs["expert_counts"]) == 0).all()
+    dwr = torch.full((sp.D, sp.E), 7.0, dtype=torch.float32, device="cuda")
+    dw1 = torch.full(w1.shape, 7.0, dtype=bf, device="cuda")
+    bws = torch.empty(max(B.backward_workspace_size(p), 1), dtype=torch.uint8, device="cuda")
+    B.moe_backward_saved(p, x, wr, w1, w3, w2, outs["expert_indices"], outs["gates"],
+                         outs["expert_counts"], outs["expert_offsets"], outs["slot_row"], None,
+                         torch.empty((0, sp.D_out), dtype=bf, device="cuda"), 0.5,
+                         torch.empty((0, sp.D), dtype=bf, device="cuda"), dwr, None, dw1,
+                         torch.empty_like(w3), torch.empty_like(w2), bws)
+    torch.cuda.synchronize()
+    assert bool((dwr == 7.0).all()) and bool((dw1 == 7.0).all())
