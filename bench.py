@@ -94,10 +94,11 @@ def device_tensor(a):
 
 
 def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4, N=None,
-                 renormalise: bool = True) -> dict:
+                 renormalise: bool = True, dout=None, d_aux: float = 0.0) -> dict:
     """The oracle as it stands, on the first `tokens` tokens of the same inputs (and router
     options), repeated until at least `min_seconds` of wall time (at most `max_passes`
-    passes)."""
+    passes). With `dout` (host values, (T, D_out)), each pass is the oracle's backward (its
+    forward and every gradient), the work of a forward+backward step."""
     from threadpoolctl import threadpool_info
 
     import oracle
@@ -106,6 +107,12 @@ def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4,
     wr, w1, w2, w3 = I.values("w_router"), I.values("w1"), I.values("w2"), I.values("w3")
     passes, t0 = 0, time.perf_counter()
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        if dout is not None:
+            oracle.moe_backward(x, wr, sp.top_k, sp.kind, w1, w2, w3, bias=I.bias,
+                                capacity_factor=sp.capacity_factor, dout=dout[:tokens],
+                                d_aux=d_aux)
+            passes += 1
+            continue
         oracle.moe_forward(x, wr, sp.top_k, sp.kind, w1, w2, w3, bias=I.bias,
                            capacity_factor=sp.capacity_factor,
                            w_noise=None if N is None else N.w_values(),
@@ -117,10 +124,12 @@ def cpu_baseline(I, tokens: int, min_seconds: float = 10.0, max_passes: int = 4,
     threads = min(threads, len(os.sched_getaffinity(0)))
     return {"value": passes * tokens / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"oracle.moe_forward (NumPy float64, BLAS on {threads} threads) over the "
+            "sample": f"oracle.{'moe_backward (forward and all gradients)' if dout is not None else 'moe_forward'}"
+                      f" (NumPy float64, BLAS on {threads} threads) over the "
                       f"first {tokens} of {sp.T} tokens of the same seeded inputs, {passes} "
-                      f"pass(es), {dt:.1f} s wall; each pass widens every expert's weights to "
-                      f"float64 one expert at a time"}
+                      f"pass(es), {dt:.1f} s wall"
+                      + ("" if dout is not None else "; each pass widens every expert's "
+                                                     "weights to float64 one expert at a time")}
 
 
 def main() -> int:
@@ -394,9 +403,16 @@ def main() -> int:
                                                "the pre-activations, h, y, logits and perm"}
             result["roofline"]["kernel"] += ", timed in plain forward steps beside the timed ones"
     if not args.no_cpu_baseline:
-        n = min(args.cpu_baseline_tokens, T) if args.cpu_baseline_tokens > 0 else T
+        # the whole batch for the forward; the backward oracle (about ten times the work a
+        # token) on a 1024-token sample unless asked otherwise
+        n = (min(args.cpu_baseline_tokens, T) if args.cpu_baseline_tokens > 0
+             else (min(T, 1024) if bwd is not None else T))
         log(f"[bench] CPU oracle baseline on {n} tokens")
-        result["cpu_baseline"] = cpu_baseline(I, n, N=N, renormalise=not args.no_renormalise)
+        dout_host = None
+        if bwd is not None:
+            dout_host = bwd["dout"].float().cpu().numpy().astype(np.float64)
+        result["cpu_baseline"] = cpu_baseline(I, n, N=N, renormalise=not args.no_renormalise,
+                                              dout=dout_host, d_aux=0.01)
     print(json.dumps(result), flush=True)
     return 0
 
