@@ -37,20 +37,38 @@ __global__ __launch_bounds__(kThreads) void combine_bf16x8_kernel(
   const int64_t t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + wave_id()));
   if (t >= T) return;
   const int lane = lane_id();
-  for (int64_t c = lane; c < n_vec; c += kWave) {
-    float acc[8];
+  // 4 column chunks a pass, so 4 k loads are in flight; each output is still the sum over
+  // j ascending
+  constexpr int U = 4;
+  for (int64_t c0 = lane; c0 < n_vec; c0 += U * kWave) {
+    float acc[U][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
     for (int j = 0; j < k; ++j) {
-      const int r = slot_row[t * k + j];
+      const int r = __builtin_amdgcn_readfirstlane(slot_row[t * k + j]);
       if (r < 0) continue;
       const float g = gates[t * k + j];
-      float v[8];
-      unpack8(y[(int64_t)r * n_vec + c], v);
+      uint4 w[U];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + u * kWave;
+        w[u] = c < n_vec ? y[(int64_t)r * n_vec + c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float v[8];
+        unpack8(w[u], v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g, v[i], acc[u][i]);
+      }
     }
-    out[t * n_vec + c] = pack8(acc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kWave;
+      if (c < n_vec) out[t * n_vec + c] = pack8(acc[u]);
+    }
   }
 }
 
