@@ -1161,7 +1161,10 @@ hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
   uint16_t* dxr2 = dxr1 + (size_t)q.slots() * q.D;
   float* dgates = at<float>(ws, L.dgates);
   float* dl = at<float>(ws, L.dl);
-  const unsigned ew_grid = 2048;
+  // elementwise kernels: about two 8-element vectors a thread over the worst-case rows
+  const unsigned ew_grid = (unsigned)std::max<int64_t>(
+      1, std::min<int64_t>(((int64_t)q.slots() * std::max<int64_t>(q.DH, 8) / 8 + 511) / 512,
+                           65536));
   // K-grouped weight gradients: per-expert K ranges, group rows, the column map
   const bool kg = L.kg && queue != nullptr;
   int32_t* grow1 = at<int32_t>(ws, L.kg_grow1);  // e * D
