@@ -280,3 +280,50 @@ def test_training_pair_with_no_tokens():
                          torch.empty_like(w3), torch.empty_like(w2), bws)
     torch.cuda.synchronize()
     assert bool((dwr == 7.0).all()) and bool((dw1 == 7.0).all())
+
+
+def test_training_pair_full_size_matches_recompute():
+    """The Mixtral-shaped layer at full size, as bench.py --train runs it: the training
+    forward's outputs equal moe_forward's, and the saved backward's gradients equal
+    moe_backward's, bit for bit."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = spec("mixtral_swiglu_bf16")
+    _say(f"[gpu] full-size training pair {sp}")
+    I = make_inputs(sp, seed=0)
+    p = B.Problem.from_spec(sp)
+    d = device_inputs(I)
+    ref = B.forward(p, d["x"], d["w_router"], d["bias"], d["w1"], d["w3"], d["w2"])
+    outs = B.alloc_outputs(p)
+    saved = torch.empty(B.saved_size(p), dtype=torch.uint8, device="cuda")
+    ws = B.alloc_workspace(p)
+    B.moe_forward_train(p, d["x"], d["w_router"], d["bias"], d["w1"], d["w3"], d["w2"],
+                        outs["out"], outs["expert_indices"], outs["gates"], outs["aux_loss"],
+                        outs["expert_counts"], outs["expert_offsets"], outs["slot_row"], saved,
+                        ws)
+    torch.cuda.synchronize()
+    for k in ("out", "expert_indices", "gates", "aux_loss", "expert_counts", "slot_row"):
+        assert torch.equal(outs[k], ref[k]), k
+    del ws
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dout = torch.randn((sp.T, sp.D_out), generator=gen, device="cuda").to(torch.bfloat16)
+
+    def grads():
+        return dict(dx=torch.empty_like(d["x"]),
+                    dwr=torch.empty((sp.D, sp.E), dtype=torch.float32, device="cuda"),
+                    db=torch.empty((sp.E,), dtype=torch.float32, device="cuda"),
+                    dw1=torch.empty_like(d["w1"]), dw3=torch.empty_like(d["w3"]),
+                    dw2=torch.empty_like(d["w2"]))
+    bws = torch.empty(B.backward_workspace_size(p), dtype=torch.uint8, device="cuda")
+    a = grads()
+    B.moe_backward(p, d["x"], d["w_router"], d["bias"], d["w1"], d["w3"], d["w2"], dout, 0.01,
+                   a["dx"], a["dwr"], a["db"], a["dw1"], a["dw3"], a["dw2"], bws)
+    b = grads()
+    B.moe_backward_saved(p, d["x"], d["w_router"], d["w1"], d["w3"], d["w2"],
+                         outs["expert_indices"], outs["gates"], outs["expert_counts"],
+                         outs["expert_offsets"], outs["slot_row"], saved, dout, 0.01, b["dx"],
+                         b["dwr"], b["db"], b["dw1"], b["dw3"], b["dw2"], bws)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+        assert bool(torch.isfinite(a[k].float()).all()), k
