@@ -336,6 +336,80 @@ __global__ __launch_bounds__(kThreads) void combine_backward_kernel(
   }
 }
 
+// The activation backward fused with the gate gradient, one wave per kept row r (slot
+// s = perm[r]), for bf16 ReLU / SwiGLU layers with DH % 8 == 0. g = dout_t W2^T (the dgrad of
+// the unscaled output gradient); h = act(a, b) from the stored pre-activations; then
+// dgate[s] = <g, h> (float64 in column order per lane, then a fixed butterfly), which equals
+// <dout_t, h W2> = <dout_t, y>, and with dh = gate * g: SwiGLU da = dh b silu'(a),
+// db = dh silu(a); ReLU da = dh [a > 0].
+__global__ __launch_bounds__(kThreads) void act_backward_rows_bf16x8_kernel(
+    int64_t DH, int kind, const int32_t* __restrict__ offsets, int E,
+    const int32_t* __restrict__ perm, const float* __restrict__ gates,
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b,
+    const uint16_t* __restrict__ g, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
+    float* __restrict__ dgates) {
+  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (r >= offsets[E]) return;
+  const int lane = lane_id();
+  const int slot = perm[r];
+  const float gate = gates[slot];
+  const bool swiglu = kind == MOE_EXPERT_SWIGLU;
+  double acc = 0.0;
+  for (int64_t c = 8 * lane; c < DH; c += 8 * kWave) {
+    const int64_t i = r * DH + c;
+    float av[8], gv[8], bv[8], ra[8], rb[8];
+    unpack8(*(const uint4*)(a + i), av);
+    unpack8(*(const uint4*)(g + i), gv);
+    if (swiglu) unpack8(*(const uint4*)(b + i), bv);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float dh = gate * gv[q];
+      if (swiglu) {
+        const float sg = 1.f / (1.f + __expf(-av[q]));
+        const float h = av[q] * sg * bv[q];
+        acc += (double)gv[q] * (double)h;
+        ra[q] = dh * bv[q] * sg * (1.f + av[q] * (1.f - sg));
+        rb[q] = dh * av[q] * sg;
+      } else {
+        acc += (double)gv[q] * (double)fmaxf(av[q], 0.f);
+        ra[q] = av[q] > 0.f ? dh : 0.f;
+      }
+    }
+    *(uint4*)(da + i) = pack8(ra);
+    if (swiglu) *(uint4*)(db + i) = pack8(rb);
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) dgates[slot] = (float)acc;
+}
+
+// dy[row] = gate[t, j] * dout[t] for each kept slot (bf16, Dout % 8 == 0), and dgate = 0 for
+// each dropped slot; one wave per token.
+__global__ __launch_bounds__(kThreads) void scale_dout_rows_bf16x8_kernel(
+    int64_t T, int k, int64_t Dout, const uint16_t* __restrict__ dout,
+    const int32_t* __restrict__ slot_row, const float* __restrict__ gates,
+    uint16_t* __restrict__ dy, float* __restrict__ dgates) {
+  const int lane = lane_id();
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + wave_id();
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int64_t s = t * k + j;
+    const int row = slot_row[s];
+    if (row < 0) {
+      if (lane == 0) dgates[s] = 0.f;
+      continue;
+    }
+    const float gt = gates[s];
+    for (int64_t c = 8 * lane; c < Dout; c += 8 * kWave) {
+      float d[8], o[8];
+      unpack8(*(const uint4*)(dout + t * Dout + c), d);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = gt * d[q];
+      *(uint4*)(dy + (int64_t)row * Dout + c) = pack8(o);
+    }
+  }
+}
+
 // bf16 version of combine_backward, 8 columns a lane (Dout % 8 == 0): lane l takes columns
 // 8 (l + 64 i) .. + 7, its float64 partial in column order, then the same butterfly.
 __global__ __launch_bounds__(kThreads) void combine_backward_bf16x8_kernel(
@@ -832,14 +906,16 @@ struct GemmRes {
 
 hipError_t nt(const Problem& q, const void* A0, const void* A1, const void* W0, const void* W1,
               int64_t K, int64_t N, const int32_t* offsets, void* C, bool c_f32, hipStream_t s,
-              const GemmRes& res) {
+              const GemmRes& res, const int32_t* a_gather = nullptr) {
+  if (a_gather && !(q.dtype == MOE_BF16 && !A1 && !c_f32 && K % 128 == 0 && res.queue))
+    return hipErrorInvalidValue;  // only the 256 x 256 path gathers A's rows
   if (q.dtype == MOE_BF16 && !A1 && !c_f32 && K % 128 == 0 && res.queue) {
     // the forward's 256 x 256 pipeline, reading the weight K-major
     GroupedGemm f{};
     f.A = A0;
     f.lda = K;
-    f.a_gather = nullptr;
-    f.gather_div = 1;
+    f.a_gather = a_gather;  // row r reads A row a_gather[r] / top_k (a token's row)
+    f.gather_div = a_gather ? q.top_k : 1;
     f.B0 = W0;
     f.B1 = nullptr;
     f.C = C;
@@ -1004,6 +1080,13 @@ hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
                          void* dw1, void* dw3, void* dw2, void* ws, bool tickets_zeroed,
                          hipStream_t s);
 
+// bf16 ReLU / SwiGLU layers whose dgrad runs on the 256 x 256 path take the gate gradient
+// from h and g = dout W2^T (act_backward_rows) instead of from y, so they need no y.
+bool dgate_from_h(const Problem& q, const void* dout) {
+  return q.dtype == MOE_BF16 && q.kind != MOE_EXPERT_LINEAR && q.T > 0 && q.D_out % 128 == 0 &&
+         q.DH % 8 == 0 && (uintptr_t)dout % 16 == 0;
+}
+
 }  // namespace
 
 hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* perm,
@@ -1048,7 +1131,7 @@ hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* pe
     if (err == hipSuccess && swiglu)
       err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_ctr, queue, ncu, s);
   }
-  if (err == hipSuccess)
+  if (err == hipSuccess && y)  // (the backward of a bf16 layer does without y: dgate_from_h)
     err = fwd_gemm(q, h, DH, nullptr, w2, DH, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
   return err;
 }
@@ -1083,7 +1166,7 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   const int ncu = bf16 ? device_split_cus() : 0;
   int32_t* queue = tickets ? tickets + kSplitSlots : nullptr;
   err = run_experts_saving(q, x, perm, offsets, w1, w3, w2, at<void>(ws, L.a), at<void>(ws, L.b),
-                           at<void>(ws, L.h), at<void>(ws, L.y),
+                           at<void>(ws, L.h), dgate_from_h(q, dout) ? nullptr : at<void>(ws, L.y),
                            (tickets && ncu > 0) ? at<float>(ws, L.gsplit) : nullptr,
                            (tickets && ncu > 0) ? tickets : nullptr, queue, ncu, s);
   if (err != hipSuccess) return err;
@@ -1184,8 +1267,15 @@ hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
       err = hipGetLastError();
     }
   };
-  // 4. combine backward: dy rows and dgates
-  if (err == hipSuccess) {
+  // 4. combine backward: dy rows and dgates (with dgate_from_h: dy rows here, kept slots'
+  //    dgates in the activation backward)
+  const bool from_h = dgate_from_h(q, dout) && queue != nullptr;
+  if (err == hipSuccess && from_h) {
+    hipLaunchKernelGGL(scale_dout_rows_bf16x8_kernel, dim3((unsigned)((q.T + 3) / 4)),
+                       dim3(kThreads), 0, s, q.T, q.top_k, Do, (const uint16_t*)dout, slot_row,
+                       gates, (uint16_t*)dy, dgates);
+    err = hipGetLastError();
+  } else if (err == hipSuccess) {
     const unsigned grid = (unsigned)((q.T + 3) / 4);
     if (bf16 && Do % 8 == 0 && (uintptr_t)dout % 16 == 0)
       hipLaunchKernelGGL(combine_backward_bf16x8_kernel, dim3(grid), dim3(kThreads), 0, s, q.T,
@@ -1211,11 +1301,22 @@ hipError_t backward_from(const Problem& q, const BwdInputs& in, const void* x,
       err = bf16 ? nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr1, false, s, res)
                  : nt(q, dy, nullptr, w1, nullptr, Do, D, offsets, dxr, true, s, res);
   } else {
-    if (err == hipSuccess) err = nt(q, dy, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s, res);
+    // dh = dy W2^T; with from_h, g = dout W2^T over the slots' token rows (the gate is applied
+    // in the activation backward)
+    if (err == hipSuccess)
+      err = from_h ? nt(q, dout, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s, res, perm)
+                   : nt(q, dy, nullptr, w2, nullptr, Do, DH, offsets, dh, false, s, res);
     if (err == hipSuccess)
       err = kg ? tn_kg(q, L, ws, h, nullptr, 1, DH, grow2, dy, Do, offsets, dw2, res, s)
                : tn(q, h, DH, nullptr, 1, dy, DH, Do, offsets, dw2, s);
-    if (err == hipSuccess) {
+    if (err == hipSuccess && from_h) {
+      hipLaunchKernelGGL(act_backward_rows_bf16x8_kernel,
+                         dim3((unsigned)((q.slots() + kThreads / kWave - 1) / (kThreads / kWave))),
+                         dim3(kThreads), 0, s, DH, q.kind, offsets, q.E, perm, gates,
+                         (const uint16_t*)a, (const uint16_t*)b, (const uint16_t*)dh,
+                         (uint16_t*)da, (uint16_t*)db, dgates);
+      err = hipGetLastError();
+    } else if (err == hipSuccess) {
       if (bf16 && DH % 8 == 0)
         hipLaunchKernelGGL(act_backward_bf16x8_kernel, dim3(ew_grid), dim3(256), 0, s, DH, q.kind,
                            offsets, q.E, (const uint4*)a, (const uint4*)b, (const uint4*)dh,
