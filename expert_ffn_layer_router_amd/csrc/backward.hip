@@ -5,7 +5,9 @@
 // Experts (MoE) Routing", the load-balancing step; "Mixture of Experts: the Sparsely-Gated
 // Layer", Hot shards). In reverse order of the forward:
 //  * combine:  dgate[t, j] = <dout[t], y[row]> for a kept slot (0 for a dropped one),
-//              dy[row] = gate[t, j] * dout[t];
+//              dy[row] = gate[t, j] * dout[t]. For bf16 ReLU / SwiGLU layers the same
+//              dgate is taken as <dout[t] W2^T, h[row]> in the activation backward, so y
+//              is never needed;
 //  * experts:  dh = dy W2^T, then through the activation (ReLU: relu'(0) = 0; SwiGLU:
 //              silu'(a) = s (1 + a (1 - s)), s = sigmoid(a)); dx_rows = da W1^T (+ db W3^T);
 //              dW2 = h^T dy, dW1 = x^T da (, dW3 = x^T db), each over the expert's kept rows;
@@ -13,9 +15,9 @@
 //  * loss:     aux = E sum_e f_e P_e, P_e = mean_t p[t, e]: dL/dp[t, e] = d_aux E f_e / T, then
 //              through the full softmax: dl[t, e] += p[t, e] (a_e - sum_j p[t, j] a_j);
 //  * router:   dW_router = x^T dl, dbias = sum_t dl, dx += dl W_router^T.
-// The forward quantities it needs (decisions, gates, logits, the experts' pre-activations and
-// outputs) are recomputed with the forward's own kernels, so the call needs only the inputs
-// and dout. Every reduction runs in a fixed order, so the result does not depend on
+// The forward quantities it needs (decisions, gates, logits, the experts' pre-activations,
+// h, and y where it is used) are recomputed with the forward's own kernels, so the call needs
+// only the inputs and dout; or they come from a training forward's saved state. Every reduction runs in a fixed order, so the result does not depend on
 // scheduling.
 //
 // GEMM shapes that the forward does not have get their own kernels (bf16: 128 x 128 tiles,
