@@ -17,8 +17,8 @@
 //  * router:   dW_router = x^T dl, dbias = sum_t dl, dx += dl W_router^T.
 // The forward quantities it needs (decisions, gates, logits, the experts' pre-activations,
 // h, and y where it is used) are recomputed with the forward's own kernels, so the call needs
-// only the inputs and dout; or they come from a training forward's saved state. Every reduction runs in a fixed order, so the result does not depend on
-// scheduling.
+// only the inputs and dout; or they come from a training forward's saved state. Every
+// reduction runs in a fixed order, so the result does not depend on scheduling.
 //
 // GEMM shapes that the forward does not have get their own kernels (bf16: 128 x 128 tiles,
 // 2 x 2 waves of 64 x 64, v_mfma_f32_32x32x16_bf16, fp32 accumulation):
