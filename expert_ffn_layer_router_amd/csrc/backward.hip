@@ -357,6 +357,7 @@ __global__ __launch_bounds__(kThreads) void act_backward_rows_bf16x8_kernel(
   const float gate = gates[slot];
   const bool swiglu = kind == MOE_EXPERT_SWIGLU;
   double acc = 0.0;
+#pragma unroll 2
   for (int64_t c = 8 * lane; c < DH; c += 8 * kWave) {
     const int64_t i = r * DH + c;
     float av[8], gv[8], bv[8], ra[8], rb[8];
