@@ -90,6 +90,10 @@ CASES = {
     "single_expert_bf16": spec("mixtral_swiglu_bf16", T=300, D=128, DH=256, E=1, top_k=1),
     "dense_k_equals_e_bf16": spec("mixtral_swiglu_bf16", T=260, D=128, DH=128, E=4, top_k=4),
     "dense_k_equals_e_f32": spec("small_relu_f32", T=40, D=16, DH=24, E=3, top_k=3),
+    # many tokens: the router-weight gradient's token chunks pass 64 tokens (256 chunks of
+    # 79), so each chunk stages its dl rows in several rounds
+    "relu_long_t": spec("switch_top1_cap_bf16", T=20000, D=64, DH=64, E=64, top_k=2,
+                        capacity_factor=0.0),
 }
 
 
