@@ -94,6 +94,9 @@ CASES = {
     # 79), so each chunk stages its dl rows in several rounds
     "relu_long_t": spec("switch_top1_cap_bf16", T=20000, D=64, DH=64, E=64, top_k=2,
                         capacity_factor=0.0),
+    # bf16 SwiGLU with D not a multiple of 128: the 128 x 128 dgrad, y recomputed, the gate
+    # gradient from y
+    "swiglu_bf16_d200": spec("mixtral_swiglu_bf16", T=300, D=200, DH=136, E=4, top_k=2),
 }
 
 
@@ -200,7 +203,7 @@ SAVED_CASES = {
     "relu_f32_ragged_cap": CASES["relu_f32_ragged_cap"],
     # bf16 with D not a multiple of 128: the 128 x 128 GEMM, pre-activations by products of
     # their own
-    "swiglu_bf16_d200": spec("mixtral_swiglu_bf16", T=300, D=200, DH=136, E=4, top_k=2),
+    "swiglu_bf16_d200": CASES["swiglu_bf16_d200"],
 }
 
 
