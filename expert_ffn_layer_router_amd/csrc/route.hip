@@ -546,7 +546,8 @@ __global__ __launch_bounds__(256) void router_prep_kernel(int64_t D, int E,
   const int e = blockIdx.x;
   if (e == 0 && threadIdx.x == 0) {
     *ticket = 0;
-    *nlist = 0;
+    nlist[0] = 0;
+    nlist[1] = 0;
   }
   const uint16_t* src = e < E ? w : w_noise;
   const int col = e < E ? e : e - E;
@@ -654,6 +655,8 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
 }
 
 constexpr int kSelWaves = kRouteTokensPerBlock;  // one token per wave
+constexpr int kInWaveExact = 16;  // up to this many experts, the select kernel recomputes a
+                                  // flagged token's logits itself
 constexpr int kSelThreads = kSelWaves * kWave;
 constexpr int kFbThreads = 1024;  // threads per uncertified token in the fallback
 
@@ -768,7 +771,23 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
     const double B = gamma * xnb * wmax + rnd * 0x1p-23 + lmax * 0x1p-50 + 1e-30 + bnoise;
     const double gap = topk_rounds_keys<EPL>(E, k, lg, sel, my_v, my_e);
     flagged = !renorm || !(gap > 2.0 * B + lmax * 0x1p-22);
-    if (flagged) {
+    if (flagged && EPL == 1 && E <= kInWaveExact) {
+      // few experts: this wave takes all E logits exactly (exact bf16 products, float64
+      // sums; with noise also the E noise rows, + noise * softplus) and decides from them,
+      // as the fallback would
+      double ex = 0.0, zx = 0.0;
+      token_dots_f64<8>(x, wt, t, D, NOISE ? 2 * E : E, [](int j) { return j; },
+                        [&](int j, double v) {
+                          if (j == lane) ex = v;
+                          if (NOISE && j - E == lane) zx = v;
+                        });
+      lg[0] = ex;
+      add_bias<EPL>(bias, E, lg);
+      if (NOISE && lane < E) lg[0] += (double)noise[t * E + lane] * softplus_f64(zx);
+      topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);
+      flagged = false;
+      if (lane == 0) atomicAdd(nlist + 1, 1);
+    } else if (flagged) {
       // decided (or, without renormalisation, finished) by route_fallback_kernel from
       // exact logits
       if (lane == 0) list[atomicAdd(nlist, 1)] = (int32_t)t;
@@ -782,7 +801,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(
   bp.zero();
   if (valid) {
     write_logits<EPL>(logits_out, t, E, lg);
-    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates);
+    // (renorm is false only for tokens recomputed in this wave; listed ones are rewritten
+    // by the fallback)
+    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, idx, gates, renorm || flagged);
     // the loss probabilities come from these logits for every token; the counts of a
     // listed token are added by the fallback once its experts are known
     if (flagged)
@@ -811,8 +832,8 @@ __global__ __launch_bounds__(kFbThreads) void route_fallback_kernel(
     int32_t* __restrict__ uncertified) {
   __shared__ double s_red[kFbThreads];
   __shared__ double s_lg[2 * kMaxExperts];
-  const int n = *nlist;
-  if (blockIdx.x == 0 && threadIdx.x == 0 && uncertified) *uncertified = n;
+  const int n = nlist[0];
+  if (blockIdx.x == 0 && threadIdx.x == 0 && uncertified) *uncertified = n + nlist[1];
   const int rows = NOISE ? 2 * E : E;
   int NE = 1;
   while (NE < rows) NE <<= 1;
@@ -1006,7 +1027,8 @@ struct RouteScratch {
   int64_t* ce;       // per-expert counts (aux reduction)
   int32_t* ticket;   // blocks of the aux reduction done; zeroed by the first routing kernel
   int32_t* list;     // uncertified tokens (bf16), appended by the select kernel
-  int32_t* nlist;    // their number; zeroed by the first routing kernel
+  int32_t* nlist;    // [0] their number, [1] the tokens the select kernel recomputed itself;
+                     // zeroed by the first routing kernel
   double* imp;       // importance partials (nblk per expert) and ...
   double* ie;        // ... per-expert gate sums
   uint16_t* wt;      // (2E, D): the router's rows, then the noise rows (when there is noise)
@@ -1032,7 +1054,7 @@ RouteScratch route_scratch(const Problem& p, void* base) {
   r.ce = (int64_t*)take((size_t)p.E * sizeof(int64_t));
   r.ticket = (int32_t*)take(sizeof(int32_t));
   r.list = (int32_t*)take((size_t)p.T * sizeof(int32_t));
-  r.nlist = (int32_t*)take(sizeof(int32_t));
+  r.nlist = (int32_t*)take(2 * sizeof(int32_t));
   r.imp = (double*)take((size_t)nblk * p.E * sizeof(double));
   r.ie = (double*)take((size_t)p.E * sizeof(double));
   if (p.dtype == MOE_BF16) {  // sized for router noise (2E rows) either way
