@@ -655,7 +655,13 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
 }
 
 constexpr int kSelWaves = kRouteTokensPerBlock;  // one token per wave
-constexpr int kInWaveExact = 16;  // up to this many experts, the select kernel recomputes a
+constexpr int kInWaveExact = 16;
+
+// uncertified = the listed tokens plus those the select kernel recomputed itself.
+__global__ void report_uncertified_kernel(const int32_t* __restrict__ nlist,
+                                          int32_t* __restrict__ uncertified) {
+  *uncertified = nlist[0] + nlist[1];
+}  // up to this many experts, the select kernel recomputes a
                                   // flagged token's logits itself
 constexpr int kSelThreads = kSelWaves * kWave;
 constexpr int kFbThreads = 1024;  // threads per uncertified token in the fallback
@@ -1178,6 +1184,13 @@ hipError_t launch_route(const Problem& p, const void* x, const void* w_router, c
 #undef MOE_ROUTE_SELECT_EPL
 #undef MOE_ROUTE_SELECT_CG
 #undef MOE_ROUTE_SELECT
+  // With E <= kInWaveExact the select kernel lists no token (it recomputes flagged ones
+  // itself), so the fallback is skipped and only the count is reported.
+  if (epl <= 1 && p.E <= kInWaveExact) {
+    if (uncertified)
+      hipLaunchKernelGGL(report_uncertified_kernel, dim3(1), dim3(1), 0, s, r.nlist, uncertified);
+    return hipGetLastError();
+  }
   // one block per listed token, at most 512 blocks (a grid-stride loop covers the rest)
   const unsigned fgrid = (unsigned)std::min<int64_t>(p.T, 512);
 #define MOE_ROUTE_FALLBACK(EPLV, NZ)                                                           \
