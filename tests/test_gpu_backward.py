@@ -147,22 +147,37 @@ def test_backward_is_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_backward_full_size_sampled_tokens():
-    """The Mixtral-shaped layer at full size: dx of sampled tokens (the oracle restricted to
-    them; routing, drops and loss counts over all tokens) within the bar, and finite
-    gradients everywhere."""
+def _max_abs_rel_chunked(got, ref):
+    """max |got - ref| / max |ref| over a whole (E, ...) tensor, one expert at a time, so that
+    the full-size weight gradients are compared without a float64 copy of each."""
+    err, scale = 0.0, 0.0
+    for e in range(ref.shape[0]):
+        r = np.asarray(ref[e], dtype=np.float64)
+        err = max(err, float(np.abs(got[e].astype(np.float64) - r).max()) if r.size else 0.0)
+        scale = max(scale, float(np.abs(r).max()) if r.size else 0.0)
+    return err / scale if scale > 0 else err
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+def test_backward_full_size():
+    """The Mixtral-shaped layer at full size: every gradient (dx, dW_router, dbias, dW1, dW3,
+    dW2), every element, against the oracle's full float64 backward."""
     sp = spec("mixtral_swiglu_bf16")
     _say(f"[gpu] full-size backward {sp}")
     I = make_inputs(sp, seed=0)
     stored, values = _dout(sp)
     g = run_backward(I, stored, 0.01)
-    for k, v in g.items():
-        assert np.isfinite(v).all(), k
-    tokens = [0, 1, 2, 1000, 2047, 3000, 4094, 4095]
-    r = run_oracle_backward(I, values, 0.01, tokens=tokens)
-    err = max_abs_rel(g["dx"][tokens], r["dx"][tokens])
-    _say(f"  dx on {len(tokens)} sampled tokens: max-abs-rel {err:.2e}")
-    assert err <= GRAD_TOL["bf16"]
+    _say("  GPU backward done; oracle backward over all tokens")
+    r = run_oracle_backward(I, values, 0.01)
+    errs = {}
+    for k in ("dx", "dw_router", "dbias"):
+        errs[k] = max_abs_rel(g[k], r[k])
+    for k in ("dw1", "dw3", "dw2"):
+        errs[k] = _max_abs_rel_chunked(g[k], r[k])
+    _say("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= GRAD_TOL["bf16"], (k, v)
 
 
 def test_backward_with_no_tokens():
