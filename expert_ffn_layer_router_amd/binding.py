@@ -18,7 +18,9 @@ from typing import Optional
 
 LIB_PATH = Path(__file__).resolve().with_name("libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+ MOE_ERR_SCRATCH_LIMIT) = range(6)
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 MOE_F32, MOE_BF16 = 0, 1
 KINDS = {"linear": 0, "relu2": 1, "swiglu": 2}
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16}
@@ -29,7 +31,7 @@ EXPORTED = (
     "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
     "moe_forward_timed", "moe_workspace_size_ex", "moe_route_ex", "moe_dispatch_padded",
     "moe_expert_ffn_ex", "moe_forward_ex", "moe_backward_workspace_size", "moe_backward",
-    "moe_saved_size", "moe_forward_train", "moe_backward_saved",
+    "moe_saved_size", "moe_forward_train", "moe_backward_saved", "moe_route_noalloc",
 )
 STAGES = ("route", "dispatch", "expert_up", "expert_down", "combine")
 
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                 _P]
+        L.moe_route_noalloc.restype = ctypes.c_int
+        L.moe_route_noalloc.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_expert_ffn.restype = ctypes.c_int
@@ -307,6 +311,14 @@ def moe_route(p: Problem, x, w_router, router_bias, expert_indices, gates, aux_l
                            _ptr(expert_counts), _ptr(logits_out), _ptr(uncertified), _ptr(ws),
                            0 if ws is None else ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_route")
+
+
+def moe_route_noalloc(p: Problem, x, w_router, router_bias, expert_indices, gates, aux_loss,
+                      expert_counts=None, logits_out=None, uncertified=None, stream=None):
+    _check(lib().moe_route_noalloc(ctypes.byref(p.c()), _ptr(x), _ptr(w_router),
+                                   _ptr(router_bias), _ptr(expert_indices), _ptr(gates),
+                                   _ptr(aux_loss), _ptr(expert_counts), _ptr(logits_out),
+                                   _ptr(uncertified), _stream(stream)), "moe_route_noalloc")
 
 
 def moe_dispatch(p: Problem, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,

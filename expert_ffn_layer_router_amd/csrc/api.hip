@@ -3,6 +3,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -222,6 +224,63 @@ bool weights_ok(const moe_problem* p, const void* w1, const void* w3, const void
   return true;
 }
 
+// Routing (launch_route + the loss reduction) with its scratch at `ws` (route_end bytes of the
+// layout, 256-byte aligned). Arguments already checked.
+moe_status route_into(const Problem& q, const RouteOpts& ro, float* importance, const void* x,
+                      const void* w_router, const float* router_bias, int32_t* expert_indices,
+                      float* gates, float* aux_loss, int32_t* expert_counts, float* logits_out,
+                      int32_t* uncertified, void* route_ws, hipStream_t stream) {
+  hipError_t err = launch_route(q, x, w_router, router_bias, ro, expert_indices, gates,
+                                logits_out, uncertified, route_ws, stream);
+  if (err == hipSuccess)
+    err = launch_aux_finalize(q, route_ws, aux_loss, expert_counts, stream, expert_indices,
+                              gates, importance);
+  return hip_status(err);
+}
+
+moe_status route_args_ok(const moe_problem* p, const void* x, const void* w_router,
+                         int32_t* expert_indices, float* gates, float* aux_loss) {
+  if (!aux_loss) return MOE_ERR_INVALID_ARG;
+  if (p->T > 0 && (!x || !w_router || !expert_indices || !gates)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// ---- the allocation-free routing entry point -------------------------------------------------
+// Its scratch is this file-scope device array: each device that loads the library holds its own
+// copy until the process ends. In host code `scratch` names a host-side stand-in, so its device
+// address is looked up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is ever passed to a kernel.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`; the stream (when not the null stream) must belong
+// to that device, since the address is only valid there.
+moe_status scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOE_ERR_HIP;
+    if ((int)sdev != dev) return MOE_ERR_INVALID_ARG;
+  }
+  void* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+      g_scratch_dev[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,6 +292,9 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: a shape, dtype or expert kind this library does not handle";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, too small or not 256-byte aligned";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "MOE_ERR_SCRATCH_LIMIT: the problem needs more routing scratch than the "
+             "allocation-free entry point's fixed device array (MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown moe_status";
 }
@@ -270,18 +332,14 @@ moe_status moe_route_ex(const moe_problem* p, const moe_options* opts, const voi
   float* importance;
   st = options_of(p, opts, ro, padded, importance);
   if (st != MOE_OK) return st;
-  if (!aux_loss) return MOE_ERR_INVALID_ARG;
-  if (p->T > 0 && (!x || !w_router || !expert_indices || !gates)) return MOE_ERR_INVALID_ARG;
+  st = route_args_ok(p, x, w_router, expert_indices, gates, aux_loss);
+  if (st != MOE_OK) return st;
   const Problem q = internal(p);
   const Layout L = layout_of(q, padded);
   st = check_ws(ws, ws_bytes, L.route_end);
   if (st != MOE_OK) return st;
-  hipError_t err = launch_route(q, x, w_router, router_bias, ro, expert_indices, gates,
-                                logits_out, uncertified, at<void>(ws, L.route), stream);
-  if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, expert_counts, stream,
-                              expert_indices, gates, importance);
-  return hip_status(err);
+  return route_into(q, ro, importance, x, w_router, router_bias, expert_indices, gates, aux_loss,
+                    expert_counts, logits_out, uncertified, at<void>(ws, L.route), stream);
 }
 
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
@@ -290,6 +348,27 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      int32_t* uncertified, void* ws, size_t ws_bytes, hipStream_t stream) {
   return moe_route_ex(p, nullptr, x, w_router, router_bias, expert_indices, gates, aux_loss,
                       expert_counts, logits_out, uncertified, ws, ws_bytes, stream);
+}
+
+moe_status moe_route_noalloc(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, float* logits_out,
+                             int32_t* uncertified, hipStream_t stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  st = route_args_ok(p, x, w_router, expert_indices, gates, aux_loss);
+  if (st != MOE_OK) return st;
+  const Problem q = internal(p);
+  const Layout L = layout_of(q);
+  if (L.route_end > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  st = scratch_of_current_device(stream, &ws);
+  if (st != MOE_OK) return st;
+  // every counter of the routing scratch is cleared by the routing kernels themselves, so the
+  // previous call's contents need no reset here
+  return route_into(q, RouteOpts{}, nullptr, x, w_router, router_bias, expert_indices, gates,
+                    aux_loss, expert_counts, logits_out, uncertified, at<void>(ws, L.route),
+                    stream);
 }
 
 moe_status moe_dispatch(const moe_problem* p, const int32_t* expert_indices, const void* x,

@@ -56,7 +56,9 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARG = 1, /* a null required pointer, a size out of range, top_k not in [1, E] */
   MOE_ERR_UNSUPPORTED = 2, /* E > 256, an unknown dtype/kind, widths not multiples of 8 in bf16 */
   MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_size(), or ws misaligned */
-  MOE_ERR_HIP = 4          /* a HIP launch error */
+  MOE_ERR_HIP = 4,         /* a HIP launch error */
+  MOE_ERR_SCRATCH_LIMIT = 5 /* moe_route_noalloc: the problem needs more routing scratch than
+                               MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -113,6 +115,28 @@ moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* router_bias, int32_t* expert_indices, float* gates,
                      float* aux_loss, int32_t* expert_counts, float* logits_out,
                      int32_t* uncertified, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Size of the fixed device array that moe_route_noalloc uses as its scratch (32 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* moe_route without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, outputs and errors as moe_route (no router options), minus ws and ws_bytes; the
+ * results are bit-identical to moe_route's for the same inputs.
+ *   Scratch: a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per
+ *   device, held from the library's load until the process ends. Its device address is looked
+ *   up once per device, on that device's first call. The call allocates nothing (no hipMalloc,
+ *   hipFree or allocating library routine) and clears what must start at zero itself.
+ *   Every call on a device shares that device's array, so calls that overlap on one device
+ *   (concurrent streams or host threads) race and give undefined results; calls on one stream
+ *   are safe. `stream` must belong to the current device (else MOE_ERR_INVALID_ARG).
+ *   MOE_ERR_SCRATCH_LIMIT (nothing written or launched) when the routing scratch this problem
+ *   needs exceeds the array; it grows with T and E (the five workloads of the pages' shapes
+ *   need at most about 19 MiB). */
+moe_status moe_route_noalloc(const moe_problem* p, const void* x, const void* w_router,
+                             const float* router_bias, int32_t* expert_indices, float* gates,
+                             float* aux_loss, int32_t* expert_counts, float* logits_out,
+                             int32_t* uncertified, hipStream_t stream);
 
 /* Dispatch (ML Grind, Algorithm step 3 "gather the tokens routed to it"; capacity as in
  * the Sparsely-Gated Layer page's moe_forward, first come, first served).

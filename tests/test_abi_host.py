@@ -129,8 +129,23 @@ def test_error_paths_return_before_any_launch():
     assert lib.moe_forward(None, *([fake] * 14), 1 << 30, None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_no_alloc_route_host_checks():
+    """moe_route_noalloc: invalid arguments, and a problem whose routing scratch exceeds the
+    fixed device array, are refused by host checks before the device is touched."""
+    lib = B.lib()
+    fake = 1 << 20
+    assert lib.moe_route_noalloc(ctypes.byref(P(top_k=0).c()), fake, fake, None, fake, fake,
+                                 fake, None, None, None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_noalloc(ctypes.byref(P().c()), fake, fake, None, fake, fake, None,
+                                 None, None, None, None) == B.MOE_ERR_INVALID_ARG
+    big = P(T=1 << 20, D=2048, E=256, top_k=8)
+    assert lib.moe_route_noalloc(ctypes.byref(big.c()), fake, fake, None, fake, fake, fake,
+                                 None, None, None, None) == B.MOE_ERR_SCRATCH_LIMIT
+    assert "MOE_NOALLOC_SCRATCH_BYTES" in B.status_string(B.MOE_ERR_SCRATCH_LIMIT)
+
+
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert B.status_string(s).startswith("MOE_")
     assert "unknown" in B.status_string(99)
 
