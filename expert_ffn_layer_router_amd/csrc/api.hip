@@ -230,12 +230,9 @@ moe_status route_into(const Problem& q, const RouteOpts& ro, float* importance, 
                       const void* w_router, const float* router_bias, int32_t* expert_indices,
                       float* gates, float* aux_loss, int32_t* expert_counts, float* logits_out,
                       int32_t* uncertified, void* route_ws, hipStream_t stream) {
-  hipError_t err = launch_route(q, x, w_router, router_bias, ro, expert_indices, gates,
-                                logits_out, uncertified, route_ws, stream);
-  if (err == hipSuccess)
-    err = launch_aux_finalize(q, route_ws, aux_loss, expert_counts, stream, expert_indices,
-                              gates, importance);
-  return hip_status(err);
+  return hip_status(launch_route_full(q, x, w_router, router_bias, ro, expert_indices, gates,
+                                     logits_out, uncertified, aux_loss, expert_counts,
+                                     importance, route_ws, stream));
 }
 
 moe_status route_args_ok(const moe_problem* p, const void* x, const void* w_router,
@@ -469,11 +466,14 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
   if (st != MOE_OK) return st;
   int32_t* perm = at<int32_t>(ws, L.perm);
   mark(ev, 2 * MOE_STAGE_ROUTE, stream);
-  hipError_t err = launch_route(q, x, w_router, router_bias, ro, expert_indices, gates, nullptr,
-                                nullptr, at<void>(ws, L.route), stream);
-  if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream,
-                              expert_indices, gates, importance);
+  // the fused routing kernel also leaves the offsets and the dispatch ranks' bases (not with
+  // the padded layout, whose dispatch has its own kernels)
+  bool dispatched = false;
+  hipError_t err = launch_route_full(q, x, w_router, router_bias, ro, expert_indices, gates,
+                                     nullptr, nullptr, aux_loss, expert_counts, importance,
+                                     at<void>(ws, L.route), stream,
+                                     padded ? nullptr : expert_offsets,
+                                     padded ? nullptr : &dispatched);
   mark(ev, 2 * MOE_STAGE_ROUTE + 1, stream);
   mark(ev, 2 * MOE_STAGE_DISPATCH, stream);
   // the dispatch scan also zeroes the GEMMs' K-split tickets and work queue
@@ -491,6 +491,10 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
                             tickets ? kSplitSlots + kQueueInts : 0, expert_offsets);
       A = at<void>(ws, L.xpad);
       gather = nullptr;
+    } else if (dispatched) {
+      err = launch_place_after_route(q, expert_indices, at<void>(ws, L.route), aux_loss,
+                                     expert_counts, nullptr, expert_offsets, perm, slot_row,
+                                     stream, tickets, tickets ? kSplitSlots + kQueueInts : 0);
     } else {
       err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
                             nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
@@ -578,14 +582,18 @@ moe_status moe_forward_train(const moe_problem* p, const void* x, const void* w_
   if (st != MOE_OK) return st;
   char* sv = (char*)saved;
   int32_t* perm = p->T > 0 ? (int32_t*)(sv + S.perm) : at<int32_t>(ws, L.perm);
-  hipError_t err = launch_route(q, x, w_router, router_bias, RouteOpts{}, expert_indices, gates,
-                                p->T > 0 ? (float*)(sv + S.logits) : nullptr, nullptr,
-                                at<void>(ws, L.route), stream);
-  if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<void>(ws, L.route), aux_loss, nullptr, stream);
-  // the dispatch scan also zeroes the GEMMs' K-split tickets and work queue
+  bool dispatched = false;
+  hipError_t err = launch_route_full(q, x, w_router, router_bias, RouteOpts{}, expert_indices,
+                                     gates, p->T > 0 ? (float*)(sv + S.logits) : nullptr, nullptr,
+                                     aux_loss, expert_counts, nullptr, at<void>(ws, L.route),
+                                     stream, expert_offsets, &dispatched);
+  // the dispatch also zeroes the GEMMs' K-split tickets and work queue
   int32_t* tickets = (q.dtype == MOE_BF16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
-  if (err == hipSuccess)
+  if (err == hipSuccess && dispatched)
+    err = launch_place_after_route(q, expert_indices, at<void>(ws, L.route), aux_loss,
+                                   expert_counts, nullptr, expert_offsets, perm, slot_row, stream,
+                                   tickets, tickets ? kSplitSlots + kQueueInts : 0);
+  else if (err == hipSuccess)
     err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
                           nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,
                           tickets, tickets ? kSplitSlots + kQueueInts : 0);

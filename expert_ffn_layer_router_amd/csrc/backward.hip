@@ -1153,14 +1153,18 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   int32_t* perm = at<int32_t>(ws, L.perm);
   int32_t* slot_row = at<int32_t>(ws, L.slot_row);
   // 1. decisions, gates and logits, exactly as the forward takes them
-  hipError_t err = launch_route(q, x, w_router, bias, RouteOpts{}, idx, gates, logits, nullptr,
-                                at<void>(ws, L.route), s);
-  if (err == hipSuccess)
-    err = launch_aux_finalize(q, at<void>(ws, L.route), at<float>(ws, L.aux), nullptr, s);
-  // 2. dispatch (counts, offsets, permutation, slot rows); the scan also clears the GEMMs'
-  //    split tickets and work queue
+  bool dispatched = false;
+  hipError_t err = launch_route_full(q, x, w_router, bias, RouteOpts{}, idx, gates, logits,
+                                     nullptr, at<float>(ws, L.aux), counts, nullptr,
+                                     at<void>(ws, L.route), s, offsets, &dispatched);
+  // 2. dispatch (counts, offsets, permutation, slot rows); it also clears the GEMMs' split
+  //    tickets and work queue
   int32_t* tickets = (bf16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
-  if (err == hipSuccess)
+  if (err == hipSuccess && dispatched)
+    err = launch_place_after_route(q, idx, at<void>(ws, L.route), at<float>(ws, L.aux), counts,
+                                   nullptr, offsets, perm, slot_row, s, tickets,
+                                   tickets ? kSplitSlots + kQueueInts : 0);
+  else if (err == hipSuccess)
     err = launch_dispatch(q, idx, x, counts, offsets, perm, slot_row, nullptr,
                           at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), s, tickets,
                           tickets ? kSplitSlots + kQueueInts : 0);

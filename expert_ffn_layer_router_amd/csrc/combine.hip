@@ -29,7 +29,11 @@ __device__ __forceinline__ uint4 pack8(const float f[8]) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// bf16 rows, N % 8 == 0, 16-byte aligned.
+// bf16 rows, N % 8 == 0, 16-byte aligned, top_k <= 64. Lane j first loads slot j's row and
+// gate (one round of loads for the whole token), then each pass over the row issues the KG x U
+// 16-byte loads of KG slots and U column chunks per lane before any of them is used, so a
+// wave has KG x U row loads in flight; the sum still runs over j ascending.
+template <int KG, int U>
 __global__ __launch_bounds__(kThreads) void combine_bf16x8_kernel(
     int64_t T, int k, int64_t n_vec, const uint4* __restrict__ y,
     const int32_t* __restrict__ slot_row, const float* __restrict__ gates,
@@ -37,31 +41,42 @@ __global__ __launch_bounds__(kThreads) void combine_bf16x8_kernel(
   const int64_t t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + wave_id()));
   if (t >= T) return;
   const int lane = lane_id();
-  // 4 column chunks a pass, so 4 k loads are in flight; each output is still the sum over
-  // j ascending
-  constexpr int U = 4;
+  const int rl = lane < k ? slot_row[t * k + lane] : -1;
+  const float gl = lane < k ? gates[t * k + lane] : 0.f;
   for (int64_t c0 = lane; c0 < n_vec; c0 += U * kWave) {
     float acc[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = __builtin_amdgcn_readfirstlane(slot_row[t * k + j]);
-      if (r < 0) continue;
-      const float g = gates[t * k + j];
-      uint4 w[U];
+    for (int j0 = 0; j0 < k; j0 += KG) {
+      int r[KG];
+      float g[KG];
+      uint4 w[KG][U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + u * kWave;
-        w[u] = c < n_vec ? y[(int64_t)r * n_vec + c] : make_uint4(0u, 0u, 0u, 0u);
+      for (int jj = 0; jj < KG; ++jj) {
+        const int j = j0 + jj;
+        r[jj] = j < k ? __builtin_amdgcn_readlane(rl, j) : -1;
+        g[jj] = j < k ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, gl), j))
+                      : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t c = c0 + u * kWave;
+          w[jj][u] = (r[jj] >= 0 && c < n_vec) ? y[(int64_t)r[jj] * n_vec + c]
+                                               : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float v[8];
-        unpack8(w[u], v);
+      for (int jj = 0; jj < KG; ++jj) {
+        if (r[jj] < 0) continue;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g, v[i], acc[u][i]);
+        for (int u = 0; u < U; ++u) {
+          float v[8];
+          unpack8(w[jj][u], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g[jj], v[i], acc[u][i]);
+        }
       }
     }
 #pragma unroll
@@ -98,9 +113,17 @@ hipError_t launch_combine(const Problem& p, const void* y, const int32_t* slot_r
   if (p.T == 0) return hipSuccess;
   const unsigned grid = (unsigned)((p.T + kWaves - 1) / kWaves);
   const bool al16 = ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0);
-  if (p.dtype == MOE_BF16 && p.D_out % 8 == 0 && al16) {
-    hipLaunchKernelGGL(combine_bf16x8_kernel, dim3(grid), dim3(kThreads), 0, s, p.T, p.top_k,
-                       p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
+  if (p.dtype == MOE_BF16 && p.D_out % 8 == 0 && al16 && p.top_k <= kWave) {
+    // 16 row loads in flight per wave: slots x column chunks
+    if (p.top_k <= 2)
+      hipLaunchKernelGGL((combine_bf16x8_kernel<2, 8>), dim3(grid), dim3(kThreads), 0, s, p.T,
+                         p.top_k, p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
+    else if (p.top_k <= 4)
+      hipLaunchKernelGGL((combine_bf16x8_kernel<4, 4>), dim3(grid), dim3(kThreads), 0, s, p.T,
+                         p.top_k, p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
+    else
+      hipLaunchKernelGGL((combine_bf16x8_kernel<8, 2>), dim3(grid), dim3(kThreads), 0, s, p.T,
+                         p.top_k, p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
   } else if (p.dtype == MOE_BF16) {
     hipLaunchKernelGGL(combine_scalar_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, p.T,
                        p.top_k, p.D_out, (const uint16_t*)y, slot_row, gates, (uint16_t*)out);

@@ -84,6 +84,34 @@ hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* 
                                hipStream_t s, const int32_t* idx = nullptr,
                                const float* gates = nullptr, float* importance = nullptr);
 
+// Routing with its losses in one call: the fused bf16 path (prep + one routing kernel + one
+// block that forms the loss and the counts) when it applies, else launch_route +
+// launch_aux_finalize. With `dispatch_done` (nullable) and `offsets_out`, the fused path
+// instead leaves the loss, the counts, the offsets and the placement to
+// launch_place_after_route, which the caller must then run with the same aux / counts /
+// uncertified pointers (it writes perm and slot_row as launch_dispatch does); *dispatch_done
+// tells which happened.
+hipError_t launch_route_full(const Problem& p, const void* x, const void* w_router,
+                             const float* bias, const RouteOpts& o, int32_t* idx, float* gates,
+                             float* logits_out, int32_t* uncertified, float* aux,
+                             int32_t* counts_out, float* importance, void* ws, hipStream_t s,
+                             int32_t* offsets_out = nullptr, bool* dispatch_done = nullptr);
+hipError_t launch_place_after_route(const Problem& p, const int32_t* idx, void* ws, float* aux,
+                                    int32_t* counts_out, int32_t* uncertified,
+                                    int32_t* offsets, int32_t* perm, int32_t* slot_row,
+                                    hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
+// route_fused.hip (used through the two calls above)
+bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance);
+size_t fused_route_ws_bytes(const Problem& p);
+hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
+                              const float* bias, int32_t* idx, float* gates, float* logits_out,
+                              void* fws, hipStream_t s);
+// perm null: one block forms the loss and the counts (and the offsets, if given) only
+hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* fws, float* aux,
+                              int32_t* counts_out, int32_t* uncertified, int32_t* offsets,
+                              int32_t* perm, int32_t* slot_row, hipStream_t s, int32_t* zero,
+                              int nzero);
+
 // Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
 int64_t dispatch_blocks(const Problem& p);
 // `zero` (nullable): nzero int32 that the scan kernel sets to 0 on the way (the GEMMs'

@@ -47,6 +47,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "route_util.hpp"
 
 namespace moe {
 namespace {
@@ -59,19 +60,6 @@ constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kLT = 64;     // tokens per block (4 waves x 16)
 constexpr int kLKB = 256;   // K per stage (LDS router chunk, A registers)
 constexpr int kMinKSplit = 256;
-
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
-}
-
-// xor-butterfly sum: every lane ends with the same, order-fixed value.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // softplus(z) = log(1 + e^z), in float64 without overflow.
 __device__ __forceinline__ double softplus_f64(double z) {
@@ -94,19 +82,6 @@ __device__ __forceinline__ void logits_f64(const TIn* __restrict__ x, const TIn*
       if (e < E) lg[i] = fma(xv, load_as_f64(wr, e), lg[i]);
     }
   }
-}
-
-__device__ __forceinline__ double dot8_f64(const uint4& xv, const uint4& wv) {
-  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-  const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
-  double a = 0.0, b = 0.0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    a = fma((double)__uint_as_float(xw[q] << 16), (double)__uint_as_float(ww[q] << 16), a);
-    b = fma((double)__uint_as_float(xw[q] & 0xffff0000u),
-            (double)__uint_as_float(ww[q] & 0xffff0000u), b);
-  }
-  return a + b;
 }
 
 // Float64 dot products of one bf16 token row with n rows of the transposed router, CG rows
@@ -217,204 +192,6 @@ __device__ __forceinline__ void chosen_logits_noisy_f64(
   for (int i = 0; i < EPL; ++i) my_v[i] = my_g[i] + my_b[i] + my_n[i] * softplus_f64(my_z[i]);
 }
 
-// k rounds of a wave-wide argmax over the not-yet-chosen experts: larger logit first,
-// equal logits -> smaller expert index. Lane j (+64i) keeps the j-th choice. When
-// `want_gap`, one more round finds the best unchosen logit, and the smallest difference
-// between consecutive values of the chosen sequence (extended by that one) is returned.
-template <int EPL>
-__device__ __forceinline__ double topk_rounds(int E, int k, const double lg[EPL], bool sel[EPL],
-                                              double my_v[EPL], int my_e[EPL],
-                                              bool want_gap) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    sel[i] = false;
-    my_v[i] = 0.0;
-    my_e[i] = 0;
-  }
-  double prev = 0.0, min_gap = DBL_MAX;
-  const int rounds = (want_gap && k < E) ? k + 1 : k;
-  for (int j = 0; j < rounds; ++j) {
-    double bv = -DBL_MAX;
-    int be = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && !sel[i] && (lg[i] > bv || (lg[i] == bv && e < be))) {
-        bv = lg[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      const double ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if (j > 0) min_gap = fmin(min_gap, prev - bv);
-    prev = bv;
-    if (j == k) break;  // the extra round only measures the boundary gap
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (be == lane + kWave * i) sel[i] = true;
-      if (j == lane + kWave * i) {
-        my_v[i] = bv;
-        my_e[i] = be;
-      }
-    }
-  }
-  return min_gap;
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  return __longlong_as_double((long long)readlane64((uint64_t)__double_as_longlong(v), l));
-}
-// Wave-wide maximum of a 64-bit key, the same in every lane: within each row of 16 lanes by
-// four DPP exchanges (lanes l ^ 1, l ^ 2, then the mirrored lane of the half row and of the
-// row), then the four row maxima read out.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t m) {
-  uint64_t o;
-  o = dpp64<0xB1>(m);   // quad_perm [1,0,3,2]
-  m = o > m ? o : m;
-  o = dpp64<0x4E>(m);   // quad_perm [2,3,0,1]
-  m = o > m ? o : m;
-  o = dpp64<0x141>(m);  // row_half_mirror
-  m = o > m ? o : m;
-  o = dpp64<0x140>(m);  // row_mirror
-  m = o > m ? o : m;
-  const uint64_t r0 = readlane64(m, 0), r1 = readlane64(m, 16);
-  const uint64_t r2 = readlane64(m, 32), r3 = readlane64(m, 48);
-  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
-  return a > b ? a : b;
-}
-
-// The same selection as topk_rounds with want_gap, for the certified fast path: each round's
-// argmax runs on 64-bit keys (the logit rounded to float32, mapped to an order-preserving
-// unsigned integer, above the complemented expert index, so equal keys go to the lower index),
-// and the chosen expert's float64 value is read from its lane. Rounding to float32 can only
-// reorder logits that lie within one float32 ulp of each other; the gaps returned are float64
-// differences of the chosen sequence, and the caller's certification threshold includes two
-// float32 ulps of the largest logit, so any such token is sent to the exact path.
-template <int EPL>
-__device__ __forceinline__ double topk_rounds_keys(int E, int k, const double lg[EPL],
-                                                   bool sel[EPL], double my_v[EPL],
-                                                   int my_e[EPL]) {
-  const int lane = lane_id();
-  uint64_t key[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    const uint32_t u = __float_as_uint((float)lg[i]);
-    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    key[i] = e < E ? (((uint64_t)o << 32) | (0xFFFFFFFFu - (uint32_t)e)) : 0ull;
-    sel[i] = false;
-    my_v[i] = 0.0;
-    my_e[i] = 0;
-  }
-  double prev = 0.0, min_gap = DBL_MAX;
-  const int rounds = k < E ? k + 1 : k;
-  for (int j = 0; j < rounds; ++j) {
-    uint64_t best = 0;
-    double cand = 0.0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (!sel[i] && key[i] > best) {
-        best = key[i];
-        cand = lg[i];
-      }
-    const uint64_t w = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)w);
-    const double bv = readlane_f64(cand, e & (kWave - 1));
-    if (j > 0) min_gap = fmin(min_gap, prev - bv);
-    prev = bv;
-    if (j == k) break;  // the extra round only measures the boundary gap
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (e == lane + kWave * i) sel[i] = true;
-      if (j == lane + kWave * i) {
-        my_v[i] = bv;
-        my_e[i] = e;
-      }
-    }
-  }
-  return min_gap;
-}
-
-// Probabilities over all experts (returned in prob[]), and the index/gate rows: the gates are
-// the softmax of the chosen logits my_v when `renorm`, else the chosen experts' probabilities.
-template <int EPL>
-__device__ __forceinline__ void finish_token(int E, int k, int64_t t, const double lg[EPL],
-                                             const double my_v[EPL], const int my_e[EPL],
-                                             double prob[EPL], int32_t* __restrict__ idx,
-                                             float* __restrict__ gates, bool renorm = true) {
-  const int lane = lane_id();
-  double m = -DBL_MAX;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i)
-    if (lane + kWave * i < E) m = fmax(m, lg[i]);
-  m = wave_max(m);
-  double s = 0.0;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    prob[i] = (lane + kWave * i < E) ? exp(lg[i] - m) : 0.0;
-    s += prob[i];
-  }
-  s = wave_sum(s);
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) prob[i] /= s;
-  if (!renorm) {
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int j = lane + kWave * i;
-      // the probability of choice j's expert, read from the lane that holds that expert
-      double pv = 0.0;
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) {
-        const double c = __shfl(prob[q], my_e[i] & (kWave - 1));
-        if ((my_e[i] >> 6) == q) pv = c;
-      }
-      if (j < k) {
-        idx[t * k + j] = my_e[i];
-        gates[t * k + j] = (float)pv;
-      }
-    }
-    return;
-  }
-  // gates: softmax over the chosen logits, shifted by the first (largest) of them
-  const double v0 = __shfl(my_v[0], 0);
-  double ev[EPL];
-  double gs = 0.0;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    ev[i] = (lane + kWave * i < k) ? exp(my_v[i] - v0) : 0.0;
-    gs += ev[i];
-  }
-  gs = wave_sum(gs);
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int j = lane + kWave * i;
-    if (j < k) {
-      idx[t * k + j] = my_e[i];
-      gates[t * k + j] = (float)(ev[i] / gs);
-    }
-  }
-}
-
 // Per-block partials of sum_t probs[t, e] and of the expert counts, in fixed order.
 template <int EPL>
 struct BlockPartials {
@@ -460,29 +237,6 @@ __device__ __forceinline__ void write_block_partials(const BlockPartials<EPL>& b
     // expert-major: the loss reduction then reads each expert's partials contiguously
     psum_blk[(int64_t)e * gridDim.x + blockIdx.x] = a;
     count_blk[(int64_t)e * gridDim.x + blockIdx.x] = c;
-  }
-}
-
-template <int EPL>
-__device__ __forceinline__ void add_bias(const float* __restrict__ bias, int E, double lg[EPL]) {
-  if (!bias) return;
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) lg[i] += (double)bias[e];
-  }
-}
-
-template <int EPL>
-__device__ __forceinline__ void write_logits(float* __restrict__ logits_out, int64_t t, int E,
-                                             const double lg[EPL]) {
-  if (!logits_out) return;
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) logits_out[t * E + e] = (float)lg[i];
   }
 }
 
@@ -1092,7 +846,13 @@ int route_splits(const Problem& p) {
   return S;
 }
 
-size_t route_ws_bytes(const Problem& p) { return route_scratch(p, nullptr).bytes; }
+// The fused path's region follows the multi-kernel path's scratch.
+size_t route_ws_bytes(const Problem& p) {
+  return a256(route_scratch(p, nullptr).bytes) + fused_route_ws_bytes(p);
+}
+static void* fused_region(const Problem& p, void* ws) {
+  return (char*)ws + a256(route_scratch(p, nullptr).bytes);
+}
 
 hipError_t launch_route(const Problem& p, const void* x, const void* w_router, const float* bias,
                         const RouteOpts& o, int32_t* idx, float* gates, float* logits_out,
@@ -1240,6 +1000,37 @@ hipError_t launch_aux_finalize(const Problem& p, void* ws, float* aux, int32_t* 
                      p.top_k, r.psum, r.pcnt, r.pe, r.ce, r.ticket, aux, counts_out,
                      importance ? r.imp : nullptr, r.ie, importance);
   return hipGetLastError();
+}
+
+hipError_t launch_route_full(const Problem& p, const void* x, const void* w_router,
+                             const float* bias, const RouteOpts& o, int32_t* idx, float* gates,
+                             float* logits_out, int32_t* uncertified, float* aux,
+                             int32_t* counts_out, float* importance, void* ws, hipStream_t s,
+                             int32_t* offsets_out, bool* dispatch_done) {
+  if (dispatch_done) *dispatch_done = false;
+  if (fused_route_applies(p, o, importance != nullptr)) {
+    hipError_t err =
+        launch_route_fused(p, x, w_router, bias, idx, gates, logits_out, fused_region(p, ws), s);
+    if (err != hipSuccess) return err;
+    if (dispatch_done && offsets_out) {
+      *dispatch_done = true;  // the caller's launch_place_after_route finishes the loss
+      return hipSuccess;
+    }
+    return launch_place_fused(p, idx, fused_region(p, ws), aux, counts_out, uncertified, nullptr,
+                              nullptr, nullptr, s, nullptr, 0);
+  }
+  hipError_t err = launch_route(p, x, w_router, bias, o, idx, gates, logits_out, uncertified, ws, s);
+  if (err == hipSuccess)
+    err = launch_aux_finalize(p, ws, aux, counts_out, s, idx, gates, importance);
+  return err;
+}
+
+hipError_t launch_place_after_route(const Problem& p, const int32_t* idx, void* ws, float* aux,
+                                    int32_t* counts_out, int32_t* uncertified,
+                                    int32_t* offsets, int32_t* perm, int32_t* slot_row,
+                                    hipStream_t s, int32_t* zero, int nzero) {
+  return launch_place_fused(p, idx, fused_region(p, ws), aux, counts_out, uncertified, offsets,
+                            perm, slot_row, s, zero, nzero);
 }
 
 }  // namespace moe

@@ -1,0 +1,845 @@
+// Fused bf16 routing: router logits, row softmax, top-k, gates, the Switch loss and the
+// per-expert counts in one pass over x (ML Grind "Mixture-of-Experts (MoE) Routing",
+// Algorithm steps 1 and 2 and the load-balancing step; ties go to the lower expert index,
+// "Edge cases and conventions"), plus the dispatch ranks and row offsets that follow from the
+// counts (Algorithm step 3 and Follow-up; capacity with the first routed tokens kept, as in
+// "Mixture of Experts: the Sparsely-Gated Layer", "Switch: top-1, one loss, and a rate limit").
+//
+// Three launches:
+//  1. prep (one block per 64 router rows): the router transposed to (E, D), so that both the
+//     MFMA operand and the exact dot products read an expert's weights K-contiguous; for each
+//     64-row block b, m_b = max_e ||W[64b .. 64b+63, e]||_2 rounded up; the routing counters
+//     cleared.
+//  2. route (one 256-thread block per TT tokens, TT chosen so the token tile fills at most
+//     64 KB of LDS and two blocks share a CU):
+//     a. the block's token tile goes from HBM into LDS once (global_load_lds_dwordx4; the
+//        16-byte chunk c of row r is stored at chunk c ^ (r % 16), so the 16 rows an MFMA
+//        operand read touches fall in distinct banks);
+//     b. logits: v_mfma_f32_16x16x32_bf16 over the tile and the transposed router; every MFMA
+//        sums 32 exact bf16 products from a zero accumulator and is folded into float64 at
+//        once;
+//     c. one wave per token: a rigorous bound B_t on |logit - exact logit| (every 32-term
+//        float32 sum is within 32 * 2^-23 of the sum of its |products|, which Cauchy-Schwarz
+//        bounds by ||x_chunk|| ||w_chunk||; over each 64-row block by ||x_t,b|| m_b), then the
+//        top k + 1 by descending logit. When every gap in that sequence exceeds 2 B_t the
+//        order is the exact logits' order; the k chosen logits are then recomputed exactly
+//        (float64 sums of exact products, read from the LDS tile) and the gates come from
+//        them. Otherwise all E logits are recomputed exactly and the top-k is taken on them;
+//     d. per-block sums of the probabilities (fixed order, then rounded to multiples of 2^-40
+//        and added as 64-bit integers, so the totals do not depend on block order) and counts
+//        go to global counters; the last block to finish (a ticket) forms aux = E sum_e f_e P_e,
+//        the counts, the row offsets (kept_e = min(count_e, capacity)) and, per group of 256
+//        tokens and expert, the number of earlier routed slots (the rank base of the group).
+//  3. place (one block per group of 256 tokens): each slot's rank among the group's earlier
+//     slots of its expert (64-bit lane masks in LDS and popcounts), plus the group's rank base:
+//     kept iff rank < capacity, row = offsets[e] + rank, perm[row] = slot, slot_row[slot] = row
+//     or -1.
+// Everything is deterministic: no floating-point atomics, fixed summation orders.
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+#include "route_util.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kFT = 256;  // threads of a routing block: 4 waves, two blocks a CU
+constexpr int kFW = kFT / kWave;
+constexpr int kPrepRows = 64;                    // router rows per prep block (and per bound block)
+constexpr int kGroup = kDispatchTokensPerBlock;  // tokens per dispatch group
+constexpr double kPScale = 1099511627776.0;      // 2^40, the probability sums' fixed point
+constexpr int kCountShift = 55;                  // the counts' place in a group slot
+constexpr int kMaxTT = 256;
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr size_t kStaticLds = 1024;  // headroom for the routing kernel's own __shared__ words
+
+typedef __attribute__((address_space(3))) const char lds_cchar_t;
+
+__device__ __forceinline__ uint32_t lds_u32addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+// 16 bytes per lane from `src` to LDS byte address lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void wait_all_vm() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  return *(lds_u32x4*)(uintptr_t)addr;
+}
+
+// Sum over the 8 lanes of each aligned group of 8 (xor 1, 2, 4); every lane of the group ends
+// with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f32<0x141>(v);  // row_half_mirror: the other quad of the group of 8
+  return v;
+}
+// Sum over the wave, the same value in every lane: the rows of 16 by DPP, then the 4 rows.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = group8_sum(v);
+  v += dpp_f32<0x140>(v);  // row_mirror: the other group of 8 of the row
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Float64 dot products of token row `xrow` of the LDS tile (chunk swizzle `sw`) with n rows of
+// the transposed router, CG rows per pass (row row_of(j) for the j-th product): lane l takes
+// the 16-byte chunks c = l (mod 64), NB of them per round, and every router load of a round
+// (NB x CG, 16 bytes each) is issued before any is used, so a round costs one memory latency.
+// Every product of two bf16 values is exact in float64, so each sum carries float64 rounding
+// only; the lane sums are added by a fixed butterfly, so the value of a product does not
+// depend on which others share its pass. put(j, v) receives the wave-uniform j-th sum.
+template <int CG, class RowOf, class Put>
+__device__ __forceinline__ void tile_dots_f64(uint32_t xrow, int sw, const uint16_t* __restrict__ wt,
+                                              int64_t D, int n, RowOf row_of, Put put) {
+  constexpr int NB = 32 / CG;  // chunks per lane and round: 32 loads in flight
+  const int lane = lane_id();
+  const int nch = (int)(D / 8);
+  for (int j0 = 0; j0 < n; j0 += CG) {
+    const int nj = min(CG, n - j0);
+    const uint4* wr[CG];
+#pragma unroll
+    for (int jj = 0; jj < CG; ++jj)
+      wr[jj] = (const uint4*)(wt + (int64_t)row_of(j0 + (jj < nj ? jj : 0)) * D);
+    double acc[CG];
+#pragma unroll
+    for (int jj = 0; jj < CG; ++jj) acc[jj] = 0.0;
+    for (int c0 = 0; c0 < nch; c0 += NB * kWave) {
+      uint4 wv[NB][CG];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c = c0 + b * kWave + lane;
+#pragma unroll
+        for (int jj = 0; jj < CG; ++jj)  // rows past nj repeat row j0 (not used)
+          wv[b][jj] = c < nch ? wr[jj][c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c = c0 + b * kWave + lane;
+        if (c0 + b * kWave >= nch) break;
+        u32x4 xv = {0u, 0u, 0u, 0u};
+        if (c < nch) xv = lds_read16(xrow + 16u * (uint32_t)(c ^ sw));
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        double xd[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xd[2 * q] = (double)__uint_as_float(xw[q] << 16);
+          xd[2 * q + 1] = (double)__uint_as_float(xw[q] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int jj = 0; jj < CG; ++jj) {
+          const uint32_t ww[4] = {wv[b][jj].x, wv[b][jj].y, wv[b][jj].z, wv[b][jj].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[jj] = fma(xd[2 * q], (double)__uint_as_float(ww[q] << 16), acc[jj]);
+            acc[jj] = fma(xd[2 * q + 1], (double)__uint_as_float(ww[q] & 0xffff0000u), acc[jj]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < CG; ++jj) {
+      if (jj >= nj) break;
+      put(j0 + jj, wave_sum(acc[jj]));
+    }
+  }
+}
+
+template <class RowOf, class Put>
+__device__ __forceinline__ void tile_dots_any(int cg, uint32_t xrow, int sw,
+                                              const uint16_t* __restrict__ wt, int64_t D, int n,
+                                              RowOf row_of, Put put) {
+  if (cg <= 2)
+    tile_dots_f64<2>(xrow, sw, wt, D, n, row_of, put);
+  else if (cg <= 4)
+    tile_dots_f64<4>(xrow, sw, wt, D, n, row_of, put);
+  else if (cg <= 6)
+    tile_dots_f64<6>(xrow, sw, wt, D, n, row_of, put);
+  else
+    tile_dots_f64<8>(xrow, sw, wt, D, n, row_of, put);
+}
+
+// ---- prep ----------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void route_prep_fused_kernel(int64_t D, int E,
+                                                               const uint16_t* __restrict__ w,
+                                                               uint16_t* __restrict__ wt,
+                                                               float* __restrict__ mb,
+                                                               int32_t* __restrict__ zero,
+                                                               int64_t nzero) {
+  __shared__ uint16_t s_w[kPrepRows * kMaxExperts];
+  __shared__ double s_n[kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < nzero; i += (int64_t)gridDim.x * 256)
+    zero[i] = 0;
+  const int64_t d0 = (int64_t)blockIdx.x * kPrepRows;
+  const int rows = (int)min<int64_t>(kPrepRows, D - d0);
+  const uint16_t* src = w + d0 * E;  // rows d0 .. d0 + rows - 1 are contiguous
+  for (int i = tid; i < rows * E; i += 256) s_w[i] = src[i];
+  __syncthreads();
+  for (int i = tid; i < E * kPrepRows; i += 256) {
+    const int e = i / kPrepRows, dd = i % kPrepRows;
+    if (dd < rows) wt[(int64_t)e * D + d0 + dd] = s_w[dd * E + e];
+  }
+  if (tid < E) {
+    double acc = 0.0;
+    for (int dd = 0; dd < rows; ++dd) {
+      const double f = (double)bf16_to_f32(s_w[dd * E + tid]);
+      acc = fma(f, f, acc);
+    }
+    s_n[tid] = acc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double m = 0.0;
+    for (int e = 0; e < E; ++e) m = fmax(m, s_n[e]);
+    // an upper bound on sqrt(m), as a float
+    const double up = sqrt(m) * (1.0 + 0x1p-40);
+    float f = (float)up;
+    if ((double)f < up) f = nextafterf(f, INFINITY);
+    mb[blockIdx.x] = f;
+  }
+}
+
+// ---- route ---------------------------------------------------------------------------------
+
+struct FusedArgs {
+  int64_t T, D;
+  int E, k, TT, MT, NT, ksf;
+  const uint16_t* x;
+  const uint16_t* wt;
+  const float* mb;
+  const float* bias;
+  int32_t* idx;
+  float* gates;
+  float* logits_out;        // nullable
+  int32_t* nflag;           // tokens recomputed in float64 (a counter)
+  unsigned long long* gslot;  // (nG, E): count << kCountShift plus the 2^-40 probability sum
+};
+
+template <int PPW, int EPL>
+// (two blocks share a CU: at least 2 waves per SIMD, at most 256 VGPRs each)
+__global__ __launch_bounds__(kFT, 2) void route_fused_kernel(FusedArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());
+  const int TT = a.TT, E = a.E, k = a.k;
+  const int64_t D = a.D, T = a.T;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int nvalid = (int)min<int64_t>(TT, T - t0);
+  const uint32_t row_bytes = (uint32_t)(2 * D);
+  const uint32_t lds_x = lds_u32addr(smem);
+  double* region = (double*)(smem + (size_t)TT * row_bytes);
+  const int nch = (int)(D / 8);     // 16-byte chunks per row
+  const int nseg = (nch + 63) / 64;  // 1 KB segments per row
+  const int nIc = (nch + kWave - 1) / kWave;
+
+  // b0. the MFMA operands of the router: wave w takes tile pairs pbase + j * pstep and
+  //     k-steps ks = w % ksf (mod ksf), the operands of kB of them loaded together
+  const int P = a.MT * a.NT, ksf = a.ksf;
+  const int pbase = wv / ksf, pstep = kFW / ksf;
+  const int nks = (int)(D / 32);
+  constexpr int kB = PPW == 1 ? 32 : 16 / PPW;  // k-steps whose router operands load together
+  uint32_t arow[PPW];
+  int asw[PPW];
+  const uint16_t* bptr[PPW];
+  bool pv[PPW];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j) {
+    const int p = pbase + j * pstep;
+    pv[j] = p < P;
+    const int m = pv[j] ? p / a.NT : 0, n = pv[j] ? p % a.NT : 0;
+    int r = m * 16 + (lane & 15);
+    if (r >= TT) r &= TT - 1;  // TT < 16: rows repeat (their results are not used)
+    arow[j] = lds_x + (uint32_t)r * row_bytes;
+    asw[j] = r & 15;
+    const int e = n * 16 + (lane & 15);  // columns past E load nothing (their logits are unused)
+    bptr[j] = e < E ? a.wt + (int64_t)e * D + 8 * (lane >> 4) : nullptr;
+  }
+  bf16x8 bv[kB][PPW];
+  auto load_b = [&](int ks0) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int ks = min(ks0 + u * ksf, nks - 1);
+#pragma unroll
+      for (int j = 0; j < PPW; ++j) {
+        bv[u][j] = bf16x8{};
+        if (bptr[j]) bv[u][j] = *(const bf16x8*)(bptr[j] + (int64_t)ks * 32);
+      }
+    }
+  };
+
+  // a. the token tile, straight into LDS
+  for (int i = wv; i < TT * nseg; i += kFW) {
+    const int r = i / nseg, sg = i % nseg;
+    if (r >= nvalid) break;
+    const int pos = sg * 64 + lane;
+    if (pos < nch) {
+      const int c = sg * 64 + (lane ^ (r & 15));
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(lds_x + (uint32_t)r * row_bytes + (uint32_t)sg * 1024u);
+      lds_dma16(a.x + (t0 + r) * D + 8 * (int64_t)c, dst);
+    }
+  }
+  load_b(wv % ksf);  // (completes after the tile: memory operations finish in issue order)
+  // the 64-row blocks' router norm bounds (D <= 8192: at most 128 of them), and the biases
+  __shared__ float s_mb[128];
+  __shared__ float s_bias[kMaxExperts];
+  __shared__ double s_mnorm;
+  for (int i = tid; i < (nch + 7) / 8; i += kFT) s_mb[i] = a.mb[i];
+  for (int i = tid; i < E; i += kFT) s_bias[i] = a.bias ? a.bias[i] : 0.f;
+  wait_all_vm();
+  __syncthreads();
+  if (wv == 0) {
+    // ||m|| = sqrt(sum_b m_b^2), an upper bound (float64 sum of float32 squares, then inflated)
+    double m2 = 0.0;
+    for (int b = lane; b < (nch + 7) / 8; b += kWave) m2 = fma((double)s_mb[b], (double)s_mb[b], m2);
+    m2 = wave_sum(m2);
+    if (lane == 0) s_mnorm = sqrt(m2) * (1.0 + 0x1p-40);
+  }
+
+  // b. logits: every MFMA sums 32 products from zero; the results of kF consecutive steps are
+  //    added in float32 (kF - 1 more roundings of at most 2^-24 of their running sum) and that
+  //    sum is folded into float64
+  constexpr int kF = kB < 8 ? kB : 8;
+  double acc[PPW][4];
+#pragma unroll
+  for (int j = 0; j < PPW; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[j][v] = 0.0;
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 part[PPW];  // the float32 sum of the current group of kF steps
+  static_assert(kB % kF == 0, "fold groups within a batch");
+  // a step past the end (the last batch's tail) multiplies zero operands, so every batch runs
+  // all kB steps: the operand reads and the MFMAs of groups of 4 steps are issued together
+  // before their results are folded
+  for (int ks0 = wv % ksf; ks0 < nks; ks0 += kB * ksf) {
+    if (ks0 != wv % ksf) load_b(ks0);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (ks0 + u * ksf >= nks)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) bv[u][j] = bf16x8{};
+    constexpr int kG = 4 / PPW;  // steps whose MFMAs are issued together
+#pragma unroll
+    for (int u0 = 0; u0 < kB; u0 += kG) {
+      bf16x8 av[kG][PPW];
+#pragma unroll
+      for (int u = u0; u < u0 + kG; ++u) {
+        const int c = min(ks0 + u * ksf, nks - 1) * 4 + (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < PPW; ++j)
+          av[u - u0][j] =
+              __builtin_bit_cast(bf16x8, lds_read16(arow[j] + 16u * (uint32_t)(c ^ asw[j])));
+      }
+      f32x4 cc[kG][PPW];
+#pragma unroll
+      for (int u = 0; u < kG; ++u)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j)
+          cc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][j], bv[u0 + u][j], zero4, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kG; ++u)
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+          if ((u0 + u) % kF == 0)
+            part[j] = cc[u][j];
+          else
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part[j][v] += cc[u][j][v];
+          if ((u0 + u) % kF == kF - 1)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[j][v] += (double)part[j][v];
+        }
+    }
+  }
+  // partial logits (ksf x TT x E, float64) into the region; C layout: lane l holds column
+  // l % 16 and rows 4 (l / 16) + v of its tile
+  {
+    const int slot = wv % ksf;
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+      if (!pv[j]) continue;
+      const int p = pbase + j * pstep, m = p / a.NT, n = p % a.NT;
+      const int col = n * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m * 16 + 4 * (lane >> 4) + v;
+        if (row < TT && col < E) region[((int64_t)slot * TT + row) * E + col] = acc[j][v];
+      }
+    }
+  }
+  __syncthreads();
+
+  // c. the tokens, one wave each (the wave's tokens are r = wv, wv + 4, ...): logits, bound,
+  //    top k + 1; when the bound certifies the order, the k chosen logits exactly (gates need
+  //    them to ~1e-7; with k = 1 the gate is 1 whatever the logit), else every logit exactly
+  //    and the decision from them; then probabilities, gates and counts.
+  double psum[EPL];
+  int cnt[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    psum[i] = 0.0;
+    cnt[i] = 0;
+  }
+  int nflag = 0;
+  // every 32-term MFMA sum is within 31 * 2^-23 of the sum of its |products| (any order, either
+  // rounding), the float32 additions of a fold group add at most 7 * 2^-24, the float64 folds far
+  // less
+  const double gamma = 35.0 * 0x1p-23;
+  for (int r = wv; r < nvalid; r += kFW) {
+    const int64_t t = t0 + r;
+    double lg[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + kWave * i;
+      lg[i] = 0.0;
+      if (e < E) {
+        for (int s = 0; s < ksf; ++s) lg[i] += region[(s * TT + r) * E + e];
+        lg[i] += (double)s_bias[e];
+      }
+    }
+    const uint32_t xrow = lds_x + (uint32_t)r * row_bytes;
+    const int sw = r & 15;
+    // ||x_t||^2 by dot2 of bf16 pairs (float32; inflated to cover its roundings). By
+    // Cauchy-Schwarz over the 64-row blocks, sum_b ||x_t,b|| m_b <= ||x_t|| ||m||.
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    float xs = 0.f;
+    for (int i0 = 0; i0 < nIc; i0 += 4) {
+      u32x4 xv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = lane + kWave * (i0 + u);
+        xv[u] = u32x4{0u, 0u, 0u, 0u};
+        if (c < nch) xv[u] = lds_read16(xrow + 16u * (uint32_t)(c ^ sw));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const bf16x2_t v2 = __builtin_bit_cast(bf16x2_t, xw[h]);
+          xs = __builtin_amdgcn_fdot2_f32_bf16(v2, v2, xs, false);
+        }
+      }
+    }
+    const double xn2 = (double)wave_sum_f32(xs) * (1.0 + (double)D * 0x1p-20) + 1e-300;
+    const double bx = sqrt(xn2) * s_mnorm * (1.0 + 0x1p-30);
+    double lmax = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + kWave * i < E) lmax = fmax(lmax, fabs(lg[i]));
+    lmax = wave_max(lmax);
+    const double B = gamma * bx + lmax * 0x1p-50 + 1e-30;
+    double my_v[EPL];
+    int my_e[EPL];
+    bool sel[EPL];
+    const double gap = topk_rounds_keys<EPL>(E, k, lg, sel, my_v, my_e);
+    const bool flagged = !(gap > 2.0 * B + lmax * 0x1p-22);
+    if (flagged) {
+      // every logit exactly, and the decision from them
+      tile_dots_any(8, xrow, sw, a.wt, D, E, [](int j) { return j; }, [&](int j, double v) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (j == lane + kWave * i) lg[i] = v;
+      });
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        lg[i] = lane + kWave * i < E ? lg[i] + (double)s_bias[lane + kWave * i] : 0.0;
+      topk_rounds<EPL>(E, k, lg, sel, my_v, my_e, false);
+      ++nflag;
+    } else if (k > 1) {
+      // the k chosen logits exactly (the order is already the exact one)
+      auto row_of = [&](int j) {
+        int e = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if ((j >> 6) == i) e = __builtin_amdgcn_readlane(my_e[i], j & 63);
+        return e;
+      };
+      tile_dots_any(k, xrow, sw, a.wt, D, k, row_of, [&](int j, double v) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (j == lane + kWave * i) my_v[i] = v + (double)s_bias[my_e[i]];
+      });
+    }
+    write_logits<EPL>(a.logits_out, t, E, lg);
+    double prob[EPL];
+    finish_token<EPL>(E, k, t, lg, my_v, my_e, prob, a.idx, a.gates, true);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      psum[i] += prob[i];
+      cnt[i] += sel[i] ? 1 : 0;
+    }
+  }
+
+  // d. block sums (waves in order), added to the token group's slots as one 64-bit integer
+  //    per expert: the count above kCountShift, the probability sum in units of 2^-40 below
+  //    (a group's sums stay below 2^48, its counts below 2^9), so the totals do not depend on
+  //    the order the blocks add them in
+  __syncthreads();  // the region's partial logits are no longer read
+  double* s_ps = region;                         // [kFW][E]
+  int32_t* s_cn = (int32_t*)(region + kFW * E);  // [kFW][E]
+  __shared__ int s_nf[kFW];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      s_ps[wv * E + e] = psum[i];
+      s_cn[wv * E + e] = cnt[i];
+    }
+  }
+  if (lane == 0) s_nf[wv] = nflag;
+  __syncthreads();
+  const int64_t g = t0 / kGroup;
+  for (int e = tid; e < E; e += kFT) {
+    double ps = 0.0;
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kFW; ++q) {
+      ps += s_ps[q * E + e];
+      c += s_cn[q * E + e];
+    }
+    const unsigned long long v =
+        ((unsigned long long)c << kCountShift) + (unsigned long long)llrint(ps * kPScale);
+    if (v) atomicAdd(a.gslot + g * E + e, v);
+  }
+  if (tid == 0) {
+    int nf = 0;
+#pragma unroll
+    for (int q = 0; q < kFW; ++q) nf += s_nf[q];
+    if (nf) atomicAdd(a.nflag, nf);
+  }
+}
+
+// ---- place ----------------------------------------------------------------------------------
+
+struct PlaceArgs {
+  int64_t T, capacity;
+  int E, k, nG;
+  const int32_t* idx;
+  const unsigned long long* gslot;  // (nG, E), from the routing kernel
+  const int32_t* nflag;
+  float* aux;
+  int32_t* counts_out;   // nullable
+  int32_t* uncertified;  // nullable
+  int32_t* offsets;      // (E + 1); with perm null, nullable
+  int32_t* perm;         // null: only the loss and the counts (one block)
+  int32_t* slot_row;
+  int32_t* zero;         // nullable: nzero int32 cleared by block 0 (a later kernel's counters)
+  int nzero;
+};
+
+// One block per group of 256 tokens, one token per thread.
+//  1. From the group slots: each expert's total count (all groups) and rank base (the groups
+//     before this one), its kept rows min(count, capacity) and the row offsets; block 0 also
+//     writes the counts, the uncertified count and aux = E sum_e (count_e / (T k)) (P_e / T).
+//     Every sum is over integers or in a fixed order, so the result does not depend on the
+//     order of the routing blocks.
+//  2. A slot's rank among the group's earlier slots of the same expert is the popcount of the
+//     lower lanes' bits in its wave's 64-bit mask for that expert plus the counts of the
+//     earlier waves (integer OR and popcount: order-independent); with the group's rank base
+//     it is the slot's rank among all earlier tokens: kept iff rank < capacity, row =
+//     offsets[e] + rank, perm[row] = slot, slot_row[slot] = row or -1.
+__global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
+  constexpr int kW = kGroup / kWave;
+  __shared__ unsigned long long s_mask[kW][kMaxExperts];
+  __shared__ int s_base[kW][kMaxExperts];
+  __shared__ int s_tot[kGroup], s_gb[kGroup];
+  __shared__ unsigned long long s_p[kGroup];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ double s_term[kGroup];
+  const int tid = threadIdx.x, wv = wave_id(), lane = lane_id();
+  const int E = a.E, k = a.k;
+  const int g = blockIdx.x;
+  if (g == 0 && a.zero)
+    for (int i = tid; i < a.nzero; i += kGroup) a.zero[i] = 0;
+  for (int i = tid; i < kW * kMaxExperts; i += kGroup) (&s_mask[0][0])[i] = 0ull;
+  // 1. Q threads per expert, each over the groups q, q + Q, ...
+  const int Q = max(1, kGroup / E);
+  {
+    int tot = 0, gb = 0;
+    unsigned long long ps = 0;
+    if (tid < Q * E) {
+      const int e = tid % E, q = tid / E;
+      constexpr int kC = 16;  // loads in flight
+      for (int g0 = q; g0 < a.nG; g0 += kC * Q) {
+        unsigned long long v[kC];
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+          const int gg = g0 + u * Q;
+          v[u] = gg < a.nG ? a.gslot[(int64_t)gg * E + e] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kC; ++u) {
+          const int gg = g0 + u * Q;
+          const int c = (int)(v[u] >> kCountShift);
+          tot += c;
+          if (gg < g) gb += c;
+          ps += v[u] & ((1ull << kCountShift) - 1ull);
+        }
+      }
+    }
+    s_tot[tid] = tot;
+    s_gb[tid] = gb;
+    s_p[tid] = ps;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int tot = 0, gb = 0;
+    unsigned long long ps = 0;
+    for (int q = 0; q < Q; ++q) {
+      tot += s_tot[q * E + tid];
+      gb += s_gb[q * E + tid];
+      ps += s_p[q * E + tid];
+    }
+    s_tot[tid] = tot;  // (rows q > 0 are no longer read)
+    s_gb[tid] = gb;
+    s_p[tid] = ps;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      s_off[e] = run;
+      run += a.capacity < 0 ? s_tot[e] : (int)min<int64_t>((int64_t)s_tot[e], a.capacity);
+    }
+    s_off[E] = run;
+  }
+  if (g == 0) {
+    double term = 0.0;
+    if (tid < E) {
+      if (a.counts_out) a.counts_out[tid] = s_tot[tid];
+      term = ((double)s_tot[tid] / ((double)a.T * (double)k)) *
+             (((double)s_p[tid] / kPScale) / (double)a.T);
+    }
+    s_term[tid] = term;
+    __syncthreads();
+    for (int h = kGroup / 2; h >= 1; h >>= 1) {
+      if (tid < h) s_term[tid] += s_term[tid + h];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      *a.aux = (float)((double)E * s_term[0]);
+      if (a.uncertified) *a.uncertified = *a.nflag;
+    }
+    if (a.offsets)
+      for (int e = tid; e <= E; e += kGroup) a.offsets[e] = s_off[e];
+  }
+  if (!a.perm) return;
+  // 2. ranks within the group and placement
+  const int64_t t = (int64_t)g * kGroup + tid;
+  const bool valid = t < a.T;
+  if (valid)
+    for (int j = 0; j < k; ++j) atomicOr(&s_mask[wv][a.idx[t * k + j]], 1ull << lane);
+  __syncthreads();
+  for (int e = tid; e < E; e += kGroup) {
+    int run = s_gb[e];
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      s_base[q][e] = run;
+      run += __popcll(s_mask[q][e]);
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const unsigned long long lower = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const int64_t sl = t * k + j;
+    const int e = a.idx[sl];
+    const int rank = s_base[wv][e] + __popcll(s_mask[wv][e] & lower);
+    int row = -1;
+    if (a.capacity < 0 || rank < a.capacity) {
+      row = s_off[e] + rank;
+      a.perm[row] = (int32_t)sl;
+    }
+    a.slot_row[sl] = row;
+  }
+}
+
+// ---- host side -----------------------------------------------------------------------------
+
+int pow2_floor(int64_t v) {
+  int p = 1;
+  while ((int64_t)p * 2 <= v) p *= 2;
+  return p;
+}
+
+struct FusedShape {
+  int TT, MT, NT, P, ksf, ppw, epl;
+  size_t region, lds;
+};
+
+FusedShape fused_shape(const Problem& p) {
+  FusedShape f{};
+  f.NT = (p.E + 15) / 16;
+  // the token tile fills at most 64 KB of LDS (two blocks per CU); at most 16 MFMA tile pairs
+  int TT = pow2_floor(std::max<int64_t>(4, 32768 / p.D));
+  TT = std::min(TT, kMaxTT);
+  while (TT > 4 && ((TT + 15) / 16) * f.NT > 16) TT /= 2;
+  f.TT = TT;
+  f.MT = (TT + 15) / 16;
+  f.P = f.MT * f.NT;
+  f.ksf = 1;  // waves sharing a tile pair split its k-steps
+  while (f.P * f.ksf * 2 <= kFW) f.ksf *= 2;
+  const int pairs_per_wave = (f.P * f.ksf + kFW - 1) / kFW;
+  f.ppw = pairs_per_wave <= 1 ? 1 : pairs_per_wave <= 2 ? 2 : 4;
+  f.epl = p.E <= 64 ? 1 : p.E <= 128 ? 2 : 4;
+  f.region = std::max<size_t>({(size_t)f.ksf * TT * p.E * 8, (size_t)kFW * p.E * 12,
+                               (size_t)kFT * 8 + kMaxExperts * 4});
+  f.region = (f.region + 15) & ~size_t(15);
+  f.lds = (size_t)TT * 2 * p.D + f.region;
+  return f;
+}
+
+struct FusedLayout {
+  size_t wt, mb, zero, nflag, gslot, bytes;
+  int64_t nP, nG, nzero;
+};
+
+FusedLayout fused_layout(const Problem& p) {
+  FusedLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = (off + n + 255) & ~size_t(255);
+    return o;
+  };
+  L.nP = (p.D + kPrepRows - 1) / kPrepRows;
+  L.nG = (p.T + kGroup - 1) / kGroup;
+  L.wt = take((size_t)p.E * p.D * 2);
+  L.mb = take((size_t)L.nP * 4);
+  // the counters cleared by prep, contiguous: the recomputed-token count, then the group slots
+  L.zero = off;
+  L.nflag = L.zero;
+  L.gslot = L.zero + 8;
+  const size_t end = L.gslot + (size_t)L.nG * p.E * 8;
+  L.nzero = (int64_t)((end - L.zero) / 4);
+  take(end - L.zero);
+  L.bytes = off;
+  return L;
+}
+
+template <int PPW, int EPL>
+hipError_t launch_fused_inst(const FusedShape& f, const FusedArgs& a, unsigned nblk,
+                             hipStream_t s) {
+  // dynamic LDS past 64 KB needs the kernel's limit raised to it (once per size reached)
+  static size_t lds_allowed = 64 * 1024;
+  if (f.lds > lds_allowed) {
+    const hipError_t e = hipFuncSetAttribute((const void*)route_fused_kernel<PPW, EPL>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)f.lds);
+    if (e != hipSuccess) return e;
+    lds_allowed = f.lds;
+  }
+  hipLaunchKernelGGL((route_fused_kernel<PPW, EPL>), dim3(nblk), dim3(kFT), f.lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance) {
+  if (p.dtype != MOE_BF16 || o.w_noise || !o.renorm || importance) return false;
+  if (p.T <= 0 || p.D % 128 != 0 || p.D > 8192 || p.E > kMaxExperts) return false;
+  if (p.T >= (int64_t)1 << 23) return false;  // the 2^-40 probability sums stay below 2^63
+  // with many choices per token the exact chosen logits (k D float64 products a token, on the
+  // vector units) outweigh the pass over x that the fused path saves
+  if (p.top_k > 2) return false;
+  return fused_shape(p).lds + kStaticLds <= kMaxLds;
+}
+
+size_t fused_route_ws_bytes(const Problem& p) { return fused_layout(p).bytes; }
+
+hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
+                              const float* bias, int32_t* idx, float* gates, float* logits_out,
+                              void* fws, hipStream_t s) {
+  const FusedLayout L = fused_layout(p);
+  const FusedShape f = fused_shape(p);
+  char* b = (char*)fws;
+  hipLaunchKernelGGL(route_prep_fused_kernel, dim3((unsigned)L.nP), dim3(256), 0, s, p.D, p.E,
+                     (const uint16_t*)w_router, (uint16_t*)(b + L.wt), (float*)(b + L.mb),
+                     (int32_t*)(b + L.zero), L.nzero);
+  FusedArgs a{};
+  a.T = p.T;
+  a.D = p.D;
+  a.E = p.E;
+  a.k = p.top_k;
+  a.TT = f.TT;
+  a.MT = f.MT;
+  a.NT = f.NT;
+  a.ksf = f.ksf;
+  a.x = (const uint16_t*)x;
+  a.wt = (const uint16_t*)(b + L.wt);
+  a.mb = (const float*)(b + L.mb);
+  a.bias = bias;
+  a.idx = idx;
+  a.gates = gates;
+  a.logits_out = logits_out;
+  a.nflag = (int32_t*)(b + L.nflag);
+  a.gslot = (unsigned long long*)(b + L.gslot);
+  const unsigned nblk = (unsigned)((p.T + f.TT - 1) / f.TT);
+#define MOE_FUSED(PPWV, EPLV) return launch_fused_inst<PPWV, EPLV>(f, a, nblk, s)
+  if (f.epl == 1) {
+    if (f.ppw == 1) MOE_FUSED(1, 1);
+    if (f.ppw == 2) MOE_FUSED(2, 1);
+    MOE_FUSED(4, 1);
+  } else if (f.epl == 2) {
+    if (f.ppw == 1) MOE_FUSED(1, 2);
+    if (f.ppw == 2) MOE_FUSED(2, 2);
+    MOE_FUSED(4, 2);
+  } else {
+    if (f.ppw == 1) MOE_FUSED(1, 4);
+    if (f.ppw == 2) MOE_FUSED(2, 4);
+    MOE_FUSED(4, 4);
+  }
+#undef MOE_FUSED
+}
+
+hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* fws, float* aux,
+                              int32_t* counts_out, int32_t* uncertified, int32_t* offsets,
+                              int32_t* perm, int32_t* slot_row, hipStream_t s, int32_t* zero,
+                              int nzero) {
+  const FusedLayout L = fused_layout(p);
+  PlaceArgs a{};
+  a.T = p.T;
+  a.capacity = p.capacity;
+  a.E = p.E;
+  a.k = p.top_k;
+  a.nG = (int)L.nG;
+  a.idx = idx;
+  a.gslot = (const unsigned long long*)((const char*)fws + L.gslot);
+  a.nflag = (const int32_t*)((const char*)fws + L.nflag);
+  a.aux = aux;
+  a.counts_out = counts_out;
+  a.uncertified = uncertified;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.slot_row = slot_row;
+  a.zero = zero;
+  a.nzero = nzero;
+  const unsigned grid = perm ? (unsigned)L.nG : 1u;
+  hipLaunchKernelGGL(place_fused_kernel, dim3(grid), dim3(kGroup), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

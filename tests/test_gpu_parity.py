@@ -39,6 +39,14 @@ MID_CASES = {
     "swiglu_long_k_split2": spec("mixtral_swiglu_bf16", T=300, D=256, DH=4096, E=4, top_k=2),
     "relu_long_k_split4": spec("switch_top1_cap_bf16", T=200, D=128, DH=8192, E=2,
                                capacity_factor=0.0),
+    # the fused bf16 routing kernel's edges: 256 experts (16 expert tiles, 4 per lane in the
+    # select), 128 experts with D = 640 (a partial 1 KB segment per row), k = E, and D = 8192
+    # (4-token tiles)
+    "fused_e256_k8_cap": spec("switch_top1_cap_bf16", T=700, D=256, DH=128, E=256, top_k=8,
+                              capacity_factor=1.5),
+    "fused_e128_d640": spec("fine_grained_zipf_bf16", T=900, D=640, DH=128, E=128, top_k=3),
+    "fused_k_equals_e": spec("mixtral_swiglu_bf16", T=333, D=128, DH=128, E=8, top_k=8),
+    "fused_d8192": spec("mixtral_swiglu_bf16", T=130, D=8192, DH=128, E=8),
 }
 
 
