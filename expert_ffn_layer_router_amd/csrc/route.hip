@@ -409,14 +409,14 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(
 }
 
 constexpr int kSelWaves = kRouteTokensPerBlock;  // one token per wave
+// Up to this many experts, the select kernel recomputes a flagged token's logits itself.
 constexpr int kInWaveExact = 16;
 
 // uncertified = the listed tokens plus those the select kernel recomputed itself.
 __global__ void report_uncertified_kernel(const int32_t* __restrict__ nlist,
                                           int32_t* __restrict__ uncertified) {
   *uncertified = nlist[0] + nlist[1];
-}  // up to this many experts, the select kernel recomputes a
-                                  // flagged token's logits itself
+}
 constexpr int kSelThreads = kSelWaves * kWave;
 constexpr int kFbThreads = 1024;  // threads per uncertified token in the fallback
 

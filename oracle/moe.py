@@ -177,20 +177,20 @@ def dispatch_from_indices(idx: np.ndarray, E: int, capacity: Optional[int]) -> d
     """
     idx = np.asarray(idx)
     T, k = idx.shape
-    counts = np.zeros(E, dtype=np.int64)
-    kept = np.zeros(E, dtype=np.int64)
-    per_expert = []
-    for e in range(E):
-        hit = idx == e  # (T, k); at most one True per row
-        sent = np.flatnonzero(hit.any(axis=1))  # routed tokens, ascending
-        counts[e] = sent.size
-        if capacity is not None and sent.size > capacity:
-            sent = sent[:capacity]  # first come, first served
-        kept[e] = sent.size
-        j = np.argmax(hit[sent], axis=1)  # the rank j at which token t chose e
-        per_expert.append(sent * k + j)
+    flat = idx.reshape(-1).astype(np.int64)  # slot s = t*k + j chose expert flat[s]
+    # Group the slots by expert with a stable sort: within one expert the slot ids, and so
+    # the token indices (a token picks an expert at most once), stay ascending.
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(counts)])
+    # rank of each slot among the slots of its expert, in token order
+    rank = np.empty(T * k, dtype=np.int64)
+    rank[order] = np.arange(T * k) - start[flat[order]]
+    # capacity keeps the `capacity` earliest tokens of each expert and drops the rest
+    keep = np.ones(T * k, dtype=bool) if capacity is None else rank < capacity
+    kept = np.bincount(flat[keep], minlength=E).astype(np.int64)
+    perm = order[keep[order]]  # kept slots in (expert, token) order
     offsets = np.concatenate([[0], np.cumsum(kept)]).astype(np.int64)
-    perm = np.concatenate(per_expert).astype(np.int64) if per_expert else np.zeros(0, np.int64)
     slot_row = np.full(T * k, -1, dtype=np.int64)
     slot_row[perm] = np.arange(perm.size)
     return dict(counts=counts, kept=kept, offsets=offsets, perm=perm, slot_row=slot_row,
@@ -278,7 +278,7 @@ def moe_forward(x, w_router, top_k: int, kind: str, w1, w2=None, w3=None, bias=N
         if want is not None:
             rows = rows[want[rows // top_k]]
         if rows.size == 0:
-            continue  # idle expert: no work
+            continue
         t = rows // top_k
         y = expert_forward(kind, x[t], *_expert_weights(e, w1, w2, w3))
         # one slot per (token, expert), so no two rows of t repeat here
