@@ -282,8 +282,8 @@ moe_status scratch_of_current_device(hipStream_t stream, void** out) {
 
 extern "C" {
 
-const char* moe_status_string(moe_status s) {
-  switch (s) {
+const char* moe_status_string(int status) {
+  switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: a null required pointer or a size out of range";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: a shape, dtype or expert kind this library does not handle";

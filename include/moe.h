@@ -86,8 +86,9 @@ typedef struct moe_problem {
   int32_t kind;           /* moe_expert_kind */
 } moe_problem;
 
-/* Human-readable name of a status code (static storage, never NULL). */
-const char* moe_status_string(moe_status s);
+/* Human-readable name of a status code (static storage, never NULL). Takes any int: a value
+ * that is not a moe_status gives "unknown moe_status". */
+const char* moe_status_string(int status);
 
 /* Checks a problem statement (host only). Returns MOE_OK, MOE_ERR_INVALID_ARG or
  * MOE_ERR_UNSUPPORTED. */
