@@ -32,9 +32,12 @@ __device__ __forceinline__ uint4 pack8(const float f[8]) {
 // bf16 rows, N % 8 == 0, 16-byte aligned, top_k <= 64. Lane j first loads slot j's row and
 // gate (one round of loads for the whole token), then each pass over the row issues the KG x U
 // 16-byte loads of KG slots and U column chunks per lane before any of them is used, so a
-// wave has KG x U row loads in flight; the sum still runs over j ascending.
-template <int KG, int U>
-__global__ __launch_bounds__(kThreads) void combine_bf16x8_kernel(
+// wave has KG x U row loads in flight; the sum still runs over j ascending. With ONE (top_k <=
+// KG) the token's slots are a single group, and each column chunk is summed, packed and stored
+// as soon as its loads are in, so only the loads hold registers: 4 waves a SIMD fit, and a
+// token per wave keeps every row load of a 4-waves-a-SIMD grid in flight at once.
+template <int KG, int U, bool ONE>
+__global__ __launch_bounds__(kThreads, 4) void combine_bf16x8_kernel(
     int64_t T, int k, int64_t n_vec, const uint4* __restrict__ y,
     const int32_t* __restrict__ slot_row, const float* __restrict__ gates,
     uint4* __restrict__ out) {
@@ -44,11 +47,13 @@ __global__ __launch_bounds__(kThreads) void combine_bf16x8_kernel(
   const int rl = lane < k ? slot_row[t * k + lane] : -1;
   const float gl = lane < k ? gates[t * k + lane] : 0.f;
   for (int64_t c0 = lane; c0 < n_vec; c0 += U * kWave) {
-    float acc[U][8];
+    float acc[ONE ? 1 : U][8];
+    if (!ONE) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < (ONE ? 1 : U); ++u)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+        for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+    }
     for (int j0 = 0; j0 < k; j0 += KG) {
       int r[KG];
       float g[KG];
@@ -67,22 +72,43 @@ __global__ __launch_bounds__(kThreads) void combine_bf16x8_kernel(
                                                : make_uint4(0u, 0u, 0u, 0u);
         }
       }
-#pragma unroll
-      for (int jj = 0; jj < KG; ++jj) {
-        if (r[jj] < 0) continue;
+      if (ONE) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          float v[8];
-          unpack8(w[jj][u], v);
+          float a[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g[jj], v[i], acc[u][i]);
+          for (int i = 0; i < 8; ++i) a[i] = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < KG; ++jj) {
+            if (r[jj] < 0) continue;
+            float v[8];
+            unpack8(w[jj][u], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] = fmaf(g[jj], v[i], a[i]);
+          }
+          const int64_t c = c0 + u * kWave;
+          if (c < n_vec) out[t * n_vec + c] = pack8(a);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < KG; ++jj) {
+          if (r[jj] < 0) continue;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float v[8];
+            unpack8(w[jj][u], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(g[jj], v[i], acc[u][i]);
+          }
         }
       }
     }
+    if (!ONE) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + u * kWave;
-      if (c < n_vec) out[t * n_vec + c] = pack8(acc[u]);
+      for (int u = 0; u < (ONE ? 1 : U); ++u) {
+        const int64_t c = c0 + u * kWave;
+        if (c < n_vec) out[t * n_vec + c] = pack8(acc[u]);
+      }
     }
   }
 }
@@ -114,16 +140,27 @@ hipError_t launch_combine(const Problem& p, const void* y, const int32_t* slot_r
   const unsigned grid = (unsigned)((p.T + kWaves - 1) / kWaves);
   const bool al16 = ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0);
   if (p.dtype == MOE_BF16 && p.D_out % 8 == 0 && al16 && p.top_k <= kWave) {
-    // 16 row loads in flight per wave: slots x column chunks
-    if (p.top_k <= 2)
-      hipLaunchKernelGGL((combine_bf16x8_kernel<2, 8>), dim3(grid), dim3(kThreads), 0, s, p.T,
-                         p.top_k, p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
-    else if (p.top_k <= 4)
-      hipLaunchKernelGGL((combine_bf16x8_kernel<4, 4>), dim3(grid), dim3(kThreads), 0, s, p.T,
-                         p.top_k, p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
-    else
-      hipLaunchKernelGGL((combine_bf16x8_kernel<8, 2>), dim3(grid), dim3(kThreads), 0, s, p.T,
-                         p.top_k, p.D_out / 8, (const uint4*)y, slot_row, gates, (uint4*)out);
+    // slots x column chunks of loads in flight per lane; a token's slots in one group when
+    // top_k <= 8, with as many column chunks as the row has (up to 8 a lane)
+    const int64_t nv = p.D_out / 8;
+    const uint4* yv = (const uint4*)y;
+    uint4* ov = (uint4*)out;
+#define MOE_COMBINE(KG, U, ONE)                                                            \
+  hipLaunchKernelGGL((combine_bf16x8_kernel<KG, U, ONE>), dim3(grid), dim3(kThreads), 0, s, \
+                     p.T, p.top_k, nv, yv, slot_row, gates, ov)
+    if (p.top_k <= 2) {
+      if (nv > 4 * kWave) MOE_COMBINE(2, 8, true);
+      else if (nv > 2 * kWave) MOE_COMBINE(2, 4, true);
+      else MOE_COMBINE(2, 2, true);
+    } else if (p.top_k <= 4) {
+      if (nv > 2 * kWave) MOE_COMBINE(4, 4, true);
+      else MOE_COMBINE(4, 2, true);
+    } else if (p.top_k <= 8) {
+      MOE_COMBINE(8, 2, true);
+    } else {
+      MOE_COMBINE(8, 2, false);
+    }
+#undef MOE_COMBINE
   } else if (p.dtype == MOE_BF16) {
     hipLaunchKernelGGL(combine_scalar_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s, p.T,
                        p.top_k, p.D_out, (const uint16_t*)y, slot_row, gates, (uint16_t*)out);

@@ -104,8 +104,8 @@ hipError_t launch_place_after_route(const Problem& p, const int32_t* idx, void* 
 bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance);
 size_t fused_route_ws_bytes(const Problem& p);
 hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
-                              const float* bias, int32_t* idx, float* gates, float* logits_out,
-                              void* fws, hipStream_t s);
+                              const float* bias, bool renorm, int32_t* idx, float* gates,
+                              float* logits_out, void* fws, hipStream_t s);
 // perm null: one block forms the loss and the counts (and the offsets, if given) only
 hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* fws, float* aux,
                               int32_t* counts_out, int32_t* uncertified, int32_t* offsets,

@@ -56,6 +56,7 @@ constexpr int kCountShift = 55;                  // the counts' place in a group
 constexpr int kMaxTT = 256;
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr size_t kStaticLds = 1024;  // headroom for the routing kernel's own __shared__ words
+constexpr int kMaxExpertsExact = 64;  // the exact route's limit on E
 
 typedef __attribute__((address_space(3))) const char lds_cchar_t;
 
@@ -532,14 +533,336 @@ __global__ __launch_bounds__(kFT, 2) void route_fused_kernel(FusedArgs a) {
   }
 }
 
+// ---- exact route (E <= 64) ------------------------------------------------------------------
+
+// Every logit exactly: the float64 matrix cores (v_mfma_f64_16x16x4f64) sum the products of the
+// bf16 inputs, each exact in float64, with float64 rounding only; nothing is left to certify.
+// One block per TT = 16 MT tokens (MT M-tiles of 16 rows), Wv waves: wave w takes M-tile
+// w / KP and the K-chunks c = w % KP (mod KP), KP = Wv / MT, where a chunk is 32 of D and its
+// step j (0..7) gives lane group g (lane / 16) the column d = 32 c + 8 g + j, so a lane's A
+// values for a chunk are 8 consecutive bf16 of its token row (one 16-byte load) and its B
+// values the router entries W[d][16 n + lane % 16] of those 8 rows (E-strided, from L2).
+constexpr int kXT = 16;  // tokens per M-tile: the float64 MFMA's 16 rows
+
+struct ExactArgs {
+  int64_t T, D;
+  int E, k, MT, KP;
+  bool renorm;
+  const uint16_t* x;
+  const uint16_t* w;
+  const float* bias;
+  int32_t* idx;
+  float* gates;
+  float* logits_out;          // nullable
+  unsigned long long* bslot;  // (blocks, E): count << kCountShift plus the 2^-40 probability sum
+};
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double bf16_lo_f64(uint32_t u) { return (double)__uint_as_float(u << 16); }
+__device__ __forceinline__ double bf16_hi_f64(uint32_t u) {
+  return (double)__uint_as_float(u & 0xffff0000u);
+}
+
+// Reductions over a row of 16 lanes (lane ^ 1, lane ^ 2, the mirrored lane of the half row, of
+// the row): every lane of the row ends with the same value, in a fixed order.
+__device__ __forceinline__ double row_sum16(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  return v;
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(double& bv, int& be) {
+  const double ov = dpp_f64<CTRL>(bv);
+  const int oe = __builtin_amdgcn_mov_dpp(be, CTRL, 0xf, 0xf, true);
+  if (ov > bv || (ov == bv && oe < be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+// The larger logit, equal logits to the smaller expert index (a total order, so every lane of
+// the row ends with the same pair).
+__device__ __forceinline__ void row_argmax16(double& bv, int& be) {
+  argmax_step<0xB1>(bv, be);
+  argmax_step<0x4E>(bv, be);
+  argmax_step<0x141>(bv, be);
+  argmax_step<0x140>(bv, be);
+}
+
+// The chunk ring of a wave: slot = the chunk's A tile (16 token rows x 32 of D, 1 KB, lane l's
+// MFMA operand at byte 16 l) then NT router tiles (32 rows of D x 16 experts, 32 bytes a row).
+// Both arrive by global_load_lds_dwordx4, which no register waits for: the waits are explicit.
+constexpr int kExactRing = 3;  // chunks in flight per wave
+
+template <int NT>
+__device__ __forceinline__ void exact_issue(const char* asrc, const char* const (&bsrc)[NT],
+                                            int64_t c, int64_t brow_bytes, uint32_t slot) {
+  lds_dma16(asrc + c * 64, slot);
+#pragma unroll
+  for (int n = 0; n < NT; ++n) lds_dma16(bsrc[n] + c * brow_bytes, slot + 1024u * (1 + n));
+}
+
+// s_waitcnt vmcnt(after * (1 + NT)): the loads of the `after` chunks issued after this one may
+// stay in flight (vector memory operations complete in issue order)
+template <int NT>
+__device__ __forceinline__ void exact_wait(int after) {
+  constexpr int L = 1 + NT;
+  if (after >= 2)
+    __builtin_amdgcn_s_waitcnt(((2 * L) & 15) | (((2 * L) >> 4) << 14) | 0xF70);
+  else if (after == 1)
+    __builtin_amdgcn_s_waitcnt((L & 15) | ((L >> 4) << 14) | 0xF70);
+  else
+    __builtin_amdgcn_s_waitcnt(0xF70);  // (expcnt and lgkmcnt at their maxima: not waited for)
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+template <int NT>
+constexpr int exact_waves() {
+  return NT == 1 ? 16 : NT == 2 ? 8 : 4;
+}
+
+template <int NT>
+__global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(ExactArgs a) {
+  constexpr int Wv = exact_waves<NT>();
+  // dynamic LDS: the waves' chunk rings, then (after the chunk loop) the partial logits of
+  // every wave (Wv x NT tiles of 16 x 16, float64: 32 KB), then the probability sums and counts
+  extern __shared__ __align__(16) char smem[];
+  double* s_part = (double*)smem;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int KP = a.KP, E = a.E, k = a.k;
+  const int64_t D = a.D, T = a.T;
+  const int TT = kXT * a.MT;
+  const int64_t tb = (int64_t)blockIdx.x * TT;
+  const int m = w / KP, kp = w % KP;
+  const int nch = (int)(D / 32);
+  const int col = lane & 15, g = lane >> 4;
+
+  // 1. partial logits. Wave w's chunks c = kp + i KP go through its ring of kExactRing slots:
+  //    chunk i is waited for, its operands read (A by ds_read_b128; B by two transposed reads a
+  //    tile, which turn the experts-contiguous rows into 4 consecutive rows of one expert per
+  //    lane), multiplied, and its slot refilled with chunk i + kExactRing. Rows past T repeat
+  //    the last token, router columns past E repeat column 0 (neither result is used).
+  {
+    const int nvalid = (int)min<int64_t>(TT, T - tb);
+    int arow = kXT * m + col;
+    if (arow >= nvalid) arow = nvalid - 1;
+    const char* asrc = (const char*)(a.x + (tb + arow) * D + 8 * g);
+    const char* bsrc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int cg = 16 * n + 8 * (lane & 1);
+      bsrc[n] = (const char*)(a.w + (int64_t)(lane >> 1) * E + (cg < E ? cg : 0));
+    }
+    const int64_t brow_bytes = 32 * (int64_t)E * 2;  // one chunk of router rows
+    constexpr uint32_t kSlot = 1024u * (1 + NT);
+    const uint32_t ring = lds_u32addr(smem) + (uint32_t)w * kExactRing * kSlot;
+    const int nc = kp < nch ? (nch - kp + KP - 1) / KP : 0;
+    f64x4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int i = 0; i < kExactRing && i < nc; ++i)
+      exact_issue<NT>(asrc, bsrc, kp + (int64_t)i * KP, brow_bytes, ring + i * kSlot);
+    // the lane's transposed-read offset in a router tile: rows 8 g + (lane % 16) / 4, expert
+    // columns 4 (lane % 4) .. + 3
+    const uint32_t toff = (uint32_t)((8 * g + ((lane & 15) >> 2)) * 32 + 8 * (lane & 3));
+    for (int i = 0; i < nc; ++i) {
+      exact_wait<NT>(min(kExactRing - 1, nc - 1 - i));
+      const uint32_t slot = ring + (uint32_t)(i % kExactRing) * kSlot;
+      const u32x4 av = lds_read16(slot + 16u * (uint32_t)lane);
+      v4i16_t bl[NT], bh[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const uint32_t t0 = slot + 1024u * (1 + n) + toff;
+        bl[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)t0);
+        bh[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)(t0 + 128u));
+      }
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double x64 = (j & 1) ? bf16_hi_f64(aw[j >> 1]) : bf16_lo_f64(aw[j >> 1]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const short bs = j < 4 ? bl[n][j] : bh[n][j - 4];
+          const double w64 = bf16_lo_f64((uint32_t)(uint16_t)bs);
+          acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(x64, w64, acc[n], 0, 0, 0);
+        }
+      }
+      if (i + kExactRing < nc)
+        exact_issue<NT>(asrc, bsrc, kp + (int64_t)(i + kExactRing) * KP, brow_bytes, slot);
+    }
+    __syncthreads();  // every ring is drained: the partials may overwrite them
+    // result layout of the float64 MFMA: lane l holds column l % 16 and rows l / 16 + 4 r
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s_part[((w * NT + n) * 16 + g + 4 * r) * 16 + col] = acc[n][r];
+  }
+  __syncthreads();
+
+  // 2. tokens, four at a time per wave (one per row of 16 lanes; lane i of a row holds experts
+  //    i + 16 n): logits (K-parts added in order, then the bias), top-k by descending logit
+  //    with ties to the lower index, the row softmax, gates; choice j sits in lane j % 16 of
+  //    the row, slot j / 16
+  const int i = col, r = g;
+  double psum[NT];
+  int cnt[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    psum[n] = 0.0;
+    cnt[n] = 0;
+  }
+  for (int q = w; q < TT / 4; q += Wv) {
+    const int tt = 4 * q + r;
+    const int mm = tt / kXT, trow = tt % kXT;
+    const int64_t t = tb + tt;
+    const bool valid = t < T;
+    double lg[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int e = 16 * n + i;
+      double v = 0.0;
+      if (e < E) {
+        for (int p = 0; p < KP; ++p)
+          v += s_part[(((mm * KP + p) * NT + n) * 16 + trow) * 16 + i];
+        if (a.bias) v += (double)a.bias[e];
+      }
+      lg[n] = v;
+    }
+    bool sel[NT];
+    double my_v[NT];
+    int my_e[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      sel[n] = false;
+      my_v[n] = 0.0;
+      my_e[n] = 0;
+    }
+    double v0 = 0.0;
+    for (int j = 0; j < k; ++j) {
+      double bv = -DBL_MAX;
+      int be = INT_MAX;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int e = 16 * n + i;
+        if (e < E && !sel[n] && (lg[n] > bv || (lg[n] == bv && e < be))) {
+          bv = lg[n];
+          be = e;
+        }
+      }
+      row_argmax16(bv, be);
+      if (j == 0) v0 = bv;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        if (be == 16 * n + i) sel[n] = true;
+        if (j == 16 * n + i) {
+          my_v[n] = bv;
+          my_e[n] = be;
+        }
+      }
+    }
+    // probabilities, shifted by the largest logit (the first choice)
+    double prob[NT];
+    double ps = 0.0;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      prob[n] = (16 * n + i < E) ? exp(lg[n] - v0) : 0.0;
+      ps += prob[n];
+    }
+    ps = row_sum16(ps);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) prob[n] /= ps;
+    double gate[NT];
+    if (a.renorm) {
+      double gs = 0.0;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        gate[n] = (16 * n + i < k) ? exp(my_v[n] - v0) : 0.0;
+        gs += gate[n];
+      }
+      gs = row_sum16(gs);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) gate[n] /= gs;
+    } else {
+      // the chosen expert's probability, from the lane of this row that holds it
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int src = (lane & ~15) | (my_e[n] & 15);
+        double pv = 0.0;
+#pragma unroll
+        for (int n2 = 0; n2 < NT; ++n2) {
+          const double c = __shfl(prob[n2], src);
+          if ((my_e[n] >> 4) == n2) pv = c;
+        }
+        gate[n] = pv;
+      }
+    }
+    if (valid) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int j = 16 * n + i;
+        if (j < k) {
+          a.idx[t * k + j] = my_e[n];
+          a.gates[t * k + j] = (float)gate[n];
+        }
+        if (a.logits_out && j < E) a.logits_out[t * E + j] = (float)lg[n];
+        psum[n] += prob[n];
+        cnt[n] += sel[n] ? 1 : 0;
+      }
+    }
+  }
+
+  // 3. the block's probability sums and counts (the wave's four rows by two exchanges, then
+  //    the waves in order), as one 64-bit integer per expert in the block's own slot (no
+  //    atomics, nothing to clear beforehand)
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    psum[n] += __shfl_xor(psum[n], 16);
+    psum[n] += __shfl_xor(psum[n], 32);
+    cnt[n] += __shfl_xor(cnt[n], 16);
+    cnt[n] += __shfl_xor(cnt[n], 32);
+  }
+  __syncthreads();  // the partial logits are no longer read
+  double* s_ps = s_part;                        // [Wv][E]
+  int32_t* s_cn = (int32_t*)(s_part + Wv * E);  // [Wv][E]
+  if (r == 0) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int e = 16 * n + i;
+      if (e < E) {
+        s_ps[w * E + e] = psum[n];
+        s_cn[w * E + e] = cnt[n];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += Wv * kWave) {
+    double ps = 0.0;
+    int c = 0;
+    for (int q = 0; q < Wv; ++q) {
+      ps += s_ps[q * E + e];
+      c += s_cn[q * E + e];
+    }
+    a.bslot[(int64_t)blockIdx.x * E + e] =
+        ((unsigned long long)c << kCountShift) + (unsigned long long)llrint(ps * kPScale);
+  }
+}
+
 // ---- place ----------------------------------------------------------------------------------
 
 struct PlaceArgs {
   int64_t T, capacity;
   int E, k, nG;
+  int spg;                          // slots per group: slot s belongs to group s / spg
+  int64_t nS;                       // slots
   const int32_t* idx;
-  const unsigned long long* gslot;  // (nG, E), from the routing kernel
-  const int32_t* nflag;
+  const unsigned long long* gslot;  // (nS, E), from the routing kernel
+  const int32_t* nflag;             // nullable: no token was recomputed
   float* aux;
   int32_t* counts_out;   // nullable
   int32_t* uncertified;  // nullable
@@ -551,7 +874,8 @@ struct PlaceArgs {
 };
 
 // One block per group of 256 tokens, one token per thread.
-//  1. From the group slots: each expert's total count (all groups) and rank base (the groups
+//  1. From the slots (each holds a count and a probability sum of part of a group, or of a
+//     whole group): each expert's total count (all groups) and rank base (the groups
 //     before this one), its kept rows min(count, capacity) and the row offsets; block 0 also
 //     writes the counts, the uncertified count and aux = E sum_e (count_e / (T k)) (P_e / T).
 //     Every sum is over integers or in a fixed order, so the result does not depend on the
@@ -575,6 +899,21 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
   if (g == 0 && a.zero)
     for (int i = tid; i < a.nzero; i += kGroup) a.zero[i] = 0;
   for (int i = tid; i < kW * kMaxExperts; i += kGroup) (&s_mask[0][0])[i] = 0ull;
+  // this thread's token's choices, loaded now so that their latency overlaps the slots' (up to
+  // 8 of them in registers; more are read again where they are used)
+  constexpr int kPre = 8;
+  const int64_t t = (int64_t)g * kGroup + tid;
+  const bool valid = t < a.T;
+  int pre[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) pre[j] = (valid && j < k) ? a.idx[t * k + j] : 0;
+  auto choice = [&](int j) -> int {
+    int e = 0;
+#pragma unroll
+    for (int q = 0; q < kPre; ++q)
+      if (q == j) e = pre[q];
+    return j < kPre ? e : a.idx[t * k + j];
+  };
   // 1. Q threads per expert, each over the groups q, q + Q, ...
   const int Q = max(1, kGroup / E);
   {
@@ -582,20 +921,21 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
     unsigned long long ps = 0;
     if (tid < Q * E) {
       const int e = tid % E, q = tid / E;
-      constexpr int kC = 16;  // loads in flight
-      for (int g0 = q; g0 < a.nG; g0 += kC * Q) {
+      constexpr int kC = 32;  // loads in flight
+      const int64_t gend = (int64_t)g * a.spg;  // slots of the groups before this one
+      for (int64_t g0 = q; g0 < a.nS; g0 += kC * Q) {
         unsigned long long v[kC];
 #pragma unroll
         for (int u = 0; u < kC; ++u) {
-          const int gg = g0 + u * Q;
-          v[u] = gg < a.nG ? a.gslot[(int64_t)gg * E + e] : 0ull;
+          const int64_t gg = g0 + (int64_t)u * Q;
+          v[u] = gg < a.nS ? a.gslot[gg * E + e] : 0ull;
         }
 #pragma unroll
         for (int u = 0; u < kC; ++u) {
-          const int gg = g0 + u * Q;
+          const int64_t gg = g0 + (int64_t)u * Q;
           const int c = (int)(v[u] >> kCountShift);
           tot += c;
-          if (gg < g) gb += c;
+          if (gg < gend) gb += c;
           ps += v[u] & ((1ull << kCountShift) - 1ull);
         }
       }
@@ -641,17 +981,15 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
     }
     if (tid == 0) {
       *a.aux = (float)((double)E * s_term[0]);
-      if (a.uncertified) *a.uncertified = *a.nflag;
+      if (a.uncertified) *a.uncertified = a.nflag ? *a.nflag : 0;
     }
     if (a.offsets)
       for (int e = tid; e <= E; e += kGroup) a.offsets[e] = s_off[e];
   }
   if (!a.perm) return;
   // 2. ranks within the group and placement
-  const int64_t t = (int64_t)g * kGroup + tid;
-  const bool valid = t < a.T;
   if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&s_mask[wv][a.idx[t * k + j]], 1ull << lane);
+    for (int j = 0; j < k; ++j) atomicOr(&s_mask[wv][choice(j)], 1ull << lane);
   __syncthreads();
   for (int e = tid; e < E; e += kGroup) {
     int run = s_gb[e];
@@ -666,7 +1004,7 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
   const unsigned long long lower = (1ull << lane) - 1ull;
   for (int j = 0; j < k; ++j) {
     const int64_t sl = t * k + j;
-    const int e = a.idx[sl];
+    const int e = choice(j);
     const int rank = s_base[wv][e] + __popcll(s_mask[wv][e] & lower);
     int row = -1;
     if (a.capacity < 0 || rank < a.capacity) {
@@ -740,6 +1078,64 @@ FusedLayout fused_layout(const Problem& p) {
   return L;
 }
 
+// The exact route: E <= 64 experts in NT tiles of 16; the block's M-tiles grow (fewer,
+// larger blocks) only past 512 blocks of one M-tile, which bounds the slots the place kernel
+// reads; a group of 256 tokens is always whole blocks.
+struct ExactShape {
+  int NT, Wv, MT, KP, TT;
+  int64_t nblk;
+};
+
+bool exact_route_shape(const Problem& p) {
+  return p.dtype == MOE_BF16 && p.E >= 1 && p.E <= kMaxExpertsExact && p.top_k <= p.E &&
+         p.D >= 32 && p.D % 32 == 0 && p.T > 0 && p.T < ((int64_t)1 << 23);
+}
+
+ExactShape exact_shape(const Problem& p) {
+  ExactShape f{};
+  f.NT = (p.E + 15) / 16;
+  f.Wv = f.NT == 1 ? 16 : f.NT == 2 ? 8 : 4;
+  f.MT = 1;
+  while (f.MT < 4 && f.MT < f.Wv && (p.T + kXT * f.MT - 1) / (kXT * f.MT) > 512) f.MT *= 2;
+  f.KP = f.Wv / f.MT;
+  f.TT = kXT * f.MT;
+  f.nblk = (p.T + f.TT - 1) / f.TT;
+  return f;
+}
+
+// Dynamic LDS of the exact route: the larger of the waves' chunk rings and the partial logits.
+template <int NT>
+size_t exact_lds_bytes() {
+  const size_t ring = (size_t)exact_waves<NT>() * kExactRing * 1024 * (1 + NT);
+  const size_t part = (size_t)exact_waves<NT>() * NT * 256 * 8;
+  return ring > part ? ring : part;
+}
+
+template <int NT>
+hipError_t launch_exact_inst(const ExactShape& f, const ExactArgs& a, hipStream_t s) {
+  const size_t lds = exact_lds_bytes<NT>();
+  // dynamic LDS past 64 KB needs the kernel's limit raised to it (once per device)
+  static bool raised[64] = {};
+  int dev = 0;
+  if (lds > 64 * 1024) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!raised[dev]) {
+      const hipError_t e = hipFuncSetAttribute((const void*)route_exact_kernel<NT>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+      if (e != hipSuccess) return e;
+      raised[dev] = true;
+    }
+  }
+  hipLaunchKernelGGL(route_exact_kernel<NT>, dim3((unsigned)f.nblk),
+                     dim3((unsigned)(exact_waves<NT>() * kWave)), lds, s, a);
+  return hipGetLastError();
+}
+
+size_t exact_ws_bytes(const Problem& p) {
+  return (((size_t)exact_shape(p).nblk * p.E * 8) + 255) & ~size_t(255);
+}
+
 template <int PPW, int EPL>
 hipError_t launch_fused_inst(const FusedShape& f, const FusedArgs& a, unsigned nblk,
                              hipStream_t s) {
@@ -759,7 +1155,9 @@ hipError_t launch_fused_inst(const FusedShape& f, const FusedArgs& a, unsigned n
 }  // namespace
 
 bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance) {
-  if (p.dtype != MOE_BF16 || o.w_noise || !o.renorm || importance) return false;
+  if (p.dtype != MOE_BF16 || o.w_noise || importance) return false;
+  if (exact_route_shape(p)) return true;  // either gate rule
+  if (!o.renorm) return false;
   if (p.T <= 0 || p.D % 128 != 0 || p.D > 8192 || p.E > kMaxExperts) return false;
   if (p.T >= (int64_t)1 << 23) return false;  // the 2^-40 probability sums stay below 2^63
   // with many choices per token the exact chosen logits (k D float64 products a token, on the
@@ -768,11 +1166,37 @@ bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance) 
   return fused_shape(p).lds + kStaticLds <= kMaxLds;
 }
 
-size_t fused_route_ws_bytes(const Problem& p) { return fused_layout(p).bytes; }
+size_t fused_route_ws_bytes(const Problem& p) {
+  return exact_route_shape(p) ? exact_ws_bytes(p) : fused_layout(p).bytes;
+}
 
 hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
-                              const float* bias, int32_t* idx, float* gates, float* logits_out,
-                              void* fws, hipStream_t s) {
+                              const float* bias, bool renorm, int32_t* idx, float* gates,
+                              float* logits_out, void* fws, hipStream_t s) {
+  if (exact_route_shape(p)) {
+    const ExactShape f = exact_shape(p);
+    ExactArgs a{};
+    a.T = p.T;
+    a.D = p.D;
+    a.E = p.E;
+    a.k = p.top_k;
+    a.MT = f.MT;
+    a.KP = f.KP;
+    a.renorm = renorm;
+    a.x = (const uint16_t*)x;
+    a.w = (const uint16_t*)w_router;
+    a.bias = bias;
+    a.idx = idx;
+    a.gates = gates;
+    a.logits_out = logits_out;
+    a.bslot = (unsigned long long*)fws;
+    switch (f.NT) {
+      case 1: return launch_exact_inst<1>(f, a, s);
+      case 2: return launch_exact_inst<2>(f, a, s);
+      case 3: return launch_exact_inst<3>(f, a, s);
+      default: return launch_exact_inst<4>(f, a, s);
+    }
+  }
   const FusedLayout L = fused_layout(p);
   const FusedShape f = fused_shape(p);
   char* b = (char*)fws;
@@ -827,8 +1251,18 @@ hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* 
   a.k = p.top_k;
   a.nG = (int)L.nG;
   a.idx = idx;
-  a.gslot = (const unsigned long long*)((const char*)fws + L.gslot);
-  a.nflag = (const int32_t*)((const char*)fws + L.nflag);
+  if (exact_route_shape(p)) {  // one slot per routing block, nothing recomputed
+    const ExactShape f = exact_shape(p);
+    a.spg = kGroup / f.TT;
+    a.nS = f.nblk;
+    a.gslot = (const unsigned long long*)fws;
+    a.nflag = nullptr;
+  } else {
+    a.spg = 1;
+    a.nS = L.nG;
+    a.gslot = (const unsigned long long*)((const char*)fws + L.gslot);
+    a.nflag = (const int32_t*)((const char*)fws + L.nflag);
+  }
   a.aux = aux;
   a.counts_out = counts_out;
   a.uncertified = uncertified;

@@ -39,14 +39,22 @@ MID_CASES = {
     "swiglu_long_k_split2": spec("mixtral_swiglu_bf16", T=300, D=256, DH=4096, E=4, top_k=2),
     "relu_long_k_split4": spec("switch_top1_cap_bf16", T=200, D=128, DH=8192, E=2,
                                capacity_factor=0.0),
-    # the fused bf16 routing kernel's edges: 256 experts (16 expert tiles, 4 per lane in the
-    # select), 128 experts with D = 640 (a partial 1 KB segment per row), k = E, and D = 8192
-    # (4-token tiles)
+    # the certified bf16 routing paths' edges: 256 experts (16 expert tiles, 4 per lane in the
+    # select), 128 experts with D = 640 (a partial 1 KB segment per row), and the single-pass
+    # path at 96 and 200 experts (top 2 and top 1, with D = 8192: 4-token tiles)
     "fused_e256_k8_cap": spec("switch_top1_cap_bf16", T=700, D=256, DH=128, E=256, top_k=8,
                               capacity_factor=1.5),
     "fused_e128_d640": spec("fine_grained_zipf_bf16", T=900, D=640, DH=128, E=128, top_k=3),
-    "fused_k_equals_e": spec("mixtral_swiglu_bf16", T=333, D=128, DH=128, E=8, top_k=8),
-    "fused_d8192": spec("mixtral_swiglu_bf16", T=130, D=8192, DH=128, E=8),
+    "fused_e96_k2": spec("mixtral_swiglu_bf16", T=777, D=512, DH=128, E=96, top_k=2),
+    "fused_e200_k1_d8192": spec("switch_top1_cap_bf16", T=130, D=8192, DH=128, E=200,
+                                capacity_factor=0.0),
+    # the exact route's edges: k = E, D = 8192, D = 32 (one chunk), E = 17 and 48 (partial
+    # expert tiles), E = 64 with T past 8192 tokens (two M-tiles a block) and a ragged block
+    "exact_k_equals_e": spec("mixtral_swiglu_bf16", T=333, D=128, DH=128, E=8, top_k=8),
+    "exact_d8192": spec("mixtral_swiglu_bf16", T=130, D=8192, DH=128, E=8),
+    "exact_d32_e17": spec("fine_grained_zipf_bf16", T=257, D=32, DH=64, E=17, top_k=3),
+    "exact_e48_k5": spec("fine_grained_zipf_bf16", T=515, D=96, DH=64, E=48, top_k=5),
+    "exact_e64_two_mtiles": spec("switch_top1_cap_bf16", T=8205, D=64, DH=64, E=64),
 }
 
 
@@ -369,23 +377,33 @@ def _check_route(g, r):
     assert rel_err(g["aux_loss"][0], r["aux_loss"]) <= AUX_TOL
 
 
-def test_bf16_zero_router_ties_fall_back_to_float64():
-    """All logits tie at 0: nothing can be certified, every token is recomputed, and the
-    ties go to the lower expert index as in the oracle; aux_loss is 1."""
-    sp = spec("fine_grained_zipf_bf16", T=300, D=256, DH=64, bias="none")
+def _exact_route(sp) -> bool:
+    """bf16 layers with at most 64 experts route on exact float64 logits (the float64 matrix
+    cores), so no token is left uncertified; wider layers take the certified bf16 path."""
+    return sp.dtype == "bf16" and sp.E <= 64 and sp.D % 32 == 0
+
+
+@pytest.mark.parametrize("E", [64, 128])
+def test_bf16_zero_router_ties_go_to_the_lower_index(E):
+    """All logits tie at 0: the ties go to the lower expert index as in the oracle, and
+    aux_loss is 1. On the certified path nothing can be certified, so every token is
+    recomputed; on the exact path no token needs it."""
+    sp = spec("fine_grained_zipf_bf16", T=300, D=256, DH=64, E=E, bias="none")
     I = make_inputs(sp, seed=4, router_zero=True)
     g, r = _route(I, sp), run_oracle(I, tokens=[])
     _check_route(g, r)
-    assert g["uncertified"] == sp.T
+    assert g["uncertified"] == (0 if _exact_route(sp) else sp.T)
     assert (g["expert_indices"] == np.arange(sp.top_k)).all()
     assert abs(float(g["aux_loss"][0]) - 1.0) <= 1e-6
 
 
-def test_bf16_near_ties_are_decided_exactly():
+@pytest.mark.parametrize("E", [8, 96])
+def test_bf16_near_ties_are_decided_exactly(E):
     """Router columns 0 and 1 differ in one element by one bf16 ulp of its smallest entry,
     so the tokens that rank both of them near the top have gaps far below the float32
-    accumulation error; the fallback must decide them as the exact logits do."""
-    sp = spec("mixtral_swiglu_bf16", T=2000, D=1024, DH=64, E=8, top_k=2)
+    accumulation error; both paths must decide them as the exact logits do (the certified
+    path by sending them to its float64 fallback)."""
+    sp = spec("mixtral_swiglu_bf16", T=2000, D=1024, DH=64, E=E, top_k=2)
     I = make_inputs(sp, seed=6)
     w = I.w_router.copy()
     w[:, 1] = w[:, 0]
@@ -396,7 +414,11 @@ def test_bf16_near_ties_are_decided_exactly():
     g, r = _route(I, sp), run_oracle(I, tokens=[])
     _check_route(g, r)
     both = (np.sort(r["expert_indices"], axis=1)[:, :2] == [0, 1]).all(axis=1)
-    assert both.sum() > 10 and g["uncertified"] >= both.sum()
+    assert both.sum() > 10
+    if _exact_route(sp):
+        assert g["uncertified"] == 0
+    else:
+        assert g["uncertified"] >= both.sum()
 
 
 @pytest.mark.parametrize("name", FULL)

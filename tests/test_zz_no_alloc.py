@@ -63,12 +63,17 @@ def _same(a, b, what):
 
 # pairs (first call, second call on a smaller problem)
 PAIRS = {
-    # 64 experts: uncertified tokens go through the fallback kernel's list in the scratch
+    # 64 and 8 experts: exact float64 logits, one slot per routing block in the scratch
     "bf16_zipf_e64": (spec("fine_grained_zipf_bf16", T=3000, D=512, DH=64),
                       spec("fine_grained_zipf_bf16", T=700, D=512, DH=64)),
-    # 8 experts, long K split over blocks (partial logits in the scratch)
     "bf16_mixtral_e8": (spec("mixtral_swiglu_bf16", T=1500, D=4096, DH=64),
                         spec("mixtral_swiglu_bf16", T=129, D=4096, DH=64)),
+    # 128 experts, top 6: the certified path, its partial logits and fallback list in the scratch
+    "bf16_e128_k6": (spec("fine_grained_zipf_bf16", T=2000, D=512, DH=64, E=128),
+                     spec("fine_grained_zipf_bf16", T=333, D=512, DH=64, E=128)),
+    # 96 experts, top 2: the certified single-pass path, its group slots in the scratch
+    "bf16_e96_k2": (spec("mixtral_swiglu_bf16", T=1500, D=1024, DH=64, E=96),
+                    spec("mixtral_swiglu_bf16", T=200, D=1024, DH=64, E=96)),
     "f32_relu": (spec("small_relu_f32", T=500, D=96, DH=32, E=12, top_k=3),
                  spec("small_relu_f32", T=37, D=96, DH=32, E=12, top_k=3)),
 }
