@@ -43,8 +43,12 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("2e0c7c0e1ccb066c47bd33c989376a2dcc779772d9b549c6f3b9675e17ddf4c2",
-                            3366065.0089285714, 236435.5982142857),
+    "mixtral_swiglu_bf16": ("9212fbe5cd20ed4fee32ad0c6f01472deeb2f4a52a2e540d9d3050f3741b14e6",
+                            3094270.6071428573, 235070.01785714287),
+    "switch_top1_cap_bf16": ("9212fbe5cd20ed4fee32ad0c6f01472deeb2f4a52a2e540d9d3050f3741b14e6",
+                             223820.7232142857, 27077.76785714286),
+    "fine_grained_zipf_bf16": ("9212fbe5cd20ed4fee32ad0c6f01472deeb2f4a52a2e540d9d3050f3741b14e6",
+                               1015708.4553571428, 144798.1517857143),
 }
 
 
@@ -312,14 +316,26 @@ def main() -> int:
     peak_tf = BF16_PEAK_TFLOPS if sp.dtype == "bf16" else FP32_PEAK_TFLOPS
     used_tokens = int(np.count_nonzero((outs["slot_row"].view(T, k) >= 0).any(dim=1).cpu()))
 
-    # algorithmic work per launch
+    # algorithmic work per launch: flops, and the bytes a launch must move at least (the
+    # weights of the experts that have rows, the rows read, the rows written)
+    kept = np.diff(outs["expert_offsets"].cpu().numpy().astype(np.int64))
+    if args.padded:
+        kept = np.full(E, B.capacity(p), dtype=np.int64)
+    active = int(np.count_nonzero(kept))
     if sp.kind == "linear":
         up_flops, down_flops = 2 * D * Do * R, 0
         up_w = E * D * Do * es
+        up_bytes = active * D * Do * es + rows * (D + Do) * es
+        down_bytes = 0
     else:
         up_mult = 4 if sp.kind == "swiglu" else 2
         up_flops, down_flops = up_mult * D * DH * R, 2 * DH * Do * R
-        up_w = (2 if sp.kind == "swiglu" else 1) * E * D * DH * es
+        wmats = 2 if sp.kind == "swiglu" else 1
+        up_w = wmats * E * D * DH * es
+        up_bytes = wmats * active * D * DH * es + rows * (D + DH) * es
+        down_bytes = active * DH * Do * es + rows * (DH + Do) * es
+    # a GEMM whose flops per algorithmic byte fall below the machine balance is bound by HBM
+    balance = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     route_b = A.route_bytes(T, D, E, k, es)
     if N is not None:
         route_b += A.route_noise_bytes(T, D, E, es)
@@ -332,6 +348,7 @@ def main() -> int:
         return b / (ms_ * 1e-3) / 1e9 if ms_ > 0 else 0.0
 
     up_tf = tf(up_flops, stage_ms["expert_up"])
+    up_hbm = up_flops < balance * up_bytes
     stages = {
         "route": {"us": stage_ms["route"] * 1e3, "GB/s": gbs(route_b, stage_ms["route"]),
                   "hbm_frac": gbs(route_b, stage_ms["route"]) / HBM_PEAK_GBS,
@@ -341,11 +358,19 @@ def main() -> int:
             "GB/s": gbs(A.padded_permute_bytes(used_tokens, rows, D, es), stage_ms["dispatch"]),
             "algorithmic_bytes": A.padded_permute_bytes(used_tokens, rows, D, es)},
         "expert_up": {"us": stage_ms["expert_up"] * 1e3, "TFLOP/s": up_tf,
-                      "mfma_frac": up_tf / peak_tf, "algorithmic_flops": up_flops},
+                      "mfma_frac": up_tf / peak_tf, "algorithmic_flops": up_flops,
+                      "GB/s": gbs(up_bytes, stage_ms["expert_up"]),
+                      "hbm_frac": gbs(up_bytes, stage_ms["expert_up"]) / HBM_PEAK_GBS,
+                      "algorithmic_bytes": up_bytes,
+                      "bound": "hbm" if up_hbm else "mfma"},
         "expert_down": {"us": stage_ms["expert_down"] * 1e3,
                         "TFLOP/s": tf(down_flops, stage_ms["expert_down"]),
                         "mfma_frac": tf(down_flops, stage_ms["expert_down"]) / peak_tf,
-                        "algorithmic_flops": down_flops},
+                        "algorithmic_flops": down_flops,
+                        "GB/s": gbs(down_bytes, stage_ms["expert_down"]),
+                        "hbm_frac": gbs(down_bytes, stage_ms["expert_down"]) / HBM_PEAK_GBS,
+                        "algorithmic_bytes": down_bytes,
+                        "bound": "hbm" if down_flops < balance * down_bytes else "mfma"},
         "combine": {"us": stage_ms["combine"] * 1e3, "GB/s": gbs(combine_b, stage_ms["combine"]),
                     "hbm_frac": gbs(combine_b, stage_ms["combine"]) / HBM_PEAK_GBS,
                     "algorithmic_bytes": combine_b},
@@ -372,9 +397,14 @@ def main() -> int:
                    "expert": sp.kind, "capacity_factor": sp.capacity_factor,
                    "kept_slots": R, "dropped_slots": T * k - R, "used_tokens": used_tokens,
                    "expert_rows": rows},
-        "roofline": {"kernel": "expert up-projection grouped GEMM (stage expert_up)",
-                     "bound": "mfma", "achieved": up_tf, "peak": peak_tf, "unit": "TFLOP/s",
-                     "frac": up_tf / peak_tf,
+        "roofline": ({"kernel": "expert up-projection grouped GEMM (stage expert_up)",
+                      "bound": "hbm", "achieved": gbs(up_bytes, stage_ms["expert_up"]),
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": gbs(up_bytes, stage_ms["expert_up"]) / HBM_PEAK_GBS,
+                      "algorithmic_bytes_per_launch": up_bytes} if up_hbm else
+                     {"kernel": "expert up-projection grouped GEMM (stage expert_up)",
+                      "bound": "mfma", "achieved": up_tf, "peak": peak_tf, "unit": "TFLOP/s",
+                      "frac": up_tf / peak_tf}) | {
                      "traffic": None if options else measured_traffic(sp.name),
                      "algorithmic_flops_per_launch": up_flops,
                      "launch_us": stage_ms["expert_up"] * 1e3,

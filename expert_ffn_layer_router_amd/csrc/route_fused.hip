@@ -1086,8 +1086,11 @@ struct ExactShape {
   int64_t nblk;
 };
 
+// (E % 8 == 0: a router row is whole 16-byte granules, so every granule a DMA reads lies in
+// its row)
 bool exact_route_shape(const Problem& p) {
-  return p.dtype == MOE_BF16 && p.E >= 1 && p.E <= kMaxExpertsExact && p.top_k <= p.E &&
+  return p.dtype == MOE_BF16 && p.E >= 8 && p.E <= kMaxExpertsExact && p.E % 8 == 0 &&
+         p.top_k <= p.E &&
          p.D >= 32 && p.D % 32 == 0 && p.T > 0 && p.T < ((int64_t)1 << 23);
 }
 

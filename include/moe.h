@@ -110,7 +110,10 @@ size_t moe_workspace_size(const moe_problem* p);
  *   summing to 1; aux_loss (1) float32; expert_counts (E) int32 routed slots per expert before
  *   capacity, or NULL; logits_out (T, E) float32 copy of the router logits, or NULL;
  *   uncertified (1) int32, or NULL: the number of tokens whose top-k order the fast bf16
- *   logits could not certify and that were therefore recomputed in float64 (0 for MOE_F32).
+ *   logits could not certify and that were therefore recomputed in float64. 0 wherever every
+ *   logit is already exact to float64 rounding: MOE_F32, and MOE_BF16 with 8 <= E <= 64,
+ *   E % 8 == 0, D % 32 == 0 and no router noise (float64 matrix-core sums of the exact
+ *   products of the bf16 inputs).
  *   With T = 0, aux_loss is 0 and expert_counts are zeros. */
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* router_bias, int32_t* expert_indices, float* gates,
@@ -217,8 +220,9 @@ moe_status moe_forward_timed(const moe_problem* p, const void* x, const void* w_
  *     probabilities, top-k, gates and both losses use them. Both NULL or both set.
  *   no_renormalise: nonzero = the gates are the chosen experts' probabilities over all E
  *     experts (router(..., renormalise=False): stage (5) skipped), so a gate row sums to at
- *     most 1. Every token's logits are then recomputed exactly in float64 (these gates need
- *     all E of them to the gates' accuracy), and `uncertified` counts every token.
+ *     most 1. These gates need all E logits to the gates' accuracy: where the logits are not
+ *     exact already (see moe_route), every token's are recomputed in float64 and
+ *     `uncertified` counts every token.
  *   padded: nonzero = expert batches padded to the capacity ("Switch: top-1, one loss, and a
  *     rate limit": experts run as fixed-size batches); needs capacity_factor > 0. Expert e's
  *     kept slots take rows e * capacity + rank (rank in token order) and the rest of its batch

@@ -48,11 +48,13 @@ MID_CASES = {
     "fused_e96_k2": spec("mixtral_swiglu_bf16", T=777, D=512, DH=128, E=96, top_k=2),
     "fused_e200_k1_d8192": spec("switch_top1_cap_bf16", T=130, D=8192, DH=128, E=200,
                                 capacity_factor=0.0),
-    # the exact route's edges: k = E, D = 8192, D = 32 (one chunk), E = 17 and 48 (partial
+    # E not a multiple of 8 takes the certified path
+    "certified_e17_k3": spec("fine_grained_zipf_bf16", T=257, D=64, DH=64, E=17, top_k=3),
+    # the exact route's edges: k = E, D = 8192, D = 32 (one chunk), E = 24 and 48 (partial
     # expert tiles), E = 64 with T past 8192 tokens (two M-tiles a block) and a ragged block
     "exact_k_equals_e": spec("mixtral_swiglu_bf16", T=333, D=128, DH=128, E=8, top_k=8),
     "exact_d8192": spec("mixtral_swiglu_bf16", T=130, D=8192, DH=128, E=8),
-    "exact_d32_e17": spec("fine_grained_zipf_bf16", T=257, D=32, DH=64, E=17, top_k=3),
+    "exact_d32_e24": spec("fine_grained_zipf_bf16", T=257, D=32, DH=64, E=24, top_k=3),
     "exact_e48_k5": spec("fine_grained_zipf_bf16", T=515, D=96, DH=64, E=48, top_k=5),
     "exact_e64_two_mtiles": spec("switch_top1_cap_bf16", T=8205, D=64, DH=64, E=64),
 }
@@ -378,9 +380,10 @@ def _check_route(g, r):
 
 
 def _exact_route(sp) -> bool:
-    """bf16 layers with at most 64 experts route on exact float64 logits (the float64 matrix
-    cores), so no token is left uncertified; wider layers take the certified bf16 path."""
-    return sp.dtype == "bf16" and sp.E <= 64 and sp.D % 32 == 0
+    """bf16 layers with 8 to 64 experts (a multiple of 8) route on exact float64 logits (the
+    float64 matrix cores), so no token is left uncertified; the others take the certified bf16
+    path."""
+    return sp.dtype == "bf16" and 8 <= sp.E <= 64 and sp.E % 8 == 0 and sp.D % 32 == 0
 
 
 @pytest.mark.parametrize("E", [64, 128])
