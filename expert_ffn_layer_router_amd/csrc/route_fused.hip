@@ -594,27 +594,58 @@ __device__ __forceinline__ void row_argmax16(double& bv, int& be) {
 // The chunk ring of a wave: slot = the chunk's A tile (16 token rows x 32 of D, 1 KB, lane l's
 // MFMA operand at byte 16 l) then NT router tiles (32 rows of D x 16 experts, 32 bytes a row).
 // Both arrive by global_load_lds_dwordx4, which no register waits for: the waits are explicit.
-constexpr int kExactRing = 3;  // chunks in flight per wave
-
-template <int NT>
-__device__ __forceinline__ void exact_issue(const char* asrc, const char* const (&bsrc)[NT],
-                                            int64_t c, int64_t brow_bytes, uint32_t slot) {
-  lds_dma16(asrc + c * 64, slot);
-#pragma unroll
-  for (int n = 0; n < NT; ++n) lds_dma16(bsrc[n] + c * brow_bytes, slot + 1024u * (1 + n));
+// A chunk is 64 of D: two halves h of 32. Its A tile (16 token rows x 128 bytes, 2 KB) arrives
+// by two DMAs in which lanes 8 a .. 8 a + 7 fetch one row's 128 contiguous bytes (whole cache
+// lines); 16-byte segment s of row r lands in slot 8 r + (s ^ (r % 8)), so the 16 rows an A
+// operand read touches fall in distinct banks. The router tiles follow: with 8 experts one DMA
+// of the chunk's 64 rows x 16 bytes, else per expert tile n and half h 32 rows x 16 experts
+// (32 bytes a row, 1 KB).
+template <int NT, bool E8>
+constexpr int exact_ring() {  // chunks in flight per wave
+  return E8 ? 3 : 2;
+}
+template <int NT, bool E8>
+constexpr uint32_t exact_slot() {
+  return 2048u + (E8 ? 1024u : 2048u * NT);
+}
+template <int NT, bool E8>
+constexpr int exact_dmas() {  // loads a chunk takes
+  return 2 + (E8 ? 1 : 2 * NT);
 }
 
-// s_waitcnt vmcnt(after * (1 + NT)): the loads of the `after` chunks issued after this one may
-// stay in flight (vector memory operations complete in issue order)
-template <int NT>
+template <int NT, bool E8>
+__device__ __forceinline__ void exact_issue(const char* const (&asrc)[2],
+                                            const char* const (&bsrc)[NT], int64_t c,
+                                            int64_t brow_bytes, uint32_t slot) {
+  lds_dma16(asrc[0] + c * 128, slot);
+  lds_dma16(asrc[1] + c * 128, slot + 1024u);
+  if (E8) {
+    lds_dma16(bsrc[0] + c * brow_bytes, slot + 2048u);
+  } else {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        lds_dma16(bsrc[n] + c * brow_bytes + h * (brow_bytes / 2), slot + 2048u + 1024u * (2 * n + h));
+  }
+}
+
+// s_waitcnt vmcnt(after * L): the loads of the `after` chunks issued after this one may stay
+// in flight (vector memory operations complete in issue order); expcnt and lgkmcnt at their
+// maxima, so not waited for
+template <int L, int A>
+__device__ __forceinline__ void exact_wait_n() {
+  constexpr int n = L * A;
+  static_assert(n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0xF70);
+}
+template <int L, int R>
 __device__ __forceinline__ void exact_wait(int after) {
-  constexpr int L = 1 + NT;
-  if (after >= 2)
-    __builtin_amdgcn_s_waitcnt(((2 * L) & 15) | (((2 * L) >> 4) << 14) | 0xF70);
-  else if (after == 1)
-    __builtin_amdgcn_s_waitcnt((L & 15) | ((L >> 4) << 14) | 0xF70);
-  else
-    __builtin_amdgcn_s_waitcnt(0xF70);  // (expcnt and lgkmcnt at their maxima: not waited for)
+  switch (after) {
+    case 0: exact_wait_n<L, 0>(); break;
+    case 1: exact_wait_n<L, 1>(); break;
+    default: if constexpr (R > 2) exact_wait_n<L, 2>(); break;
+  }
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -625,8 +656,12 @@ constexpr int exact_waves() {
   return NT == 1 ? 16 : NT == 2 ? 8 : 4;
 }
 
-template <int NT>
+// E8: exactly 8 experts. The products then run on v_mfma_f64_4x4x4f64 (four blocks of 4 tokens
+// x 4 experts x 4 of K, two a k-step for the two expert quads), which wastes no columns where
+// the 16 x 16 instruction would leave half of its 16 expert columns empty.
+template <int NT, bool E8 = false>
 __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(ExactArgs a) {
+  static_assert(!E8 || NT == 1, "8 experts are one expert tile");
   constexpr int Wv = exact_waves<NT>();
   // dynamic LDS: the waves' chunk rings, then (after the chunk loop) the partial logits of
   // every wave (Wv x NT tiles of 16 x 16, float64: 32 KB), then the probability sums and counts
@@ -639,69 +674,125 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
   const int TT = kXT * a.MT;
   const int64_t tb = (int64_t)blockIdx.x * TT;
   const int m = w / KP, kp = w % KP;
-  const int nch = (int)(D / 32);
+  const int nch = (int)(D / 64);
   const int col = lane & 15, g = lane >> 4;
+  // the bias of this lane's experts (col + 16 n), loaded now so its latency is hidden
+  float bias_n[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) bias_n[n] = (a.bias && 16 * n + col < E) ? a.bias[16 * n + col] : 0.f;
 
-  // 1. partial logits. Wave w's chunks c = kp + i KP go through its ring of kExactRing slots:
-  //    chunk i is waited for, its operands read (A by ds_read_b128; B by two transposed reads a
-  //    tile, which turn the experts-contiguous rows into 4 consecutive rows of one expert per
-  //    lane), multiplied, and its slot refilled with chunk i + kExactRing. Rows past T repeat
-  //    the last token, router columns past E repeat column 0 (neither result is used).
+  // 1. partial logits. Wave w's chunks c = kp + i KP (64 of D each) go through its ring of
+  //    slots: chunk i is waited for, its operands read (A by two ds_read_b128; B by single
+  //    bf16 reads with 8 experts, else by two transposed reads a tile and half, which turn the
+  //    expert-contiguous rows into 4 consecutive rows of one expert per lane), multiplied, and
+  //    its slot refilled with the chunk a ring length later. In half h, step j gives lane
+  //    group g the column d = 64 c + 32 h + 8 g + j. Rows past T repeat the last token, router
+  //    columns past E repeat column 0 (neither result is used).
   {
     const int nvalid = (int)min<int64_t>(TT, T - tb);
-    int arow = kXT * m + col;
-    if (arow >= nvalid) arow = nvalid - 1;
-    const char* asrc = (const char*)(a.x + (tb + arow) * D + 8 * g);
+    const char* asrc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 8 * q + (lane >> 3), sg = (lane & 7) ^ (r & 7);
+      int arow = kXT * m + r;
+      if (arow >= nvalid) arow = nvalid - 1;
+      asrc[q] = (const char*)(a.x + (tb + arow) * D + 8 * sg);
+    }
+    // the lane's A operand slots: row col, segment 4 h + g
+    uint32_t aoff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) aoff[h] = 16u * (uint32_t)(8 * col + ((4 * h + g) ^ (col & 7)));
     const char* bsrc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int cg = 16 * n + 8 * (lane & 1);
       bsrc[n] = (const char*)(a.w + (int64_t)(lane >> 1) * E + (cg < E ? cg : 0));
     }
-    const int64_t brow_bytes = 32 * (int64_t)E * 2;  // one chunk of router rows
-    constexpr uint32_t kSlot = 1024u * (1 + NT);
-    const uint32_t ring = lds_u32addr(smem) + (uint32_t)w * kExactRing * kSlot;
+    if (E8) bsrc[0] = (const char*)(a.w + (int64_t)lane * 8);  // row lane of the chunk's 64
+    const int64_t brow_bytes = 64 * (int64_t)E * 2;  // one chunk of router rows
+    constexpr int kR = exact_ring<NT, E8>();
+    constexpr uint32_t kSlot = exact_slot<NT, E8>();
+    constexpr int kL = exact_dmas<NT, E8>();
+    const uint32_t ring = lds_u32addr(smem) + (uint32_t)w * kR * kSlot;
     const int nc = kp < nch ? (nch - kp + KP - 1) / KP : 0;
+    // the wave's i-th chunk; each block starts at its own place in the row, so the blocks that
+    // run at once spread their reads over the whole address range (and so over all memory
+    // channels) instead of all reading the same column window of rows a fixed stride apart
+    const int rot = nc > 0 ? (int)(blockIdx.x % (unsigned)nc) : 0;
+    auto chunk = [&](int i) -> int64_t {
+      int j = i + rot;
+      if (j >= nc) j -= nc;
+      return kp + (int64_t)j * KP;
+    };
     f64x4 acc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f64x4{0.0, 0.0, 0.0, 0.0};
-    for (int i = 0; i < kExactRing && i < nc; ++i)
-      exact_issue<NT>(asrc, bsrc, kp + (int64_t)i * KP, brow_bytes, ring + i * kSlot);
+    double acc8[2] = {0.0, 0.0};  // E8: the two expert quads
+    for (int i = 0; i < kR && i < nc; ++i)
+      exact_issue<NT, E8>(asrc, bsrc, chunk(i), brow_bytes, ring + i * kSlot);
     // the lane's transposed-read offset in a router tile: rows 8 g + (lane % 16) / 4, expert
     // columns 4 (lane % 4) .. + 3
     const uint32_t toff = (uint32_t)((8 * g + ((lane & 15) >> 2)) * 32 + 8 * (lane & 3));
     for (int i = 0; i < nc; ++i) {
-      exact_wait<NT>(min(kExactRing - 1, nc - 1 - i));
-      const uint32_t slot = ring + (uint32_t)(i % kExactRing) * kSlot;
-      const u32x4 av = lds_read16(slot + 16u * (uint32_t)lane);
-      v4i16_t bl[NT], bh[NT];
+      exact_wait<kL, kR>(min(kR - 1, nc - 1 - i));
+      const uint32_t slot = ring + (uint32_t)(i % kR) * kSlot;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const uint32_t t0 = slot + 1024u * (1 + n) + toff;
-        bl[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)t0);
-        bh[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)(t0 + 128u));
-      }
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 av = lds_read16(slot + aoff[h]);
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+        if constexpr (E8) {
+          // B lane l: expert 4 q + l % 4 of quad q, one bf16 of router row 32 h + 8 g + j
+          typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+          const uint32_t b0 =
+              slot + 2048u + (uint32_t)(32 * h + 8 * g) * 16u + 2u * (uint32_t)(lane & 3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double x64 = (j & 1) ? bf16_hi_f64(aw[j >> 1]) : bf16_lo_f64(aw[j >> 1]);
+          for (int j = 0; j < 8; ++j) {
+            const double x64 = (j & 1) ? bf16_hi_f64(aw[j >> 1]) : bf16_lo_f64(aw[j >> 1]);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const short bs = j < 4 ? bl[n][j] : bh[n][j - 4];
-          const double w64 = bf16_lo_f64((uint32_t)(uint16_t)bs);
-          acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(x64, w64, acc[n], 0, 0, 0);
+            for (int q = 0; q < 2; ++q) {
+              const uint16_t wb = *(lds_u16*)(uintptr_t)(b0 + 16u * j + 8u * q);
+              acc8[q] =
+                  __builtin_amdgcn_mfma_f64_4x4x4f64(x64, bf16_lo_f64(wb), acc8[q], 0, 0, 0);
+            }
+          }
+        } else {
+          v4i16_t bl[NT], bh[NT];
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const uint32_t t0 = slot + 2048u + 1024u * (2 * n + h) + toff;
+            bl[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)t0);
+            bh[n] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(uintptr_t)(t0 + 128u));
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const double x64 = (j & 1) ? bf16_hi_f64(aw[j >> 1]) : bf16_lo_f64(aw[j >> 1]);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              const short bs = j < 4 ? bl[n][j] : bh[n][j - 4];
+              const double w64 = bf16_lo_f64((uint32_t)(uint16_t)bs);
+              acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(x64, w64, acc[n], 0, 0, 0);
+            }
+          }
         }
       }
-      if (i + kExactRing < nc)
-        exact_issue<NT>(asrc, bsrc, kp + (int64_t)(i + kExactRing) * KP, brow_bytes, slot);
+      if (i + kR < nc) exact_issue<NT, E8>(asrc, bsrc, chunk(i + kR), brow_bytes, slot);
     }
     __syncthreads();  // every ring is drained: the partials may overwrite them
-    // result layout of the float64 MFMA: lane l holds column l % 16 and rows l / 16 + 4 r
+    if constexpr (E8) {
+      // result layout of the 4 x 4 x 4 instruction: lane l holds token 4 ((l % 16) / 4) + l / 16,
+      // expert 4 q + l % 4 (the tile's other columns are never read)
+      const int tt = 4 * ((lane & 15) >> 2) + (lane >> 4);
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+      for (int q = 0; q < 2; ++q) s_part[(w * 16 + tt) * 16 + 4 * q + (lane & 3)] = acc8[q];
+    } else {
+      // result layout of the 16 x 16 x 4 instruction: lane l holds column l % 16 and rows
+      // l / 16 + 4 r
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s_part[((w * NT + n) * 16 + g + 4 * r) * 16 + col] = acc[n][r];
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_part[((w * NT + n) * 16 + g + 4 * r) * 16 + col] = acc[n][r];
+    }
   }
   __syncthreads();
 
@@ -730,7 +821,7 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
       if (e < E) {
         for (int p = 0; p < KP; ++p)
           v += s_part[(((mm * KP + p) * NT + n) * 16 + trow) * 16 + i];
-        if (a.bias) v += (double)a.bias[e];
+        if (a.bias) v += (double)bias_n[n];
       }
       lg[n] = v;
     }
@@ -1091,7 +1182,7 @@ struct ExactShape {
 bool exact_route_shape(const Problem& p) {
   return p.dtype == MOE_BF16 && p.E >= 8 && p.E <= kMaxExpertsExact && p.E % 8 == 0 &&
          p.top_k <= p.E &&
-         p.D >= 32 && p.D % 32 == 0 && p.T > 0 && p.T < ((int64_t)1 << 23);
+         p.D >= 64 && p.D % 64 == 0 && p.T > 0 && p.T < ((int64_t)1 << 23);
 }
 
 ExactShape exact_shape(const Problem& p) {
@@ -1107,30 +1198,30 @@ ExactShape exact_shape(const Problem& p) {
 }
 
 // Dynamic LDS of the exact route: the larger of the waves' chunk rings and the partial logits.
-template <int NT>
+template <int NT, bool E8>
 size_t exact_lds_bytes() {
-  const size_t ring = (size_t)exact_waves<NT>() * kExactRing * 1024 * (1 + NT);
+  const size_t ring = (size_t)exact_waves<NT>() * exact_ring<NT, E8>() * exact_slot<NT, E8>();
   const size_t part = (size_t)exact_waves<NT>() * NT * 256 * 8;
   return ring > part ? ring : part;
 }
 
-template <int NT>
+template <int NT, bool E8 = false>
 hipError_t launch_exact_inst(const ExactShape& f, const ExactArgs& a, hipStream_t s) {
-  const size_t lds = exact_lds_bytes<NT>();
+  const size_t lds = exact_lds_bytes<NT, E8>();
   // dynamic LDS past 64 KB needs the kernel's limit raised to it (once per device)
   static bool raised[64] = {};
   int dev = 0;
   if (lds > 64 * 1024) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (!raised[dev]) {
-      const hipError_t e = hipFuncSetAttribute((const void*)route_exact_kernel<NT>,
+      const hipError_t e = hipFuncSetAttribute((const void*)route_exact_kernel<NT, E8>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                (int)lds);
       if (e != hipSuccess) return e;
       raised[dev] = true;
     }
   }
-  hipLaunchKernelGGL(route_exact_kernel<NT>, dim3((unsigned)f.nblk),
+  hipLaunchKernelGGL((route_exact_kernel<NT, E8>), dim3((unsigned)f.nblk),
                      dim3((unsigned)(exact_waves<NT>() * kWave)), lds, s, a);
   return hipGetLastError();
 }
@@ -1194,7 +1285,7 @@ hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_rou
     a.logits_out = logits_out;
     a.bslot = (unsigned long long*)fws;
     switch (f.NT) {
-      case 1: return launch_exact_inst<1>(f, a, s);
+      case 1: return p.E == 8 ? launch_exact_inst<1, true>(f, a, s) : launch_exact_inst<1>(f, a, s);
       case 2: return launch_exact_inst<2>(f, a, s);
       case 3: return launch_exact_inst<3>(f, a, s);
       default: return launch_exact_inst<4>(f, a, s);

@@ -50,11 +50,11 @@ MID_CASES = {
                                 capacity_factor=0.0),
     # E not a multiple of 8 takes the certified path
     "certified_e17_k3": spec("fine_grained_zipf_bf16", T=257, D=64, DH=64, E=17, top_k=3),
-    # the exact route's edges: k = E, D = 8192, D = 32 (one chunk), E = 24 and 48 (partial
+    # the exact route's edges: k = E, D = 8192, D = 64 (one chunk), E = 24 and 48 (partial
     # expert tiles), E = 64 with T past 8192 tokens (two M-tiles a block) and a ragged block
     "exact_k_equals_e": spec("mixtral_swiglu_bf16", T=333, D=128, DH=128, E=8, top_k=8),
     "exact_d8192": spec("mixtral_swiglu_bf16", T=130, D=8192, DH=128, E=8),
-    "exact_d32_e24": spec("fine_grained_zipf_bf16", T=257, D=32, DH=64, E=24, top_k=3),
+    "exact_d64_e24": spec("fine_grained_zipf_bf16", T=257, D=64, DH=64, E=24, top_k=3),
     "exact_e48_k5": spec("fine_grained_zipf_bf16", T=515, D=96, DH=64, E=48, top_k=5),
     "exact_e64_two_mtiles": spec("switch_top1_cap_bf16", T=8205, D=64, DH=64, E=64),
 }
@@ -383,7 +383,7 @@ def _exact_route(sp) -> bool:
     """bf16 layers with 8 to 64 experts (a multiple of 8) route on exact float64 logits (the
     float64 matrix cores), so no token is left uncertified; the others take the certified bf16
     path."""
-    return sp.dtype == "bf16" and 8 <= sp.E <= 64 and sp.E % 8 == 0 and sp.D % 32 == 0
+    return sp.dtype == "bf16" and 8 <= sp.E <= 64 and sp.E % 8 == 0 and sp.D % 64 == 0
 
 
 @pytest.mark.parametrize("E", [64, 128])
