@@ -17,8 +17,10 @@
 //    fills 2 K-rows; chunk c of K-row k is stored at c ^ (4 (k % 4)), and the MFMA operands
 //    come from transposed reads (ds_read_b64_tr_b16), which turn the N-contiguous layout into
 //    8 consecutive K values per lane.
-// Four stage buffers (A then B, 32 KB each, 128 KB in all), used in rotation. The loads of a
-// stage are issued four stages before it is computed, so about three stages (96 KB per CU)
+// Four stage buffers (A then B, 32 KB each, 128 KB in all), used in rotation: every unit (a
+// tile, or a K part of one) has a multiple of four stages, so stage s of any unit uses buffer
+// s % 4 and the stage loop is written out four stages a trip, with every LDS offset a
+// constant. The loads of a stage are issued four stages before it is computed, so about three stages (96 KB per CU)
 // are in flight while the waves compute. The block synchronises once per stage, before the
 // stage's last k-step: that k-step's operands are already in registers, so its MFMAs cover
 // the reads of the next buffer's first operands and the issue of the loads four stages ahead
@@ -65,16 +67,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// One global_load_lds_dwordx4: 16 bytes per lane from `src` to LDS byte address
-// lds + 16 * lane (lds is wave-uniform). No register receives data, so nothing in the wave
-// depends on it until an explicit s_waitcnt vmcnt.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
-}
-
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14)
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
@@ -101,22 +93,38 @@ struct Loader {
   int64_t b_row_bytes;
 };
 
+// One global_load_lds_dwordx4: 16 bytes per lane from p + off to LDS byte address
+// lds + 16 * lane (off and lds are wave-uniform, off held in SGPRs). No register receives
+// data, so nothing in the wave depends on it until an explicit s_waitcnt vmcnt. The 64-bit add
+// is written next to the load, so that a stage's address arithmetic is one VALU operation per
+// load (left to itself the compiler rebuilt the addresses with 64-bit multiply-adds in every
+// stage, between the MFMAs).
+__device__ __forceinline__ void dma16_at(const void* p, int64_t off, uint32_t lds) {
+  uint64_t t;
+  asm volatile("v_lshl_add_u64 %0, %1, 0, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %0, off"
+               : "=&v"(t)
+               : "v"(p), "s"(off), "s"(lds)
+               : "memory", "m0");
+}
+
 // Load d (0..7) of this wave for a stage at K offset k0 into the buffer at LDS byte address
-// sa: even d -> A instruction d / 2 (16 rows), odd d -> B instruction d / 2 (2 K-rows).
-// With BT (B stored K-major, (N, K) per expert), B's stage is laid out and loaded exactly like
-// A's: 256 columns x 32 K, 64 bytes a column, an instruction fills 16 columns.
+// sa: even d -> A instruction d / 2 (16 rows), odd d -> B instruction d / 2 (2 K-rows). bk is
+// k0 times B's row pitch in bytes. With BT (B stored K-major, (N, K) per expert), B's stage is
+// laid out and loaded exactly like A's: 256 columns x 32 K, 64 bytes a column, an instruction
+// fills 16 columns.
 template <bool BT>
 __device__ __forceinline__ void load_one(const Loader& ld, int64_t k0, int64_t bk, uint32_t sa,
                                          int wv, int d) {
   const int j = d >> 1;
   if (d & 1) {
     if (BT)
-      dma16(ld.bt[j] + k0 * 2, sa + kHalf + (4 * wv + j) * 1024);
+      dma16_at(ld.bt[j], k0 * 2, sa + kHalf + (4 * wv + j) * 1024);
     else
-      dma16(ld.b[j & 1] + bk + (int64_t)(2 * j) * ld.b_row_bytes,
-            sa + kHalf + (4 * wv + j) * 1024);
+      dma16_at(ld.b[j & 1], bk + (int64_t)(2 * j) * ld.b_row_bytes,
+               sa + kHalf + (4 * wv + j) * 1024);
   } else {
-    dma16(ld.a[j] + k0 * 2, sa + (4 * wv + j) * 1024);
+    dma16_at(ld.a[j], k0 * 2, sa + (4 * wv + j) * 1024);
   }
 }
 template <bool BT>
@@ -300,9 +308,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     full = total / nblk * nblk;
     r = total - full;
     split = min(kMaxSplit, nblk / r);
-    // each part needs an even number of stages, and enough of them (kMinPartStages) to pay
-    // for storing and adding its float32 partial
-    while (split > 1 && (nst_all % split != 0 || nst_all / split < kMinPartStages)) --split;
+    // each part needs a multiple of kNBuf stages (like every unit: see the stage loop), and
+    // enough of them (kMinPartStages) to pay for storing and adding its float32 partial
+    while (split > 1 && (nst_all % split != 0 || nst_all / split < kMinPartStages ||
+                         (nst_all / split) % kNBuf != 0))
+      --split;
     if (split == 1) full = total;
   }
   const int xcd = b & 7, per = nblk >> 3, jb = b >> 3;
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     u.rows = __builtin_amdgcn_readfirstlane(u.rows);
     u.n_tile = __builtin_amdgcn_readfirstlane(u.n_tile);
     u.parts = L >= full ? split : 1;  // K parts of this tile
-    u.nst = nst_all / u.parts;        // >= 4: K % 128 == 0, and parts have kMinPartStages
+    u.nst = nst_all / u.parts;        // a multiple of 4: K % 128 == 0, and so are the parts
     u.kbeg = (int64_t)ks * u.nst * kBK;
     u.acol = 0;
     u.brow = 0;
@@ -474,7 +484,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   }
   const uint32_t lbase = lds_addr(sbuf);
 
-  uint32_t co = 0;  // buffer offset of the current unit's first stage
 
   int L0, ks0;
   if (unit_at(jb * 8 + xcd, L0, ks0)) {
@@ -528,45 +537,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         constexpr int NN = decltype(nn_tag)::value;
         uint32_t vab[2], vbb[4];  // read bases in buffer 0
         unit_bases<NN, BT>(lbase, lbase + kHalf, aoff, boff, wv, vab, vbb);
-        uint32_t ab[2], bb[4];
+        bf16x8 a0 = read_a(vab, 0, 0), a1 = read_a(vab, 1, 0), bq[8];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) ab[t] = vab[t] + co;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) bb[c] = vbb[c] + co;
-        bf16x8 a0 = read_a(ab, 0, 0), a1 = read_a(ab, 1, 0), bq[8];
-#pragma unroll
-        for (int c = 0; c < NN; ++c) bq[c] = read_b_any<BT>(bb, c, 0);
+        for (int c = 0; c < NN; ++c) bq[c] = read_b_any<BT>(vbb, c, 0);
         const int nst = cu.nst;
         const int64_t kbeg = cu.kbeg;
-        // One stage on buffer co (the next one is no): loads through loader LDR of the stage
-        // at K offset KL go into buffer co when LOAD; KEEP of this wave's loads may stay in
-        // flight at the stage's barrier. (A macro, not a lambda: captured operand arrays would
-        // live in scratch memory.)
-#define MOE_STAGE(LDR, KL, LOAD, KEEP)                                                      \
+        // One stage on buffer CI (the next one is CI + 1 mod kNBuf): loads through loader LDR
+        // of the stage at K offset KL go into buffer CI when LOAD; KEEP of this wave's loads may
+        // stay in flight at the stage's barrier. Every unit has a multiple of kNBuf stages, so
+        // each starts in buffer 0 and the loop below runs kNBuf stages per trip with the buffer
+        // offsets as constants (they end up in the DS instructions' offset fields). (A macro,
+        // not a lambda: captured operand arrays would live in scratch memory.)
+#define MOE_STAGE(CI, LDR, KL, LOAD, KEEP)                                                  \
   {                                                                                         \
-    uint32_t no = co + kBuf;                                                                \
-    no = no == kNBuf * kBuf ? 0u : no;                                                      \
-    no = __builtin_amdgcn_readfirstlane(no);                                                \
-    uint32_t abn[2], bbn[4];                                                                \
-    _Pragma("unroll") for (int t = 0; t < 2; ++t) abn[t] = vab[t] + no;                     \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c) bbn[c] = vbb[c] + no;                     \
-    stage<NN, BT>(ab, bb, abn, bbn, acc, a0, a1, bq, LDR, KL, LOAD, lbase + co, wv, KEEP);  \
-    co = no;                                                                                \
-    _Pragma("unroll") for (int t = 0; t < 2; ++t) ab[t] = abn[t];                           \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c) bb[c] = bbn[c];                           \
+    constexpr uint32_t kco = (CI) * kBuf, kno = ((CI) + 1) % kNBuf * kBuf;                  \
+    uint32_t ab[2], bb[4], abn[2], bbn[4];                                                  \
+    _Pragma("unroll") for (int t = 0; t < 2; ++t) {                                         \
+      ab[t] = vab[t] + kco;                                                                 \
+      abn[t] = vab[t] + kno;                                                                \
+    }                                                                                       \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                         \
+      bb[c] = vbb[c] + kco;                                                                 \
+      bbn[c] = vbb[c] + kno;                                                                \
+    }                                                                                       \
+    stage<NN, BT>(ab, bb, abn, bbn, acc, a0, a1, bq, LDR, KL, LOAD, lbase + kco, wv, KEEP); \
   }
-        for (int s = 0; s + kNBuf < nst; ++s)
-          MOE_STAGE(ld, kbeg + (int64_t)(s + kNBuf) * kBK, true, kKeep)
+        static_assert(kNBuf == 4, "the stage loop is written out for four buffers");
+        for (int s = 0; s + kNBuf < nst; s += kNBuf) {
+          MOE_STAGE(0, ld, kbeg + (int64_t)(s + 4) * kBK, true, kKeep)
+          MOE_STAGE(1, ld, kbeg + (int64_t)(s + 5) * kBK, true, kKeep)
+          MOE_STAGE(2, ld, kbeg + (int64_t)(s + 6) * kBK, true, kKeep)
+          MOE_STAGE(3, ld, kbeg + (int64_t)(s + 7) * kBK, true, kKeep)
+        }
         // Publish the unit after next (its slot was last read before this unit's barriers),
         // then let the last kNBuf stages load the next unit's first kNBuf. With no next unit
         // those stages load nothing, so fewer loads are left to keep in flight.
         if (tid == 0) s_unit[i & 1] = after_next;
         if (has_next) ld = make_loader(nx, nsrc);
-#pragma unroll 1
-        for (int q = 0; q < kNBuf; ++q) {
-          const int keep = has_next ? kKeep : (kNBuf - 2 - q > 0 ? (kNBuf - 2 - q) * 8 : 0);
-          MOE_STAGE(ld, nx.kbeg + (int64_t)q * kBK, has_next, keep)
-        }
+        MOE_STAGE(0, ld, nx.kbeg, has_next, has_next ? kKeep : 16)
+        MOE_STAGE(1, ld, nx.kbeg + kBK, has_next, has_next ? kKeep : 8)
+        MOE_STAGE(2, ld, nx.kbeg + 2 * kBK, has_next, has_next ? kKeep : 0)
+        MOE_STAGE(3, ld, nx.kbeg + 3 * kBK, has_next, has_next ? kKeep : 0)
 #undef MOE_STAGE
 
         const int row0 = cu.row0, rows = cu.rows, parts = cu.parts, L = cu.L, ks = cu.ks;
