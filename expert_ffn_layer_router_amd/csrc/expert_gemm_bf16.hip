@@ -609,35 +609,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
         auto put = [&](int mi, int v0, int cq, float x0, float x1) { put_at(C, mi, v0, cq, x0, x1); };
         if (parts == 1) {
           if (wr0 < rows) {  // a whole tile: store this wave's part from the accumulators
+            // Rows outer: one 64-bit add per row (the lane's row pointer), then the row's
+            // column tiles at immediate offsets. The bounds are tested only in a tile at an edge
+            // of C (a scalar branch picks the copy of the loop).
+            uint16_t* const pal = SAVE ? pa + lofs : nullptr;
+            uint16_t* const pbl = SAVE ? pb + lofs : nullptr;
+            auto store2 = [&](uint16_t* ptr, float x0, float x1, bool ok) {
+              const float recv = swap_adjacent_lanes(odd ? x0 : x1);
+              const uint32_t pk = odd ? pack_bf16x2(recv, x1) : pack_bf16x2(x0, recv);
+              if (ok) *(uint32_t*)ptr = pk;
+            };
+            auto store_tile = [&](auto chk_tag) {
+              constexpr bool kChk = decltype(chk_tag)::value;
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-              for (int q = 0; q < (kSwiGLU ? NN / 2 : NN); ++q)
+              for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int v0 = 0; v0 < 16; v0 += 2) {
-                  float x0, x1;
-                  if (kSwiGLU) {  // gate in the wave's column tile 2q, up in 2q + 1
-                    const float g0 = acc_get(acc[mi][2 * q][v0]);
-                    const float g1 = acc_get(acc[mi][2 * q][v0 + 1]);
-                    const float u0 = acc_get(acc[mi][2 * q + 1][v0]);
-                    const float u1 = acc_get(acc[mi][2 * q + 1][v0 + 1]);
-                    x0 = silu_f(g0) * u0;
-                    x1 = silu_f(g1) * u1;
-                    if constexpr (SAVE) {
-                      put_at(pa, mi, v0, ccol0 + 32 * q, g0, g1);
-                      put_at(pb, mi, v0, ccol0 + 32 * q, u0, u1);
+                  const int dr = 32 * mi + 8 * (v0 >> 2) + (v0 & 3);
+                  const int64_t ro = (int64_t)dr * N;
+                  const bool rok = !kChk || lrow + dr < rows;
+#pragma unroll
+                  for (int q = 0; q < (kSwiGLU ? NN / 2 : NN); ++q) {
+                    const int cq = ccol0 + 32 * q;
+                    const bool ok = !kChk || (rok && n0 + cq + colp < N);
+                    float x0, x1;
+                    if (kSwiGLU) {  // gate in the wave's column tile 2q, up in 2q + 1
+                      const float g0 = acc_get(acc[mi][2 * q][v0]);
+                      const float g1 = acc_get(acc[mi][2 * q][v0 + 1]);
+                      const float u0 = acc_get(acc[mi][2 * q + 1][v0]);
+                      const float u1 = acc_get(acc[mi][2 * q + 1][v0 + 1]);
+                      x0 = silu_f(g0) * u0;
+                      x1 = silu_f(g1) * u1;
+                      if constexpr (SAVE) {
+                        store2(pal + ro + cq, g0, g1, ok);
+                        store2(pbl + ro + cq, u0, u1, ok);
+                      }
+                    } else {
+                      x0 = acc_get(acc[mi][q][v0]);
+                      x1 = acc_get(acc[mi][q][v0 + 1]);
+                      if (EPI == EPI_RELU) {
+                        if constexpr (SAVE) store2(pal + ro + cq, x0, x1, ok);
+                        x0 = fmaxf(x0, 0.f);
+                        x1 = fmaxf(x1, 0.f);
+                      }
                     }
-                  } else {
-                    x0 = acc_get(acc[mi][q][v0]);
-                    x1 = acc_get(acc[mi][q][v0 + 1]);
-                    if (EPI == EPI_RELU) {
-                      if constexpr (SAVE) put_at(pa, mi, v0, ccol0 + 32 * q, x0, x1);
-                      x0 = fmaxf(x0, 0.f);
-                      x1 = fmaxf(x1, 0.f);
-                    }
+                    store2(lp + ro + cq, x0, x1, ok);
                   }
-                  put(mi, v0, ccol0 + 32 * q, x0, x1);
                 }
+            };
+            if (whole)
+              store_tile(std::false_type{});
+            else
+              store_tile(std::true_type{});
           }
         } else if constexpr (NN == 8) {
           // A K part: store the float32 partial tile (each lane's accumulators, 16 bytes at a
