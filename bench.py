@@ -43,12 +43,12 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("9212fbe5cd20ed4fee32ad0c6f01472deeb2f4a52a2e540d9d3050f3741b14e6",
-                            3094270.6071428573, 235070.01785714287),
-    "switch_top1_cap_bf16": ("9212fbe5cd20ed4fee32ad0c6f01472deeb2f4a52a2e540d9d3050f3741b14e6",
-                             223820.7232142857, 27077.76785714286),
-    "fine_grained_zipf_bf16": ("9212fbe5cd20ed4fee32ad0c6f01472deeb2f4a52a2e540d9d3050f3741b14e6",
-                               1015708.4553571428, 144798.1517857143),
+    "mixtral_swiglu_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
+                            3464545.910714286, 229562.23214285713),
+    "switch_top1_cap_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
+                             224074.49107142858, 26562.651785714286),
+    "fine_grained_zipf_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
+                               1002634.2678571428, 143433.08035714287),
 }
 
 
