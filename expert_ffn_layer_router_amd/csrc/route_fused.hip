@@ -983,7 +983,8 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
   __shared__ int s_tot[kGroup], s_gb[kGroup];
   __shared__ unsigned long long s_p[kGroup];
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ double s_term[kGroup];
+  __shared__ double s_term[kW];
+  __shared__ int s_wtot[kW];
   const int tid = threadIdx.x, wv = wave_id(), lane = lane_id();
   const int E = a.E, k = a.k;
   const int g = blockIdx.x;
@@ -1036,42 +1037,55 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
     s_p[tid] = ps;
   }
   __syncthreads();
-  if (tid < E) {
-    int tot = 0, gb = 0;
-    unsigned long long ps = 0;
-    for (int q = 0; q < Q; ++q) {
-      tot += s_tot[q * E + tid];
-      gb += s_gb[q * E + tid];
-      ps += s_p[q * E + tid];
+  // the Q partial rows of each expert (row q of expert e at q E + e), summed by halving: after
+  // the step of width h, entries q < h hold everything at q, q + h (any Q)
+  {
+    int qp = 1;
+    while (qp < Q) qp *= 2;
+    for (int h = qp >> 1; h >= 1; h >>= 1) {
+      if (tid < h * E && tid + h * E < Q * E) {
+        s_tot[tid] += s_tot[tid + h * E];
+        s_gb[tid] += s_gb[tid + h * E];
+        s_p[tid] += s_p[tid + h * E];
+      }
+      __syncthreads();
     }
-    s_tot[tid] = tot;  // (rows q > 0 are no longer read)
-    s_gb[tid] = gb;
-    s_p[tid] = ps;
   }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = run;
-      run += a.capacity < 0 ? s_tot[e] : (int)min<int64_t>((int64_t)s_tot[e], a.capacity);
+  // expert offsets: an exclusive scan of the kept counts, within each wave of 64 experts, then
+  // the waves' totals (E <= kGroup)
+  {
+    const int kept = tid < E ? (a.capacity < 0 ? s_tot[tid]
+                                               : (int)min<int64_t>((int64_t)s_tot[tid], a.capacity))
+                             : 0;
+    int incl = kept;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int o = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += o;
     }
-    s_off[E] = run;
+    if (lane == kWave - 1) s_wtot[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int q = 0; q < wv; ++q) before += s_wtot[q];
+    if (tid < E) s_off[tid] = before + incl - kept;
+    if (tid == E - 1) s_off[E] = before + incl;
   }
   if (g == 0) {
+    // the loss: each expert's term, summed over a wave by exchanges, then the waves in order
     double term = 0.0;
     if (tid < E) {
       if (a.counts_out) a.counts_out[tid] = s_tot[tid];
       term = ((double)s_tot[tid] / ((double)a.T * (double)k)) *
              (((double)s_p[tid] / kPScale) / (double)a.T);
     }
-    s_term[tid] = term;
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) term += __shfl_xor(term, d, kWave);
+    if (lane == 0) s_term[wv] = term;
     __syncthreads();
-    for (int h = kGroup / 2; h >= 1; h >>= 1) {
-      if (tid < h) s_term[tid] += s_term[tid + h];
-      __syncthreads();
-    }
     if (tid == 0) {
-      *a.aux = (float)((double)E * s_term[0]);
+      double sum = 0.0;
+      for (int q = 0; q < kW; ++q) sum += s_term[q];
+      *a.aux = (float)((double)E * sum);
       if (a.uncertified) *a.uncertified = a.nflag ? *a.nflag : 0;
     }
     if (a.offsets)
