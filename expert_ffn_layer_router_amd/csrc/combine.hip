@@ -39,8 +39,8 @@ __device__ __forceinline__ uint4 pack8(const float f[8]) {
 // lane before any of them is used, so a wave has KG x U row loads in flight; the sum still runs
 // over j ascending. With ONE (top_k <= KG) the token's slots are a single group, and each column
 // chunk is summed, packed and stored as soon as its loads are in, so only the loads hold
-// registers. (Passes spread over more waves beat longer passes: at the Mixtral shape, 2 waves
-// of 4 chunks a lane per token took 18.8 us against 20.8 us for one wave of 8.)
+// registers. (Passes spread over more waves beat longer passes: at the Mixtral shape, 4 waves
+// of 2 chunks a lane per token took 18.5 us, 2 waves of 4 18.8-19.3 us, one wave of 8 20.4 us.)
 template <int KG, int U, bool ONE, int LW>
 __global__ __launch_bounds__(kThreads, 4) void combine_bf16x8_kernel(
     int64_t T, int k, int64_t n_vec, const uint4* __restrict__ y,
@@ -171,8 +171,7 @@ hipError_t launch_combine(const Problem& p, const void* y, const int32_t* slot_r
     }                                                                                        \
   } while (0)
     if (p.top_k <= 2) {
-      if (nv > 2 * kWave) MOE_COMBINE(2, 4, true);
-      else MOE_COMBINE(2, 2, true);
+      MOE_COMBINE(2, 2, true);
     } else if (p.top_k <= 4) {
       if (nv > 2 * kWave) MOE_COMBINE(4, 4, true);
       else MOE_COMBINE(4, 2, true);
