@@ -543,6 +543,7 @@ __global__ __launch_bounds__(kFT, 2) void route_fused_kernel(FusedArgs a) {
 // values for a chunk are 8 consecutive bf16 of its token row (one 16-byte load) and its B
 // values the router entries W[d][16 n + lane % 16] of those 8 rows (E-strided, from L2).
 constexpr int kXT = 16;  // tokens per M-tile: the float64 MFMA's 16 rows
+constexpr int kMaxKP = 16;  // K-parts of an M-tile at most (waves a block / M-tiles)
 
 struct ExactArgs {
   int64_t T, D;
@@ -819,8 +820,14 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
       const int e = 16 * n + i;
       double v = 0.0;
       if (e < E) {
-        for (int p = 0; p < KP; ++p)
-          v += s_part[(((mm * KP + p) * NT + n) * 16 + trow) * 16 + i];
+        // every K-part read first (KP <= kMaxKP), then added in order
+        double pv[kMaxKP];
+#pragma unroll
+        for (int p = 0; p < kMaxKP; ++p)
+          pv[p] = p < KP ? s_part[(((mm * KP + p) * NT + n) * 16 + trow) * 16 + i] : 0.0;
+#pragma unroll
+        for (int p = 0; p < kMaxKP; ++p)
+          if (p < KP) v += pv[p];
         if (a.bias) v += (double)bias_n[n];
       }
       lg[n] = v;
@@ -858,22 +865,31 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
       }
     }
     // probabilities, shifted by the largest logit (the first choice)
-    double prob[NT];
+    double prob[NT], ex[NT];
     double ps = 0.0;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      prob[n] = (16 * n + i < E) ? exp(lg[n] - v0) : 0.0;
-      ps += prob[n];
+      ex[n] = (16 * n + i < E) ? exp(lg[n] - v0) : 0.0;
+      ps += ex[n];
     }
     ps = row_sum16(ps);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) prob[n] /= ps;
+    for (int n = 0; n < NT; ++n) prob[n] = ex[n] / ps;
     double gate[NT];
     if (a.renorm) {
+      // the chosen logits' exponentials are their experts' ex values (the same exp of the same
+      // difference), taken from the lanes of this row that hold them
       double gs = 0.0;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        gate[n] = (16 * n + i < k) ? exp(my_v[n] - v0) : 0.0;
+        const int src = (lane & ~15) | (my_e[n] & 15);
+        double ev = 0.0;
+#pragma unroll
+        for (int n2 = 0; n2 < NT; ++n2) {
+          const double c = __shfl(ex[n2], src);
+          if ((my_e[n] >> 4) == n2) ev = c;
+        }
+        gate[n] = (16 * n + i < k) ? ev : 0.0;
         gs += gate[n];
       }
       gs = row_sum16(gs);
