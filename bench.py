@@ -44,11 +44,11 @@ WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
     "mixtral_swiglu_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
-                            3464545.910714286, 229562.23214285713),
+                            3502768.9375, 229564.36607142858),
     "switch_top1_cap_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
-                             224074.49107142858, 26562.651785714286),
+                             224131.29464285713, 26562.66964285714),
     "fine_grained_zipf_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
-                               1002634.2678571428, 143433.08035714287),
+                               1000470.9196428572, 143433.26785714287),
 }
 
 
