@@ -314,6 +314,42 @@ def test_combine_stage(dtype):
     assert max_abs_rel(to_host(out), ref) <= tol
 
 
+@pytest.mark.parametrize("d_out", [8, 1032, 4104, 16392])
+@pytest.mark.parametrize("k", [1, 2, 6, 9])
+def test_combine_widths(d_out, k):
+    """Combine at row widths of 1 to 2049 16-byte column chunks (a row's passes on 1 to 8 waves,
+    then more than one pass a wave) and k from 1 to 9 (one slot group a token, then two), with
+    about 15% of the slots dropped: every output element against the definition, the sum over
+    kept slots of gate times row (ML Grind "Mixture-of-Experts (MoE) Routing", Algorithm step 3
+    formula); rows whose slots were all dropped are exact zeros."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    T = 97
+    sp = spec("mixtral_swiglu_bf16", T=T, D=d_out, DH=64, E=16, top_k=k)
+    p = B.Problem.from_spec(sp)
+    rng = np.random.default_rng(1000 + 17 * k + d_out)
+    R = T * k
+    slot_row = rng.permutation(R).astype(np.int32)
+    slot_row[rng.random(R) < 0.15] = -1
+    gates = rng.random((T, k)).astype(np.float32)
+    y_bits = f32_to_bf16_bits(rng.standard_normal((R, d_out)).astype(np.float32))
+    y = bf16_bits_to_f32(y_bits).astype(np.float64)
+    out = torch.empty((T, d_out), dtype=torch.bfloat16, device="cuda")
+    B.moe_combine(p, to_dev(y_bits), torch.from_numpy(slot_row).cuda(),
+                  torch.from_numpy(gates).cuda(), out)
+    torch.cuda.synchronize()
+    idx = slot_row.reshape(T, k)
+    ref = np.zeros((T, d_out))
+    for j in range(k):
+        kept = idx[:, j] >= 0
+        ref[kept] += gates[kept, j, None].astype(np.float64) * y[idx[kept, j]]
+    got = to_host(out)
+    assert max_abs_rel(got, ref) <= 1e-2
+    none = (idx < 0).all(axis=1)
+    assert np.all(got[none] == 0.0)
+
+
 # --- the five configurations at full size ---------------------------------------------------
 
 FULL = ["switch_top1_cap_bf16", "mixtral_swiglu_bf16", "fine_grained_zipf_bf16"]
