@@ -66,6 +66,7 @@ struct Layout {
   size_t offc;          // padded layout: the compact offsets, (E+1) int32
   size_t hbuf;          // expert hidden activations, (rows, DH)
   size_t gsplit, gctr;  // bf16 GEMM: K-split partial tiles; K-split tickets + work queue
+  int64_t nsplit;       // K-split partial tiles reserved (what the layer's GEMMs can use)
   size_t perm;          // moe_forward's own permutation, (rows) int32
   size_t xpad;          // padded layout: the padded copy of x, (rows, D)
   size_t ybuf;          // moe_forward's expert outputs, (rows, D_out)
@@ -93,7 +94,14 @@ Layout layout_of(const Problem& q, bool padded = false) {
   L.dispatch_end = off;
   L.hbuf = take(q.kind == MOE_EXPERT_LINEAR ? 0 : rows * (size_t)q.DH * es);
   const bool split = q.dtype == MOE_BF16 && q.T > 0;
-  L.gsplit = take(split ? (size_t)kSplitSlots * kSplitSlotFloats * sizeof(float) : 0);
+  // partial tiles for a K split of either GEMM (none when neither K can be split)
+  L.nsplit = 0;
+  if (split) {
+    const bool lin = q.kind == MOE_EXPERT_LINEAR, swi = q.kind == MOE_EXPERT_SWIGLU;
+    L.nsplit = gemm_bf16_split_slots(rows, q.E, q.D, lin ? q.D_out : q.DH, swi);
+    if (!lin) L.nsplit = std::max(L.nsplit, gemm_bf16_split_slots(rows, q.E, q.DH, q.D_out, false));
+  }
+  L.gsplit = take((size_t)L.nsplit * kSplitSlotFloats * sizeof(float));
   L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
   L.ffn_end = off;
   L.perm = take(rows * sizeof(int32_t));
@@ -152,7 +160,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   if (q.dtype == MOE_BF16 && q.T > 0) {
     int32_t* ctr = at<int32_t>(ws, Lw.gctr);
     queue = ctr + kSplitSlots;
-    if (ncu > 0) {
+    if (ncu > 0 && Lw.nsplit > 0) {
       split_ws = at<float>(ws, Lw.gsplit);
       split_ctr = ctr;
     }
@@ -165,6 +173,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   }
   GroupedGemm g{};
   g.split_ws = split_ws;
+  g.split_slots = Lw.nsplit;
   g.split_ctr = split_ctr;
   g.ncu = ncu;
   g.queue = queue;
@@ -190,6 +199,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   if (err == hipSuccess && !linear) {
     GroupedGemm d{};
     d.split_ws = split_ws;
+    d.split_slots = Lw.nsplit;
     d.split_ctr = split_ctr;
     d.ncu = ncu;
     d.queue = queue;
@@ -600,7 +610,9 @@ moe_status moe_forward_train(const moe_problem* p, const void* x, const void* w_
   if (err != hipSuccess || q.T == 0) return hip_status(err);
   const int ncu = tickets ? device_split_cus() : 0;
   err = run_experts_saving(q, x, perm, expert_offsets, w1, w3, w2, sv + S.a, sv + S.b, sv + S.h,
-                           sv + S.y, (tickets && ncu > 0) ? at<float>(ws, L.gsplit) : nullptr,
+                           sv + S.y,
+                           (tickets && ncu > 0 && L.nsplit > 0) ? at<float>(ws, L.gsplit) : nullptr,
+                           L.nsplit,
                            (tickets && ncu > 0) ? tickets : nullptr,
                            tickets ? tickets + kSplitSlots : nullptr, ncu, stream);
   if (err == hipSuccess) err = launch_combine(q, sv + S.y, slot_row, gates, out, stream);

@@ -930,6 +930,7 @@ hipError_t nt(const Problem& q, const void* A0, const void* A1, const void* W0, 
     f.epilogue = EPI_NONE;
     f.dtype = q.dtype;
     f.split_ws = res.split_ws;
+    f.split_slots = kSplitSlots;
     f.split_ctr = res.split_ctr;
     f.queue = res.queue;
     f.ncu = res.ncu;
@@ -1038,7 +1039,8 @@ hipError_t tn_kg(const Problem& q, const BwdLayout& L, void* ws, const void* src
 // The forward GEMM A_rows -> C without an epilogue (to recompute pre-activations / outputs).
 hipError_t fwd_gemm(const Problem& q, const void* A, int64_t lda, const int32_t* gather,
                     const void* W, int64_t K, int64_t N, const int32_t* offsets, void* C,
-                    float* split_ws, int32_t* split_ctr, int32_t* queue, int ncu, hipStream_t s) {
+                    float* split_ws, int64_t split_slots, int32_t* split_ctr, int32_t* queue,
+                    int ncu, hipStream_t s) {
   GroupedGemm g{};
   g.A = A;
   g.lda = lda;
@@ -1055,6 +1057,7 @@ hipError_t fwd_gemm(const Problem& q, const void* A, int64_t lda, const int32_t*
   g.epilogue = EPI_NONE;
   g.dtype = q.dtype;
   g.split_ws = split_ws;
+  g.split_slots = split_slots;
   g.split_ctr = split_ctr;
   g.ncu = ncu;
   g.queue = queue;
@@ -1095,11 +1098,11 @@ bool dgate_from_h(const Problem& q, const void* dout) {
 hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* perm,
                               const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* a, void* b, void* h, void* y,
-                              float* split_ws, int32_t* split_ctr, int32_t* queue, int ncu,
-                              hipStream_t s) {
+                              float* split_ws, int64_t split_slots, int32_t* split_ctr,
+                              int32_t* queue, int ncu, hipStream_t s) {
   const int64_t D = q.D, DH = q.DH, Do = q.D_out;
   if (q.kind == MOE_EXPERT_LINEAR)
-    return fwd_gemm(q, x, D, perm, w1, D, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
+    return fwd_gemm(q, x, D, perm, w1, D, Do, offsets, y, split_ws, split_slots, split_ctr, queue, ncu, s);
   const bool swiglu = q.kind == MOE_EXPERT_SWIGLU;
   GroupedGemm g{};
   g.A = x;
@@ -1117,6 +1120,7 @@ hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* pe
   g.epilogue = swiglu ? EPI_SWIGLU : EPI_RELU;
   g.dtype = q.dtype;
   g.split_ws = split_ws;
+  g.split_slots = split_slots;
   g.split_ctr = split_ctr;
   g.ncu = ncu;
   g.queue = queue;
@@ -1130,12 +1134,12 @@ hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* pe
   hipError_t err = launch_grouped_gemm(g, s);
   if (!saving) {
     if (err == hipSuccess)
-      err = fwd_gemm(q, x, D, perm, w1, D, DH, offsets, a, split_ws, split_ctr, queue, ncu, s);
+      err = fwd_gemm(q, x, D, perm, w1, D, DH, offsets, a, split_ws, split_slots, split_ctr, queue, ncu, s);
     if (err == hipSuccess && swiglu)
-      err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_ctr, queue, ncu, s);
+      err = fwd_gemm(q, x, D, perm, w3, D, DH, offsets, b, split_ws, split_slots, split_ctr, queue, ncu, s);
   }
   if (err == hipSuccess && y)  // (the backward of a bf16 layer does without y: dgate_from_h)
-    err = fwd_gemm(q, h, DH, nullptr, w2, DH, Do, offsets, y, split_ws, split_ctr, queue, ncu, s);
+    err = fwd_gemm(q, h, DH, nullptr, w2, DH, Do, offsets, y, split_ws, split_slots, split_ctr, queue, ncu, s);
   return err;
 }
 
@@ -1174,7 +1178,7 @@ hipError_t launch_backward(const Problem& q, const void* x, const void* w_router
   int32_t* queue = tickets ? tickets + kSplitSlots : nullptr;
   err = run_experts_saving(q, x, perm, offsets, w1, w3, w2, at<void>(ws, L.a), at<void>(ws, L.b),
                            at<void>(ws, L.h), dgate_from_h(q, dout) ? nullptr : at<void>(ws, L.y),
-                           (tickets && ncu > 0) ? at<float>(ws, L.gsplit) : nullptr,
+                           (tickets && ncu > 0) ? at<float>(ws, L.gsplit) : nullptr, kSplitSlots,
                            (tickets && ncu > 0) ? tickets : nullptr, queue, ncu, s);
   if (err != hipSuccess) return err;
   const BwdInputs in{idx, gates, logits, counts, offsets, perm, slot_row,

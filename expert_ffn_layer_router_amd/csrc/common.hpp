@@ -139,8 +139,8 @@ SavedLayout saved_layout(const Problem& q);
 hipError_t run_experts_saving(const Problem& q, const void* x, const int32_t* perm,
                               const int32_t* offsets, const void* w1, const void* w3,
                               const void* w2, void* a, void* b, void* h, void* y,
-                              float* split_ws, int32_t* split_ctr, int32_t* queue, int ncu,
-                              hipStream_t s);
+                              float* split_ws, int64_t split_slots, int32_t* split_ctr,
+                              int32_t* queue, int ncu, hipStream_t s);
 hipError_t launch_backward_saved(const Problem& q, const int32_t* idx, const float* gates,
                                  const int32_t* counts, const int32_t* offsets,
                                  const int32_t* slot_row, const void* saved, const void* x,
@@ -171,9 +171,11 @@ struct GroupedGemm {
   int epilogue;
   int dtype;
   // K-split tail (bf16 256x256 kernel only; null split_ws: no split). split_ws holds
-  // kSplitSlots partial tiles of kSplitSlotFloats floats, split_ctr kSplitSlots tickets;
-  // ncu = compute units used to size waves (at most kSplitSlots, a multiple of 8).
+  // split_slots (at most kSplitSlots) partial tiles of kSplitSlotFloats floats, split_ctr
+  // kSplitSlots tickets; a launch that could need more slots does not split. ncu = compute
+  // units used to size waves (at most kSplitSlots, a multiple of 8).
   float* split_ws;
+  int64_t split_slots;
   int32_t* split_ctr;
   int ncu;
   // Work queue of the 256 x 256 kernel (kQueueInts int32, zero on entry, left zero): one
@@ -207,6 +209,9 @@ constexpr int kQueueInts = 16;
 constexpr int64_t kSplitSlotFloats = 256 * 256;
 // Compute units of the current device, capped at kSplitSlots (0 when not a multiple of 8).
 int device_split_cus();
+// Partial-tile slots that a K split of a bf16 product (max_rows rows over E experts, K x N,
+// SwiGLU column tiles or not) can use: 0 when K is too short to split.
+int64_t gemm_bf16_split_slots(int64_t max_rows, int E, int64_t K, int64_t N, bool swiglu);
 hipError_t launch_grouped_gemm(const GroupedGemm& g, hipStream_t s);
 // bf16, 256 x 256 tiles (expert_gemm_bf16.hip). The K-split tickets (split_ctr) must be zero
 // on entry; the kernel leaves them zero.

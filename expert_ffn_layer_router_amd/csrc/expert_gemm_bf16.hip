@@ -801,6 +801,17 @@ int device_split_cus() {
   return cache[dev] > 0 ? cache[dev] : 0;
 }
 
+// A K split needs at least two parts of kMinPartStages stages each; its parts never outnumber
+// the launch's blocks (at most one a block), whose count is capped by the tile bound (rounded up
+// to 8) and by kSplitSlots.
+int64_t gemm_bf16_split_slots(int64_t max_rows, int E, int64_t K, int64_t N, bool swiglu) {
+  if (K % 128 != 0 || K / kBK < 2 * kMinPartStages) return 0;
+  const int64_t mt_max = (max_rows + kBM - 1) / kBM + E;
+  const int64_t cols = swiglu ? kBN / 2 : kBN;
+  const int64_t tiles = (mt_max * ((N + cols - 1) / cols) + 7) / 8 * 8;
+  return tiles < kSplitSlots ? tiles : kSplitSlots;
+}
+
 hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) {
   GroupedGemm g = g_in;
   // A K split needs at least two parts of kMinPartStages stages each; below that the split
@@ -820,6 +831,11 @@ hipError_t launch_grouped_gemm_bf16_256(const GroupedGemm& g_in, hipStream_t s) 
   G = G / 8 * 8;
   const int64_t tiles_max = (mt_max * nt + 7) / 8 * 8;
   if (G > tiles_max) G = tiles_max;
+  // (the parts of a split never outnumber the blocks: a workspace with fewer slots is not used)
+  if (g.split_ws && G > g.split_slots) {
+    g.split_ws = nullptr;
+    g.split_ctr = nullptr;
+  }
   const dim3 grid((unsigned)G);
   // The start/stop events (if any) are recorded by the kernel's own dispatch, so timing adds
   // no packets, and no gaps, to the stream.

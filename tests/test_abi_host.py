@@ -90,6 +90,27 @@ def test_workspace_size():
     assert B.workspace_size(P(T=0)) >= 0
 
 
+def test_workspace_split_slots_follow_k():
+    """The bf16 GEMMs' split-K partial tiles (64 MiB at most) are reserved only where a K can
+    be split (K >= 4096, at least two parts of 2048), and only as many as the launch's tile
+    bound allows: a 16-token layer with short K needs none of them."""
+    mib, tile = 1 << 20, 256 * 256 * 4
+    small = B.workspace_size(P(T=16, D=512, DH=1024, D_out=512, E=8, top_k=2))
+    assert small < mib
+    # the same layer with DH = 4096: the down product's K can be split, into at most as many
+    # parts as its launch has blocks: (1 M-tile + 8 experts' last tiles) x 2 column tiles,
+    # rounded up to 8 = 24 tiles of 256 KiB
+    deep = B.workspace_size(P(T=16, D=512, DH=4096, D_out=512, E=8, top_k=2))
+    extra_h = 32 * (4096 - 1024) * 2  # the larger hidden activations
+    assert deep - small - extra_h == 24 * tile
+    # fp32 layers never split
+    f32 = B.workspace_size(P(T=16, D=512, DH=4096, D_out=512, E=8, top_k=2, dtype="f32"))
+    assert f32 < deep
+    # the Mixtral-shaped layer reserves all 256 slots (64 MiB)
+    big = B.workspace_size(P(T=4096, D=4096, DH=14336, D_out=4096, E=8, top_k=2))
+    assert big >= 8192 * (14336 + 4096) * 2 + 256 * tile
+
+
 def _call(fn, p, *ptrs, ws_bytes=0):
     lib = B.lib()
     return getattr(lib, fn)(ctypes.byref(p.c()), *ptrs)
