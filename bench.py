@@ -43,12 +43,12 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
-                            3502768.9375, 229564.36607142858),
-    "switch_top1_cap_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
-                             224131.29464285713, 26562.66964285714),
-    "fine_grained_zipf_bf16": ("a5973ef32815a2908a0b0f75691c535d3c6b0bde8aa25db379975940964f2072",
-                               1000470.9196428572, 143433.26785714287),
+    "mixtral_swiglu_bf16": ("e5f000e6ec69633b06a28a19f4d6e9f7e4a17e2c96ab2e626ce63125b94577d1",
+                            3448633.723214286, 229562.60714285713),
+    "switch_top1_cap_bf16": ("e5f000e6ec69633b06a28a19f4d6e9f7e4a17e2c96ab2e626ce63125b94577d1",
+                             223989.17857142858, 26562.741071428572),
+    "fine_grained_zipf_bf16": ("e5f000e6ec69633b06a28a19f4d6e9f7e4a17e2c96ab2e626ce63125b94577d1",
+                               997459.5535714285, 143432.85714285713),
 }
 
 
