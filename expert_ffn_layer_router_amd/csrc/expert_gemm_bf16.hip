@@ -34,8 +34,10 @@
 //  * Epilogue: lanes l and l ^ 1 hold adjacent columns; one swap per pair of rows lets each
 //    lane convert two outputs with one v_cvt_pk_bf16_f32 and store them in 4 bytes.
 //  * Tile order: expert by expert, in blocks of (that expert's M-tiles) x 8 column tiles with
-//    the M-tiles fastest; each XCD (blocks b with the same b % 8) works through a contiguous
-//    eighth of the real tiles, so the tiles it runs at once share rows and columns in its L2.
+//    the M-tiles fastest (when the launch's split-K tail can hold every expert's short last
+//    tile, those go last and make up the tail); each XCD (blocks b with the same b % 8) works
+//    through a contiguous eighth of the real tiles, so the tiles it runs at once share rows and
+//    columns in its L2.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -287,6 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   __shared__ __align__(16) char sbuf[kNBuf * kBuf];
   __shared__ int s_unit[2];  // work positions of later units, by unit parity
   __shared__ int s_last;
+  __shared__ int s_scan[kThreads / kWave][kScanWords];  // each wave's tile scan
 
   // One block per CU (gridDim.x blocks: a multiple of 8, at most kSplitSlots). Tiles that fill
   // whole waves of the blocks run over all of K. When the count leaves a partial last wave of
@@ -297,10 +300,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
   // the tiles an XCD runs at once are neighbours that share rows and columns in its L2, and a
   // block that finishes early simply takes the next one.
   const int b = blockIdx.x, nblk = gridDim.x;
-  const TileScan sc = tile_scan(g.offsets, g.E, kBM, nt);
+  int total_main, total;  // tiles that are not short, all tiles (wave-uniform)
+  {
+    const TileScan sc = tile_scan(g.offsets, g.E, kBM, nt);
+    scan_store(sc, s_scan[threadIdx.x >> 6]);
+    total_main = __builtin_amdgcn_readfirstlane(sc.total_main);
+    total = __builtin_amdgcn_readfirstlane(sc.total);
+  }
   // every value that steers the loops is wave-uniform; saying so keeps them under scalar
   // control (a divergent trip count would make the compiler copy the accumulators)
-  const int total = __builtin_amdgcn_readfirstlane(sc.total);
   if (total == 0) return;
   const int nst_all = (int)(g.K / kBK);
   int full = total, r = 0, split = 1;
@@ -315,6 +323,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
       --split;
     if (split == 1) full = total;
   }
+  // Short tiles last (see tile_of) when the split tail holds all of them.
+  const bool short_last =
+      split > 1 && total - total_main <= r;
   const int xcd = b & 7, per = nblk >> 3, jb = b >> 3;
   // Work positions: q * 8 + x stands for entry q of XCD x's list (its eighth of the whole
   // tiles, or of all tiles when nothing is split); -2: no whole tile is left anywhere; -1:
@@ -383,8 +394,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     u.ks = ks;
     // M-blocks for the weight gradients (16 to 56 M-tiles a group, all whole); the forward's
     // experts have a few M-tiles, the last often ragged, and keep them in one block
-    tile_of(sc, g.offsets, kBM, nt, KG ? kTileBlockM : INT_MAX, kTileBlockN, L, u.e, u.row0,
-            u.rows, u.n_tile);
+    tile_of(scan_load(s_scan[threadIdx.x >> 6], total_main, total), g.offsets, kBM, nt,
+            KG ? kTileBlockM : INT_MAX, kTileBlockN, short_last, L, u.e, u.row0, u.rows, u.n_tile);
     u.e = __builtin_amdgcn_readfirstlane(u.e);
     u.row0 = __builtin_amdgcn_readfirstlane(u.row0);
     u.rows = __builtin_amdgcn_readfirstlane(u.rows);
