@@ -43,12 +43,12 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("e5f000e6ec69633b06a28a19f4d6e9f7e4a17e2c96ab2e626ce63125b94577d1",
-                            3448633.723214286, 229562.60714285713),
-    "switch_top1_cap_bf16": ("e5f000e6ec69633b06a28a19f4d6e9f7e4a17e2c96ab2e626ce63125b94577d1",
-                             223989.17857142858, 26562.741071428572),
-    "fine_grained_zipf_bf16": ("e5f000e6ec69633b06a28a19f4d6e9f7e4a17e2c96ab2e626ce63125b94577d1",
-                               997459.5535714285, 143432.85714285713),
+    "mixtral_swiglu_bf16": ("903f255b12cb181f0f6640fd5673b2125a9d8db2312cd8e627de55daf62b6aa7",
+                            3488240.1428571427, 229563.0),
+    "switch_top1_cap_bf16": ("903f255b12cb181f0f6640fd5673b2125a9d8db2312cd8e627de55daf62b6aa7",
+                             224151.5892857143, 26562.64285714286),
+    "fine_grained_zipf_bf16": ("903f255b12cb181f0f6640fd5673b2125a9d8db2312cd8e627de55daf62b6aa7",
+                               988840.2321428572, 143432.9642857143),
 }
 
 
