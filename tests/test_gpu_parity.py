@@ -238,17 +238,25 @@ def test_expert_ffn_stage(kind, dtype):
     assert max_abs_rel(got, ref) <= OUT_TOL[dtype]
 
 
-@pytest.mark.parametrize("kind,D,DH", [("swiglu", 4096, 4096), ("swiglu", 512, 4096),
-                                        ("relu2", 512, 4096)])
-def test_expert_ffn_designed_row_counts(kind, D, DH):
+EDGE_COUNTS = (1, 64, 65, 128, 129, 256, 257, 300)
+SHORT_TAIL_COUNTS = (256,) * 7 + (200, 64)
+
+
+@pytest.mark.parametrize("kind,D,DH,counts", [("swiglu", 4096, 4096, EDGE_COUNTS),
+                                               ("swiglu", 512, 4096, EDGE_COUNTS),
+                                               ("relu2", 512, 4096, EDGE_COUNTS),
+                                               ("swiglu", 4096, 4096, SHORT_TAIL_COUNTS)])
+def test_expert_ffn_designed_row_counts(kind, D, DH, counts):
     """Rows per expert at each edge of the bf16 GEMM's tile row layouts (1, 64, 65, 128, 129,
     256 and 257 rows, and an expert of two tiles). With D = DH = 4096 the up-projection has
-    9 x 32 = 288 tiles: a whole wave of 256 and a tail of 32 split along K. Two calls on one
-    workspace must give the same bits (the work queue and the split tickets are left ready for
-    the next call)."""
+    10 x 32 = 320 tiles: a whole wave of 256 and a tail of 64 split along K. The second layout
+    (seven experts of 256 rows, one of 200, one of 64) gives 9 x 32 = 288 tiles, whose tail of
+    32 is exactly the 64-row expert's short tiles, taken out of the expert order and split along
+    K. Two calls on one workspace must give the same bits (the work queue and the split tickets
+    are left ready for the next call)."""
     import torch
     from expert_ffn_layer_router_amd import binding as B
-    counts = [1, 64, 65, 128, 129, 256, 257, 300]
+    counts = list(counts)
     E, R = len(counts), sum(counts)
     sp = spec("mixtral_swiglu_bf16", T=R, D=D, DH=DH, E=E, top_k=1, kind=kind,
               capacity_factor=0.0)
