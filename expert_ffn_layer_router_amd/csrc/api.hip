@@ -504,7 +504,8 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
     } else if (dispatched) {
       err = launch_place_after_route(q, expert_indices, at<void>(ws, L.route), aux_loss,
                                      expert_counts, nullptr, expert_offsets, perm, slot_row,
-                                     stream, tickets, tickets ? kSplitSlots + kQueueInts : 0);
+                                     stream, tickets, tickets ? kSplitSlots + kQueueInts : 0,
+                                     importance);
     } else {
       err = launch_dispatch(q, expert_indices, x, expert_counts, expert_offsets, perm, slot_row,
                             nullptr, at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream,

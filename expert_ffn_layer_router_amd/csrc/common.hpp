@@ -99,18 +99,20 @@ hipError_t launch_route_full(const Problem& p, const void* x, const void* w_rout
 hipError_t launch_place_after_route(const Problem& p, const int32_t* idx, void* ws, float* aux,
                                     int32_t* counts_out, int32_t* uncertified,
                                     int32_t* offsets, int32_t* perm, int32_t* slot_row,
-                                    hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
+                                    hipStream_t s, int32_t* zero = nullptr, int nzero = 0,
+                                    float* importance = nullptr);
 // route_fused.hip (used through the two calls above)
 bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance);
 size_t fused_route_ws_bytes(const Problem& p);
 hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
                               const float* bias, bool renorm, int32_t* idx, float* gates,
-                              float* logits_out, void* fws, hipStream_t s);
+                              float* logits_out, void* fws, hipStream_t s,
+                              bool importance = false);
 // perm null: one block forms the loss and the counts (and the offsets, if given) only
 hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* fws, float* aux,
                               int32_t* counts_out, int32_t* uncertified, int32_t* offsets,
                               int32_t* perm, int32_t* slot_row, hipStream_t s, int32_t* zero,
-                              int nzero);
+                              int nzero, float* importance = nullptr);
 
 // Dispatch: per-block histogram + stable local ranks, scan + capacity, placement (+ copy).
 int64_t dispatch_blocks(const Problem& p);

@@ -1011,14 +1011,14 @@ hipError_t launch_route_full(const Problem& p, const void* x, const void* w_rout
   if (fused_route_applies(p, o, importance != nullptr)) {
     hipError_t err =
         launch_route_fused(p, x, w_router, bias, o.renorm, idx, gates, logits_out,
-                           fused_region(p, ws), s);
+                           fused_region(p, ws), s, importance != nullptr);
     if (err != hipSuccess) return err;
     if (dispatch_done && offsets_out) {
       *dispatch_done = true;  // the caller's launch_place_after_route finishes the loss
       return hipSuccess;
     }
     return launch_place_fused(p, idx, fused_region(p, ws), aux, counts_out, uncertified, nullptr,
-                              nullptr, nullptr, s, nullptr, 0);
+                              nullptr, nullptr, s, nullptr, 0, importance);
   }
   hipError_t err = launch_route(p, x, w_router, bias, o, idx, gates, logits_out, uncertified, ws, s);
   if (err == hipSuccess)
@@ -1029,9 +1029,9 @@ hipError_t launch_route_full(const Problem& p, const void* x, const void* w_rout
 hipError_t launch_place_after_route(const Problem& p, const int32_t* idx, void* ws, float* aux,
                                     int32_t* counts_out, int32_t* uncertified,
                                     int32_t* offsets, int32_t* perm, int32_t* slot_row,
-                                    hipStream_t s, int32_t* zero, int nzero) {
+                                    hipStream_t s, int32_t* zero, int nzero, float* importance) {
   return launch_place_fused(p, idx, fused_region(p, ws), aux, counts_out, uncertified, offsets,
-                            perm, slot_row, s, zero, nzero);
+                            perm, slot_row, s, zero, nzero, importance);
 }
 
 }  // namespace moe

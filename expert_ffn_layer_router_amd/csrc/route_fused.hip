@@ -556,6 +556,8 @@ struct ExactArgs {
   float* gates;
   float* logits_out;          // nullable
   unsigned long long* bslot;  // (blocks, E): count << kCountShift plus the 2^-40 probability sum
+  unsigned long long* islot;  // nullable: (blocks, E), the block's final gates summed per expert
+                              // in units of 2^-40 (for the importance loss)
 };
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
@@ -802,11 +804,12 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
   //    with ties to the lower index, the row softmax, gates; choice j sits in lane j % 16 of
   //    the row, slot j / 16
   const int i = col, r = g;
-  double psum[NT];
+  double psum[NT], gsum[NT];
   int cnt[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     psum[n] = 0.0;
+    gsum[n] = 0.0;
     cnt[n] = 0;
   }
   for (int q = w; q < TT / 4; q += Wv) {
@@ -876,6 +879,7 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
 #pragma unroll
     for (int n = 0; n < NT; ++n) prob[n] = ex[n] / ps;
     double gate[NT];
+    double gs_chosen = 1.0;  // the chosen exponentials' sum (renormalised gates)
     if (a.renorm) {
       // the chosen logits' exponentials are their experts' ex values (the same exp of the same
       // difference), taken from the lanes of this row that hold them
@@ -893,6 +897,7 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
         gs += gate[n];
       }
       gs = row_sum16(gs);
+      gs_chosen = gs;
 #pragma unroll
       for (int n = 0; n < NT; ++n) gate[n] /= gs;
     } else {
@@ -920,6 +925,10 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
         if (a.logits_out && j < E) a.logits_out[t * E + j] = (float)lg[n];
         psum[n] += prob[n];
         cnt[n] += sel[n] ? 1 : 0;
+        // the lane's own expert's final gate, rounded as it is stored (its choice slot holds
+        // the same quotient), for the importance sums
+        if (a.islot && sel[n])
+          gsum[n] += (double)(float)(a.renorm ? ex[n] / gs_chosen : prob[n]);
       }
     }
   }
@@ -933,10 +942,13 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
     psum[n] += __shfl_xor(psum[n], 32);
     cnt[n] += __shfl_xor(cnt[n], 16);
     cnt[n] += __shfl_xor(cnt[n], 32);
+    gsum[n] += __shfl_xor(gsum[n], 16);
+    gsum[n] += __shfl_xor(gsum[n], 32);
   }
   __syncthreads();  // the partial logits are no longer read
   double* s_ps = s_part;                        // [Wv][E]
   int32_t* s_cn = (int32_t*)(s_part + Wv * E);  // [Wv][E]
+  double* s_gs = s_part + Wv * E + Wv * E / 2;  // [Wv][E] (E % 8 == 0: 8-byte aligned)
   if (r == 0) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -944,19 +956,22 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
       if (e < E) {
         s_ps[w * E + e] = psum[n];
         s_cn[w * E + e] = cnt[n];
+        s_gs[w * E + e] = gsum[n];
       }
     }
   }
   __syncthreads();
   for (int e = tid; e < E; e += Wv * kWave) {
-    double ps = 0.0;
+    double ps = 0.0, gs = 0.0;
     int c = 0;
     for (int q = 0; q < Wv; ++q) {
       ps += s_ps[q * E + e];
       c += s_cn[q * E + e];
+      gs += s_gs[q * E + e];
     }
     a.bslot[(int64_t)blockIdx.x * E + e] =
         ((unsigned long long)c << kCountShift) + (unsigned long long)llrint(ps * kPScale);
+    if (a.islot) a.islot[(int64_t)blockIdx.x * E + e] = (unsigned long long)llrint(gs * kPScale);
   }
 }
 
@@ -978,6 +993,8 @@ struct PlaceArgs {
   int32_t* slot_row;
   int32_t* zero;         // nullable: nzero int32 cleared by block 0 (a later kernel's counters)
   int nzero;
+  const unsigned long long* islot;  // nullable: (nS, E) gate sums in units of 2^-40
+  float* importance;                // with islot: the importance loss
 };
 
 // One block per group of 256 tokens, one token per thread.
@@ -992,12 +1009,15 @@ struct PlaceArgs {
 //     earlier waves (integer OR and popcount: order-independent); with the group's rank base
 //     it is the slot's rank among all earlier tokens: kept iff rank < capacity, row =
 //     offsets[e] + rank, perm[row] = slot, slot_row[slot] = row or -1.
+// IMP: block 0 also adds the gate sums and forms the importance loss (a.islot non-null).
+template <bool IMP>
 __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
   constexpr int kW = kGroup / kWave;
   __shared__ unsigned long long s_mask[kW][kMaxExperts];
   __shared__ int s_base[kW][kMaxExperts];
   __shared__ int s_tot[kGroup], s_gb[kGroup];
   __shared__ unsigned long long s_p[kGroup];
+  __shared__ unsigned long long s_i[IMP ? kGroup : 1];  // the gate sums (block 0, IMP)
   __shared__ int s_off[kMaxExperts + 1];
   __shared__ double s_term[kW];
   __shared__ int s_wtot[kW];
@@ -1024,9 +1044,10 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
   };
   // 1. Q threads per expert, each over the groups q, q + Q, ...
   const int Q = max(1, kGroup / E);
+  const bool imp = IMP && g == 0;  // block 0 also adds the gate sums (importance loss)
   {
     int tot = 0, gb = 0;
-    unsigned long long ps = 0;
+    unsigned long long ps = 0, is = 0;
     if (tid < Q * E) {
       const int e = tid % E, q = tid / E;
       constexpr int kC = 32;  // loads in flight
@@ -1046,11 +1067,21 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
           if (gg < gend) gb += c;
           ps += v[u] & ((1ull << kCountShift) - 1ull);
         }
+        if (IMP && imp) {
+#pragma unroll
+          for (int u = 0; u < kC; ++u) {
+            const int64_t gg = g0 + (int64_t)u * Q;
+            v[u] = gg < a.nS ? a.islot[gg * E + e] : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < kC; ++u) is += v[u];
+        }
       }
     }
     s_tot[tid] = tot;
     s_gb[tid] = gb;
     s_p[tid] = ps;
+    if (IMP) s_i[tid] = is;
   }
   __syncthreads();
   // the Q partial rows of each expert (row q of expert e at q E + e), summed by halving: after
@@ -1063,6 +1094,7 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
         s_tot[tid] += s_tot[tid + h * E];
         s_gb[tid] += s_gb[tid + h * E];
         s_p[tid] += s_p[tid + h * E];
+        if (IMP && imp) s_i[tid] += s_i[tid + h * E];
       }
       __syncthreads();
     }
@@ -1103,6 +1135,21 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
       for (int q = 0; q < kW; ++q) sum += s_term[q];
       *a.aux = (float)((double)E * sum);
       if (a.uncertified) *a.uncertified = a.nflag ? *a.nflag : 0;
+    }
+    if (IMP && imp && wv == 0) {
+      // the importance loss (E <= 64: one wave): each expert's gate total (an integer sum of
+      // the slots above, so in no particular order), then the squared coefficient of
+      // variation of the E totals (population variance over the squared mean), by exchanges
+      // in a fixed order
+      const double ge = lane < E ? (double)s_i[lane] / kPScale : 0.0;
+      double m = ge;
+#pragma unroll
+      for (int d = kWave / 2; d >= 1; d >>= 1) m += __shfl_xor(m, d, kWave);
+      m /= (double)E;
+      double v = lane < E ? (ge - m) * (ge - m) : 0.0;
+#pragma unroll
+      for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+      if (lane == 0) *a.importance = m > 0.0 ? (float)((v / (double)E) / (m * m)) : 0.f;
     }
     if (a.offsets)
       for (int e = tid; e <= E; e += kGroup) a.offsets[e] = s_off[e];
@@ -1256,9 +1303,11 @@ hipError_t launch_exact_inst(const ExactShape& f, const ExactArgs& a, hipStream_
   return hipGetLastError();
 }
 
-size_t exact_ws_bytes(const Problem& p) {
+// the probability-sum slots, then the gate-sum slots (the importance loss), each (blocks, E)
+size_t exact_slot_bytes(const Problem& p) {
   return (((size_t)exact_shape(p).nblk * p.E * 8) + 255) & ~size_t(255);
 }
+size_t exact_ws_bytes(const Problem& p) { return 2 * exact_slot_bytes(p); }
 
 template <int PPW, int EPL>
 hipError_t launch_fused_inst(const FusedShape& f, const FusedArgs& a, unsigned nblk,
@@ -1279,8 +1328,9 @@ hipError_t launch_fused_inst(const FusedShape& f, const FusedArgs& a, unsigned n
 }  // namespace
 
 bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance) {
-  if (p.dtype != MOE_BF16 || o.w_noise || importance) return false;
-  if (exact_route_shape(p)) return true;  // either gate rule
+  if (p.dtype != MOE_BF16 || o.w_noise) return false;
+  if (exact_route_shape(p)) return true;  // either gate rule, with or without importance
+  if (importance) return false;
   if (!o.renorm) return false;
   if (p.T <= 0 || p.D % 128 != 0 || p.D > 8192 || p.E > kMaxExperts) return false;
   if (p.T >= (int64_t)1 << 23) return false;  // the 2^-40 probability sums stay below 2^63
@@ -1296,7 +1346,7 @@ size_t fused_route_ws_bytes(const Problem& p) {
 
 hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
                               const float* bias, bool renorm, int32_t* idx, float* gates,
-                              float* logits_out, void* fws, hipStream_t s) {
+                              float* logits_out, void* fws, hipStream_t s, bool importance) {
   if (exact_route_shape(p)) {
     const ExactShape f = exact_shape(p);
     ExactArgs a{};
@@ -1314,6 +1364,7 @@ hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_rou
     a.gates = gates;
     a.logits_out = logits_out;
     a.bslot = (unsigned long long*)fws;
+    a.islot = importance ? (unsigned long long*)((char*)fws + exact_slot_bytes(p)) : nullptr;
     switch (f.NT) {
       case 1: return p.E == 8 ? launch_exact_inst<1, true>(f, a, s) : launch_exact_inst<1>(f, a, s);
       case 2: return launch_exact_inst<2>(f, a, s);
@@ -1366,7 +1417,7 @@ hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_rou
 hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* fws, float* aux,
                               int32_t* counts_out, int32_t* uncertified, int32_t* offsets,
                               int32_t* perm, int32_t* slot_row, hipStream_t s, int32_t* zero,
-                              int nzero) {
+                              int nzero, float* importance) {
   const FusedLayout L = fused_layout(p);
   PlaceArgs a{};
   a.T = p.T;
@@ -1381,6 +1432,10 @@ hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* 
     a.nS = f.nblk;
     a.gslot = (const unsigned long long*)fws;
     a.nflag = nullptr;
+    if (importance) {  // the gate sums follow the probability sums
+      a.islot = (const unsigned long long*)((const char*)fws + exact_slot_bytes(p));
+      a.importance = importance;
+    }
   } else {
     a.spg = 1;
     a.nS = L.nG;
@@ -1396,7 +1451,10 @@ hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* 
   a.zero = zero;
   a.nzero = nzero;
   const unsigned grid = perm ? (unsigned)L.nG : 1u;
-  hipLaunchKernelGGL(place_fused_kernel, dim3(grid), dim3(kGroup), 0, s, a);
+  if (a.islot)
+    hipLaunchKernelGGL(place_fused_kernel<true>, dim3(grid), dim3(kGroup), 0, s, a);
+  else
+    hipLaunchKernelGGL(place_fused_kernel<false>, dim3(grid), dim3(kGroup), 0, s, a);
   return hipGetLastError();
 }
 

@@ -178,7 +178,34 @@ def test_padded_forward(name):
     _say(f"  cap {cap}, padded rows {sp.E * cap}, kept {r['offsets'][-1]}, out {err:.3e}")
     assert err <= OUT_TOL[sp.dtype]
     compact = run_forward_ex(I)
+    check_route(compact, r)
     assert max_abs_rel(g["out"], compact["out"]) <= OUT_TOL[sp.dtype]
+
+
+IMPORTANCE_CASES = {
+    "swiglu_e8_k2": spec("mixtral_swiglu_bf16", T=700, D=256, DH=384, E=8),
+    "swiglu_zipf_cap": spec("fine_grained_zipf_bf16", T=1000, D=512, DH=320),
+    "relu_top1_cap": spec("switch_top1_cap_bf16", T=1500, D=256, DH=512),
+    "relu_e24_k3": spec("switch_top1_cap_bf16", T=901, D=192, DH=256, E=24, top_k=3,
+                        capacity_factor=0.0),
+}
+
+
+@pytest.mark.parametrize("renormalise", [True, False], ids=["renorm", "probs"])
+@pytest.mark.parametrize("name", sorted(IMPORTANCE_CASES))
+def test_importance_loss_without_noise(name, renormalise):
+    """The importance loss (Sparsely-Gated Layer page, the importance loss: CV^2 of the
+    per-expert gate sums) on the plain router, compact layout, with and without renormalised
+    gates, at shapes the single-launch exact route takes (bf16, 8 to 64 experts): routing,
+    placement and outputs as for the plain layer, the loss within its bar."""
+    sp = IMPORTANCE_CASES[name]
+    _say(f"[gpu] importance without noise {name} renormalise={renormalise} {sp}")
+    I = make_inputs(sp, seed=21)
+    g, r = run_forward_ex(I, renormalise=renormalise), run_oracle_ex(I, renormalise=renormalise)
+    check_route(g, r)
+    assert np.array_equal(g["expert_offsets"], r["offsets"])
+    assert np.array_equal(g["slot_row"], r["slot_row"])
+    assert max_abs_rel(g["out"], r["output"]) <= OUT_TOL[sp.dtype]
 
 
 @pytest.mark.parametrize("name", ["relu_top1_cap", "swiglu_zipf_cap2", "relu_f32_cap"])
