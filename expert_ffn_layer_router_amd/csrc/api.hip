@@ -68,10 +68,15 @@ struct Layout {
   size_t gsplit, gctr;  // bf16 GEMM: K-split partial tiles; K-split tickets + work queue
   int64_t nsplit;       // K-split partial tiles reserved (what the layer's GEMMs can use)
   size_t perm;          // moe_forward's own permutation, (rows) int32
-  size_t xpad;          // padded layout: the padded copy of x, (rows, D)
+  size_t xpad;          // padded layout: the padded copy of x, (rows, D), or one zero row
   size_t ybuf;          // moe_forward's expert outputs, (rows, D_out)
   size_t route_end, dispatch_end, ffn_end, total;
 };
+
+// The padded layout's first GEMM gathers x through the padded permutation, its empty rows
+// reading one zero row, where the 256 x 256 bf16 kernel runs it (bf16, D % 128 == 0); other
+// layers read a padded copy of x.
+bool padded_gather(const Problem& q) { return q.dtype == MOE_BF16 && q.D % 128 == 0 && q.T > 0; }
 
 Layout layout_of(const Problem& q, bool padded = false) {
   Layout L;
@@ -105,7 +110,7 @@ Layout layout_of(const Problem& q, bool padded = false) {
   L.gctr = take(split ? (size_t)(kSplitSlots + kQueueInts) * sizeof(int32_t) : 0);
   L.ffn_end = off;
   L.perm = take(rows * sizeof(int32_t));
-  L.xpad = take(padded ? rows * (size_t)q.D * es : 0);
+  L.xpad = take(padded ? (padded_gather(q) ? 1 : rows) * (size_t)q.D * es : 0);
   L.ybuf = take(rows * (size_t)q.D_out * es);
   L.total = off;
   return L;
@@ -151,7 +156,7 @@ hipEvent_t event_at(hipEvent_t* ev, int i) { return ev ? ev[i] : nullptr; }
 hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, const int32_t* offsets,
                        const void* w1, const void* w3, const void* w2, void* hbuf, void* y,
                        void* ws, const Layout& Lw, bool tickets_zeroed, hipStream_t s,
-                       hipEvent_t* ev) {
+                       hipEvent_t* ev, const void* a_zero = nullptr) {
   const int64_t max_rows = Lw.rows;  // upper bound of offsets[E]
   float* split_ws = nullptr;
   int32_t* split_ctr = nullptr;
@@ -181,6 +186,7 @@ hipError_t run_experts(const Problem& q, const void* A, const int32_t* gather, c
   g.lda = q.D;
   g.a_gather = gather;
   g.gather_div = q.top_k;
+  g.a_zero = a_zero;
   g.offsets = offsets;
   g.E = q.E;
   g.max_rows = max_rows;
@@ -489,18 +495,23 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
   // the dispatch scan also zeroes the GEMMs' K-split tickets and work queue
   int32_t* tickets = (q.dtype == MOE_BF16 && q.T > 0) ? at<int32_t>(ws, L.gctr) : nullptr;
   const void* A = x;
+  const void* a_zero = nullptr;
   const int32_t* gather = perm;
   const int32_t* offsets = expert_offsets;
   if (err == hipSuccess) {
     if (padded) {
-      // compact offsets into the workspace, the batch starts into expert_offsets, and a
-      // padded copy of x that the first GEMM reads row by row
+      // compact offsets into the workspace and the batch starts into expert_offsets; then
+      // either the first GEMM gathers x through the padded permutation (its empty rows, -1,
+      // read a zero row), or a padded copy of x is written for it to read row by row
+      const bool pg = padded_gather(q);
       err = launch_dispatch(q, expert_indices, x, expert_counts, at<int32_t>(ws, L.offc), perm,
-                            slot_row, at<void>(ws, L.xpad), at<int32_t>(ws, L.blkc),
-                            at<int32_t>(ws, L.lrank), stream, tickets,
-                            tickets ? kSplitSlots + kQueueInts : 0, expert_offsets);
-      A = at<void>(ws, L.xpad);
-      gather = nullptr;
+                            slot_row, pg ? nullptr : at<void>(ws, L.xpad),
+                            at<int32_t>(ws, L.blkc), at<int32_t>(ws, L.lrank), stream, tickets,
+                            tickets ? kSplitSlots + kQueueInts : 0, expert_offsets,
+                            pg ? at<void>(ws, L.xpad) : nullptr);
+      A = pg ? x : at<void>(ws, L.xpad);
+      gather = pg ? perm : nullptr;
+      a_zero = pg ? at<void>(ws, L.xpad) : nullptr;
     } else if (dispatched) {
       err = launch_place_after_route(q, expert_indices, at<void>(ws, L.route), aux_loss,
                                      expert_counts, nullptr, expert_offsets, perm, slot_row,
@@ -515,7 +526,7 @@ moe_status moe_forward_ex(const moe_problem* p, const moe_options* opts, const v
   mark(ev, 2 * MOE_STAGE_DISPATCH + 1, stream);
   if (err == hipSuccess)
     err = run_experts(q, A, gather, offsets, w1, w3, w2, at<void>(ws, L.hbuf),
-                      at<void>(ws, L.ybuf), ws, L, tickets != nullptr, stream, ev);
+                      at<void>(ws, L.ybuf), ws, L, tickets != nullptr, stream, ev, a_zero);
   mark(ev, 2 * MOE_STAGE_COMBINE, stream);
   if (err == hipSuccess) err = launch_combine(q, at<void>(ws, L.ybuf), slot_row, gates, out, stream);
   mark(ev, 2 * MOE_STAGE_COMBINE + 1, stream);

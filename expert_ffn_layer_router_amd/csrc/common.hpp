@@ -126,7 +126,7 @@ hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x,
                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* slot_row,
                            void* x_perm, int32_t* blk_counts, int32_t* local_rank,
                            hipStream_t s, int32_t* zero = nullptr, int nzero = 0,
-                           int32_t* pad_offsets = nullptr);
+                           int32_t* pad_offsets = nullptr, void* zero_row = nullptr);
 
 // Backward of the layer (backward.hip): workspace bytes and the launch sequence.
 // A training forward's saved state (byte offsets in the caller's buffer, 256-byte aligned):
@@ -163,6 +163,9 @@ struct GroupedGemm {
   int64_t lda;
   const int32_t* a_gather;  // optional: row r of A is A[a_gather[r] / gather_div]
   int gather_div;
+  // optional (bf16 256 x 256 kernel only): rows whose a_gather entry is negative read this
+  // row of lda zeros instead (the empty rows of capacity-padded batches)
+  const void* a_zero;
   const void* B0;           // (E, K, N) row-major
   const void* B1;           // second (E, K, N) for SwiGLU, else null
   void* C;                  // (rows, N) row-major, ldc = N

@@ -144,14 +144,22 @@ __global__ __launch_bounds__(kThreads) void dispatch_place_kernel(
 
 // Empty rows of the padded batches, one wave per row: row i of batch e is empty when i is not
 // below kept_e = offsets[e + 1] - offsets[e] (the compact offsets of the scan): perm = -1 and,
-// with a copy, a zero row. Thread 0 of block 0 also writes the batch starts e * capacity.
+// with a copy, a zero row. Block 0 also writes the batch starts e * capacity and, without a
+// copy, clears `zero_row` (one row of x: the GEMM reads it for the empty rows).
 template <typename U>
 __global__ __launch_bounds__(kThreads) void dispatch_pad_fill_kernel(
     int E, int64_t capacity, const int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    U* __restrict__ x_pad, int64_t row_units, int32_t* __restrict__ pad_offsets) {
-  if (blockIdx.x == 0)
+    U* __restrict__ x_pad, int64_t row_units, int32_t* __restrict__ pad_offsets,
+    U* __restrict__ zero_row) {
+  if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= E; i += kThreads)
       pad_offsets[i] = (int32_t)((int64_t)i * capacity);
+    if (zero_row) {
+      U zero;
+      __builtin_memset(&zero, 0, sizeof(U));
+      for (int64_t c = threadIdx.x; c < row_units; c += kThreads) zero_row[c] = zero;
+    }
+  }
   const int64_t row = (int64_t)blockIdx.x * kWaves + wave_id();
   if (row >= (int64_t)E * capacity) return;
   const int e = (int)(row / capacity);
@@ -174,7 +182,7 @@ int64_t dispatch_blocks(const Problem& p) {
 hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* perm, int32_t* slot_row, void* x_perm,
                            int32_t* blk_counts, int32_t* local_rank, hipStream_t s,
-                           int32_t* zero, int nzero, int32_t* pad_offsets) {
+                           int32_t* zero, int nzero, int32_t* pad_offsets, void* zero_row) {
   const bool padded = pad_offsets != nullptr;
   const int64_t nblk = dispatch_blocks(p);
   if (nblk > 0) {
@@ -209,15 +217,16 @@ hipError_t launch_dispatch(const Problem& p, const int32_t* idx, const void* x, 
     const unsigned grid = (unsigned)std::max<int64_t>(1, (rows + kWaves - 1) / kWaves);
     if (unit == 16)
       hipLaunchKernelGGL(dispatch_pad_fill_kernel<uint4>, dim3(grid), dim3(kThreads), 0, s, p.E,
-                         p.capacity, offsets, perm, (uint4*)x_perm, row_bytes / 16, pad_offsets);
+                         p.capacity, offsets, perm, (uint4*)x_perm, row_bytes / 16, pad_offsets,
+                         (uint4*)zero_row);
     else if (unit == 4)
       hipLaunchKernelGGL(dispatch_pad_fill_kernel<uint32_t>, dim3(grid), dim3(kThreads), 0, s,
                          p.E, p.capacity, offsets, perm, (uint32_t*)x_perm, row_bytes / 4,
-                         pad_offsets);
+                         pad_offsets, (uint32_t*)zero_row);
     else
       hipLaunchKernelGGL(dispatch_pad_fill_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s,
                          p.E, p.capacity, offsets, perm, (uint16_t*)x_perm, row_bytes / 2,
-                         pad_offsets);
+                         pad_offsets, (uint16_t*)zero_row);
   }
   return hipGetLastError();
 }

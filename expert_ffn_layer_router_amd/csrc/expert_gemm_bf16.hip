@@ -426,10 +426,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
     for (int j = 0; j < 4; ++j) {
       const int rr = 16 * (4 * wv + j) + (lane >> 2);
       const int64_t gr = u.row0 + (rr < u.rows ? rr : 0);
-      if (KG)  // row m of the group's transposed operand
+      if (KG) {  // row m of the group's transposed operand
         src[j] = (int32_t)(gr - (int64_t)u.e * g.group_rows);
-      else
-        src[j] = g.a_gather ? g.a_gather[gr] / g.gather_div : (int32_t)gr;
+      } else if (g.a_gather) {  // a negative entry: an empty padded row (the zero row)
+        const int32_t v = g.a_gather[gr];
+        src[j] = v < 0 ? -1 : v / g.gather_div;
+      } else {
+        src[j] = (int32_t)gr;
+      }
     }
   };
   auto make_loader = [&](const Unit& u, const int32_t (&src)[4]) {
@@ -437,7 +441,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(const Groupe
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = (lane & 3) ^ ((lane >> 4) & 3);
-      ld.a[j] = (const char*)g.A + ((int64_t)src[j] * g.lda + u.acol + 8 * c) * 2;
+      ld.a[j] = (src[j] < 0 && g.a_zero)
+                    ? (const char*)g.a_zero + (u.acol + 8 * c) * 2
+                    : (const char*)g.A + ((int64_t)src[j] * g.lda + u.acol + 8 * c) * 2;
     }
     // B: instruction j of wave w fills K-rows 8w + 2j + lane / 32; position lane % 32 of the
     // K-row holds logical chunk (lane % 32) ^ (4 (K-row % 4)), K-row % 4 = 2 (j % 2) + lane / 32.
