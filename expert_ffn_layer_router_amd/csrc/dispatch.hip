@@ -2,7 +2,7 @@
 // into expert-contiguous order, and the optional capacity with overflow dropped in token
 // order. (ML Grind "Mixture-of-Experts (MoE) Routing", Algorithm step 3 and Follow-up;
 // "Mixture of Experts: the Sparsely-Gated Layer", "Switch: top-1, one loss, and a rate
-// limit" and its moe_forward, first come, first served.)
+// limit" and its moe_forward: earlier tokens are kept before later ones.)
 //
 // Three kernels, all deterministic (no order-dependent atomics):
 //  1. rank:  blocks of 256 tokens. Each wave builds, in LDS, one 64-bit lane mask per

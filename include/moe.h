@@ -142,8 +142,8 @@ moe_status moe_route_noalloc(const moe_problem* p, const void* x, const void* w_
                              float* aux_loss, int32_t* expert_counts, float* logits_out,
                              int32_t* uncertified, hipStream_t stream);
 
-/* Dispatch (ML Grind, Algorithm step 3 "gather the tokens routed to it"; capacity as in
- * the Sparsely-Gated Layer page's moe_forward, first come, first served).
+/* Dispatch (ML Grind, Algorithm step 3: each expert's tokens collected; capacity as in the
+ * Sparsely-Gated Layer page's moe_forward, earlier tokens kept before later ones).
  *   expert_indices (T, top_k) int32 in [0, E) with distinct entries per row (unchecked);
  *   x (T, D) in p->dtype, or NULL when x_perm is NULL.
  *   Outputs: expert_counts (E) int32 before capacity; expert_offsets (E+1) int32, the
@@ -253,7 +253,7 @@ moe_status moe_route_ex(const moe_problem* p, const moe_options* opts, const voi
                         hipStream_t stream);
 
 /* Dispatch into the capacity-padded layout (Sparsely-Gated Layer page, "Switch: top-1, one
- * loss, and a rate limit"; first come, first served as in moe_dispatch). Needs
+ * loss, and a rate limit"; earlier tokens kept first, as in moe_dispatch). Needs
  * capacity_factor > 0 (else MOE_ERR_INVALID_ARG); with capacity 0 every slot is dropped.
  *   expert_indices, x as in moe_dispatch. Outputs: expert_counts (E) int32 before capacity;
  *   expert_offsets (E+1) int32, the batch starts e * capacity (what moe_expert_ffn_ex takes);
