@@ -43,12 +43,12 @@ FETCH_PER_BYTE = 0.500
 WRITE_PER_BYTE = 1.000
 MEASURED_TRAFFIC = {
     # config: (sha256 of GEMM_SOURCES, FETCH_SIZE KiB per launch, WRITE_SIZE KiB per launch)
-    "mixtral_swiglu_bf16": ("903f255b12cb181f0f6640fd5673b2125a9d8db2312cd8e627de55daf62b6aa7",
-                            3488240.1428571427, 229563.0),
-    "switch_top1_cap_bf16": ("903f255b12cb181f0f6640fd5673b2125a9d8db2312cd8e627de55daf62b6aa7",
-                             224151.5892857143, 26562.64285714286),
-    "fine_grained_zipf_bf16": ("903f255b12cb181f0f6640fd5673b2125a9d8db2312cd8e627de55daf62b6aa7",
-                               988840.2321428572, 143432.9642857143),
+    "mixtral_swiglu_bf16": ("24d43825e0129a9bca595627fdc1e58621428b9200f9e57bb1a0e837ee2aa0dd",
+                            3467390.5803571427, 229562.7142857143),
+    "switch_top1_cap_bf16": ("24d43825e0129a9bca595627fdc1e58621428b9200f9e57bb1a0e837ee2aa0dd",
+                             224213.6517857143, 26562.758928571428),
+    "fine_grained_zipf_bf16": ("24d43825e0129a9bca595627fdc1e58621428b9200f9e57bb1a0e837ee2aa0dd",
+                               1007214.1339285715, 143432.9107142857),
 }
 
 
