@@ -107,7 +107,8 @@ size_t fused_route_ws_bytes(const Problem& p);
 hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
                               const float* bias, bool renorm, int32_t* idx, float* gates,
                               float* logits_out, void* fws, hipStream_t s,
-                              bool importance = false);
+                              bool importance = false, const void* w_noise = nullptr,
+                              const float* noise = nullptr);
 // perm null: one block forms the loss and the counts (and the offsets, if given) only
 hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* fws, float* aux,
                               int32_t* counts_out, int32_t* uncertified, int32_t* offsets,

@@ -1011,7 +1011,7 @@ hipError_t launch_route_full(const Problem& p, const void* x, const void* w_rout
   if (fused_route_applies(p, o, importance != nullptr)) {
     hipError_t err =
         launch_route_fused(p, x, w_router, bias, o.renorm, idx, gates, logits_out,
-                           fused_region(p, ws), s, importance != nullptr);
+                           fused_region(p, ws), s, importance != nullptr, o.w_noise, o.noise);
     if (err != hipSuccess) return err;
     if (dispatch_done && offsets_out) {
       *dispatch_done = true;  // the caller's launch_place_after_route finishes the loss

@@ -548,9 +548,12 @@ constexpr int kMaxKP = 16;  // K-parts of an M-tile at most (waves a block / M-t
 struct ExactArgs {
   int64_t T, D;
   int E, k, MT, KP;
+  int Ec;  // router columns computed: E, or 2 E with the noise router's E columns after them
   bool renorm;
   const uint16_t* x;
   const uint16_t* w;
+  const uint16_t* wn;  // nullable: the noise router (D, E)
+  const float* noise;  // with wn: the standard-normal draw (T, E)
   const float* bias;
   int32_t* idx;
   float* gates;
@@ -705,11 +708,16 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
     uint32_t aoff[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) aoff[h] = 16u * (uint32_t)(8 * col + ((4 * h + g) ^ (col & 7)));
+    // router column c < E is W[:, c], E <= c < Ec the noise router's column c - E (both
+    // matrices are D x E, so a chunk of 64 rows spans the same bytes of either)
     const char* bsrc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int cg = 16 * n + 8 * (lane & 1);
-      bsrc[n] = (const char*)(a.w + (int64_t)(lane >> 1) * E + (cg < E ? cg : 0));
+      const int64_t ro = (int64_t)(lane >> 1) * E;
+      bsrc[n] = cg < E       ? (const char*)(a.w + ro + cg)
+                : cg < a.Ec ? (const char*)(a.wn + ro + (cg - E))
+                             : (const char*)(a.w + ro);
     }
     if (E8) bsrc[0] = (const char*)(a.w + (int64_t)lane * 8);  // row lane of the chunk's 64
     const int64_t brow_bytes = 64 * (int64_t)E * 2;  // one chunk of router rows
@@ -822,7 +830,7 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
     for (int n = 0; n < NT; ++n) {
       const int e = 16 * n + i;
       double v = 0.0;
-      if (e < E) {
+      if (e < a.Ec) {
         // every K-part read first (KP <= kMaxKP), then added in order
         double pv[kMaxKP];
 #pragma unroll
@@ -831,9 +839,30 @@ __global__ __launch_bounds__(exact_waves<NT>() * kWave) void route_exact_kernel(
 #pragma unroll
         for (int p = 0; p < kMaxKP; ++p)
           if (p < KP) v += pv[p];
-        if (a.bias) v += (double)bias_n[n];
+        if (a.bias) v += (double)bias_n[n];  // 0 past column E
       }
       lg[n] = v;
+    }
+    if (a.wn) {
+      // noisy logits: expert e's logit plus noise[t, e] softplus(column E + e), that column
+      // fetched from the lane of this row that holds it (every addend taken before any lg
+      // changes; the columns past E keep their values and take no further part)
+      const int64_t tc = valid ? t : T - 1;
+      double add[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int e = 16 * n + i, ce = e + E;
+        const int src = (lane & ~15) | (ce & 15);
+        double z = 0.0;
+#pragma unroll
+        for (int n2 = 0; n2 < NT; ++n2) {
+          const double c = __shfl(lg[n2], src);
+          if ((ce >> 4) == n2) z = c;
+        }
+        add[n] = e < E ? (double)a.noise[tc * E + e] * (fmax(z, 0.0) + log1p(exp(-fabs(z)))) : 0.0;
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) lg[n] += add[n];
     }
     bool sel[NT];
     double my_v[NT];
@@ -1262,9 +1291,11 @@ bool exact_route_shape(const Problem& p) {
          p.D >= 64 && p.D % 64 == 0 && p.T > 0 && p.T < ((int64_t)1 << 23);
 }
 
-ExactShape exact_shape(const Problem& p) {
+// cols: the router columns computed (E, or 2 E with router noise). MT, and so the block count,
+// does not depend on it (MT <= 4 <= Wv).
+ExactShape exact_shape(const Problem& p, int cols = 0) {
   ExactShape f{};
-  f.NT = (p.E + 15) / 16;
+  f.NT = ((cols > 0 ? cols : p.E) + 15) / 16;
   f.Wv = f.NT == 1 ? 16 : f.NT == 2 ? 8 : 4;
   f.MT = 1;
   while (f.MT < 4 && f.MT < f.Wv && (p.T + kXT * f.MT - 1) / (kXT * f.MT) > 512) f.MT *= 2;
@@ -1328,7 +1359,9 @@ hipError_t launch_fused_inst(const FusedShape& f, const FusedArgs& a, unsigned n
 }  // namespace
 
 bool fused_route_applies(const Problem& p, const RouteOpts& o, bool importance) {
-  if (p.dtype != MOE_BF16 || o.w_noise) return false;
+  if (p.dtype != MOE_BF16) return false;
+  // router noise: the noise router's E columns beside the E logit columns, 2 E <= 64
+  if (o.w_noise) return exact_route_shape(p) && 2 * p.E <= kMaxExpertsExact;
   if (exact_route_shape(p)) return true;  // either gate rule, with or without importance
   if (importance) return false;
   if (!o.renorm) return false;
@@ -1346,9 +1379,11 @@ size_t fused_route_ws_bytes(const Problem& p) {
 
 hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_router,
                               const float* bias, bool renorm, int32_t* idx, float* gates,
-                              float* logits_out, void* fws, hipStream_t s, bool importance) {
+                              float* logits_out, void* fws, hipStream_t s, bool importance,
+                              const void* w_noise, const float* noise) {
   if (exact_route_shape(p)) {
-    const ExactShape f = exact_shape(p);
+    const bool nz = w_noise != nullptr;
+    const ExactShape f = exact_shape(p, nz ? 2 * p.E : p.E);
     ExactArgs a{};
     a.T = p.T;
     a.D = p.D;
@@ -1357,8 +1392,11 @@ hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_rou
     a.MT = f.MT;
     a.KP = f.KP;
     a.renorm = renorm;
+    a.Ec = nz ? 2 * p.E : p.E;
     a.x = (const uint16_t*)x;
     a.w = (const uint16_t*)w_router;
+    a.wn = (const uint16_t*)w_noise;
+    a.noise = nz ? noise : nullptr;
     a.bias = bias;
     a.idx = idx;
     a.gates = gates;
@@ -1366,7 +1404,8 @@ hipError_t launch_route_fused(const Problem& p, const void* x, const void* w_rou
     a.bslot = (unsigned long long*)fws;
     a.islot = importance ? (unsigned long long*)((char*)fws + exact_slot_bytes(p)) : nullptr;
     switch (f.NT) {
-      case 1: return p.E == 8 ? launch_exact_inst<1, true>(f, a, s) : launch_exact_inst<1>(f, a, s);
+      case 1:
+        return p.E == 8 && !nz ? launch_exact_inst<1, true>(f, a, s) : launch_exact_inst<1>(f, a, s);
       case 2: return launch_exact_inst<2>(f, a, s);
       case 3: return launch_exact_inst<3>(f, a, s);
       default: return launch_exact_inst<4>(f, a, s);

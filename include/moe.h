@@ -112,8 +112,9 @@ size_t moe_workspace_size(const moe_problem* p);
  *   uncertified (1) int32, or NULL: the number of tokens whose top-k order the fast bf16
  *   logits could not certify and that were therefore recomputed in float64. 0 wherever every
  *   logit is already exact to float64 rounding: MOE_F32, and MOE_BF16 with 8 <= E <= 64,
- *   E % 8 == 0, D % 64 == 0 and no router noise (float64 matrix-core sums of the exact
- *   products of the bf16 inputs).
+ *   E % 8 == 0, D % 64 == 0 (float64 matrix-core sums of the exact products of the bf16
+ *   inputs); with router noise (moe_route_ex) where also E <= 32, the noise router's E columns
+ *   then summed beside the logits' in the same pass.
  *   With T = 0, aux_loss is 0 and expert_counts are zeros. */
 moe_status moe_route(const moe_problem* p, const void* x, const void* w_router,
                      const float* router_bias, int32_t* expert_indices, float* gates,

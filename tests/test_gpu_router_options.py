@@ -82,7 +82,20 @@ NOISY_CASES = {
     "relu_f32_ragged": spec("small_relu_f32", T=333, D=40, DH=70, E=5, top_k=3,
                             capacity_factor=1.3),
     "swiglu_f32": spec("small_relu_f32", T=50, D=12, DH=20, E=6, top_k=2, kind="swiglu"),
+    # 2 E router columns (logits, then the noise router's) in 2, 3 and 4 tiles of 16 on the
+    # exact float64 route, ragged token counts
+    "swiglu_e16_k4": spec("mixtral_swiglu_bf16", T=909, D=320, DH=256, E=16, top_k=4),
+    "swiglu_e24_k3_cap": spec("fine_grained_zipf_bf16", T=611, D=128, DH=192, E=24, top_k=3,
+                              capacity_factor=1.5),
+    "relu_e32_top1_cap": spec("switch_top1_cap_bf16", T=517, D=192, DH=128, E=32),
 }
+
+
+def _exact_noisy_route(sp) -> bool:
+    """bf16 layers whose 2 E router columns (the logits' and the noise router's) fit the exact
+    float64 route's 64 (E a multiple of 8): every noisy logit exact to float64 rounding, no
+    token recomputed."""
+    return sp.dtype == "bf16" and 8 <= sp.E <= 32 and sp.E % 8 == 0 and sp.D % 64 == 0
 
 
 @pytest.mark.parametrize("renormalise", [True, False], ids=["renorm", "probs"])
@@ -288,7 +301,9 @@ def test_noisy_route_full_size(case):
     assert rel_err(to_host(aux)[0], oracle.switch_aux_loss(ridx, probs, sp.E)) <= AUX_TOL
     c = oracle.importance_loss(ridx, rg, sp.E)
     assert abs(float(imp.cpu()[0]) - c) <= importance_tol(c)
-    if not renorm:
+    if _exact_noisy_route(sp):
+        assert int(unc.cpu()[0]) == 0
+    elif not renorm:
         assert int(unc.cpu()[0]) == sp.T
 
 
