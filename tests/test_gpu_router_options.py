@@ -116,6 +116,38 @@ def test_noisy_router_forward(name, renormalise):
         assert (g["gates"].sum(axis=1) <= 1.0 + 1e-6).all()
 
 
+@pytest.mark.parametrize("name", sorted(n for n, c in NOISY_CASES.items()
+                                         if c.dtype == "f32" or _exact_noisy_route(c)))
+def test_noisy_route_exports_noisy_logits(name):
+    """moe_route_ex's logits_out holds the noisy logits (the ones the top-k, probabilities and
+    gates use), as the float32 rounding of the oracle's float64 values: on the exact float64
+    route and on the float32 layers every noisy logit is exact to float64 rounding."""
+    import torch
+    from expert_ffn_layer_router_amd import binding as B
+    sp = NOISY_CASES[name]
+    _say(f"[gpu] noisy logits {name} {sp}")
+    I = make_inputs(sp, seed=13)
+    N = make_router_noise(sp, seed=13)
+    p = B.Problem.from_spec(sp)
+    o = _options(B, N, True, False, None)
+    ws = B.alloc_workspace(p, o=o)
+    T, k, E = sp.T, sp.top_k, sp.E
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    aux = torch.empty(1, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    logits = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    unc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    B.moe_route_ex(p, o, to_dev(I.x), to_dev(I.w_router), to_dev(I.bias), idx, gates, aux,
+                   counts, logits, unc, ws)
+    torch.cuda.synchronize()
+    ref = oracle.noisy_router_logits(I.values("x"), I.values("w_router"), I.bias,
+                                     N.w_values(), N.noise)
+    assert max_abs_rel(to_host(logits), ref) <= 1e-6
+    assert np.array_equal(to_host(idx), oracle.top_k_sorted(ref, k))
+    assert int(unc.cpu()[0]) == 0
+
+
 def test_noise_changes_decisions_and_zero_noise_does_not():
     """Noise of the size of the logit gaps moves some choices; a zero draw moves none, and
     then the layer is the plain one bit for bit."""
