@@ -88,6 +88,10 @@ NOISY_CASES = {
     "swiglu_e24_k3_cap": spec("fine_grained_zipf_bf16", T=611, D=128, DH=192, E=24, top_k=3,
                               capacity_factor=1.5),
     "relu_e32_top1_cap": spec("switch_top1_cap_bf16", T=517, D=192, DH=128, E=32),
+    # edges of the exact noisy route: one token, k = E (every expert chosen), the smallest D
+    "swiglu_e8_k8_one_token": spec("mixtral_swiglu_bf16", T=1, D=64, DH=64, E=8, top_k=8),
+    "relu_e32_k32": spec("switch_top1_cap_bf16", T=17, D=64, DH=64, E=32, top_k=32,
+                         capacity_factor=0.0),
 }
 
 
