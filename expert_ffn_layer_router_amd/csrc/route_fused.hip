@@ -51,6 +51,9 @@ constexpr int kFT = 256;  // threads of a routing block: 4 waves, two blocks a C
 constexpr int kFW = kFT / kWave;
 constexpr int kPrepRows = 64;                    // router rows per prep block (and per bound block)
 constexpr int kGroup = kDispatchTokensPerBlock;  // tokens per dispatch group
+// Threads of a placement block: all of them add up the routing slots, the first kGroup (one
+// per token of the group) then place the group's slots.
+constexpr int kPlaceThreads = 1024;
 constexpr double kPScale = 1099511627776.0;      // 2^40, the probability sums' fixed point
 constexpr int kCountShift = 55;                  // the counts' place in a group slot
 constexpr int kMaxTT = 256;
@@ -1026,7 +1029,9 @@ struct PlaceArgs {
   float* importance;                // with islot: the importance loss
 };
 
-// One block per group of 256 tokens, one token per thread.
+// One block per group of 256 tokens, one token per thread of the first 256; the block has
+// kPlaceThreads threads, so that the slot sums of step 1 take one round of loads per thread
+// where there are many slots (512 routing blocks x 64 experts at T = 8192 or 16384).
 //  1. From the slots (each holds a count and a probability sum of part of a group, or of a
 //     whole group): each expert's total count (all groups) and rank base (the groups
 //     before this one), its kept rows min(count, capacity) and the row offsets; block 0 also
@@ -1040,27 +1045,29 @@ struct PlaceArgs {
 //     offsets[e] + rank, perm[row] = slot, slot_row[slot] = row or -1.
 // IMP: block 0 also adds the gate sums and forms the importance loss (a.islot non-null).
 template <bool IMP>
-__global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
-  constexpr int kW = kGroup / kWave;
+__global__ __launch_bounds__(kPlaceThreads) void place_fused_kernel(PlaceArgs a) {
+  constexpr int kW = kGroup / kWave;          // the token waves
+  constexpr int kPW = kPlaceThreads / kWave;  // all waves
+  static_assert(kMaxExperts <= kGroup, "one token thread per expert in the scans");
   __shared__ unsigned long long s_mask[kW][kMaxExperts];
   __shared__ int s_base[kW][kMaxExperts];
-  __shared__ int s_tot[kGroup], s_gb[kGroup];
-  __shared__ unsigned long long s_p[kGroup];
-  __shared__ unsigned long long s_i[IMP ? kGroup : 1];  // the gate sums (block 0, IMP)
+  __shared__ int s_tot[kPlaceThreads], s_gb[kPlaceThreads];
+  __shared__ unsigned long long s_p[kPlaceThreads];
+  __shared__ unsigned long long s_i[IMP ? kPlaceThreads : 1];  // the gate sums (block 0, IMP)
   __shared__ int s_off[kMaxExperts + 1];
-  __shared__ double s_term[kW];
-  __shared__ int s_wtot[kW];
+  __shared__ double s_term[kPW];
+  __shared__ int s_wtot[kPW];
   const int tid = threadIdx.x, wv = wave_id(), lane = lane_id();
   const int E = a.E, k = a.k;
   const int g = blockIdx.x;
   if (g == 0 && a.zero)
-    for (int i = tid; i < a.nzero; i += kGroup) a.zero[i] = 0;
-  for (int i = tid; i < kW * kMaxExperts; i += kGroup) (&s_mask[0][0])[i] = 0ull;
+    for (int i = tid; i < a.nzero; i += kPlaceThreads) a.zero[i] = 0;
+  for (int i = tid; i < kW * kMaxExperts; i += kPlaceThreads) (&s_mask[0][0])[i] = 0ull;
   // this thread's token's choices, loaded now so that their latency overlaps the slots' (up to
   // 8 of them in registers; more are read again where they are used)
   constexpr int kPre = 8;
   const int64_t t = (int64_t)g * kGroup + tid;
-  const bool valid = t < a.T;
+  const bool valid = tid < kGroup && t < a.T;
   int pre[kPre];
 #pragma unroll
   for (int j = 0; j < kPre; ++j) pre[j] = (valid && j < k) ? a.idx[t * k + j] : 0;
@@ -1071,15 +1078,16 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
       if (q == j) e = pre[q];
     return j < kPre ? e : a.idx[t * k + j];
   };
-  // 1. Q threads per expert, each over the groups q, q + Q, ...
-  const int Q = max(1, kGroup / E);
+  // 1. Q threads per expert, each over the slots q, q + Q, ...: as many as one round of kC loads
+  // each needs, at least kGroup / E and at most kPlaceThreads / E
+  constexpr int kC = 16;  // loads in flight (more spill at 128 VGPRs, the bound of 16 waves)
+  const int Q = max(1, min(kPlaceThreads / E, max(kGroup / E, (int)((a.nS + kC - 1) / kC))));
   const bool imp = IMP && g == 0;  // block 0 also adds the gate sums (importance loss)
   {
     int tot = 0, gb = 0;
     unsigned long long ps = 0, is = 0;
     if (tid < Q * E) {
       const int e = tid % E, q = tid / E;
-      constexpr int kC = 32;  // loads in flight
       const int64_t gend = (int64_t)g * a.spg;  // slots of the groups before this one
       for (int64_t g0 = q; g0 < a.nS; g0 += kC * Q) {
         unsigned long long v[kC];
@@ -1096,14 +1104,12 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
           if (gg < gend) gb += c;
           ps += v[u] & ((1ull << kCountShift) - 1ull);
         }
-        if (IMP && imp) {
-#pragma unroll
+        if (IMP && imp) {  // block 0 only; four loads in flight keep it within 128 VGPRs
+#pragma unroll 4
           for (int u = 0; u < kC; ++u) {
             const int64_t gg = g0 + (int64_t)u * Q;
-            v[u] = gg < a.nS ? a.islot[gg * E + e] : 0ull;
+            is += gg < a.nS ? a.islot[gg * E + e] : 0ull;
           }
-#pragma unroll
-          for (int u = 0; u < kC; ++u) is += v[u];
         }
       }
     }
@@ -1161,7 +1167,7 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
     __syncthreads();
     if (tid == 0) {
       double sum = 0.0;
-      for (int q = 0; q < kW; ++q) sum += s_term[q];
+      for (int q = 0; q < kW; ++q) sum += s_term[q];  // waves past kW hold no expert
       *a.aux = (float)((double)E * sum);
       if (a.uncertified) *a.uncertified = a.nflag ? *a.nflag : 0;
     }
@@ -1181,14 +1187,14 @@ __global__ __launch_bounds__(kGroup) void place_fused_kernel(PlaceArgs a) {
       if (lane == 0) *a.importance = m > 0.0 ? (float)((v / (double)E) / (m * m)) : 0.f;
     }
     if (a.offsets)
-      for (int e = tid; e <= E; e += kGroup) a.offsets[e] = s_off[e];
+      for (int e = tid; e <= E; e += kPlaceThreads) a.offsets[e] = s_off[e];
   }
   if (!a.perm) return;
   // 2. ranks within the group and placement
   if (valid)
     for (int j = 0; j < k; ++j) atomicOr(&s_mask[wv][choice(j)], 1ull << lane);
   __syncthreads();
-  for (int e = tid; e < E; e += kGroup) {
+  for (int e = tid; e < E; e += kPlaceThreads) {
     int run = s_gb[e];
 #pragma unroll
     for (int q = 0; q < kW; ++q) {
@@ -1491,9 +1497,9 @@ hipError_t launch_place_fused(const Problem& p, const int32_t* idx, const void* 
   a.nzero = nzero;
   const unsigned grid = perm ? (unsigned)L.nG : 1u;
   if (a.islot)
-    hipLaunchKernelGGL(place_fused_kernel<true>, dim3(grid), dim3(kGroup), 0, s, a);
+    hipLaunchKernelGGL(place_fused_kernel<true>, dim3(grid), dim3(kPlaceThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(place_fused_kernel<false>, dim3(grid), dim3(kGroup), 0, s, a);
+    hipLaunchKernelGGL(place_fused_kernel<false>, dim3(grid), dim3(kPlaceThreads), 0, s, a);
   return hipGetLastError();
 }
 
